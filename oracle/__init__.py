@@ -1,0 +1,188 @@
+"""fp64 CPU oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``pda_oracle.c`` (plain C,
+fp64, OpenMP over (sequence, head) rows) with ctypes and numpy.  It shares no
+code with the HIP path and does not import it.
+
+Inputs are numpy arrays that hold the *stored bytes* the GPU would read:
+
+  dtype name  numpy array dtype   meaning
+  ----------  -----------------   -----------------------------------
+  "f32"       float32             IEEE binary32
+  "f16"       float16             IEEE binary16
+  "bf16"      uint16              bfloat16 bit patterns
+  "e4m3"      uint8               OCP FP8 E4M3FN bit patterns
+  "f64"       float64             (oracle-only, for pins)
+
+What is computed is the plain definition (see the header of pda_oracle.c):
+softmax(scale * q K^T) V over the tokens gathered through the block table,
+with the natural-log LSE of the scaled logits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_DT = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3, "f64": 4}
+_NP = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "e4m3": np.uint8,
+       "f64": np.float64}
+_ERR = {1: "invalid argument", 2: "block-table entry out of range", 3: "out of memory"}
+
+_lib = None
+_lib_path = None   # None: the library built from oracle/pda_oracle.c
+
+
+def use_library(path):
+    """Point the wrappers at another build of the oracle (the mutation tests
+    load copies with planted mistakes); ``None`` restores the default."""
+    global _lib, _lib_path
+    _lib, _lib_path = None, path
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _lib_path
+    if path is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    I64 = ctypes.c_int64
+    D = ctypes.c_double
+    lib.orc_decode.argtypes = [I, P, I64, I64, P]
+    lib.orc_paged_attention.argtypes = [P, I, P, P, I, P, I, P, P, P, I, I, I, I, I, I, I64,
+                                        D, D, D, P, P, P, I]
+    lib.orc_mla_attention.argtypes = [P, I, P, I, P, I, P, P, P, I, I, I, I, I, I64, D, P, P,
+                                      P, I]
+    lib.orc_combine.argtypes = [P, P, I64, I, I, P, P]
+    lib.orc_max_threads.argtypes = []
+    for f in (lib.orc_decode, lib.orc_paged_attention, lib.orc_mla_attention, lib.orc_combine,
+              lib.orc_max_threads):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError("oracle: " + _ERR.get(rc, "error %d" % rc))
+
+
+def _as(a, name):
+    a = np.ascontiguousarray(a)
+    want = _NP[name]
+    if a.dtype != want:
+        raise TypeError("expected %s storage (%s), got %s" % (name, want, a.dtype))
+    return a
+
+
+def max_threads() -> int:
+    return _load().orc_max_threads()
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Decode stored elements to float64 with the oracle's own decoders."""
+    a = _as(bits, dtype).reshape(-1)
+    out = np.empty(a.size, dtype=np.float64)
+    _check(_load().orc_decode(_DT[dtype], _ptr(a), 0, a.size, _ptr(out)))
+    return out.reshape(np.shape(bits))
+
+
+def _i32(a, n=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    if n is not None and a.size != n:
+        raise ValueError("expected %d entries" % n)
+    return a
+
+
+def paged_attention(q, k_cache, v_cache, block_tables, context_lens, *, scale,
+                    q_dtype, kv_dtype, k_scale=1.0, v_scale=1.0, tok_begin=None,
+                    tok_end=None, rows=None, num_threads=0):
+    """GQA/MQA/MHA paged decode attention in fp64.
+
+    q [B, Hq, dk]; k_cache [num_pages, P, Hkv, dk]; v_cache [num_pages, P, Hkv, dv];
+    block_tables [B, max_pages] int32; context_lens [B] int32.
+    tok_begin/tok_end: optional [B] token interval per sequence (a split).
+    rows: optional bool [B, Hq] selecting the rows to compute (others are NaN).
+    Returns (out [B, Hq, dv] float64, lse [B, Hq] float64).
+    """
+    q = _as(q, q_dtype)
+    k_cache = _as(k_cache, kv_dtype)
+    v_cache = _as(v_cache, kv_dtype)
+    B, Hq, dk = q.shape
+    num_pages, P, Hkv, dk2 = k_cache.shape
+    dv = v_cache.shape[3]
+    if dk2 != dk or v_cache.shape[:3] != k_cache.shape[:3]:
+        raise ValueError("cache shapes do not match q")
+    bt = _i32(block_tables)
+    if bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_pages]")
+    cl = _i32(context_lens, B)
+    tb, te = _i32(tok_begin, B), _i32(tok_end, B)
+    rm = None if rows is None else np.ascontiguousarray(rows, dtype=np.uint8).reshape(-1)
+    out = np.full((B, Hq, dv), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    rc = _load().orc_paged_attention(
+        _ptr(q), _DT[q_dtype], _ptr(k_cache), _ptr(v_cache), _DT[kv_dtype], _ptr(bt),
+        bt.shape[1], _ptr(cl), _ptr(tb), _ptr(te), B, Hq, Hkv, dk, dv, P, num_pages,
+        float(scale), float(k_scale), float(v_scale), _ptr(rm), _ptr(out), _ptr(lse),
+        int(num_threads))
+    _check(rc)
+    return out, lse
+
+
+def mla_attention(q, kv_cache, block_tables, context_lens, *, scale, d_latent, q_dtype,
+                  kv_dtype, tok_begin=None, tok_end=None, rows=None, num_threads=0):
+    """MLA paged decode attention in fp64.
+
+    q [B, Hq, d_latent + d_rope]; kv_cache [num_pages, P, d_latent + d_rope].
+    K is the whole record, V its first d_latent values.
+    Returns (out [B, Hq, d_latent] float64, lse [B, Hq] float64).
+    """
+    q = _as(q, q_dtype)
+    kv_cache = _as(kv_cache, kv_dtype)
+    B, Hq, rec = q.shape
+    num_pages, P, rec2 = kv_cache.shape
+    if rec2 != rec or not (0 < d_latent <= rec):
+        raise ValueError("record widths do not match")
+    bt = _i32(block_tables)
+    cl = _i32(context_lens, B)
+    tb, te = _i32(tok_begin, B), _i32(tok_end, B)
+    rm = None if rows is None else np.ascontiguousarray(rows, dtype=np.uint8).reshape(-1)
+    out = np.full((B, Hq, d_latent), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    rc = _load().orc_mla_attention(
+        _ptr(q), _DT[q_dtype], _ptr(kv_cache), _DT[kv_dtype], _ptr(bt), bt.shape[1],
+        _ptr(cl), _ptr(tb), _ptr(te), B, Hq, d_latent, rec - d_latent, P, num_pages,
+        float(scale), _ptr(rm), _ptr(out), _ptr(lse), int(num_threads))
+    _check(rc)
+    return out, lse
+
+
+def combine(part_o, part_lse):
+    """LSE-weighted merge of split partials: part_o [..., S, dv], part_lse [..., S]."""
+    part_o = np.ascontiguousarray(part_o, dtype=np.float64)
+    part_lse = np.ascontiguousarray(part_lse, dtype=np.float64)
+    *lead, S, dv = part_o.shape
+    if tuple(part_lse.shape) != tuple(lead) + (S,):
+        raise ValueError("part_lse shape does not match part_o")
+    R = int(np.prod(lead)) if lead else 1
+    out = np.empty(tuple(lead) + (dv,))
+    lse = np.empty(tuple(lead))
+    _check(_load().orc_combine(_ptr(part_o), _ptr(part_lse), R, S, dv, _ptr(out), _ptr(lse)))
+    return out, lse

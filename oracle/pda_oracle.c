@@ -1,0 +1,373 @@
+/*
+ * pda_oracle.c -- fp64 CPU oracle for single-token decode attention over a
+ * paged KV cache.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and
+ * the benchmark's CPU-baseline leg call it; the product path never does.
+ * It shares no code, header or constant with the HIP path.
+ *
+ * What it computes is the plain definition, written out with no blocking,
+ * fusion or reordering (each step cites the page it follows):
+ *
+ *   for every sequence b and query head h:
+ *     kvh  = floor(h / G), G = Hq / Hkv           (contiguous grouping:
+ *            "From MHA to MLA", sec. 2, the GQA kernel's kv_head line, and
+ *            the drill page, sec. 8, first pitfall)
+ *     gather, for logical token j < n_b:
+ *            page = block_tables[b][floor(j / P)], slot = j mod P
+ *            K_j = dec(k_cache[page, slot, kvh, :]) * k_scale
+ *            V_j = dec(v_cache[page, slot, kvh, :]) * v_scale
+ *            (paged addressing: "From MHA to MLA", sec. 5; drill page, sec. 4)
+ *     s_j  = scale * sum_i q_i K_j,i
+ *     m    = max_j s_j ; Z = sum_j exp(s_j - m)
+ *     out  = sum_j exp(s_j - m) V_j / Z ;  lse = m + ln Z
+ *            (softmax and natural-log LSE of the scaled logits: "From MHA to
+ *            MLA", sec. 2 kernel epilogue; FlashMLA-ETAP "Usage", lse)
+ *
+ *   MLA ("From MHA to MLA", sec. 6; "Attention Kernel Variants", MLA section):
+ *     one cache record per token [c (d_latent) | k_R (d_rope)], no head axis.
+ *     K_j = the whole record, V_j = its first d_latent values (same bytes),
+ *     s_j = scale * (q[:d_latent] . c_j + q[d_latent:] . k_R_j).
+ *
+ *   Split-KV (Flash-Decoding, "From MHA to MLA", sec. 4): attention over a
+ *   token interval gives a normalized partial O_s and L_s; the combine is
+ *     L = ln sum_s exp(L_s),  O = sum_s exp(L_s - L) O_s,
+ *   evaluated with the maximum L_s subtracted first.  Empty intervals give
+ *   O_s = 0, L_s = -inf and weight 0.
+ *
+ * Element decoders are written from the format definitions (IEEE binary16,
+ * bfloat16 = the top half of binary32, OCP FP8 E4M3FN: bias 7, no infinities,
+ * S.1111.111 is NaN).
+ *
+ * Every table entry the oracle dereferences is bounds-checked against the
+ * pool: an out-of-range entry returns ORC_ERR_TABLE instead of reading.
+ *
+ * Parity pins live in tests/test_oracle_*.py (brute force, library SDPA,
+ * closed forms, invariants, the pages' printed numbers).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_F64 = 4 };
+enum { ORC_OK = 0, ORC_ERR_ARG = 1, ORC_ERR_TABLE = 2, ORC_ERR_NOMEM = 3 };
+
+/* ---------------------------------------------------------------- decoders */
+
+static double dec_f16(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int m = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-10 * 2^-14 */
+  } else if (e == 31) {
+    v = (m == 0) ? INFINITY : NAN;
+  } else {
+    v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+  }
+  return sign ? -v : v;
+}
+
+static double dec_bf16(uint16_t b) {
+  int sign = (b >> 15) & 1;
+  int e = (b >> 7) & 0xff;
+  int m = b & 0x7f;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -133); /* subnormal: m * 2^-7 * 2^-126 */
+  } else if (e == 255) {
+    v = (m == 0) ? INFINITY : NAN;
+  } else {
+    v = ldexp(1.0 + (double)m / 128.0, e - 127);
+  }
+  return sign ? -v : v;
+}
+
+static double dec_e4m3(uint8_t x) {
+  int sign = (x >> 7) & 1;
+  int e = (x >> 3) & 0xf;
+  int m = x & 0x7;
+  double v;
+  if (e == 15 && m == 7) {
+    v = NAN; /* the only NaN encodings of E4M3FN; there is no infinity */
+  } else if (e == 0) {
+    v = ldexp((double)m, -9); /* subnormal: m * 2^-3 * 2^-6 */
+  } else {
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  }
+  return sign ? -v : v;
+}
+
+static double dec_elem(int dtype, const void* base, int64_t i) {
+  switch (dtype) {
+    case ORC_F32: {
+      float f;
+      memcpy(&f, (const char*)base + 4 * i, 4);
+      return (double)f;
+    }
+    case ORC_F16: {
+      uint16_t h;
+      memcpy(&h, (const char*)base + 2 * i, 2);
+      return dec_f16(h);
+    }
+    case ORC_BF16: {
+      uint16_t b;
+      memcpy(&b, (const char*)base + 2 * i, 2);
+      return dec_bf16(b);
+    }
+    case ORC_E4M3:
+      return dec_e4m3(((const uint8_t*)base)[i]);
+    case ORC_F64: {
+      double d;
+      memcpy(&d, (const char*)base + 8 * i, 8);
+      return d;
+    }
+  }
+  return NAN;
+}
+
+/* Decode n elements of one dtype starting at element index i0 (exported so
+ * the tests can pin the decoders against library dtype casts). */
+int orc_decode(int dtype, const void* base, int64_t i0, int64_t n, double* out) {
+  if (dtype < ORC_F32 || dtype > ORC_F64 || !base || !out || n < 0) return ORC_ERR_ARG;
+  for (int64_t k = 0; k < n; ++k) out[k] = dec_elem(dtype, base, i0 + k);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------- one head, fp64 */
+
+/* Softmax attention of one query row over n contiguous gathered rows.
+ * K is [n][dk], V is [n][dv] (fp64).  Two passes: max, then sums. */
+static void attend_rows(const double* q, const double* K, const double* V, int64_t n,
+                        int dk, int dv, double scale, double* s, double* out,
+                        double* lse) {
+  for (int e = 0; e < dv; ++e) out[e] = 0.0;
+  if (n == 0) { /* defensive definition for an empty interval */
+    *lse = -INFINITY;
+    return;
+  }
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < dk; ++i) acc += q[i] * K[j * dk + i];
+    s[j] = scale * acc;
+    if (s[j] > m) m = s[j];
+  }
+  double z = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    double w = exp(s[j] - m);
+    z += w;
+    for (int e = 0; e < dv; ++e) out[e] += w * V[j * dv + e];
+  }
+  for (int e = 0; e < dv; ++e) out[e] /= z;
+  *lse = m + log(z);
+}
+
+/* Gather tokens [t0, t1) of sequence b for one cache head into contiguous
+ * fp64 rows.  rec_stride: elements between consecutive tokens in a page;
+ * page_stride: elements between pages; off: element offset of the head's
+ * row inside a token record; width: how many elements to take. */
+static int gather_rows(const void* cache, int dtype, const int32_t* table_row,
+                       int64_t num_pages, int P, int64_t page_stride,
+                       int64_t rec_stride, int64_t off, int width, double mult,
+                       int64_t t0, int64_t t1, double* dst) {
+  for (int64_t j = t0; j < t1; ++j) {
+    int32_t page = table_row[j / P];
+    if (page < 0 || (int64_t)page >= num_pages) return ORC_ERR_TABLE;
+    int64_t slot = j % P;
+    int64_t base = (int64_t)page * page_stride + slot * rec_stride + off;
+    for (int i = 0; i < width; ++i)
+      dst[(j - t0) * width + i] = dec_elem(dtype, cache, base + i) * mult;
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------- GQA / MHA */
+
+/* Paged decode attention, GQA family.
+ *   q            [B, Hq, dk] of q_dtype
+ *   k_cache      [num_pages, P, Hkv, dk] of kv_dtype
+ *   v_cache      [num_pages, P, Hkv, dv] of kv_dtype
+ *   block_tables [B, max_pages] int32, context_lens [B] int32
+ *   tok_begin/tok_end [B] int32 or NULL: restrict to tokens [begin, end)
+ *     of each sequence (a split interval); NULL means [0, n_b).
+ *   row_mask [B*Hq] or NULL: compute only rows with a nonzero mask.
+ *   out [B, Hq, dv] fp64, lse [B, Hq] fp64 (rows not computed are untouched).
+ * Returns ORC_OK, ORC_ERR_ARG or ORC_ERR_TABLE.  num_threads <= 0: default. */
+int orc_paged_attention(const void* q, int q_dtype, const void* k_cache,
+                        const void* v_cache, int kv_dtype,
+                        const int32_t* block_tables, int max_pages,
+                        const int32_t* context_lens, const int32_t* tok_begin,
+                        const int32_t* tok_end, int B, int Hq, int Hkv, int dk,
+                        int dv, int P, int64_t num_pages, double scale,
+                        double k_scale, double v_scale, const uint8_t* row_mask,
+                        double* out, double* lse, int num_threads) {
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !lse)
+    return ORC_ERR_ARG;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || dk <= 0 || dv <= 0 || P <= 0 ||
+      max_pages < 0 || num_pages < 0)
+    return ORC_ERR_ARG;
+  const int G = Hq / Hkv;
+  int status = ORC_OK;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+  (void)num_threads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
+    if (row_mask && !row_mask[bh]) continue;
+    int b = (int)(bh / Hq), h = (int)(bh % Hq);
+    int kvh = h / G;
+    int64_t n_b = context_lens[b];
+    int64_t t0 = tok_begin ? tok_begin[b] : 0;
+    int64_t t1 = tok_end ? tok_end[b] : n_b;
+    if (n_b < 0 || t0 < 0 || t1 > n_b || t1 > (int64_t)max_pages * P) {
+#pragma omp atomic write
+      status = ORC_ERR_ARG;
+      continue;
+    }
+    if (t1 < t0) t1 = t0;
+    int64_t n = t1 - t0;
+    double* qd = (double*)malloc(sizeof(double) * dk);
+    double* K = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * dk);
+    double* V = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * dv);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    if (!qd || !K || !V || !s) {
+#pragma omp atomic write
+      status = ORC_ERR_NOMEM;
+    } else {
+      for (int i = 0; i < dk; ++i) qd[i] = dec_elem(q_dtype, q, bh * dk + i);
+      const int32_t* trow = block_tables + (int64_t)b * max_pages;
+      int rk = gather_rows(k_cache, kv_dtype, trow, num_pages, P, (int64_t)P * Hkv * dk,
+                           (int64_t)Hkv * dk, (int64_t)kvh * dk, dk, k_scale, t0, t1, K);
+      int rv = gather_rows(v_cache, kv_dtype, trow, num_pages, P, (int64_t)P * Hkv * dv,
+                           (int64_t)Hkv * dv, (int64_t)kvh * dv, dv, v_scale, t0, t1, V);
+      if (rk != ORC_OK || rv != ORC_OK) {
+#pragma omp atomic write
+        status = ORC_ERR_TABLE;
+      } else {
+        attend_rows(qd, K, V, n, dk, dv, scale, s, out + bh * dv, lse + bh);
+      }
+    }
+    free(qd);
+    free(K);
+    free(V);
+    free(s);
+  }
+  return status;
+}
+
+/* ------------------------------------------------------------------- MLA */
+
+/* Paged decode attention over an MLA latent cache (one record per token, no
+ * head axis).  q [B, Hq, d_latent + d_rope]; kv_cache [num_pages, P,
+ * d_latent + d_rope]; out [B, Hq, d_latent] fp64; lse [B, Hq] fp64.
+ * K_j is the whole record, V_j its first d_latent values. */
+int orc_mla_attention(const void* q, int q_dtype, const void* kv_cache, int kv_dtype,
+                      const int32_t* block_tables, int max_pages,
+                      const int32_t* context_lens, const int32_t* tok_begin,
+                      const int32_t* tok_end, int B, int Hq, int d_latent, int d_rope,
+                      int P, int64_t num_pages, double scale,
+                      const uint8_t* row_mask, double* out, double* lse,
+                      int num_threads) {
+  if (!q || !kv_cache || !block_tables || !context_lens || !out || !lse) return ORC_ERR_ARG;
+  if (B < 0 || Hq <= 0 || d_latent <= 0 || d_rope < 0 || P <= 0 || max_pages < 0 ||
+      num_pages < 0)
+    return ORC_ERR_ARG;
+  const int rec = d_latent + d_rope;
+  int status = ORC_OK;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+  (void)num_threads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
+    if (row_mask && !row_mask[bh]) continue;
+    int b = (int)(bh / Hq);
+    int64_t n_b = context_lens[b];
+    int64_t t0 = tok_begin ? tok_begin[b] : 0;
+    int64_t t1 = tok_end ? tok_end[b] : n_b;
+    if (n_b < 0 || t0 < 0 || t1 > n_b || t1 > (int64_t)max_pages * P) {
+#pragma omp atomic write
+      status = ORC_ERR_ARG;
+      continue;
+    }
+    if (t1 < t0) t1 = t0;
+    int64_t n = t1 - t0;
+    double* qd = (double*)malloc(sizeof(double) * rec);
+    double* K = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * rec);
+    double* V = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * d_latent);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    if (!qd || !K || !V || !s) {
+#pragma omp atomic write
+      status = ORC_ERR_NOMEM;
+    } else {
+      for (int i = 0; i < rec; ++i) qd[i] = dec_elem(q_dtype, q, bh * rec + i);
+      const int32_t* trow = block_tables + (int64_t)b * max_pages;
+      /* K: the whole record; V: the latent part of the same record. */
+      int rk = gather_rows(kv_cache, kv_dtype, trow, num_pages, P, (int64_t)P * rec, rec, 0,
+                           rec, 1.0, t0, t1, K);
+      int rv = gather_rows(kv_cache, kv_dtype, trow, num_pages, P, (int64_t)P * rec, rec, 0,
+                           d_latent, 1.0, t0, t1, V);
+      if (rk != ORC_OK || rv != ORC_OK) {
+#pragma omp atomic write
+        status = ORC_ERR_TABLE;
+      } else {
+        attend_rows(qd, K, V, n, rec, d_latent, scale, s, out + bh * d_latent, lse + bh);
+      }
+    }
+    free(qd);
+    free(K);
+    free(V);
+    free(s);
+  }
+  return status;
+}
+
+/* --------------------------------------------------------------- combine */
+
+/* LSE-weighted merge of S split partials ("From MHA to MLA", sec. 4).
+ *   part_o [R, S, dv] fp64, part_lse [R, S] fp64 -> out [R, dv], lse [R].
+ * A split with part_lse = -inf is empty and gets weight 0; if every split is
+ * empty the row is empty: out = 0, lse = -inf. */
+int orc_combine(const double* part_o, const double* part_lse, int64_t R, int S, int dv,
+                double* out, double* lse) {
+  if (!part_o || !part_lse || !out || !lse || R < 0 || S <= 0 || dv <= 0) return ORC_ERR_ARG;
+  for (int64_t r = 0; r < R; ++r) {
+    double mx = -INFINITY;
+    for (int s = 0; s < S; ++s)
+      if (part_lse[r * S + s] > mx) mx = part_lse[r * S + s];
+    for (int e = 0; e < dv; ++e) out[r * dv + e] = 0.0;
+    if (mx == -INFINITY) {
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double denom = 0.0;
+    for (int s = 0; s < S; ++s) {
+      double l = part_lse[r * S + s];
+      if (l == -INFINITY) continue;
+      double w = exp(l - mx);
+      denom += w;
+      for (int e = 0; e < dv; ++e) out[r * dv + e] += w * part_o[(r * S + s) * dv + e];
+    }
+    for (int e = 0; e < dv; ++e) out[r * dv + e] /= denom;
+    lse[r] = mx + log(denom);
+  }
+  return ORC_OK;
+}
+
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,61 @@
+"""The benchmark's byte counter against the numbers the pages print
+("Attention Kernel Variants" KV-cache table, worked example and demo output;
+the drill page's batch-64 step; "From MHA to MLA" sec. 7 ratio)."""
+import json
+import os
+
+import pytest
+
+from decode_attention_paged_02_amd import accounting as A
+from decode_attention_paged_02_amd import workloads as W
+
+
+@pytest.fixture(scope="module")
+def g(golden_dir):
+    return json.load(open(os.path.join(golden_dir, "kv_bytes_per_token.json")))
+
+
+def test_model_table(g):
+    for m in g["models"]:
+        kib = A.kv_bytes_per_token(m["layers"], m["kv_heads"], m["head_dim"],
+                                   m["dtype_bytes"]) / 1024
+        assert kib == m["kib_per_token"], m["name"]
+    for m in g["mla_models"]:
+        kib = A.mla_bytes_per_token(m["layers"], m["d_latent"], m["d_rope"],
+                                    m["dtype_bytes"]) / 1024
+        assert round(kib, 1) == m["kib_per_token"], m["name"]
+
+
+def test_worked_example_and_mha(g):
+    w = g["worked_example_bytes"]
+    assert A.kv_bytes_per_token(w["layers"], w["kv_heads"], w["head_dim"],
+                                w["dtype_bytes"]) == w["bytes"]
+    m = g["mha_same_shape_kib"]
+    assert A.kv_bytes_per_token(m["layers"], m["kv_heads"], m["head_dim"],
+                                m["dtype_bytes"]) / 1024 == m["kib_per_token"]
+    r = g["mla_vs_mha_elements"]
+    assert round(r["mha_elements"] / r["mla_elements"], 2) == r["ratio_2dp"]
+    assert round(r["mla_elements"] / (2 * 128), 2) == r["equivalent_gqa_groups_2dp"]
+    assert g["mla_vs_mqa_ratio"]["mla_elements"] / g["mla_vs_mqa_ratio"]["mqa_elements"] == 2.25
+
+
+def test_drill_step_bytes(g):
+    d = g["drill_step_bytes"]
+    got = A.step_kv_bytes([d["ctx"]] * d["batch"], num_kv_heads=d["kv_heads"],
+                          head_dim=d["head_dim"], head_dim_v=d["head_dim"], kv_dtype="f16")
+    assert got == d["bytes"] and round(got / 1e6) == 268
+
+
+def test_named_workload_bytes():
+    lens64 = [1024] * 64
+    assert A.step_kv_bytes(lens64, num_kv_heads=8, head_dim=128, head_dim_v=128,
+                           kv_dtype="f16") == 268435456
+    assert A.step_kv_bytes([32768], num_kv_heads=8, head_dim=128, head_dim_v=128,
+                           kv_dtype="f16") == 134217728
+    assert A.step_kv_bytes([65536] * 16, num_kv_heads=1, head_dim=576, head_dim_v=512,
+                           kv_dtype="bf16", mla=True) == 1207959552
+    assert A.step_flops([65536] * 16, num_q_heads=16, head_dim=576,
+                        head_dim_v=512) == 16 * 16 * 65536 * 2 * (576 + 512)
+    lens = W.ragged_fp8_lens()
+    assert lens[0] == 1 and lens[1] == 16384 and lens[2] == 17
+    assert lens.min() >= 1 and lens.max() <= 16384

@@ -1,0 +1,70 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of oracle/pda_oracle.c (on the CPU),
+builds it, and runs the pin suites against it in a child pytest; the suites
+must fail.  The unmodified oracle passes the same suites (the other test files).
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "pda_oracle.c")
+PIN_FILES = ["tests/test_oracle_pins.py", "tests/test_oracle_mla.py"]
+
+MUTATIONS = [
+    ("interleaved head grouping", "int kvh = h / G;", "int kvh = h % Hkv;"),
+    ("softmax scale dropped", "s[j] = scale * acc;", "s[j] = acc;"),
+    ("log base 2 in the LSE", "*lse = m + log(z);", "*lse = m + log2(z);"),
+    ("output not normalized", "out[e] /= z;", "out[e] /= 1.0;"),
+    ("page slot off by one", "int64_t slot = j % P;", "int64_t slot = (j + 1) % P;"),
+    ("wrong logical page", "int32_t page = table_row[j / P];",
+     "int32_t page = table_row[j / (P + 1)];"),
+    ("dequant scale dropped", "dec_elem(dtype, cache, base + i) * mult;",
+     "dec_elem(dtype, cache, base + i);"),
+    ("fp8 exponent bias", "ldexp(1.0 + (double)m / 8.0, e - 7)",
+     "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    ("fp16 mantissa width", "ldexp(1.0 + (double)m / 1024.0, e - 15)",
+     "ldexp(1.0 + (double)m / 512.0, e - 15)"),
+    ("bf16 exponent bias", "ldexp(1.0 + (double)m / 128.0, e - 127)",
+     "ldexp(1.0 + (double)m / 128.0, e - 126)"),
+    ("V read from the K cache", "int rv = gather_rows(v_cache,", "int rv = gather_rows(k_cache,"),
+    ("MLA value taken from the record's tail",
+     "P, (int64_t)P * rec, rec, 0,\n                           d_latent, 1.0,",
+     "P, (int64_t)P * rec, rec, d_rope,\n                           d_latent, 1.0,"),
+    ("MLA rope block dropped from the score",
+     "attend_rows(qd, K, V, n, rec, d_latent,", "attend_rows(qd, K, V, n, d_latent, d_latent,"),
+    ("combine: plain average of splits", "double w = exp(l - mx);", "double w = 1.0;"),
+    ("combine: LSE missing the denominator", "lse[r] = mx + log(denom);", "lse[r] = mx;"),
+    ("running max never updated", "if (s[j] > m) m = s[j];", "if (s[j] > m) m = s[0];"),
+]
+
+
+def _run_mutant(args):
+    desc, old, new, tmp = args
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not unique: %r" % old
+    path = os.path.join(tmp, "m%d.c" % abs(hash(desc)))
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = path[:-2] + ".so"
+    sys.path.insert(0, ROOT)
+    from oracle import build as ob
+    ob.build(src=path, lib=lib)
+    env = dict(os.environ, PDA_ORACLE_MUTANT=lib, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *PIN_FILES], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    return desc, r.returncode
+
+
+def test_pins_catch_planted_mistakes():
+    with tempfile.TemporaryDirectory() as tmp:
+        with cf.ThreadPoolExecutor(max_workers=4) as ex:
+            results = list(ex.map(_run_mutant, [(d, o, n, tmp) for d, o, n in MUTATIONS]))
+    survived = [d for d, rc in results if rc == 0]
+    assert not survived, "pins did not catch: %s" % survived
