@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark: effective KV-cache read GB/s (fraction of MI355X HBM peak) and
+us per decode step of paged decode attention on one GPU.
+
+Default workload: GQA decode at batch, B=64, Hq=32, Hkv=8, d=128, every context
+1024 tokens, page 16, fp16 cache and queries ~ N(0, 1), block tables a random
+permutation of a 4096-page pool, no split-KV.
+
+A step is one call of the C-ABI entry point (planner + attention kernel +
+combine when splitting) over resident device inputs.  Cold-HBM timing: the
+KV pool is replicated into several device copies (>= 1 GiB together, more
+than the 256 MB last-level cache) and the copies rotate per step.
+
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: this library runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "effective KV-cache read GB/s (% of MI355X HBM peak) + µs/decode step"
+
+
+def _log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def make_case(name):
+    from decode_attention_paged_02_amd import workloads as W
+    if name == "gqa_b64":
+        return W.gqa_batch64()
+    if name == "gqa_b1_split":
+        return W.gqa_long(1)
+    if name == "gqa_b4_split":
+        return W.gqa_long(4)
+    if name == "mla_b16":
+        return W.mla_b16()
+    if name == "ragged_fp8":
+        return W.ragged_fp8()
+    raise SystemExit("unknown workload %s" % name)
+
+
+CALL_KW = {"ragged_fp8": dict(num_splits=4, split_min_tokens=4096)}
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_paged_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".cpp", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, launches_per_step: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def run_gpu(case, workload, steps, warmup, pools):
+    import torch
+    from decode_attention_paged_02_amd import accounting as A
+    from decode_attention_paged_02_amd import pda
+
+    dev = pda.to_device(case)
+    kw = dict(CALL_KW.get(workload, {}))
+    nbytes = A.case_kv_bytes(case)
+    pool_bytes = dev.k_cache.numel() * dev.k_cache.element_size() * (1 if case.mla else 2)
+    n_pools = max(pools, math.ceil((1 << 30) / max(pool_bytes, 1))) if pools > 0 else 1
+    caches = [(dev.k_cache, dev.v_cache)]
+    for _ in range(n_pools - 1):
+        caches.append((dev.k_cache.clone(), None if dev.v_cache is None else dev.v_cache.clone()))
+    B, Hq = case.batch, case.num_q_heads
+    out = torch.empty((B, Hq, case.head_dim_v), dtype=dev.q.dtype, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    if case.mla:
+        shape = pda.mla_shape(dev.q, dev.k_cache, dev.block_tables, head_dim_v=case.d_latent,
+                              split_min_tokens=kw.get("split_min_tokens", 0))
+    else:
+        shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                              k_scale=case.k_scale, v_scale=case.v_scale,
+                              split_min_tokens=kw.get("split_min_tokens", 0))
+    nsplit = kw.get("num_splits", 0)
+    plan = pda.plan(shape, mla=case.mla, num_splits=nsplit)
+    ws = pda.workspace_for(shape, mla=case.mla, num_splits=nsplit, device="cuda")
+
+    step = pda.PreparedCall(mla=case.mla, q=dev.q, caches=caches,
+                            block_tables=dev.block_tables, context_lens=dev.context_lens,
+                            scale=case.scale, out=out, lse=lse, shape=shape,
+                            num_splits=nsplit, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # whole-job time over exactly `steps` back-to-back steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    # per-launch device time: events around every call on the same stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) * 1000.0 for a, b in evs]   # us
+    return dict(total_ms=total_ms, kernel_us_mean=statistics.mean(per),
+                kernel_us_median=statistics.median(per), kernel_us_min=min(per),
+                kv_bytes=nbytes, n_pools=len(caches), max_splits=plan.max_splits,
+                pages_per_split=plan.pages_per_split, workgroups=plan.workgroups,
+                launches=1 if plan.max_splits == 1 else 2)
+
+
+def cpu_baseline(case, budget_s=20.0):
+    """The fp64 oracle on the host cores over a bounded sample of the workload:
+    whole sequences are taken in order until about budget_s of work."""
+    import numpy as np
+    import oracle
+    from decode_attention_paged_02_amd import accounting as A
+    threads = oracle.max_threads()
+    rows = np.zeros((case.batch, case.num_q_heads), dtype=bool)
+    # time one sequence to size the sample
+    rows[0] = True
+    t = time.perf_counter()
+    _oracle_call(case, rows)
+    one = max(time.perf_counter() - t, 1e-4)
+    nseq = int(min(case.batch, max(1, budget_s / one)))
+    rows[:nseq] = True
+    t = time.perf_counter()
+    _oracle_call(case, rows)
+    dt = time.perf_counter() - t
+    nbytes = A.step_kv_bytes(case.context_lens[:nseq], num_kv_heads=case.num_kv_heads,
+                             head_dim=case.head_dim, head_dim_v=case.head_dim_v,
+                             kv_dtype=case.kv_dtype, mla=case.mla)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d sequences (all heads) of the timed workload, fp64 oracle, "
+                      "%.2f s wall" % (nseq, case.batch, dt),
+            "us_per_step_equiv": round(dt * 1e6 * case.batch / nseq, 1)}
+
+
+def _oracle_call(case, rows):
+    import oracle
+    if case.mla:
+        return oracle.mla_attention(case.q, case.k_cache, case.block_tables, case.context_lens,
+                                    scale=case.scale, d_latent=case.d_latent,
+                                    q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, rows=rows)
+    return oracle.paged_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                  case.context_lens, scale=case.scale, q_dtype=case.q_dtype,
+                                  kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+                                  v_scale=case.v_scale, rows=rows)
+
+
+def summarize(r, steps):
+    us_step = r["total_ms"] * 1000.0 / steps
+    gbs = r["kv_bytes"] / (us_step * 1e-6) / 1e9
+    kgbs = r["kv_bytes"] / (r["kernel_us_mean"] * 1e-6) / 1e9
+    return us_step, gbs, kgbs
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa_b64",
+                    choices=["gqa_b64", "gqa_b1_split", "gqa_b4_split", "mla_b16", "ragged_fp8"])
+    ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
+    ap.add_argument("--others", default="gqa_b1_split,gqa_b4_split",
+                    help="extra workloads measured into 'other_workloads' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not supported "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    from decode_attention_paged_02_amd import pda
+    pda.load()
+
+    _log("workload", args.workload)
+    case = make_case(args.workload)
+    r = run_gpu(case, args.workload, args.steps, args.warmup, args.pools)
+    us_step, gbs, kgbs = summarize(r, args.steps)
+    traffic = measured_traffic(args.workload, r["launches"])
+    roof = {"bound": "hbm", "achieved": round(kgbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "gqa_split_kernel" if not case.mla else "mla kernel",
+            "kernel_us_mean": round(r["kernel_us_mean"], 3),
+            "kernel_us_median": round(r["kernel_us_median"], 3),
+            "algorithmic_bytes_per_launch": r["kv_bytes"]}
+    others = {}
+    for w in [x for x in args.others.split(",") if x and x != args.workload]:
+        _log("other workload", w)
+        c2 = make_case(w)
+        st = max(20, args.steps // 4)
+        r2 = run_gpu(c2, w, st, 5, args.pools)
+        u2, g2, k2 = summarize(r2, st)
+        others[w] = {"us_per_step": round(u2, 2), "GB/s": round(g2, 1),
+                     "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4),
+                     "kernel_us_mean": round(r2["kernel_us_mean"], 2),
+                     "max_splits": r2["max_splits"], "kv_bytes": r2["kv_bytes"]}
+        del c2
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("cpu baseline (oracle)")
+        cpu = cpu_baseline(case, args.cpu_budget)
+    dt = {"f16": "f16", "bf16": "bf16", "f32": "f32"}[case.q_dtype]
+    if case.kv_dtype == "e4m3":
+        dt = "e4m3 cache, " + dt
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us_step / 1000, 5),
+        "us_per_step": round(us_step, 3), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": case.name, "batch": case.batch,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "page_size": case.page_size,
+                   "context_lens": "uniform %d" % int(case.context_lens[0])
+                   if len(set(case.context_lens.tolist())) == 1 else "ragged",
+                   "max_splits": r["max_splits"], "kv_bytes_per_step": r["kv_bytes"],
+                   "rotating_pools": r["n_pools"]},
+        "roofline": roof, "cpu_baseline": cpu, "other_workloads": others,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

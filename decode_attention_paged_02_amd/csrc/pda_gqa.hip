@@ -1,0 +1,616 @@
+// pda_gqa.hip -- paged decode attention for the GQA family (MHA / GQA / MQA)
+// on gfx950, plus the split-KV combine kernel.
+//
+// What is computed ("From MHA to MLA" sec. 3-5; the drill page sec. 3-5):
+// one workgroup owns a tile of GT query heads of one KV group of one sequence
+// (and one split of its pages), so every K/V row it loads from HBM serves all
+// GT heads; scores go through an online softmax; the result is either the
+// final output (one split) or a normalized partial plus its LSE (several
+// splits, merged by combine_kernel, "From MHA to MLA" sec. 4).
+//
+// Layout of the work inside a workgroup (4 waves of 64 lanes):
+//  - a "tile" is 16 consecutive tokens of one page (pages are multiples of
+//    16 tokens); wave w walks tiles w, w+4, w+8, ... of the workgroup's range
+//    with its own online-softmax state, and the four states are merged
+//    through LDS at the end (the same LSE algebra as the split combine);
+//  - a token row of one KV head (d elements) is spread over LPR consecutive
+//    lanes, each holding EPL elements loaded with one 128-bit (64-bit for
+//    fp8) buffer load; one wave load covers RPL = 64 / LPR rows, a tile
+//    NLD = 16 / RPL loads for K and as many for V;
+//  - the per-lane partial dot products (NLD rows x GT heads) are combined
+//    across the LPR lanes of a row with a reduce-scatter of DPP lane swaps,
+//    leaving each lane with the full scores of VPL (row, head) pairs;
+//  - the softmax probabilities are handed back to the lanes that hold the V
+//    rows through a 1-2 KiB per-wave LDS slot, and the PV product
+//    accumulates into GT x EPL fp32 registers per lane.
+// Scores are kept in the log2 domain (q.k * scale * log2 e) so that every
+// exponential is a native exp2.
+//
+// Addressing: each tile's K and V rows are read through a buffer resource
+// whose base is the tile's first row in its physical page and whose size
+// covers exactly the tile's valid rows, so rows past the context (stale
+// slots of a last partial page) read as zero and are never fetched, and the
+// per-lane byte offsets are loop invariant.  Block-table entries past the
+// sequence's pages are never read.
+#include "pda_internal.h"
+
+#include <type_traits>
+
+namespace pda {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+// dword 3 of a gfx9-family buffer resource: 32-bit data format, raw access.
+constexpr int kRsrcFlags = 0x00020000;
+
+struct F32 {};
+struct F16 {};
+struct BF16 {};
+struct E4M3 {};
+
+template <class T> struct Elem;
+template <> struct Elem<F32> { static constexpr int bytes = 4, epl = 4; using frag = u32x4; };
+template <> struct Elem<F16> { static constexpr int bytes = 2, epl = 8; using frag = u32x4; };
+template <> struct Elem<BF16> { static constexpr int bytes = 2, epl = 8; using frag = u32x4; };
+template <> struct Elem<E4M3> { static constexpr int bytes = 1, epl = 8; using frag = u32x2; };
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+// Reinterpret one 32-bit word as a pair of 16-bit floats.  The word is taken
+// by value: hipcc's __builtin_bit_cast applied directly to an ext_vector
+// element (v[j]) reads element 0 whatever j is, so every vector element goes
+// through a scalar first.
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+__device__ __forceinline__ u32x4 buf_load(__amdgpu_buffer_rsrc_t r, int off, u32x4*) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load(__amdgpu_buffer_rsrc_t r, int off, u32x2*) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------- decoding
+
+__device__ __forceinline__ void to_f32(F32, const u32x4& w, float (&o)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(w[i]);
+}
+__device__ __forceinline__ void to_f32(F16, const u32x4& w, float (&o)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = as_f16x2(w[i]);
+    o[2 * i] = (float)h.x;
+    o[2 * i + 1] = (float)h.y;
+  }
+}
+__device__ __forceinline__ void to_f32(BF16, const u32x4& w, float (&o)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void to_f32(E4M3, const u32x2& w, float (&o)[8]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+    o[4 * i] = lo.x;
+    o[4 * i + 1] = lo.y;
+    o[4 * i + 2] = hi.x;
+    o[4 * i + 3] = hi.y;
+  }
+}
+
+// q row fragment (EPL elements starting at element `e0` of a q row) as floats.
+template <class QT, int EPL>
+__device__ __forceinline__ void load_q_f32(const void* q, int64_t e0, float (&o)[EPL]) {
+  if constexpr (std::is_same<QT, F32>::value) {
+    const float* p = (const float*)q + e0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] = p[i];
+  } else if constexpr (std::is_same<QT, F16>::value) {
+    const _Float16* p = (const _Float16*)q + e0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] = (float)p[i];
+  } else {
+    const uint16_t* p = (const uint16_t*)q + e0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] = __uint_as_float((uint32_t)p[i] << 16);
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
+  if constexpr (std::is_same<T, F32>::value) {
+    ((float*)out)[i] = v;
+  } else if constexpr (std::is_same<T, F16>::value) {
+    ((_Float16*)out)[i] = (_Float16)v;
+  } else {
+    ((__bf16*)out)[i] = (__bf16)v;
+  }
+}
+
+// --------------------------------------------------------- lane exchanges
+
+// Value of x held by lane (this lane XOR 2^BIT).  Bits 0-3 stay inside a row
+// of 16 lanes and use DPP; bits 4-5 cross rows.
+template <int BIT>
+__device__ __forceinline__ float lane_xor(float x) {
+  if constexpr (BIT == 0) {
+    return __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
+  } else if constexpr (BIT == 1) {
+    return __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+  } else if constexpr (BIT == 2) {
+    // row_half_mirror gives lane ^ 7, then quad_perm 3,2,1,0 gives ^ 3: ^ 4
+    float y = __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, true);
+    return __builtin_amdgcn_update_dpp(0.f, y, 0x1B, 0xF, 0xF, true);
+  } else if constexpr (BIT == 3) {
+    return __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true);  // row_ror 8
+  } else {
+    return __shfl_xor(x, 1 << BIT, 64);
+  }
+}
+
+// Reduce-scatter of N partial sums across the lanes that differ in lane bits
+// BIT, BIT-1, ..., 0 (most significant first).  Each step halves the array:
+// lanes with the bit clear keep the first half, lanes with it set the second,
+// each adding its partner's copy of the half it keeps.  Once one value is
+// left, the remaining bits are summed as an all-reduce (duplicated values).
+template <int N, int BIT>
+__device__ __forceinline__ void reduce_scatter(float* v, int lane) {
+  if constexpr (BIT >= 0) {
+    if constexpr (N > 1) {
+      const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+      for (int k = 0; k < N / 2; ++k) {
+        float keep = hi ? v[k + N / 2] : v[k];
+        float send = hi ? v[k] : v[k + N / 2];
+        v[k] = keep + lane_xor<BIT>(send);
+      }
+      reduce_scatter<N / 2, BIT - 1>(v, lane);
+    } else {
+      v[0] += lane_xor<BIT>(v[0]);
+      reduce_scatter<1, BIT - 1>(v, lane);
+    }
+  }
+}
+
+// Max / sum over the lanes that differ in bits 2..5 (the lanes that share
+// the same (head) slot layout).  Bits 2 and 3 use row rotations by 4 and 8,
+// which visit all four lanes with equal bits 0-1 in a row of 16.
+__device__ __forceinline__ float wave_max_bits2to5(float x) {
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0x124, 0xF, 0xF, true));  // row_ror 4
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true));  // row_ror 8
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_bits2to5(float x) {
+  x += __builtin_amdgcn_update_dpp(0.f, x, 0x124, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true);
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// Sum over lane bits FROM..5.
+template <int FROM>
+__device__ __forceinline__ float wave_sum_from(float x) {
+  if constexpr (FROM <= 3) x += lane_xor<3>(x);
+  if constexpr (FROM <= 4) x += __shfl_xor(x, 16, 64);
+  if constexpr (FROM <= 5) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ void split_range(const SplitLayout& sp, int n, int P, int split,
+                                            int& nsplit, int& t0, int& t1) {
+  const int pages = (n + P - 1) / P;
+  if (sp.max_splits <= 1 || n <= sp.split_min_tokens) {
+    nsplit = 1;
+    t0 = 0;
+    t1 = n;
+  } else {
+    nsplit = (pages + sp.pages_per_split - 1) / sp.pages_per_split;
+    const int p0 = split * sp.pages_per_split;
+    t0 = p0 * P;
+    t1 = min((p0 + sp.pages_per_split) * P, n);
+  }
+}
+
+// ------------------------------------------------------------ main kernel
+
+template <class QT, class KT, int D, int GT>
+__global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a) {
+  using frag_t = typename Elem<KT>::frag;
+  constexpr int EPL = Elem<KT>::epl;
+  constexpr int ESZ = Elem<KT>::bytes;
+  constexpr int LPR = D / EPL;
+  constexpr int RPL = 64 / LPR;
+  constexpr int NLD = kTileTokens / RPL;
+  constexpr int NV = NLD * GT;
+  constexpr int LOG_LPR = ilog2(LPR);
+  constexpr int STEPS = ilog2(NV) < LOG_LPR ? ilog2(NV) : LOG_LPR;
+  constexpr int VPL = NV >> STEPS;
+  constexpr int DUPBITS = LOG_LPR - STEPS;
+  constexpr bool kPacked = std::is_same<QT, KT>::value &&
+                           (std::is_same<KT, F16>::value || std::is_same<KT, BF16>::value);
+  static_assert(LPR * RPL == 64 && NLD * RPL == kTileTokens, "row layout");
+  static_assert(VPL == (GT >= 4 ? GT / 4 : 1) && DUPBITS <= 2, "score layout");
+  static_assert(LPR >= 4 && LPR <= 32, "head_dim / dtype combination");
+
+  __shared__ f32x4 pbuf[kGqaWaves][RPL][NV / 4 > 0 ? NV / 4 : 1];
+  __shared__ float m_sh[kGqaWaves][GT], l_sh[kGqaWaves][GT];
+  __shared__ float acc_sh[kGqaWaves][GT][D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = lane / LPR;
+  const int c = lane % LPR;
+  const int seg = c >> DUPBITS;
+
+  const int wg = blockIdx.x;
+  const int tile = wg % a.head_tiles;
+  const int bk = wg / a.head_tiles;
+  const int kvh = bk % a.num_kv_heads;
+  const int b = bk / a.num_kv_heads;
+  const int split = blockIdx.y;
+
+  const int n = a.context_lens[b];
+  int nsplit, t0, t1;
+  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+  if (split >= nsplit) return;
+
+  const int g0 = tile * GT;                 // first group-local head of the tile
+  const int hbase = kvh * a.group + g0;     // first query head of the tile
+  const int gvalid = min(GT, a.group - g0); // heads of the tile inside the group
+
+  // q of the tile's heads, the EPL elements this lane multiplies
+  uint32_t qp[GT][EPL / 2];
+  float qf[GT][EPL];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    const int64_t e0 = ((int64_t)b * a.num_q_heads + hbase + g) * D + c * EPL;
+    if constexpr (kPacked) {
+      if (g < gvalid) {
+        u32x4 w = *(const u32x4*)((const char*)a.q + e0 * 2);
+#pragma unroll
+        for (int j = 0; j < EPL / 2; ++j) qp[g][j] = w[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < EPL / 2; ++j) qp[g][j] = 0u;
+      }
+    } else {
+      if (g < gvalid) {
+        load_q_f32<QT, EPL>(a.q, e0, qf[g]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) qf[g][j] = 0.f;
+      }
+    }
+  }
+
+  // loop-invariant byte offsets of this lane's rows inside a tile
+  const int tok_bytes = a.tok_stride * ESZ;
+  int voff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) voff[i] = (rg + RPL * i) * tok_bytes + (kvh * D + c * EPL) * ESZ;
+
+  float m_run[VPL], l_run[VPL];
+  float acc[GT][EPL];
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    m_run[k] = -INFINITY;
+    l_run[k] = 0.f;
+  }
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+
+  const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
+  const int P = a.page_size;
+
+  // Buffer resources for tile T (or empty ones when T is past the range).
+  auto tile_rsrc = [&](int T, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv,
+                       int& rows) {
+    const bool live = T < ntiles;
+    const int tok = t0 + T * kTileTokens;
+    const int lp = live ? tok / P : 0;
+    int phys = __builtin_amdgcn_readfirstlane(table[lp]);
+    phys = live ? phys : 0;
+    rows = live ? min(kTileTokens, t1 - tok) : 0;
+    const int64_t elem = (int64_t)phys * a.page_stride + (int64_t)(tok - lp * P) * a.tok_stride;
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.k_cache + elem * ESZ), 0,
+                                           rows * tok_bytes, kRsrcFlags);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.v_cache + elem * ESZ), 0,
+                                           rows * tok_bytes, kRsrcFlags);
+  };
+
+  auto compute_tile = [&](const frag_t (&kf)[NLD], const frag_t (&vf)[NLD], int rows) {
+    // partial scores of this lane: NLD rows x GT heads over its EPL elements
+    float sc[NV];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (kPacked) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          float s = 0.f;
+#pragma unroll
+          for (int j = 0; j < EPL / 2; ++j) {
+            if constexpr (std::is_same<KT, F16>::value) {
+              s = __builtin_amdgcn_fdot2(as_f16x2(qp[g][j]), as_f16x2(kf[i][j]), s, false);
+            } else {
+              s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qp[g][j]), as_bf16x2(kf[i][j]), s,
+                                                  false);
+            }
+          }
+          sc[i * GT + g] = s;
+        }
+      } else {
+        float kv[EPL];
+        to_f32(KT{}, kf[i], kv);
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) s = fmaf(qf[g][e], kv[e], s);
+          sc[i * GT + g] = s;
+        }
+      }
+    }
+    reduce_scatter<NV, LOG_LPR - 1>(sc, lane);
+
+    // this lane now holds the full scores of values seg*VPL + k
+    float p[VPL], alpha[VPL];
+    bool changed = false;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int v = seg * VPL + k;
+      const int row = rg + RPL * (v / GT);
+      const float s = row < rows ? sc[k] * a.qk_scale_log2 : -INFINITY;
+      const float m_new = fmaxf(m_run[k], wave_max_bits2to5(s));
+      alpha[k] = exp2f(m_run[k] - m_new);
+      p[k] = exp2f(s - m_new);
+      l_run[k] = l_run[k] * alpha[k] + p[k];
+      changed |= (m_new != m_run[k]);
+      m_run[k] = m_new;
+    }
+    // hand the probabilities to the lanes that hold the V rows
+    float* prow = (float*)&pbuf[wave][rg][0];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) prow[seg * VPL + k] = p[k];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // rescale the accumulators when any running max moved
+    if (__builtin_amdgcn_read_exec() & __ballot(changed)) {
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const int al_bits = __builtin_amdgcn_readlane(
+            __builtin_bit_cast(int, alpha[g % VPL]), (g / VPL) << DUPBITS);
+        const float al = __builtin_bit_cast(float, al_bits);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] *= al;
+      }
+    }
+    float pv[NV];
+#pragma unroll
+    for (int j = 0; j < NV / 4; ++j) {
+      f32x4 t = pbuf[wave][rg][j];
+      pv[4 * j] = t.x;
+      pv[4 * j + 1] = t.y;
+      pv[4 * j + 2] = t.z;
+      pv[4 * j + 3] = t.w;
+    }
+    if constexpr (NV < 4) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) pv[j] = prow[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      float vv[EPL];
+      to_f32(KT{}, vf[i], vv);
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pv[i * GT + g], vv[e], acc[g][e]);
+    }
+  };
+
+  // Two register buffers: the loads of tile T + 4 are in flight while tile T
+  // is computed.
+  frag_t kA[NLD], vA[NLD], kB[NLD], vB[NLD];
+  int rowsA, rowsB;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int T = wave;
+  tile_rsrc(T, rk, rv, rowsA);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    kA[i] = buf_load(rk, voff[i], (frag_t*)nullptr);
+    vA[i] = buf_load(rv, voff[i], (frag_t*)nullptr);
+  }
+  while (T < ntiles) {
+    tile_rsrc(T + kGqaWaves, rk, rv, rowsB);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      kB[i] = buf_load(rk, voff[i], (frag_t*)nullptr);
+      vB[i] = buf_load(rv, voff[i], (frag_t*)nullptr);
+    }
+    compute_tile(kA, vA, rowsA);
+    T += kGqaWaves;
+    if (T >= ntiles) break;
+    tile_rsrc(T + kGqaWaves, rk, rv, rowsA);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      kA[i] = buf_load(rk, voff[i], (frag_t*)nullptr);
+      vA[i] = buf_load(rv, voff[i], (frag_t*)nullptr);
+    }
+    compute_tile(kB, vB, rowsB);
+    T += kGqaWaves;
+  }
+
+  // ---- merge the four waves' states (the split-combine algebra, in LDS)
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) l_run[k] = wave_sum_bits2to5(l_run[k]);
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = wave_sum_from<LOG_LPR>(acc[g][e]);
+  if (rg == 0) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int v = seg * VPL + k;
+      if ((c & ((1 << DUPBITS) - 1)) == 0 && v < GT) {
+        m_sh[wave][v] = m_run[k];
+        l_sh[wave][v] = l_run[k];
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc_sh[wave][g][c * EPL + e] = acc[g][e];
+  }
+  __syncthreads();
+
+  const bool final_out = nsplit == 1;
+  for (int idx = threadIdx.x; idx < GT * D; idx += kGqaWaves * 64) {
+    const int g = idx / D, d = idx % D;
+    if (g >= gvalid) continue;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kGqaWaves; ++w) mx = fmaxf(mx, m_sh[w][g]);
+    float num = 0.f, den = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kGqaWaves; ++w) {
+        const float wt = exp2f(m_sh[w][g] - mx);
+        num += wt * acc_sh[w][g][d];
+        den += wt * l_sh[w][g];
+      }
+    }
+    const float o = den > 0.f ? num / den * a.v_scale : 0.f;
+    const float lse = den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+    const int h = hbase + g;
+    const int64_t row = (int64_t)b * a.num_q_heads + h;
+    if (final_out) {
+      store_out<QT>(a.out, row * D + d, o);
+      if (d == 0 && a.lse) a.lse[row] = lse;
+    } else {
+      a.part_o[(row * a.split.max_splits + split) * D + d] = o;
+      if (d == 0) a.part_lse[row * a.split.max_splits + split] = lse;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+
+// One workgroup per (sequence, query head) row whose sequence was split:
+// L = M + ln sum_s exp(L_s - M), O = sum_s exp(L_s - M) O_s / sum_s exp(L_s - M)
+// with M = max_s L_s ("From MHA to MLA" sec. 4).  Rows of unsplit sequences
+// were written by the attention kernel and are skipped.
+template <class OT>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int64_t row = blockIdx.x;
+  const int b = (int)(row / a.num_q_heads);
+  int nsplit, t0, t1;
+  split_range(a.split, a.context_lens[b], a.page_size, 0, nsplit, t0, t1);
+  if (nsplit <= 1) return;
+  const int S = a.split.max_splits;
+  const float* pl = a.part_lse + row * S;
+  float mx = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pl[s]);
+  for (int d = threadIdx.x; d < a.head_dim_v; d += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float l = pl[s];
+      if (l == -INFINITY) continue;
+      const float w = __expf(l - mx);
+      den += w;
+      num += w * a.part_o[(row * S + s) * a.head_dim_v + d];
+    }
+    store_out<OT>(a.out, row * a.head_dim_v + d, den > 0.f ? num / den : 0.f);
+    if (d == 0 && a.lse) a.lse[row] = den > 0.f ? mx + __logf(den) : -INFINITY;
+  }
+}
+
+template <class QT, class KT, int D>
+hipError_t launch_d(const GqaArgs& a, int tile_heads, int max_splits, hipStream_t s) {
+  dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.head_tiles), (unsigned)max_splits);
+  dim3 block(kGqaWaves * 64);
+  switch (tile_heads) {
+    case 1: hipLaunchKernelGGL((gqa_split_kernel<QT, KT, D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gqa_split_kernel<QT, KT, D, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gqa_split_kernel<QT, KT, D, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gqa_split_kernel<QT, KT, D, 8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class QT, class KT>
+hipError_t launch_qk(const GqaArgs& a, int head_dim, int tile_heads, int max_splits,
+                     hipStream_t s) {
+  switch (head_dim) {
+    case 64: return launch_d<QT, KT, 64>(a, tile_heads, max_splits, s);
+    case 128: return launch_d<QT, KT, 128>(a, tile_heads, max_splits, s);
+    case 256:
+      if constexpr (!std::is_same<KT, F32>::value)
+        return launch_d<QT, KT, 256>(a, tile_heads, max_splits, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool gqa_supported(int q_dtype, int kv_dtype, int head_dim, int head_dim_v) {
+  if (head_dim != head_dim_v) return false;
+  const bool pair_ok = (q_dtype == 0 && kv_dtype == 0) || (q_dtype == 1 && kv_dtype == 1) ||
+                       (q_dtype == 2 && kv_dtype == 2) ||
+                       ((q_dtype == 1 || q_dtype == 2) && kv_dtype == 3);
+  if (!pair_ok) return false;
+  if (head_dim == 64 || head_dim == 128) return true;
+  return head_dim == 256 && kv_dtype != 0;
+}
+
+int gqa_tile_heads(int group) {
+  if (group >= 8) return 8;
+  if (group > 2) return group > 4 ? 8 : 4;
+  return group;  // 1 or 2
+}
+
+hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
+                      int tile_heads, int max_splits, hipStream_t s) {
+  if (q_dtype == 0 && kv_dtype == 0) return launch_qk<F32, F32>(a, head_dim, tile_heads, max_splits, s);
+  if (q_dtype == 1 && kv_dtype == 1) return launch_qk<F16, F16>(a, head_dim, tile_heads, max_splits, s);
+  if (q_dtype == 2 && kv_dtype == 2) return launch_qk<BF16, BF16>(a, head_dim, tile_heads, max_splits, s);
+  if (q_dtype == 1 && kv_dtype == 3) return launch_qk<F16, E4M3>(a, head_dim, tile_heads, max_splits, s);
+  if (q_dtype == 2 && kv_dtype == 3) return launch_qk<BF16, E4M3>(a, head_dim, tile_heads, max_splits, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t s) {
+  dim3 grid((unsigned)(a.batch * a.num_q_heads));
+  dim3 block(a.head_dim_v >= 256 ? 256 : 128);
+  switch (out_dtype) {
+    case 0: hipLaunchKernelGGL(combine_kernel<F32>, grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL(combine_kernel<F16>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<BF16>, grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pda

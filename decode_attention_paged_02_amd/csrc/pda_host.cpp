@@ -1,0 +1,267 @@
+// pda_host.cpp -- the C ABI of libpda (include/pda.h): argument validation,
+// the split planner and kernel dispatch.  Every host-checkable argument is
+// validated before the first HIP call, so invalid calls never touch a device.
+#include "pda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "pda_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices] = {0};
+
+// Compute units of the current device (cached per device id); 0 on failure.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices && g_cu_count[dev] > 0) return g_cu_count[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDevices) g_cu_count[dev] = n;
+  return n;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool valid_dtype(int d) { return d >= PDA_F32 && d <= PDA_FP8_E4M3; }
+
+// Shape checks common to both entry points.
+int check_shape(const pda_shape* s, bool mla) {
+  if (!s) return PDA_ERR_INVALID_ARG;
+  if (s->batch < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->head_dim <= 0 ||
+      s->head_dim_v <= 0 || s->page_size <= 0 || s->max_pages_per_seq <= 0 ||
+      s->num_pages <= 0 || s->split_min_tokens < 0)
+    return PDA_ERR_INVALID_ARG;
+  if (!valid_dtype(s->q_dtype) || !valid_dtype(s->kv_dtype)) return PDA_ERR_INVALID_ARG;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PDA_ERR_INVALID_ARG;
+  if ((int64_t)s->max_pages_per_seq * s->page_size > INT32_MAX) return PDA_ERR_INVALID_ARG;
+  if (mla) {
+    if (s->num_kv_heads != 1) return PDA_ERR_INVALID_ARG;
+    if (s->head_dim != 576 || s->head_dim_v != 512) return PDA_ERR_UNSUPPORTED;
+    if (s->q_dtype != PDA_BF16 || s->kv_dtype != PDA_BF16) return PDA_ERR_UNSUPPORTED;
+    if (s->page_size % 64 != 0) return PDA_ERR_UNSUPPORTED;
+    if (s->num_q_heads > 16 && s->num_q_heads % 16 != 0) return PDA_ERR_UNSUPPORTED;
+    if (s->variant < PDA_MLA_DEFAULT || s->variant > PDA_MLA_VALU) return PDA_ERR_INVALID_ARG;
+  } else {
+    if (!pda::gqa_supported(s->q_dtype, s->kv_dtype, s->head_dim, s->head_dim_v))
+      return PDA_ERR_UNSUPPORTED;
+    if (s->page_size % pda::kTileTokens != 0) return PDA_ERR_UNSUPPORTED;
+    if (s->kv_dtype == PDA_FP8_E4M3 && !(s->k_scale > 0.f && s->v_scale > 0.f))
+      return PDA_ERR_INVALID_ARG;
+    // per-tile buffer ranges are 32-bit: 16 token rows of every KV head
+    const int64_t elem = s->kv_dtype == PDA_F32 ? 4 : s->kv_dtype == PDA_FP8_E4M3 ? 1 : 2;
+    if ((int64_t)pda::kTileTokens * s->num_kv_heads * s->head_dim * elem > INT32_MAX)
+      return PDA_ERR_UNSUPPORTED;
+  }
+  return PDA_OK;
+}
+
+int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_plan_info* p) {
+  if (!p || num_splits < 0 || num_cus < 0) return PDA_ERR_INVALID_ARG;
+  int rc = check_shape(s, mla);
+  if (rc != PDA_OK) return rc;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  const int head_tiles = mla ? (int)ceil_div(s->num_q_heads, 16)
+                             : (int)ceil_div(group, pda::gqa_tile_heads(group));
+  const int64_t units = (int64_t)s->batch * s->num_kv_heads * head_tiles;
+  const int max_pages = s->max_pages_per_seq;
+
+  int splits = 1;
+  if (num_splits > 0) {
+    splits = std::min(num_splits, max_pages);
+  } else {
+    if (num_cus == 0) num_cus = device_cus();
+    if (num_cus <= 0) return PDA_ERR_HIP;
+    // Two workgroups per compute unit; split only when the (sequence, head
+    // tile) units alone cannot reach that.
+    const int64_t target = 2 * (int64_t)num_cus;
+    if (units > 0 && units < target)
+      splits = (int)std::min<int64_t>(ceil_div(target, units), max_pages);
+  }
+  // No sequence longer than the threshold fits the table: nothing splits.
+  if ((int64_t)max_pages * s->page_size <= s->split_min_tokens) splits = 1;
+  splits = std::min(splits, 65535);  // grid y extent
+  int pps = (int)ceil_div(max_pages, splits);
+  splits = (int)ceil_div(max_pages, pps);
+
+  p->max_splits = splits;
+  p->pages_per_split = pps;
+  p->head_tiles = head_tiles;
+  p->workgroups = (int)std::min<int64_t>(units * splits, INT32_MAX);
+  p->num_cus = num_cus;
+  p->reserved = 0;
+  uint64_t ws = 0;
+  if (splits > 1) {
+    const uint64_t rows = (uint64_t)s->batch * s->num_q_heads;
+    const uint64_t o_bytes = rows * splits * s->head_dim_v * sizeof(float);
+    ws = ((o_bytes + 255) / 256) * 256 + rows * splits * sizeof(float);
+  }
+  p->workspace_bytes = ws;
+  return PDA_OK;
+}
+
+void workspace_parts(const pda_shape* s, const pda_plan_info& p, void* ws, float** po,
+                     float** pl) {
+  const uint64_t rows = (uint64_t)s->batch * s->num_q_heads;
+  const uint64_t o_bytes = rows * p.max_splits * s->head_dim_v * sizeof(float);
+  *po = (float*)ws;
+  *pl = (float*)((char*)ws + ((o_bytes + 255) / 256) * 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pda_version(void) { return 100; }
+
+const char* pda_status_string(int status) {
+  switch (status) {
+    case PDA_OK: return "ok";
+    case PDA_ERR_INVALID_ARG: return "invalid argument";
+    case PDA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PDA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int pda_plan(const pda_shape* shape, int is_mla, int num_splits, int num_cus,
+             pda_plan_info* plan) {
+  return plan_impl(shape, is_mla != 0, num_splits, num_cus, plan);
+}
+
+size_t pda_workspace_bytes(const pda_shape* shape, int is_mla, int num_splits) {
+  pda_plan_info p;
+  if (plan_impl(shape, is_mla != 0, num_splits, 0, &p) != PDA_OK) return 0;
+  return (size_t)p.workspace_bytes;
+}
+
+int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int group,
+                      float scale, int num_splits, void* out, float* lse,
+                      const pda_shape* shape, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !shape)
+    return PDA_ERR_INVALID_ARG;
+  int rc = check_shape(shape, false);
+  if (rc != PDA_OK) return rc;
+  if (group <= 0 || group * shape->num_kv_heads != shape->num_q_heads) return PDA_ERR_INVALID_ARG;
+  if (!(scale == scale) || num_splits < 0) return PDA_ERR_INVALID_ARG;
+  if (shape->batch == 0) return PDA_OK;
+
+  pda_plan_info p;
+  rc = plan_impl(shape, false, num_splits, 0, &p);
+  if (rc != PDA_OK) return rc;
+  if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
+    return PDA_ERR_WORKSPACE;
+
+  const pda_shape& s = *shape;
+  pda::GqaArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
+  if (p.max_splits > 1) workspace_parts(shape, p, workspace, &a.part_o, &a.part_lse);
+  a.batch = s.batch;
+  a.num_q_heads = s.num_q_heads;
+  a.num_kv_heads = s.num_kv_heads;
+  a.group = group;
+  a.head_tiles = p.head_tiles;
+  a.page_size = s.page_size;
+  a.max_pages = s.max_pages_per_seq;
+  a.tok_stride = s.num_kv_heads * s.head_dim;
+  a.page_stride = (int64_t)s.page_size * s.num_kv_heads * s.head_dim;
+  const float ks = s.kv_dtype == PDA_FP8_E4M3 ? s.k_scale : 1.0f;
+  a.qk_scale_log2 = scale * ks * 1.4426950408889634f;
+  a.v_scale = s.kv_dtype == PDA_FP8_E4M3 ? s.v_scale : 1.0f;
+  a.split.pages_per_split = p.pages_per_split;
+  a.split.max_splits = p.max_splits;
+  a.split.split_min_tokens = s.split_min_tokens;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (pda::launch_gqa(a, s.q_dtype, s.kv_dtype, s.head_dim, pda::gqa_tile_heads(group),
+                      p.max_splits, st) != hipSuccess)
+    return PDA_ERR_HIP;
+  if (p.max_splits > 1) {
+    pda::CombineArgs c{};
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.context_lens = context_lens;
+    c.out = out;
+    c.lse = lse;
+    c.batch = s.batch;
+    c.num_q_heads = s.num_q_heads;
+    c.head_dim_v = s.head_dim_v;
+    c.page_size = s.page_size;
+    c.split = a.split;
+    if (pda::launch_combine(c, s.q_dtype, st) != hipSuccess) return PDA_ERR_HIP;
+  }
+  return PDA_OK;
+}
+
+int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* block_tables,
+                          const int32_t* context_lens, float scale, int num_splits, void* out,
+                          float* lse, const pda_shape* shape, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!q || !kv_cache || !block_tables || !context_lens || !out || !shape)
+    return PDA_ERR_INVALID_ARG;
+  int rc = check_shape(shape, true);
+  if (rc != PDA_OK) return rc;
+  if (!(scale == scale) || num_splits < 0) return PDA_ERR_INVALID_ARG;
+  if (shape->batch == 0) return PDA_OK;
+
+  pda_plan_info p;
+  rc = plan_impl(shape, true, num_splits, 0, &p);
+  if (rc != PDA_OK) return rc;
+  if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
+    return PDA_ERR_WORKSPACE;
+
+  const pda_shape& s = *shape;
+  pda::MlaArgs a{};
+  a.q = q;
+  a.kv_cache = kv_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.lse = lse;
+  if (p.max_splits > 1) workspace_parts(shape, p, workspace, &a.part_o, &a.part_lse);
+  a.batch = s.batch;
+  a.num_q_heads = s.num_q_heads;
+  a.head_tiles = p.head_tiles;
+  a.page_size = s.page_size;
+  a.max_pages = s.max_pages_per_seq;
+  a.qk_scale_log2 = scale * 1.4426950408889634f;
+  a.split.pages_per_split = p.pages_per_split;
+  a.split.max_splits = p.max_splits;
+  a.split.split_min_tokens = s.split_min_tokens;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (pda::launch_mla(a, s.variant, p.max_splits, st) != hipSuccess) return PDA_ERR_HIP;
+  if (p.max_splits > 1) {
+    pda::CombineArgs c{};
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.context_lens = context_lens;
+    c.out = out;
+    c.lse = lse;
+    c.batch = s.batch;
+    c.num_q_heads = s.num_q_heads;
+    c.head_dim_v = s.head_dim_v;
+    c.page_size = s.page_size;
+    c.split = a.split;
+    if (pda::launch_combine(c, s.q_dtype, st) != hipSuccess) return PDA_ERR_HIP;
+  }
+  return PDA_OK;
+}
+
+}  // extern "C"

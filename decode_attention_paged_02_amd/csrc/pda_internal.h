@@ -1,0 +1,82 @@
+// pda_internal.h -- argument blocks and launchers shared by the host entry
+// points (pda_host.cpp) and the kernels (pda_gqa.hip, pda_mla.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pda {
+
+// Tokens processed per wave iteration of the GQA kernel ("tile").  Page sizes
+// must be multiples of it, so a tile never crosses a page boundary.
+constexpr int kTileTokens = 16;
+// Waves per workgroup of the GQA kernel.
+constexpr int kGqaWaves = 4;
+
+// Split layout shared by the attention kernels and the combine kernel.  For
+// sequence b with n = context_lens[b] tokens and pages = ceil(n / P):
+//   n <= split_min_tokens or max_splits == 1: one split over every page, the
+//   kernel writes the final output directly;
+//   otherwise S_b = ceil(pages / pages_per_split) splits of pages_per_split
+//   pages each (the last one shorter), written as partials and combined.
+struct SplitLayout {
+  int32_t pages_per_split;
+  int32_t max_splits;
+  int32_t split_min_tokens;
+};
+
+struct GqaArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* lse;       // nullable
+  float* part_o;    // [B, Hq, max_splits, dv] fp32 (when max_splits > 1)
+  float* part_lse;  // [B, Hq, max_splits] fp32
+  int32_t batch, num_q_heads, num_kv_heads, group, head_tiles;
+  int32_t page_size, max_pages;
+  int32_t tok_stride;    // elements between consecutive tokens of a page (Hkv * d)
+  int64_t page_stride;   // elements between consecutive pages (P * Hkv * d)
+  float qk_scale_log2;   // scale * k_scale * log2(e)
+  float v_scale;
+  SplitLayout split;
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* context_lens;
+  void* out;
+  float* lse;  // nullable
+  int32_t batch, num_q_heads, head_dim_v, page_size;
+  SplitLayout split;
+};
+
+struct MlaArgs {
+  const void* q;           // [B, Hq, 576] bf16
+  const void* kv_cache;    // [num_pages, P, 576] bf16
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;               // [B, Hq, 512] bf16
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int32_t batch, num_q_heads, head_tiles;
+  int32_t page_size, max_pages;
+  float qk_scale_log2;     // scale * log2(e)
+  SplitLayout split;
+};
+
+// Host-side support queries (no HIP calls).
+bool gqa_supported(int q_dtype, int kv_dtype, int head_dim, int head_dim_v);
+int gqa_tile_heads(int group);  // query heads per workgroup tile for a group size
+
+// Launchers (return the launch error, hipSuccess otherwise).
+hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
+                      int tile_heads, int max_splits, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t stream);
+hipError_t launch_mla(const MlaArgs& a, int variant, int max_splits, hipStream_t stream);
+
+}  // namespace pda

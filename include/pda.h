@@ -1,0 +1,165 @@
+/*
+ * pda.h -- C ABI of libpda: single-token decode attention over a paged KV
+ * cache on MI355X (gfx950).
+ *
+ * The operation (pages: "From MHA to MLA: KV Caches and Attention Kernels",
+ * sec. 2-6; "GPU kernel drills" L2 paged-decode page, sec. 2-5; FlashMLA-ETAP
+ * README, "Usage"):
+ *
+ *   for each sequence b < B and query head h < Hq, with G = Hq / Hkv and the
+ *   KV head kvh = floor(h / G) (contiguous grouping),
+ *     K_j = k_cache[block_tables[b][j / P], j % P, kvh, :] * k_scale
+ *     V_j = v_cache[block_tables[b][j / P], j % P, kvh, :] * v_scale
+ *     s_j = scale * q[b, h, :] . K_j                   for j < context_lens[b]
+ *     out[b, h, :] = sum_j softmax(s)_j V_j
+ *     lse[b, h]    = ln sum_j exp(s_j)                 (natural log, fp32)
+ *
+ *   MLA ("From MHA to MLA" sec. 6, "Attention Kernel Variants" MLA section):
+ *   one latent record per token [c (512) | k_R (64)] shared by all query
+ *   heads; K_j = the 576-wide record, V_j = its first 512 values.
+ *
+ * Long sequences may be cut into page-aligned splits (Flash-Decoding,
+ * "From MHA to MLA" sec. 4); each split writes a normalized partial output
+ * and its LSE to the workspace and a combine pass merges them with weights
+ * exp(L_s - L).  The result does not depend on the split count beyond
+ * floating-point rounding.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named *_cache, q, out, lse, block_tables, context_lens and
+ *    workspace are DEVICE pointers owned by the caller; the library neither
+ *    allocates nor retains memory.  `shape` and `plan` are HOST pointers.
+ *  - All arrays are dense row-major with the last dimension contiguous:
+ *      q            [B, Hq, head_dim]          of shape->q_dtype
+ *      k_cache      [num_pages, P, Hkv, head_dim]   of shape->kv_dtype
+ *      v_cache      [num_pages, P, Hkv, head_dim_v] of shape->kv_dtype
+ *      kv_cache     [num_pages, P, head_dim]   (MLA, K and V share it)
+ *      block_tables [B, max_pages_per_seq] int32 (logical -> physical page)
+ *      context_lens [B] int32, the number of cached tokens of each sequence
+ *      out          [B, Hq, head_dim_v]        of shape->q_dtype
+ *      lse          [B, Hq] float32, may be NULL
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous on that stream and never synchronize.  Calls that share a
+ *    workspace must be ordered on one stream.
+ *  - Errors are returned as pda_status codes; nothing aborts or throws.
+ *    Host-checkable arguments are validated before any device work:
+ *    NULL pointers, head/group divisibility, supported (dtype, head_dim,
+ *    page_size) combinations, num_splits >= 0, workspace size.
+ *  - Device-resident values are PRECONDITIONS, not checked: 0 <=
+ *    context_lens[b] <= max_pages_per_seq * P, and the first
+ *    ceil(context_lens[b] / P) entries of block_tables[b] lie in
+ *    [0, num_pages).  Entries past those are never read, nor are cache
+ *    slots past context_lens[b] in the last page.  context_lens[b] == 0
+ *    gives out = 0 and lse = -inf for that sequence.
+ */
+#ifndef PDA_H
+#define PDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  PDA_FP8_E4M3 is OCP FP8 E4M3FN (bias 7, max 448, no
+ * infinities), stored one byte per element, dequantized as
+ * value = e4m3(byte) * scale with one fp32 scale per cache tensor. */
+typedef enum pda_dtype {
+  PDA_F32 = 0,
+  PDA_F16 = 1,
+  PDA_BF16 = 2,
+  PDA_FP8_E4M3 = 3
+} pda_dtype;
+
+typedef enum pda_status {
+  PDA_OK = 0,
+  PDA_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, Hq % Hkv != 0, ...    */
+  PDA_ERR_UNSUPPORTED = 2, /* no kernel for this dtype / head_dim / page    */
+  PDA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required       */
+  PDA_ERR_HIP = 4          /* a HIP runtime call failed (launch, attribute) */
+} pda_status;
+
+/* Problem description, passed by host pointer. */
+typedef struct pda_shape {
+  int32_t batch;             /* B                                          */
+  int32_t num_q_heads;       /* Hq                                         */
+  int32_t num_kv_heads;      /* Hkv (1 for MLA)                            */
+  int32_t head_dim;          /* width of q and K rows (576 for MLA)        */
+  int32_t head_dim_v;        /* width of V rows and of out (512 for MLA)   */
+  int32_t page_size;         /* P, tokens per page                         */
+  int32_t max_pages_per_seq; /* columns of block_tables                    */
+  int32_t num_pages;         /* pages in the pool                          */
+  int32_t q_dtype;           /* pda_dtype of q and out                     */
+  int32_t kv_dtype;          /* pda_dtype of the cache                     */
+  float k_scale;             /* K dequant scale (1.0f unless FP8)          */
+  float v_scale;             /* V dequant scale (1.0f unless FP8)          */
+  int32_t split_min_tokens;  /* sequences with context_lens[b] <= this are */
+                             /* never split (0: any sequence may split)    */
+  int32_t variant;           /* kernel variant, 0 = default (see below)    */
+} pda_shape;
+
+/* MLA kernel variants (pda_shape.variant for paged_decode_attn_mla). */
+#define PDA_MLA_DEFAULT 0 /* the fastest available                          */
+#define PDA_MLA_MFMA 1    /* bf16 matrix cores, keys on the M dimension     */
+#define PDA_MLA_VALU 2    /* plain vector dot products (reference path)     */
+
+/* What the planner chose for a call (host struct). */
+typedef struct pda_plan_info {
+  int32_t max_splits;      /* split-axis extent of the launch grid          */
+  int32_t pages_per_split; /* pages per split for sequences that split      */
+  int32_t head_tiles;      /* query-head tiles per KV head                   */
+  int32_t workgroups;      /* workgroups of the main kernel                  */
+  int32_t num_cus;         /* compute units the plan was made for           */
+  int32_t reserved;
+  uint64_t workspace_bytes; /* bytes the call needs in `workspace`          */
+} pda_plan_info;
+
+/* Choose the split layout for a call (host only, no device work).
+ * num_splits: 0 = automatic (fill the GPU's compute units), otherwise the
+ * largest number of splits any sequence may use.  num_cus: compute units to
+ * plan for; 0 = query the current HIP device.  Sequences longer than
+ * shape->split_min_tokens use ceil(pages / pages_per_split) splits, others one.
+ * is_mla selects the MLA kernel's tiling.  Returns PDA_OK or an error code. */
+int pda_plan(const pda_shape* shape, int is_mla, int num_splits, int num_cus,
+             pda_plan_info* plan);
+
+/* Workspace bytes a call with these arguments needs (0 when no sequence can
+ * split).  Queries the current device's CU count when num_splits == 0.
+ * Returns 0 on invalid arguments as well. */
+size_t pda_workspace_bytes(const pda_shape* shape, int is_mla, int num_splits);
+
+/* GQA / MQA / MHA paged decode attention (layouts above).
+ * group must equal num_q_heads / num_kv_heads.  scale multiplies q.K before
+ * the softmax (k_scale/v_scale are applied on top for FP8 caches).
+ * Supported: (q, kv) dtypes (F32,F32), (F16,F16), (BF16,BF16), (F16,FP8),
+ * (BF16,FP8); head_dim == head_dim_v in {64, 128, 256} (256 not for F32);
+ * page_size a multiple of 16.
+ * workspace: at least pda_workspace_bytes(shape, 0, num_splits) bytes, may
+ * be NULL when that is 0. */
+int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int group,
+                      float scale, int num_splits, void* out, float* lse,
+                      const pda_shape* shape, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* MLA paged decode attention over a latent cache (FlashMLA-ETAP "Usage";
+ * "From MHA to MLA" sec. 6).  shape->num_kv_heads must be 1, head_dim 576,
+ * head_dim_v 512, q_dtype == kv_dtype == PDA_BF16, page_size a multiple of
+ * 64, num_q_heads a multiple of 16 or at most 16.  k_scale/v_scale are
+ * ignored.  The variant field picks the kernel (PDA_MLA_*). */
+int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* block_tables,
+                          const int32_t* context_lens, float scale, int num_splits,
+                          void* out, float* lse, const pda_shape* shape, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* pda_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDA_H */

@@ -1,0 +1,142 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/pda.h
+declares, plans splits as documented, and rejects bad host arguments before
+any device work (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_paged_02_amd import pda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "pda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pda.load()
+    names = header_functions()
+    assert set(names) == set(pda.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pda_version() == 100
+    assert lib.pda_status_string(3) == b"workspace missing or too small"
+
+
+def _shape(**kw):
+    base = dict(batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, head_dim_v=128,
+                page_size=16, max_pages_per_seq=64, num_pages=4096, q_dtype=pda.PDA_F16,
+                kv_dtype=pda.PDA_F16)
+    base.update(kw)
+    return pda.make_shape(**base)
+
+
+def test_plan_fills_compute_units():
+    # 512 (sequence, KV head) units already cover 2 workgroups per CU: no split
+    p = pda.plan(_shape(), num_cus=256)
+    assert (p.max_splits, p.pages_per_split, p.head_tiles, p.workgroups) == (1, 64, 1, 512)
+    assert p.workspace_bytes == 0
+    # B=1, 32768 tokens: 8 units -> 64 splits of 32 pages
+    p = pda.plan(_shape(batch=1, max_pages_per_seq=2048), num_cus=256)
+    assert (p.max_splits, p.pages_per_split, p.workgroups) == (64, 32, 512)
+    assert p.workspace_bytes == 32 * 64 * 128 * 4 + 32 * 64 * 4
+    # B=4 -> 16 splits of 128 pages
+    p = pda.plan(_shape(batch=4, max_pages_per_seq=2048), num_cus=256)
+    assert (p.max_splits, p.pages_per_split) == (16, 128)
+
+
+def test_plan_explicit_and_threshold():
+    p = pda.plan(_shape(max_pages_per_seq=10), num_splits=3, num_cus=256)
+    assert (p.max_splits, p.pages_per_split) == (3, 4)
+    p = pda.plan(_shape(max_pages_per_seq=10), num_splits=50, num_cus=256)
+    assert (p.max_splits, p.pages_per_split) == (10, 1)
+    # no sequence can exceed the split threshold: never split
+    p = pda.plan(_shape(max_pages_per_seq=10, split_min_tokens=160), num_splits=4, num_cus=256)
+    assert p.max_splits == 1 and p.workspace_bytes == 0
+
+
+def test_plan_head_tiles():
+    assert pda.plan(_shape(num_q_heads=64, num_kv_heads=8), num_cus=256).head_tiles == 1
+    assert pda.plan(_shape(num_q_heads=96, num_kv_heads=8), num_cus=256).head_tiles == 2
+    assert pda.plan(_shape(num_q_heads=16, num_kv_heads=1), num_cus=256).head_tiles == 2
+    p = pda.plan(_shape(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512,
+                        page_size=64, q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16),
+                 mla=True, num_cus=256)
+    assert p.head_tiles == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=30), 1),                                  # Hq % Hkv != 0
+    (dict(page_size=8), 2),                                     # not a multiple of 16
+    (dict(head_dim=96, head_dim_v=96), 2),                      # no kernel for d=96
+    (dict(head_dim=128, head_dim_v=64), 2),                     # dk != dv
+    (dict(q_dtype=pda.PDA_F32), 2),                             # f32 q with f16 cache
+    (dict(q_dtype=pda.PDA_F32, kv_dtype=pda.PDA_F32, head_dim=256, head_dim_v=256), 2),
+    (dict(kv_dtype=pda.PDA_FP8_E4M3, k_scale=0.0), 1),          # fp8 needs a positive scale
+    (dict(batch=-1), 1),
+    (dict(q_dtype=7), 1),
+])
+def test_invalid_shapes_rejected_before_device_work(kw, status):
+    s = _shape(**kw)
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    rc = pda.load().paged_decode_attn(fake, fake, fake, fake, fake, 4, 0.1, 1, fake, None,
+                                      ctypes.byref(s), None, 0, None)
+    assert rc == status
+
+
+def test_null_pointers_and_group_mismatch():
+    s = _shape()
+    fake = ctypes.c_void_p(0x1000)
+    lib = pda.load()
+    assert lib.paged_decode_attn(None, fake, fake, fake, fake, 4, 0.1, 1, fake, None,
+                                 ctypes.byref(s), None, 0, None) == 1
+    assert lib.paged_decode_attn(fake, fake, fake, fake, fake, 3, 0.1, 1, fake, None,
+                                 ctypes.byref(s), None, 0, None) == 1
+    assert lib.paged_decode_attn(fake, fake, fake, fake, fake, 4, 0.1, -1, fake, None,
+                                 ctypes.byref(s), None, 0, None) == 1
+    assert lib.paged_decode_attn(fake, fake, fake, fake, fake, 4, 0.1, 1, fake, None,
+                                 None, None, 0, None) == 1
+
+
+def test_missing_workspace_is_reported():
+    s = _shape(batch=1, max_pages_per_seq=2048)
+    fake = ctypes.c_void_p(0x1000)
+    lib = pda.load()
+    need = pda.plan(s, num_splits=8, num_cus=256).workspace_bytes
+    assert need > 0
+    assert lib.paged_decode_attn(fake, fake, fake, fake, fake, 4, 0.1, 8, fake, None,
+                                 ctypes.byref(s), None, 0, None) == 3
+    assert lib.paged_decode_attn(fake, fake, fake, fake, fake, 4, 0.1, 8, fake, None,
+                                 ctypes.byref(s), fake, need - 1, None) == 3
+
+
+def test_mla_validation():
+    s = _shape(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512, page_size=64,
+               q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16)
+    fake = ctypes.c_void_p(0x1000)
+    lib = pda.load()
+    bad = [_shape(num_q_heads=16, num_kv_heads=2, head_dim=576, head_dim_v=512, page_size=64,
+                  q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16),
+           _shape(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512, page_size=16,
+                  q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16),
+           _shape(num_q_heads=24, num_kv_heads=1, head_dim=576, head_dim_v=512, page_size=64,
+                  q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16),
+           _shape(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512, page_size=64)]
+    for b in bad:
+        assert lib.paged_decode_attn_mla(fake, fake, fake, fake, 0.1, 1, fake, None,
+                                         ctypes.byref(b), None, 0, None) in (1, 2)
+    s.variant = 9
+    assert lib.paged_decode_attn_mla(fake, fake, fake, fake, 0.1, 1, fake, None,
+                                     ctypes.byref(s), None, 0, None) == 1
+
+
+def test_empty_batch_is_a_no_op():
+    s = _shape(batch=0)
+    fake = ctypes.c_void_p(0x1000)
+    assert pda.load().paged_decode_attn(fake, fake, fake, fake, fake, 4, 0.1, 1, fake, None,
+                                        ctypes.byref(s), None, 0, None) == 0

@@ -1,0 +1,190 @@
+"""GPU parity of the GQA-family path (HIP kernels through the C ABI) against
+the fp64 oracle, element by element on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_paged_02_amd import pda
+from decode_attention_paged_02_amd import workloads as W
+from gpu_util import check, need_gpu, oracle_ref, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _gqa(seed, B, Hq, Hkv, d, P, lens, q_dtype="f16", kv_dtype="f16", **kw):
+    return W.make_gqa(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, page_size=P,
+                      context_lens=lens, q_dtype=q_dtype, kv_dtype=kv_dtype, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 0])
+def test_tiny_gqa_fp32(num_splits):
+    case = W.tiny_gqa()
+    say("tiny_gqa fp32", "splits", num_splits)
+    out, lse = pda.run_case(case, num_splits=num_splits)
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label="tiny S=%d" % num_splits)
+
+
+def test_gqa_batch64_full_size():
+    """B=64, Hq=32, Hkv=8, d=128, ctx 1024, P=16, fp16; no split (the timed workload)."""
+    case = W.gqa_batch64()
+    say(case.name)
+    dev = pda.to_device(case)
+    p = pda.plan(pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables))
+    assert p.max_splits == 1
+    out, lse = pda.run_case(case, dev)
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label=case.name)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gqa_long_context_split(batch):
+    """ctx 32768, splits chosen to fill the CUs, merged by the combine pass."""
+    case = W.gqa_long(batch)
+    say(case.name)
+    dev = pda.to_device(case)
+    p = pda.plan(pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables))
+    assert p.max_splits > 1
+    out, lse = pda.run_case(case, dev)
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label=case.name)
+
+
+def test_ragged_fp8_sampled_rows():
+    """B=128, log-uniform lengths in [1, 16384], Hq=64, Hkv=8, fp8-e4m3 cache with
+    per-tensor scales, fp16 q; sequences longer than 4096 tokens split."""
+    case = W.ragged_fp8()
+    say(case.name)
+    rng = np.random.default_rng(5)
+    rows = rng.random((case.batch, case.num_q_heads)) < 0.25
+    rows[:3] = True                                    # the forced lengths 1, 16384, 17
+    dev = pda.to_device(case)
+    out, lse = pda.run_case(case, dev, num_splits=4, split_min_tokens=4096)
+    ref_o, ref_l = oracle_ref(case, rows=rows)
+    check(case, out, lse, ref_o, ref_l, rows=rows, label=case.name)
+
+
+@pytest.mark.parametrize("lens", [[1], [15, 16, 17], [31, 32, 33, 47], [100, 1, 64, 129]])
+@pytest.mark.parametrize("dt", [("f16", "f16"), ("bf16", "bf16"), ("f32", "f32"),
+                                ("f16", "e4m3"), ("bf16", "e4m3")])
+def test_page_boundaries_and_dtypes(lens, dt):
+    case = _gqa(len(lens) * 7 + len(dt[1]), len(lens), 8, 2, 128, 16, lens, *dt, extra_pages=3)
+    say("boundaries", lens, dt)
+    out, lse = pda.run_case(case)
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label="lens=%s %s" % (lens, dt))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (16, 1), (12, 4), (24, 4), (48, 4),
+                                    (64, 8), (32, 2)])
+def test_group_sizes(Hq, Hkv):
+    """G=1 (MHA), MQA (Hkv=1), non-power-of-two groups (padded head tiles), G=16."""
+    case = _gqa(Hq * 100 + Hkv, 3, Hq, Hkv, 128, 16, [5, 200, 77], extra_pages=2)
+    say("groups", Hq, Hkv)
+    out, lse = pda.run_case(case)
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label="Hq=%d Hkv=%d" % (Hq, Hkv))
+
+
+@pytest.mark.parametrize("d,P,dt", [(64, 16, "f16"), (64, 32, "bf16"), (256, 16, "f16"),
+                                    (128, 64, "f16"), (64, 16, "f32"), (128, 32, "f32"),
+                                    (256, 16, "bf16")])
+def test_head_dims_and_page_sizes(d, P, dt):
+    case = _gqa(d + P, 2, 16, 4, d, P, [333, 70], dt, dt, extra_pages=2)
+    say("d/P", d, P, dt)
+    for s in (1, 3):
+        out, lse = pda.run_case(case, num_splits=s)
+        ref_o, ref_l = oracle_ref(case)
+        check(case, out, lse, ref_o, ref_l, label="d=%d P=%d %s S=%d" % (d, P, dt, s))
+
+
+def test_split_counts_agree_and_runs_are_deterministic():
+    case = _gqa(9, 2, 32, 8, 128, 16, [4000, 2500])
+    say("split invariance")
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case)
+    outs = {}
+    for s in (1, 2, 5, 16, 250):
+        out, lse = pda.run_case(case, dev, num_splits=s)
+        check(case, out, lse, ref_o, ref_l, label="S=%d" % s)
+        out2, lse2 = pda.run_case(case, dev, num_splits=s)
+        assert torch.equal(out, out2) and torch.equal(lse, lse2), "run-to-run differs"
+        outs[s] = out.float()
+    for s in outs:
+        assert (outs[s] - outs[1]).abs().max().item() < 2e-3
+
+
+def test_split_threshold():
+    """Sequences at or below split_min_tokens are never split; longer ones are."""
+    case = _gqa(10, 4, 16, 4, 128, 16, [4096, 4097, 100, 9000], extra_pages=1)
+    say("split threshold")
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, num_splits=8, split_min_tokens=4096)
+    check(case, out, lse, ref_o, ref_l, label="threshold")
+
+
+def test_page_permutation_bit_identical():
+    case = _gqa(11, 3, 16, 4, 128, 16, [90, 300, 17], extra_pages=9)
+    say("permutation")
+    out1, lse1 = pda.run_case(case)
+    perm = np.random.default_rng(3).permutation(case.num_pages)
+    inv = np.argsort(perm)
+    case.k_cache = case.k_cache[perm].copy()
+    case.v_cache = case.v_cache[perm].copy()
+    bt = case.block_tables.copy()
+    bt[bt >= 0] = inv[bt[bt >= 0]]
+    case.block_tables = bt
+    out2, lse2 = pda.run_case(case)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_poisoned_slots_and_table_tail_never_read():
+    """Unused pages and stale slots hold NaN, table tails hold -1 (the generator's
+    poison); on top, fill every table entry past the context with a huge index."""
+    case = _gqa(12, 4, 16, 4, 128, 16, [1, 17, 250, 33], extra_pages=6, max_pages=40)
+    case.block_tables[case.block_tables < 0] = 2 ** 30
+    say("poison")
+    out, lse = pda.run_case(case)
+    assert torch.isfinite(out).all()
+    ref_o, ref_l = oracle_ref(case)   # the oracle reports any out-of-range entry it reads
+    check(case, out, lse, ref_o, ref_l, label="poison")
+
+
+def test_empty_sequence_and_no_lse():
+    case = _gqa(13, 3, 8, 2, 128, 16, [0, 5, 40], extra_pages=1)
+    say("empty sequence")
+    out, lse = pda.run_case(case)
+    o = out.float().cpu()
+    assert (o[0] == 0).all() and torch.isinf(lse[0]).all() and (lse[0] < 0).all()
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label="empty")
+    out2, lse2 = pda.run_case(case, return_lse=False)
+    assert lse2 is None and torch.equal(out, out2)
+
+
+def test_large_pool_64bit_offsets():
+    """Physical pages beyond 4 GiB of the pool (int64 page addressing)."""
+    B, Hkv, d, P = 2, 1, 128, 16
+    lens = [100, 37]
+    small = _gqa(14, B, 4, Hkv, d, P, lens, poison=False)
+    page_bytes = P * Hkv * d * 2
+    base = (5 << 30) // page_bytes                    # first page past 5 GiB
+    num_pages = base + small.num_pages
+    say("large pool", num_pages, "pages")
+    k = torch.zeros((num_pages, P, Hkv, d), dtype=torch.float16, device="cuda")
+    v = torch.zeros_like(k)
+    k[base:] = torch.from_numpy(small.k_cache).cuda()
+    v[base:] = torch.from_numpy(small.v_cache).cuda()
+    bt = torch.from_numpy(small.block_tables + base).cuda()
+    q = torch.from_numpy(small.q).cuda()
+    cl = torch.from_numpy(small.context_lens).cuda()
+    out, lse = pda.paged_decode_attn(q, k, v, bt, cl, scale=small.scale)
+    ref_o, ref_l = oracle_ref(small)
+    check(small, out, lse, ref_o, ref_l, label="large pool")
+    del k, v
+    torch.cuda.empty_cache()
