@@ -174,6 +174,29 @@ def _oracle_call(case, rows):
                                   v_scale=case.v_scale, rows=rows)
 
 
+def bandwidth_probe(nbytes=2 << 30, reps=10):
+    """Device copy (read + write) and read-only (sum) bandwidth over nbytes
+    buffers: the practical HBM ceiling next to the published peak."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda").normal_()
+    b = torch.empty_like(a)
+    r = {}
+    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes),
+                            ("read", lambda: a.sum(dtype=torch.float32), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        r[name + "_GBs"] = round(moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return r
+
+
 def summarize(r, steps):
     us_step = r["total_ms"] * 1000.0 / steps
     gbs = r["kv_bytes"] / (us_step * 1e-6) / 1e9
@@ -193,6 +216,8 @@ def main():
                     help="extra workloads measured into 'other_workloads' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-bw-probe", action="store_true",
+                    help="skip the copy / read bandwidth probe")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -229,6 +254,9 @@ def main():
                      "kernel_us_mean": round(r2["kernel_us_mean"], 2),
                      "max_splits": r2["max_splits"], "kv_bytes": r2["kv_bytes"]}
         del c2
+    if not args.no_bw_probe:
+        _log("bandwidth probe")
+        roof["measured_device_bw"] = bandwidth_probe()
     cpu = None
     if not args.no_cpu_baseline:
         _log("cpu baseline (oracle)")

@@ -47,6 +47,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.6931471805599453f;
+// Growth of a tile's max over the running reference (log2 units) that
+// triggers a rescale; probabilities stay below 2^kLazyMax.
+constexpr float kLazyMax = 8.0f;
 // dword 3 of a gfx9-family buffer resource: 32-bit data format, raw access.
 constexpr int kRsrcFlags = 0x00020000;
 
@@ -70,11 +73,17 @@ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
 
+// Cache policy of the K/V stream loads (the buffer instruction's cache-policy
+// field; 2 marks them non-temporal).
+#ifndef PDA_KV_LOAD_POLICY
+#define PDA_KV_LOAD_POLICY 2  // non-temporal: K/V rows are read once
+#endif
+
 __device__ __forceinline__ u32x4 buf_load(__amdgpu_buffer_rsrc_t r, int off, u32x4*) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PDA_KV_LOAD_POLICY);
 }
 __device__ __forceinline__ u32x2 buf_load(__amdgpu_buffer_rsrc_t r, int off, u32x2*) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, PDA_KV_LOAD_POLICY);
 }
 
 // ---------------------------------------------------------------- decoding
@@ -141,10 +150,28 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
 
 // --------------------------------------------------------- lane exchanges
 
-// Value of x held by lane (this lane XOR 2^BIT).  Bits 0-3 stay inside a row
-// of 16 lanes and use DPP; bits 4-5 cross rows.
+// Cross-row exchanges use the gfx950 lane swaps:
+//   permlane16_swap(a, b): rows 1 and 3 of a trade places with rows 0 and 2 of b;
+//   permlane32_swap(a, b): lanes 32-63 of a trade places with lanes 0-31 of b.
+// With a == b == x every lane ends up holding {x_self, x_partner} (partner =
+// lane ^ 16, resp. lane ^ 32) in the two results, in an order that depends on
+// the row; commutative reductions just combine both.
+__device__ __forceinline__ void swap16(float a, float b, float& ra, float& rb) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  ra = __uint_as_float(r[0]);
+  rb = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float a, float b, float& ra, float& rb) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  ra = __uint_as_float(r[0]);
+  rb = __uint_as_float(r[1]);
+}
+
+// Value of x held by lane (this lane XOR 2^BIT) for BIT 0..3 (inside a row of
+// 16 lanes, DPP).
 template <int BIT>
 __device__ __forceinline__ float lane_xor(float x) {
+  static_assert(BIT >= 0 && BIT <= 3, "row-local exchange");
   if constexpr (BIT == 0) {
     return __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
   } else if constexpr (BIT == 1) {
@@ -153,10 +180,20 @@ __device__ __forceinline__ float lane_xor(float x) {
     // row_half_mirror gives lane ^ 7, then quad_perm 3,2,1,0 gives ^ 3: ^ 4
     float y = __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, true);
     return __builtin_amdgcn_update_dpp(0.f, y, 0x1B, 0xF, 0xF, true);
-  } else if constexpr (BIT == 3) {
-    return __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true);  // row_ror 8
   } else {
-    return __shfl_xor(x, 1 << BIT, 64);
+    return __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true);  // row_ror 8
+  }
+}
+
+// Sum of x over the lane pair {lane, lane ^ 2^BIT}, for any BIT 0..5.
+template <int BIT>
+__device__ __forceinline__ float pair_sum(float x) {
+  if constexpr (BIT <= 3) {
+    return x + lane_xor<BIT>(x);
+  } else {
+    float a, b;
+    if constexpr (BIT == 4) swap16(x, x, a, b); else swap32(x, x, a, b);
+    return a + b;
   }
 }
 
@@ -169,45 +206,57 @@ template <int N, int BIT>
 __device__ __forceinline__ void reduce_scatter(float* v, int lane) {
   if constexpr (BIT >= 0) {
     if constexpr (N > 1) {
-      const bool hi = (lane >> BIT) & 1;
+      if constexpr (BIT >= 4) {
+        // the swap hands even rows {first half: self, partner} and odd rows
+        // {second half: partner, self}; adding them is the scatter step
 #pragma unroll
-      for (int k = 0; k < N / 2; ++k) {
-        float keep = hi ? v[k + N / 2] : v[k];
-        float send = hi ? v[k] : v[k + N / 2];
-        v[k] = keep + lane_xor<BIT>(send);
+        for (int k = 0; k < N / 2; ++k) {
+          float a, b;
+          if constexpr (BIT == 4) swap16(v[k], v[k + N / 2], a, b);
+          else swap32(v[k], v[k + N / 2], a, b);
+          v[k] = a + b;
+        }
+      } else {
+        const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) {
+          float keep = hi ? v[k + N / 2] : v[k];
+          float send = hi ? v[k] : v[k + N / 2];
+          v[k] = keep + lane_xor<BIT>(send);
+        }
       }
       reduce_scatter<N / 2, BIT - 1>(v, lane);
     } else {
-      v[0] += lane_xor<BIT>(v[0]);
+      v[0] = pair_sum<BIT>(v[0]);
       reduce_scatter<1, BIT - 1>(v, lane);
     }
   }
 }
 
-// Max / sum over the lanes that differ in bits 2..5 (the lanes that share
-// the same (head) slot layout).  Bits 2 and 3 use row rotations by 4 and 8,
-// which visit all four lanes with equal bits 0-1 in a row of 16.
+// Max / sum over the lanes that differ in bits 2..5 (the lanes that hold the
+// same head's scores).  Bits 2 and 3 use row rotations by 4 and 8, which
+// visit all four lanes with equal bits 0-1 in a row of 16.
 __device__ __forceinline__ float wave_max_bits2to5(float x) {
+  float a, b;
   x = fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0x124, 0xF, 0xF, true));  // row_ror 4
   x = fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true));  // row_ror 8
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+  swap16(x, x, a, b);
+  x = fmaxf(a, b);
+  swap32(x, x, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float wave_sum_bits2to5(float x) {
   x += __builtin_amdgcn_update_dpp(0.f, x, 0x124, 0xF, 0xF, true);
   x += __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true);
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  return pair_sum<5>(pair_sum<4>(x));
 }
 
 // Sum over lane bits FROM..5.
 template <int FROM>
 __device__ __forceinline__ float wave_sum_from(float x) {
-  if constexpr (FROM <= 3) x += lane_xor<3>(x);
-  if constexpr (FROM <= 4) x += __shfl_xor(x, 16, 64);
-  if constexpr (FROM <= 5) x += __shfl_xor(x, 32, 64);
+  if constexpr (FROM <= 3) x = pair_sum<3>(x);
+  if constexpr (FROM <= 4) x = pair_sum<4>(x);
+  if constexpr (FROM <= 5) x = pair_sum<5>(x);
   return x;
 }
 
@@ -318,22 +367,32 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
 
   const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
-  const int P = a.page_size;
 
-  // Buffer resources for tile T (or empty ones when T is past the range).
-  auto tile_rsrc = [&](int T, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv,
+  // Page of a tile: pages hold 2^log2_page tokens (a multiple of the tile).
+  const int log2P = a.log2_page;
+  auto page_of = [&](int T) { return (t0 + T * kTileTokens) >> log2P; };
+
+  // Buffer resources of tile ordinal k (tile wave + k * kGqaWaves) in physical
+  // page `phys`; empty ones past the range (their loads return zero without
+  // touching memory).
+  auto tile_rsrc = [&](int k, int phys, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv,
                        int& rows) {
+    const int T = wave + k * kGqaWaves;
     const bool live = T < ntiles;
     const int tok = t0 + T * kTileTokens;
-    const int lp = live ? tok / P : 0;
-    int phys = __builtin_amdgcn_readfirstlane(table[lp]);
-    phys = live ? phys : 0;
     rows = live ? min(kTileTokens, t1 - tok) : 0;
-    const int64_t elem = (int64_t)phys * a.page_stride + (int64_t)(tok - lp * P) * a.tok_stride;
+    const int slot = tok & ((1 << log2P) - 1);
+    const int64_t elem = (int64_t)(live ? phys : 0) * a.page_stride + (int64_t)slot * a.tok_stride;
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.k_cache + elem * ESZ), 0,
                                            rows * tok_bytes, kRsrcFlags);
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.v_cache + elem * ESZ), 0,
                                            rows * tok_bytes, kRsrcFlags);
+  };
+  // Block-table entry of tile ordinal k (a scalar load; entries of tiles past
+  // the range are not read).
+  auto table_entry = [&](int k) {
+    const int T = wave + k * kGqaWaves;
+    return T < ntiles ? table[page_of(T)] : 0;
   };
 
   auto compute_tile = [&](const frag_t (&kf)[NLD], const frag_t (&vf)[NLD], int rows) {
@@ -370,7 +429,11 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
     }
     reduce_scatter<NV, LOG_LPR - 1>(sc, lane);
 
-    // this lane now holds the full scores of values seg*VPL + k
+    // this lane now holds the full scores of values seg*VPL + k.
+    // Lazy running max: the reference max moves only when the tile's max
+    // exceeds it by more than kLazyMax (log2 units), so p <= 2^kLazyMax and
+    // the accumulators are rescaled rarely; numerator and denominator share
+    // the reference, so the result is unchanged.
     float p[VPL], alpha[VPL];
     bool changed = false;
 #pragma unroll
@@ -378,11 +441,13 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
       const int v = seg * VPL + k;
       const int row = rg + RPL * (v / GT);
       const float s = row < rows ? sc[k] * a.qk_scale_log2 : -INFINITY;
-      const float m_new = fmaxf(m_run[k], wave_max_bits2to5(s));
+      const float tmax = wave_max_bits2to5(s);
+      const bool move = tmax > m_run[k] + kLazyMax;
+      const float m_new = move ? tmax : m_run[k];
       alpha[k] = exp2f(m_run[k] - m_new);
       p[k] = exp2f(s - m_new);
       l_run[k] = l_run[k] * alpha[k] + p[k];
-      changed |= (m_new != m_run[k]);
+      changed |= move;
       m_run[k] = m_new;
     }
     // hand the probabilities to the lanes that hold the V rows
@@ -429,39 +494,45 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
     }
   };
 
-  // Two register buffers: the loads of tile T + 4 are in flight while tile T
-  // is computed.
-  frag_t kA[NLD], vA[NLD], kB[NLD], vB[NLD];
-  int rowsA, rowsB;
-  __amdgpu_buffer_rsrc_t rk, rv;
-  int T = wave;
-  tile_rsrc(T, rk, rv, rowsA);
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    kA[i] = buf_load(rk, voff[i], (frag_t*)nullptr);
-    vA[i] = buf_load(rv, voff[i], (frag_t*)nullptr);
-  }
-  while (T < ntiles) {
-    tile_rsrc(T + kGqaWaves, rk, rv, rowsB);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      kB[i] = buf_load(rk, voff[i], (frag_t*)nullptr);
-      vB[i] = buf_load(rv, voff[i], (frag_t*)nullptr);
-    }
-    compute_tile(kA, vA, rowsA);
-    T += kGqaWaves;
-    if (T >= ntiles) break;
-    tile_rsrc(T + kGqaWaves, rk, rv, rowsA);
+  // A ring of kPF + 1 register buffers: while the tile in buffer u is
+  // computed, the loads of the next kPF tiles are in flight.  The
+  // ring index is a compile-time constant inside the unrolled body.
+  // Deep rows (d = 256, or fp32 at d = 128) keep one tile in flight, so the
+  // ring stays within ~96 registers.
+  constexpr int kTileRegs = 2 * NLD * (int)(sizeof(frag_t) / 4);
+  constexpr int kPF = (96 / kTileRegs - 1) < 1 ? 1
+                      : ((96 / kTileRegs - 1) < kGqaPrefetch ? (96 / kTileRegs - 1) : kGqaPrefetch);
+  constexpr int NB = kPF + 1;
+  frag_t kb[NB][NLD], vb[NB][NLD];
+  int rows_b[NB];
+  // The table entry of the next tile to issue is loaded one issue ahead, so
+  // its scalar-load latency hides behind a tile's compute.
+  int phys_next = table_entry(0);
+  auto issue = [&](int k, int u) {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    const int phys = __builtin_amdgcn_readfirstlane(phys_next);
+    phys_next = table_entry(k + 1);
+    tile_rsrc(k, phys, rk, rv, rows_b[u]);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      kA[i] = buf_load(rk, voff[i], (frag_t*)nullptr);
-      vA[i] = buf_load(rv, voff[i], (frag_t*)nullptr);
+      kb[u][i] = buf_load(rk, voff[i], (frag_t*)nullptr);
+      vb[u][i] = buf_load(rv, voff[i], (frag_t*)nullptr);
     }
-    compute_tile(kB, vB, rowsB);
-    T += kGqaWaves;
+  };
+#pragma unroll
+  for (int u = 0; u < kPF; ++u) issue(u, u);
+  for (int kc = 0;; kc += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int k = kc + u;
+      if (wave + k * kGqaWaves >= ntiles) goto tiles_done;
+      issue(k + kPF, (u + kPF) % NB);
+      compute_tile(kb[u], vb[u], rows_b[u]);
+    }
   }
+tiles_done:
 
-  // ---- merge the four waves' states (the split-combine algebra, in LDS)
+  // ---- merge the waves' states (the split-combine algebra, in LDS)
 #pragma unroll
   for (int k = 0; k < VPL; ++k) l_run[k] = wave_sum_bits2to5(l_run[k]);
 #pragma unroll
@@ -516,12 +587,24 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
 
 // ---------------------------------------------------------------- combine
 
+constexpr int kCombineThreads = 256;
+
 // One workgroup per (sequence, query head) row whose sequence was split:
 // L = M + ln sum_s exp(L_s - M), O = sum_s exp(L_s - M) O_s / sum_s exp(L_s - M)
 // with M = max_s L_s ("From MHA to MLA" sec. 4).  Rows of unsplit sequences
-// were written by the attention kernel and are skipped.
-template <class OT>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+// were written by the attention kernel and are skipped.  The threads form
+// kCombineThreads / (DV / 4) split groups x (DV / 4) four-float chunks of the
+// row, so every partial is loaded once with all loads of a thread in flight
+// together; the split groups are merged through LDS.
+template <class OT, int DV>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
+  constexpr int DC = DV / 4;                    // float4 chunks per row
+  constexpr int SG = kCombineThreads / DC;      // split groups
+  static_assert(DC * SG == kCombineThreads, "row width");
+  __shared__ float red[kCombineThreads / 64];
+  __shared__ f32x4 acc_sh[SG][DC];
+  __shared__ float den_sh[SG];
+
   const int64_t row = blockIdx.x;
   const int b = (int)(row / a.num_q_heads);
   int nsplit, t0, t1;
@@ -529,19 +612,50 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   if (nsplit <= 1) return;
   const int S = a.split.max_splits;
   const float* pl = a.part_lse + row * S;
+  const f32x4* po = (const f32x4*)(a.part_o + row * S * DV);
+
+  // M = max_s L_s over the workgroup
   float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pl[s]);
-  for (int d = threadIdx.x; d < a.head_dim_v; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float l = pl[s];
-      if (l == -INFINITY) continue;
-      const float w = __expf(l - mx);
+  for (int s2 = threadIdx.x; s2 < nsplit; s2 += kCombineThreads) mx = fmaxf(mx, pl[s2]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) mx = fmaxf(mx, red[w]);
+
+  const int sg = threadIdx.x / DC, dc = threadIdx.x % DC;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll 4
+    for (int s2 = sg; s2 < nsplit; s2 += SG) {
+      const float l = pl[s2];
+      const f32x4 o = po[(int64_t)s2 * DC + dc];
+      const float w = l == -INFINITY ? 0.f : __expf(l - mx);
       den += w;
-      num += w * a.part_o[(row * S + s) * a.head_dim_v + d];
+      acc += w * o;
     }
-    store_out<OT>(a.out, row * a.head_dim_v + d, den > 0.f ? num / den : 0.f);
-    if (d == 0 && a.lse) a.lse[row] = den > 0.f ? mx + __logf(den) : -INFINITY;
+  }
+  acc_sh[sg][dc] = acc;
+  if (dc == 0) den_sh[sg] = den;
+  __syncthreads();
+  if (threadIdx.x < DC) {
+    f32x4 t = acc_sh[0][threadIdx.x];
+    float d = den_sh[0];
+#pragma unroll
+    for (int g = 1; g < SG; ++g) {
+      t += acc_sh[g][threadIdx.x];
+      d += den_sh[g];
+    }
+    const float inv = d > 0.f ? 1.f / d : 0.f;
+    const int64_t o0 = row * DV + threadIdx.x * 4;
+    store_out<OT>(a.out, o0, t.x * inv);
+    store_out<OT>(a.out, o0 + 1, t.y * inv);
+    store_out<OT>(a.out, o0 + 2, t.z * inv);
+    store_out<OT>(a.out, o0 + 3, t.w * inv);
+    if (threadIdx.x == 0 && a.lse) a.lse[row] = d > 0.f ? mx + __logf(d) : -INFINITY;
   }
 }
 
@@ -601,16 +715,27 @@ hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t s) {
+template <class OT>
+hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
   dim3 grid((unsigned)(a.batch * a.num_q_heads));
-  dim3 block(a.head_dim_v >= 256 ? 256 : 128);
-  switch (out_dtype) {
-    case 0: hipLaunchKernelGGL(combine_kernel<F32>, grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL(combine_kernel<F16>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(combine_kernel<BF16>, grid, block, 0, s, a); break;
+  dim3 block(kCombineThreads);
+  switch (a.head_dim_v) {
+    case 64: hipLaunchKernelGGL((combine_kernel<OT, 64>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<OT, 128>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<OT, 256>), grid, block, 0, s, a); break;
+    case 512: hipLaunchKernelGGL((combine_kernel<OT, 512>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t s) {
+  switch (out_dtype) {
+    case 0: return launch_combine_t<F32>(a, s);
+    case 1: return launch_combine_t<F16>(a, s);
+    case 2: return launch_combine_t<BF16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pda

@@ -50,7 +50,8 @@ int check_shape(const pda_shape* s, bool mla) {
   } else {
     if (!pda::gqa_supported(s->q_dtype, s->kv_dtype, s->head_dim, s->head_dim_v))
       return PDA_ERR_UNSUPPORTED;
-    if (s->page_size % pda::kTileTokens != 0) return PDA_ERR_UNSUPPORTED;
+    if (s->page_size % pda::kTileTokens != 0 || (s->page_size & (s->page_size - 1)) != 0)
+      return PDA_ERR_UNSUPPORTED;
     if (s->kv_dtype == PDA_FP8_E4M3 && !(s->k_scale > 0.f && s->v_scale > 0.f))
       return PDA_ERR_INVALID_ARG;
     // per-tile buffer ranges are 32-bit: 16 token rows of every KV head
@@ -179,6 +180,8 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   a.head_tiles = p.head_tiles;
   a.page_size = s.page_size;
   a.max_pages = s.max_pages_per_seq;
+  a.log2_page = 0;
+  while ((1 << a.log2_page) < s.page_size) ++a.log2_page;
   a.tok_stride = s.num_kv_heads * s.head_dim;
   a.page_stride = (int64_t)s.page_size * s.num_kv_heads * s.head_dim;
   const float ks = s.kv_dtype == PDA_FP8_E4M3 ? s.k_scale : 1.0f;

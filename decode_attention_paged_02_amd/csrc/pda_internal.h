@@ -10,8 +10,16 @@ namespace pda {
 // Tokens processed per wave iteration of the GQA kernel ("tile").  Page sizes
 // must be multiples of it, so a tile never crosses a page boundary.
 constexpr int kTileTokens = 16;
-// Waves per workgroup of the GQA kernel.
-constexpr int kGqaWaves = 4;
+// Waves per workgroup of the GQA kernel and tiles each wave keeps in flight
+// ahead of the one it computes (register buffers).  Tuning constants.
+#ifndef PDA_GQA_WAVES
+#define PDA_GQA_WAVES 4
+#endif
+#ifndef PDA_GQA_PREFETCH
+#define PDA_GQA_PREFETCH 2
+#endif
+constexpr int kGqaWaves = PDA_GQA_WAVES;
+constexpr int kGqaPrefetch = PDA_GQA_PREFETCH;
 
 // Split layout shared by the attention kernels and the combine kernel.  For
 // sequence b with n = context_lens[b] tokens and pages = ceil(n / P):
@@ -37,6 +45,7 @@ struct GqaArgs {
   float* part_lse;  // [B, Hq, max_splits] fp32
   int32_t batch, num_q_heads, num_kv_heads, group, head_tiles;
   int32_t page_size, max_pages;
+  int32_t log2_page;     // page_size == 1 << log2_page
   int32_t tok_stride;    // elements between consecutive tokens of a page (Hkv * d)
   int64_t page_stride;   // elements between consecutive pages (P * Hkv * d)
   float qk_scale_log2;   // scale * k_scale * log2(e)

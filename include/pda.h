@@ -133,7 +133,7 @@ size_t pda_workspace_bytes(const pda_shape* shape, int is_mla, int num_splits);
  * the softmax (k_scale/v_scale are applied on top for FP8 caches).
  * Supported: (q, kv) dtypes (F32,F32), (F16,F16), (BF16,BF16), (F16,FP8),
  * (BF16,FP8); head_dim == head_dim_v in {64, 128, 256} (256 not for F32);
- * page_size a multiple of 16.
+ * page_size a power of two, at least 16.
  * workspace: at least pda_workspace_bytes(shape, 0, num_splits) bytes, may
  * be NULL when that is 0. */
 int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,

@@ -73,6 +73,7 @@ def test_plan_head_tiles():
 @pytest.mark.parametrize("kw,status", [
     (dict(num_q_heads=30), 1),                                  # Hq % Hkv != 0
     (dict(page_size=8), 2),                                     # not a multiple of 16
+    (dict(page_size=48), 2),                                    # not a power of two
     (dict(head_dim=96, head_dim_v=96), 2),                      # no kernel for d=96
     (dict(head_dim=128, head_dim_v=64), 2),                     # dk != dv
     (dict(q_dtype=pda.PDA_F32), 2),                             # f32 q with f16 cache
