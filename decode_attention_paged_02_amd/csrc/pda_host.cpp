@@ -44,7 +44,8 @@ int check_shape(const pda_shape* s, bool mla) {
     if (s->num_kv_heads != 1) return PDA_ERR_INVALID_ARG;
     if (s->head_dim != 576 || s->head_dim_v != 512) return PDA_ERR_UNSUPPORTED;
     if (s->q_dtype != PDA_BF16 || s->kv_dtype != PDA_BF16) return PDA_ERR_UNSUPPORTED;
-    if (s->page_size % 64 != 0) return PDA_ERR_UNSUPPORTED;
+    if (s->page_size % 64 != 0 || (s->page_size & (s->page_size - 1)) != 0)
+      return PDA_ERR_UNSUPPORTED;
     if (s->num_q_heads > 16 && s->num_q_heads % 16 != 0) return PDA_ERR_UNSUPPORTED;
     if (s->variant < PDA_MLA_DEFAULT || s->variant > PDA_MLA_VALU) return PDA_ERR_INVALID_ARG;
   } else {

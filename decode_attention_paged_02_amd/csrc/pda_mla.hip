@@ -1,8 +1,466 @@
-// pda_mla.hip -- MLA latent decode kernels (placeholder until they land).
+// pda_mla.hip -- MLA latent decode on gfx950 ("From MHA to MLA" sec. 6;
+// "Attention Kernel Variants", MLA section; FlashMLA-ETAP "Method").
+//
+// One cached record per token, [c (512) | k_R (64)] in bf16, shared by every
+// query head: K_j is the whole 576-wide record and V_j its first 512 values.
+// A workgroup owns one sequence (or one split of its pages) and a tile of up
+// to 16 query heads, and walks the range in blocks of 32 tokens staged in LDS
+// (double-buffered; rows past the context read as zero through a buffer
+// resource sized to the valid rows).
+//
+// Two kernels compute the same thing:
+//
+//  mla_mfma_kernel -- bf16 matrix cores with the keys on the M dimension
+//    (the transposed pipeline of FlashMLA-ETAP).  Per 16-key half-block each
+//    wave forms S^T = K Q^T (16 keys x 16 heads, 18 MFMA 16x16x32 over the
+//    576-wide record, K read from LDS, Q^T held in registers).  The MFMA
+//    result puts one head per lane column and four keys per lane, which is
+//    exactly the B-operand layout of a 16x16x16 MFMA with the keys as the
+//    contraction, so P^T feeds O^T += V^T P^T without moving between lanes.
+//    V^T comes from LDS with the gfx950 transposing read (ds_read_b64_tr_b16),
+//    one read per 16x16 operand.  Every wave computes the same S^T and softmax
+//    (so the running max agrees bitwise) and owns 128 of the 512 output
+//    columns, so the waves never merge.  On CDNA the 16-row MFMA needs no
+//    query padding, so the ETAP motivation (Hopper's 64-row WGMMA minimum)
+//    does not apply; the layout is kept because the softmax reduction then
+//    lands on two lane swaps and the probabilities need no exchange.
+//
+//  mla_valu_kernel -- plain dot products on the vector ALUs (packed bf16 dot2
+//    for the scores, fp32 FMA for P V), the reference the MFMA path is
+//    measured against.
+//
+// Both keep the online softmax in the log2 domain with a lazily moved
+// reference max (see the GQA kernel) and write either the final bf16 output
+// or normalized fp32 partials + LSE for the split combine.
 #include "pda_internal.h"
 
 namespace pda {
+namespace {
 
-hipError_t launch_mla(const MlaArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short ldsv4s __attribute__((__vector_size__(4 * sizeof(short))));
+
+constexpr int kRec = 576;           // record width (latent 512 + rope 64)
+constexpr int kDv = 512;            // value width
+constexpr int kHeads = 16;          // query heads per workgroup tile
+constexpr int kBlock = 32;          // tokens per LDS block
+constexpr int kThreads = 256;       // 4 waves
+constexpr int kRowBytes = kRec * 2 + 16;  // padded LDS row
+constexpr int kChunks = kBlock * kRec * 2 / 16 / kThreads;  // 16-byte loads per thread per block
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.0f;
+constexpr int kRsrcFlags = 0x00020000;
+constexpr int kLoadPolicy = 2;      // non-temporal: each record is read once per head tile
+static_assert(kChunks * kThreads * 16 == kBlock * kRec * 2, "block split over threads");
+
+__device__ __forceinline__ void split_range(const SplitLayout& sp, int n, int P, int split,
+                                            int& nsplit, int& t0, int& t1) {
+  const int pages = (n + P - 1) / P;
+  if (sp.max_splits <= 1 || n <= sp.split_min_tokens) {
+    nsplit = 1;
+    t0 = 0;
+    t1 = n;
+  } else {
+    nsplit = (pages + sp.pages_per_split - 1) / sp.pages_per_split;
+    const int p0 = split * sp.pages_per_split;
+    t0 = p0 * P;
+    t1 = min((p0 + sp.pages_per_split) * P, n);
+  }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+__device__ __forceinline__ void swap16(float a, float b, float& ra, float& rb) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  ra = __uint_as_float(r[0]);
+  rb = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float a, float b, float& ra, float& rb) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  ra = __uint_as_float(r[0]);
+  rb = __uint_as_float(r[1]);
+}
+// max / sum over the four lanes {l, l^16, l^32, l^48}
+__device__ __forceinline__ float max_x4(float x) {
+  float a, b;
+  swap16(x, x, a, b);
+  x = fmaxf(a, b);
+  swap32(x, x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_x4(float x) {
+  float a, b;
+  swap16(x, x, a, b);
+  x = a + b;
+  swap32(x, x, a, b);
+  return a + b;
+}
+
+// Shared block staging: the workgroup's 256 threads bring one block of 32
+// records (36 KiB) into registers with 16-byte loads, then into LDS.
+struct BlockLoader {
+  u32x4 r[kChunks];
+
+  // Load block `blk` of the range [t0, t1) (tokens t0 + 32 blk ...).  Rows
+  // past t1 (and a block past the range) read as zero without memory access.
+  __device__ __forceinline__ void load(const MlaArgs& a, const int32_t* table, int t0, int t1,
+                                       int blk, int log2P, int tid) {
+    const int tok = t0 + blk * kBlock;
+    const int rows = max(0, min(kBlock, t1 - tok));
+    int phys = 0;
+    if (rows > 0) phys = table[tok >> log2P];
+    phys = __builtin_amdgcn_readfirstlane(phys);
+    const int slot = tok & ((1 << log2P) - 1);
+    const int64_t rec0 = (int64_t)phys * a.page_size + slot;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)a.kv_cache + rec0 * (kRec * 2)), 0, rows * kRec * 2, kRsrcFlags);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + i * kThreads) * 16, 0, kLoadPolicy);
+  }
+
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int q = tid + i * kThreads;
+      const int row = q / (kRec * 2 / 16), col = q % (kRec * 2 / 16);
+      *(u32x4*)(lds + row * kRowBytes + col * 16) = r[i];
+    }
+  }
+};
+
+template <int WHICH>
+__device__ __forceinline__ void store_bf16x4(void* out, int64_t i, f32x4 v) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v.x) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.y) << 16);
+  const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)v.z) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.w) << 16);
+  uint2 w;
+  w.x = lo;
+  w.y = hi;
+  *(uint2*)((char*)out + i * 2) = w;
+}
+
+// ------------------------------------------------------------ MFMA kernel
+
+__global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2][kBlock * kRowBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;      // MFMA column: the head
+  const int grp = lane >> 4;      // lane group: rows 4*grp..4*grp+3 of an MFMA tile
+
+  const int tile = blockIdx.x % a.head_tiles;
+  const int b = blockIdx.x / a.head_tiles;
+  const int split = blockIdx.y;
+  const int n = a.context_lens[b];
+  int nsplit, t0, t1;
+  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+  if (split >= nsplit) return;
+  int log2P = 0;
+  while ((1 << log2P) < a.page_size) ++log2P;
+
+  const int h = tile * kHeads + col;
+  const bool hvalid = h < a.num_q_heads;
+  // Q^T as the B operand of S^T = K Q^T: lane (col, grp) holds q[h][32c + 8 grp + 0..7]
+  bf16x8 qb[kRec / 32];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * a.num_q_heads + h) * kRec;
+#pragma unroll
+    for (int c = 0; c < kRec / 32; ++c) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (hvalid) w = *(const u32x4*)(qrow + 32 * c + 8 * grp);
+      qb[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
+  const int nblocks = (t1 - t0 + kBlock - 1) / kBlock;
+
+  f32x4 acc[8];  // O^T rows 128*wave + 16*mb + 4*grp + i, column = head
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  BlockLoader ld;
+  ld.load(a, table, t0, t1, 0, log2P, tid);
+  ld.store(lds[0], tid);
+  ld.load(a, table, t0, t1, 1, log2P, tid);
+  __syncthreads();
+
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const char* L = lds[blk & 1];
+    const int rows = min(kBlock, t1 - (t0 + blk * kBlock));
+
+    // S^T for the two 16-key halves: 18 MFMAs each over the record
+    f32x4 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const char* krow = L + (16 * kb + col) * kRowBytes + 16 * grp;
+#pragma unroll
+      for (int c = 0; c < kRec / 32; c += 2) {
+        const bf16x8 k0 = *(const bf16x8*)(krow + 64 * c);
+        const bf16x8 k1 = *(const bf16x8*)(krow + 64 * (c + 1));
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[c + 1], s1, 0, 0, 0);
+      }
+      st[kb] = s0 + s1;
+    }
+    // scale, mask rows past the context; lane holds keys 16 kb + 4 grp + i of head `col`
+    float s[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * kb + 4 * grp + i;
+        const float v = key < rows ? st[kb][i] * a.qk_scale_log2 : -INFINITY;
+        s[kb * 4 + i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = max_x4(tmax);
+    if (tmax > m_run + kLazyMax) {  // per head; lanes of one head agree
+      const float alpha = exp2f(m_run - tmax);
+      m_run = tmax;
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
+    }
+    // P^T as the B operand of the 16x16x16 MFMA, split into two bf16 terms
+    // p = p_hi + p_lo (bf16 alone would leave a 2^-9 relative error per
+    // weight); both terms multiply the same V^T operand.
+    s16x4 pb_hi[2], pb_lo[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(s[kb * 4 + i] - m_run);
+        l_run += p;
+        const __bf16 hi = (__bf16)p;
+        const __bf16 lo = (__bf16)(p - (float)hi);
+        pb_hi[kb][i] = __builtin_bit_cast(short, hi);
+        pb_lo[kb][i] = __builtin_bit_cast(short, lo);
+      }
+    // O^T += V^T P^T over this wave's 128 value columns
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // transposing read: lane q of group g points at key 16 kb + 4 g + q/4,
+        // column 128 wave + 16 mb + 4 (q % 4); it returns V^T rows 16 mb + q
+        // (value columns) x keys 16 kb + 4 g + 0..3
+        const int q = col;
+        const char* p = L + (16 * kb + 4 * grp + (q >> 2)) * kRowBytes +
+                        (128 * wave + 16 * mb + 4 * (q & 3)) * 2;
+        const s16x4 vt = __builtin_bit_cast(
+            s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (__attribute__((address_space(3))) ldsv4s*)(p)));
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb_hi[kb], acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb_lo[kb], acc[mb], 0, 0, 0);
+      }
+    }
+    // stage the next block, start loading the one after, hand over the buffer
+    if (blk + 1 < nblocks) ld.store(lds[(blk + 1) & 1], tid);
+    if (blk + 2 < nblocks) ld.load(a, table, t0, t1, blk + 2, log2P, tid);
+    __syncthreads();
+  }
+
+  // epilogue: l over the four lane groups; lane holds 4 consecutive columns
+  const float l = sum_x4(l_run);
+  if (!hvalid) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+  const int64_t row = (int64_t)b * a.num_q_heads + h;
+  if (nsplit == 1) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      store_bf16x4<0>(a.out, row * kDv + 128 * wave + 16 * mb + 4 * grp, acc[mb] * inv);
+    if (wave == 0 && grp == 0 && a.lse) a.lse[row] = lse;
+  } else {
+    float* po = a.part_o + (row * a.split.max_splits + split) * kDv;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) *(f32x4*)(po + 128 * wave + 16 * mb + 4 * grp) = acc[mb] * inv;
+    if (wave == 0 && grp == 0) a.part_lse[row * a.split.max_splits + split] = lse;
+  }
+}
+
+// ------------------------------------------------------------ VALU kernel
+
+// Scores: wave w holds heads 4w..4w+3, lane (head 4w + lane/16, key pair
+// lane%16): the two dot products over 576 values from LDS (packed bf16 dot2).
+// The block max of a head is a 16-lane row reduction.  P V: thread t owns
+// value columns 8 (t%64) .. +8 of heads 4 (t/64) .. +3 and reads P from LDS.
+__global__ __launch_bounds__(kThreads, 2) void mla_valu_kernel(MlaArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2][kBlock * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t q_sh[kHeads][kRec / 2];
+  __shared__ __attribute__((aligned(16))) float p_sh[kBlock][kHeads];
+  __shared__ float alpha_sh[kHeads];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  const int tile = blockIdx.x % a.head_tiles;
+  const int b = blockIdx.x / a.head_tiles;
+  const int split = blockIdx.y;
+  const int n = a.context_lens[b];
+  int nsplit, t0, t1;
+  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+  if (split >= nsplit) return;
+  int log2P = 0;
+  while ((1 << log2P) < a.page_size) ++log2P;
+  const int hvalid_n = min(kHeads, a.num_q_heads - tile * kHeads);
+
+  // q of the tile's heads into LDS (zero for padded heads)
+  for (int i = tid; i < kHeads * kRec / 2; i += kThreads) {
+    const int hh = i / (kRec / 2), w = i % (kRec / 2);
+    uint32_t v = 0;
+    if (hh < hvalid_n)
+      v = ((const uint32_t*)a.q)[(((int64_t)b * a.num_q_heads + tile * kHeads + hh) * kRec) / 2 + w];
+    q_sh[hh][w] = v;
+  }
+
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
+  const int nblocks = (t1 - t0 + kBlock - 1) / kBlock;
+
+  // score-phase identity
+  const int sh = 4 * wave + (lane >> 4);  // head
+  const int kp = lane & 15;               // keys 2kp, 2kp+1
+  float m_run = -INFINITY, l_run = 0.f;   // of head sh (lanes of a row agree)
+  // PV-phase identity
+  const int c8 = tid & 63;                // value columns 8 c8 .. 8 c8 + 7
+  const int hq = tid >> 6;                // heads 4 hq .. 4 hq + 3
+  float acc[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+
+  BlockLoader ld;
+  ld.load(a, table, t0, t1, 0, log2P, tid);
+  ld.store(lds[0], tid);
+  ld.load(a, table, t0, t1, 1, log2P, tid);
+  __syncthreads();
+
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const char* L = lds[blk & 1];
+    const int rows = min(kBlock, t1 - (t0 + blk * kBlock));
+    // scores of (head sh, keys 2kp, 2kp+1)
+    float s0 = 0.f, s1 = 0.f;
+    const char* k0 = L + (2 * kp) * kRowBytes;
+    const char* k1 = k0 + kRowBytes;
+#pragma unroll 4
+    for (int c = 0; c < kRec / 8; ++c) {
+      const u32x4 qv = *(const u32x4*)&q_sh[sh][4 * c];
+      const u32x4 a0 = *(const u32x4*)(k0 + 16 * c);
+      const u32x4 a1 = *(const u32x4*)(k1 + 16 * c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t qj = qv[j], x0 = a0[j], x1 = a1[j];
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qj), as_bf16x2(x0), s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qj), as_bf16x2(x1), s1, false);
+      }
+    }
+    s0 = 2 * kp < rows ? s0 * a.qk_scale_log2 : -INFINITY;
+    s1 = 2 * kp + 1 < rows ? s1 * a.qk_scale_log2 : -INFINITY;
+    float tmax = fmaxf(s0, s1);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
+    float alpha = 1.f;
+    if (tmax > m_run + kLazyMax) {
+      alpha = exp2f(m_run - tmax);
+      m_run = tmax;
+    }
+    const float p0 = exp2f(s0 - m_run), p1 = exp2f(s1 - m_run);
+    l_run = l_run * alpha + p0 + p1;
+    p_sh[2 * kp][sh] = p0;
+    p_sh[2 * kp + 1][sh] = p1;
+    if (kp == 0) alpha_sh[sh] = alpha;
+    __syncthreads();
+    // P V for value columns 8 c8.. of heads 4 hq..
+    float al[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) al[j] = alpha_sh[4 * hq + j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] *= al[j];
+#pragma unroll 4
+    for (int key = 0; key < kBlock; ++key) {
+      const u32x4 v = *(const u32x4*)(L + key * kRowBytes + 16 * c8);
+      const f32x4 p4 = *(const f32x4*)&p_sh[key][4 * hq];
+      float vf[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t vj = v[j];
+        vf[2 * j] = bf16_lo(vj);
+        vf[2 * j + 1] = bf16_hi(vj);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[0][e] = fmaf(p4.x, vf[e], acc[0][e]);
+        acc[1][e] = fmaf(p4.y, vf[e], acc[1][e]);
+        acc[2][e] = fmaf(p4.z, vf[e], acc[2][e]);
+        acc[3][e] = fmaf(p4.w, vf[e], acc[3][e]);
+      }
+    }
+    if (blk + 1 < nblocks) ld.store(lds[(blk + 1) & 1], tid);
+    if (blk + 2 < nblocks) ld.load(a, table, t0, t1, blk + 2, log2P, tid);
+    __syncthreads();
+  }
+
+  // l and m of each head to LDS, then normalize
+  float lsum = l_run;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+  __shared__ float l_sh[kHeads], m_sh[kHeads];
+  if (kp == 0) {
+    l_sh[sh] = lsum;
+    m_sh[sh] = m_run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int hh = 4 * hq + j;
+    if (hh >= hvalid_n) continue;
+    const float l = l_sh[hh];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t row = (int64_t)b * a.num_q_heads + tile * kHeads + hh;
+    const f32x4 o0 = {acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv};
+    const f32x4 o1 = {acc[j][4] * inv, acc[j][5] * inv, acc[j][6] * inv, acc[j][7] * inv};
+    const float lse = l > 0.f ? (m_sh[hh] + __log2f(l)) * kLn2 : -INFINITY;
+    if (nsplit == 1) {
+      store_bf16x4<0>(a.out, row * kDv + 8 * c8, o0);
+      store_bf16x4<0>(a.out, row * kDv + 8 * c8 + 4, o1);
+      if (c8 == 0 && a.lse) a.lse[row] = lse;
+    } else {
+      float* po = a.part_o + (row * a.split.max_splits + split) * kDv + 8 * c8;
+      *(f32x4*)po = o0;
+      *(f32x4*)(po + 4) = o1;
+      if (c8 == 0) a.part_lse[row * a.split.max_splits + split] = lse;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mla(const MlaArgs& a, int variant, int max_splits, hipStream_t s) {
+  dim3 grid((unsigned)(a.batch * a.head_tiles), (unsigned)max_splits);
+  dim3 block(kThreads);
+  if (variant == 2)
+    hipLaunchKernelGGL(mla_valu_kernel, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_mfma_kernel, grid, block, 0, s, a);
+  return hipGetLastError();
+}
 
 }  // namespace pda

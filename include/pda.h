@@ -144,8 +144,8 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
 
 /* MLA paged decode attention over a latent cache (FlashMLA-ETAP "Usage";
  * "From MHA to MLA" sec. 6).  shape->num_kv_heads must be 1, head_dim 576,
- * head_dim_v 512, q_dtype == kv_dtype == PDA_BF16, page_size a multiple of
- * 64, num_q_heads a multiple of 16 or at most 16.  k_scale/v_scale are
+ * head_dim_v 512, q_dtype == kv_dtype == PDA_BF16, page_size a power of two,
+ * at least 64, num_q_heads a multiple of 16 or at most 16.  k_scale/v_scale are
  * ignored.  The variant field picks the kernel (PDA_MLA_*). */
 int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* block_tables,
                           const int32_t* context_lens, float scale, int num_splits,

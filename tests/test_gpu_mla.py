@@ -1,0 +1,114 @@
+"""GPU parity of the MLA latent path (both kernels, through the C ABI) against
+the fp64 oracle on the same seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_paged_02_amd import pda
+from decode_attention_paged_02_amd import workloads as W
+from gpu_util import check, need_gpu, oracle_ref, say
+
+pytestmark = pytest.mark.gpu
+VARIANTS = {"mfma": pda.PDA_MLA_MFMA, "valu": pda.PDA_MLA_VALU}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _mla(seed, lens, Hq=16, P=64, std=0.5, **kw):
+    return W.make_mla(batch=len(lens), num_q_heads=Hq, d_latent=512, d_rope=64, page_size=P,
+                      context_lens=lens, dtype="bf16", seed=seed, std=std,
+                      scale=1.0 / math.sqrt(192.0), **kw)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("lens", [[1], [31, 32, 33], [64, 65, 127, 1], [700, 1500]])
+def test_lengths(variant, lens):
+    case = _mla(len(lens) * 11 + lens[0], lens, extra_pages=3)
+    say("mla", variant, lens)
+    for s in (1, 3):
+        out, lse = pda.run_case(case, variant=VARIANTS[variant], num_splits=s)
+        ref_o, ref_l = oracle_ref(case)
+        check(case, out, lse, ref_o, ref_l, label="mla %s %s S=%d" % (variant, lens, s))
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("Hq", [1, 8, 16, 32, 48])
+def test_head_counts(variant, Hq):
+    """Fewer than 16 heads (padded tile) and several 16-head tiles."""
+    case = _mla(Hq, [200, 77], Hq=Hq, extra_pages=2)
+    say("mla heads", variant, Hq)
+    out, lse = pda.run_case(case, variant=VARIANTS[variant])
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label="mla %s Hq=%d" % (variant, Hq))
+
+
+@pytest.mark.parametrize("P", [64, 128])
+def test_page_sizes_and_poison(P):
+    """NaN in unused pages and stale slots; huge values in table tails."""
+    case = _mla(40 + P, [129, 1, 300, 64], P=P, extra_pages=5, max_pages=12)
+    case.block_tables[case.block_tables < 0] = 2 ** 30
+    say("mla poison", P)
+    for name, v in VARIANTS.items():
+        out, lse = pda.run_case(case, variant=v)
+        assert torch.isfinite(out.float()).all()
+        ref_o, ref_l = oracle_ref(case)
+        check(case, out, lse, ref_o, ref_l, label="mla poison %s P=%d" % (name, P))
+
+
+def test_mfma_and_valu_agree_and_are_deterministic():
+    case = _mla(50, [3000, 4096, 10], extra_pages=1)
+    say("mla agreement")
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case)
+    outs = []
+    for name, v in VARIANTS.items():
+        for s in (0, 1, 7):
+            out, lse = pda.run_case(case, dev, variant=v, num_splits=s)
+            check(case, out, lse, ref_o, ref_l, label="%s S=%d" % (name, s))
+            out2, lse2 = pda.run_case(case, dev, variant=v, num_splits=s)
+            assert torch.equal(out, out2) and torch.equal(lse, lse2)
+            outs.append(out.float())
+    for o in outs[1:]:
+        assert (o - outs[0]).abs().max().item() < 2e-3
+
+
+def test_constant_rope_columns_shift_lse_only():
+    """Rope columns equal across tokens: output unchanged, LSE shifted by
+    scale * q_R . k_R (softmax shift invariance), on the GPU path."""
+    case = _mla(60, [500, 90], extra_pages=1, poison=False)
+    say("mla rope shift")
+    base = W.PagedCase(**{**case.__dict__, "k_cache": case.k_cache.copy()})
+    base.k_cache[..., 512:] = 0
+    out0, lse0 = pda.run_case(base)
+    k_r = W.encode(np.random.default_rng(1).standard_normal(64).astype(np.float32) * 0.5, "bf16")
+    shifted = W.PagedCase(**{**case.__dict__, "k_cache": base.k_cache.copy()})
+    shifted.k_cache[..., 512:] = k_r
+    out1, lse1 = pda.run_case(shifted)
+    q_r = W.to_float32(case.q[..., 512:], "bf16").astype(np.float64)
+    shift = case.scale * (q_r @ W.to_float32(k_r, "bf16").astype(np.float64))
+    assert (out1.float() - out0.float()).abs().max().item() < 2e-3
+    np.testing.assert_allclose(lse1.double().cpu().numpy(), lse0.double().cpu().numpy() + shift,
+                               rtol=0, atol=1e-3)
+
+
+def test_mla_b16_full_size_sampled():
+    """B=16, 16 heads, ctx 65536, page 64, bf16 ~ N(0, 0.5^2): the timed MLA
+    workload in its launch configuration, on 2 sampled heads per sequence."""
+    case = W.mla_b16()
+    say(case.name)
+    rows = np.zeros((case.batch, case.num_q_heads), dtype=bool)
+    rng = np.random.default_rng(7)
+    for b in range(case.batch):
+        rows[b, rng.choice(case.num_q_heads, 2, replace=False)] = True
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case, rows=rows)
+    for name, v in VARIANTS.items():
+        out, lse = pda.run_case(case, dev, variant=v)
+        check(case, out, lse, ref_o, ref_l, rows=rows, label="%s %s" % (case.name, name))
+    del dev
+    torch.cuda.empty_cache()
