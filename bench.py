@@ -243,7 +243,7 @@ def main():
             "kernel_us_median": round(r["kernel_us_median"], 3),
             "algorithmic_bytes_per_launch": r["kv_bytes"]}
     others = {}
-    for w in [x for x in args.others.split(",") if x and x != args.workload]:
+    for w in [x for x in args.others.split(",") if x and x not in (args.workload, "none")]:
         _log("other workload", w)
         c2 = make_case(w)
         st = max(20, args.steps // 4)

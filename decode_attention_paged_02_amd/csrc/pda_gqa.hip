@@ -119,6 +119,50 @@ __device__ __forceinline__ void to_f32(E4M3, const u32x2& w, float (&o)[8]) {
   }
 }
 
+// Element pair j (elements 2j, 2j+1) of a K row fragment in q's 16-bit type.
+__device__ __forceinline__ f16x2 k_pair_f16(const u32x4& w, int j) {
+  const uint32_t x = w[j];
+  return as_f16x2(x);
+}
+__device__ __forceinline__ f16x2 k_pair_f16(const u32x2& w, int j) {
+  const uint32_t x = w[j >> 1];
+  return (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true)
+                 : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+}
+__device__ __forceinline__ bf16x2 k_pair_bf16(const u32x4& w, int j) {
+  const uint32_t x = w[j];
+  return as_bf16x2(x);
+}
+__device__ __forceinline__ bf16x2 k_pair_bf16(const u32x2& w, int j) {
+  const uint32_t x = w[j >> 1];
+  return (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true)
+                 : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+}
+
+// V of two token rows a, b regrouped into binary16 pairs per element:
+// out[e] = (a[e], b[e]).  v_perm_b32 picks bytes of {b : a} (selector values
+// 0-3 address a, 4-7 address b).
+__device__ __forceinline__ void v_pairs(const u32x4& a, const u32x4& b, uint32_t (&out)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t x = a[j], y = b[j];
+    out[2 * j] = __builtin_amdgcn_perm(y, x, 0x05040100u);      // (a.lo, b.lo)
+    out[2 * j + 1] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // (a.hi, b.hi)
+  }
+}
+__device__ __forceinline__ void v_pairs(const u32x2& a, const u32x2& b, uint32_t (&out)[8]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t x = a[j], y = b[j];
+    const uint32_t lo = __builtin_amdgcn_perm(y, x, 0x05010400u);  // a0 b0 a1 b1
+    const uint32_t hi = __builtin_amdgcn_perm(y, x, 0x07030602u);  // a2 b2 a3 b3
+    out[4 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+    out[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+    out[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+    out[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
+  }
+}
+
 // q row fragment (EPL elements starting at element `e0` of a q row) as floats.
 template <class QT, int EPL>
 __device__ __forceinline__ void load_q_f32(const void* q, int64_t e0, float (&o)[EPL]) {
@@ -167,21 +211,26 @@ __device__ __forceinline__ void swap32(float a, float b, float& ra, float& rb) {
   rb = __uint_as_float(r[1]);
 }
 
+// DPP lane move (every lane written: rows and banks all enabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
 // Value of x held by lane (this lane XOR 2^BIT) for BIT 0..3 (inside a row of
 // 16 lanes, DPP).
 template <int BIT>
 __device__ __forceinline__ float lane_xor(float x) {
   static_assert(BIT >= 0 && BIT <= 3, "row-local exchange");
   if constexpr (BIT == 0) {
-    return __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
+    return dpp<0xB1>(x);  // quad_perm 1,0,3,2
   } else if constexpr (BIT == 1) {
-    return __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+    return dpp<0x4E>(x);  // quad_perm 2,3,0,1
   } else if constexpr (BIT == 2) {
     // row_half_mirror gives lane ^ 7, then quad_perm 3,2,1,0 gives ^ 3: ^ 4
-    float y = __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, true);
-    return __builtin_amdgcn_update_dpp(0.f, y, 0x1B, 0xF, 0xF, true);
+    return dpp<0x1B>(dpp<0x141>(x));
   } else {
-    return __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true);  // row_ror 8
+    return dpp<0x128>(x);  // row_ror 8
   }
 }
 
@@ -238,16 +287,16 @@ __device__ __forceinline__ void reduce_scatter(float* v, int lane) {
 // visit all four lanes with equal bits 0-1 in a row of 16.
 __device__ __forceinline__ float wave_max_bits2to5(float x) {
   float a, b;
-  x = fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0x124, 0xF, 0xF, true));  // row_ror 4
-  x = fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true));  // row_ror 8
+  x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
+  x = fmaxf(x, dpp<0x128>(x));  // row_ror 8
   swap16(x, x, a, b);
   x = fmaxf(a, b);
   swap32(x, x, a, b);
   return fmaxf(a, b);
 }
 __device__ __forceinline__ float wave_sum_bits2to5(float x) {
-  x += __builtin_amdgcn_update_dpp(0.f, x, 0x124, 0xF, 0xF, true);
-  x += __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, true);
+  x += dpp<0x124>(x);
+  x += dpp<0x128>(x);
   return pair_sum<5>(pair_sum<4>(x));
 }
 
@@ -290,8 +339,20 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   constexpr int STEPS = ilog2(NV) < LOG_LPR ? ilog2(NV) : LOG_LPR;
   constexpr int VPL = NV >> STEPS;
   constexpr int DUPBITS = LOG_LPR - STEPS;
-  constexpr bool kPacked = std::is_same<QT, KT>::value &&
-                           (std::is_same<KT, F16>::value || std::is_same<KT, BF16>::value);
+  // Scores with packed dot2 when q and K meet in one 16-bit type (fp8 K is
+  // widened to q's type, exactly: every E4M3 value is a binary16 / bfloat16
+  // value); P.V with dot2 over token pairs when V widens exactly to binary16.
+  constexpr bool kQf16 = std::is_same<QT, F16>::value &&
+                         (std::is_same<KT, F16>::value || std::is_same<KT, E4M3>::value);
+  constexpr bool kQbf16 = std::is_same<QT, BF16>::value &&
+                          (std::is_same<KT, BF16>::value || std::is_same<KT, E4M3>::value);
+  constexpr bool kPacked = kQf16 || kQbf16;
+  // binary16 probabilities carry ~2^-12 relative error per weight: fine for a
+  // binary16 output, too coarse next to the rounding of a bfloat16 output
+  // at very short contexts, so bf16-q calls keep fp32 probabilities
+  constexpr bool kDotPV = std::is_same<QT, F16>::value &&
+                          (std::is_same<KT, F16>::value || std::is_same<KT, E4M3>::value);
+  static_assert(!kDotPV || NLD % 2 == 0, "token pairs");
   static_assert(LPR * RPL == 64 && NLD * RPL == kTileTokens, "row layout");
   static_assert(VPL == (GT >= 4 ? GT / 4 : 1) && DUPBITS <= 2, "score layout");
   static_assert(LPR >= 4 && LPR <= 32, "head_dim / dtype combination");
@@ -406,10 +467,10 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
           float s = 0.f;
 #pragma unroll
           for (int j = 0; j < EPL / 2; ++j) {
-            if constexpr (std::is_same<KT, F16>::value) {
-              s = __builtin_amdgcn_fdot2(as_f16x2(qp[g][j]), as_f16x2(kf[i][j]), s, false);
+            if constexpr (kQf16) {
+              s = __builtin_amdgcn_fdot2(as_f16x2(qp[g][j]), k_pair_f16(kf[i], j), s, false);
             } else {
-              s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qp[g][j]), as_bf16x2(kf[i][j]), s,
+              s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qp[g][j]), k_pair_bf16(kf[i], j), s,
                                                   false);
             }
           }
@@ -446,6 +507,9 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
       const float m_new = move ? tmax : m_run[k];
       alpha[k] = exp2f(m_run[k] - m_new);
       p[k] = exp2f(s - m_new);
+      // P.V runs on binary16 probabilities: round here so that the sum l uses
+      // exactly the weights the numerator gets
+      if constexpr (kDotPV) p[k] = (float)(_Float16)p[k];
       l_run[k] = l_run[k] * alpha[k] + p[k];
       changed |= move;
       m_run[k] = m_new;
@@ -483,14 +547,31 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
       for (int j = 0; j < NV; ++j) pv[j] = prow[j];
     }
     __builtin_amdgcn_wave_barrier();
+    if constexpr (kDotPV) {
+      // rows (2ip, 2ip + 1) of the lane: acc[g][e] += (p0, p1) . (V0[e], V1[e])
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      float vv[EPL];
-      to_f32(KT{}, vf[i], vv);
+      for (int ip = 0; ip < NLD / 2; ++ip) {
+        uint32_t vp[EPL];
+        v_pairs(vf[2 * ip], vf[2 * ip + 1], vp);
 #pragma unroll
-      for (int g = 0; g < GT; ++g)
+        for (int g = 0; g < GT; ++g) {
+          const f16x2 pp = __builtin_bit_cast(
+              f16x2, __builtin_amdgcn_cvt_pkrtz(pv[(2 * ip) * GT + g], pv[(2 * ip + 1) * GT + g]));
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pv[i * GT + g], vv[e], acc[g][e]);
+          for (int e = 0; e < EPL; ++e)
+            acc[g][e] = __builtin_amdgcn_fdot2(pp, as_f16x2(vp[e]), acc[g][e], false);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        float vv[EPL];
+        to_f32(KT{}, vf[i], vv);
+#pragma unroll
+        for (int g = 0; g < GT; ++g)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pv[i * GT + g], vv[e], acc[g][e]);
+      }
     }
   };
 
