@@ -675,60 +675,86 @@ constexpr int kCombineThreads = 256;
 // with M = max_s L_s ("From MHA to MLA" sec. 4).  Rows of unsplit sequences
 // were written by the attention kernel and are skipped.  The threads form
 // kCombineThreads / (DV / 4) split groups x (DV / 4) four-float chunks of the
-// row, so every partial is loaded once with all loads of a thread in flight
-// together; the split groups are merged through LDS.
+// row; each group weights its splits against its own maximum, and the groups
+// are merged through LDS with the same algebra.  The sequence length and the
+// first partials are loaded together, so the row costs one memory round trip.
 template <class OT, int DV>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
   constexpr int DC = DV / 4;                    // float4 chunks per row
   constexpr int SG = kCombineThreads / DC;      // split groups
+  constexpr int MAXL = 8;                       // splits a thread keeps in flight
   static_assert(DC * SG == kCombineThreads, "row width");
-  __shared__ float red[kCombineThreads / 64];
   __shared__ f32x4 acc_sh[SG][DC];
-  __shared__ float den_sh[SG];
+  __shared__ float den_sh[SG], mx_sh[SG];
 
   const int64_t row = blockIdx.x;
   const int b = (int)(row / a.num_q_heads);
-  int nsplit, t0, t1;
-  split_range(a.split, a.context_lens[b], a.page_size, 0, nsplit, t0, t1);
-  if (nsplit <= 1) return;
   const int S = a.split.max_splits;
   const float* pl = a.part_lse + row * S;
   const f32x4* po = (const f32x4*)(a.part_o + row * S * DV);
-
-  // M = max_s L_s over the workgroup
-  float mx = -INFINITY;
-  for (int s2 = threadIdx.x; s2 < nsplit; s2 += kCombineThreads) mx = fmaxf(mx, pl[s2]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  mx = red[0];
-#pragma unroll
-  for (int w = 1; w < kCombineThreads / 64; ++w) mx = fmaxf(mx, red[w]);
-
   const int sg = threadIdx.x / DC, dc = threadIdx.x % DC;
+
+  // Issue the sequence length and this thread's first MAXL partials together
+  // (slots past the split count hold stale data and are ignored below).
+  const int n = a.context_lens[b];
+  float l[MAXL];
+  f32x4 o[MAXL];
+#pragma unroll
+  for (int j = 0; j < MAXL; ++j) {
+    const int s2 = sg + j * SG;
+    l[j] = s2 < S ? pl[s2] : -INFINITY;
+    o[j] = s2 < S ? po[(int64_t)s2 * DC + dc] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  int nsplit, t0, t1;
+  split_range(a.split, n, a.page_size, 0, nsplit, t0, t1);
+  if (nsplit <= 1) return;
+
+  // this thread's splits: local max, then weighted sums against it
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < MAXL; ++j)
+    if (sg + j * SG < nsplit) mx = fmaxf(mx, l[j]);
+  for (int s2 = sg + MAXL * SG; s2 < nsplit; s2 += SG) mx = fmaxf(mx, pl[s2]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (mx != -INFINITY) {
-#pragma unroll 4
-    for (int s2 = sg; s2 < nsplit; s2 += SG) {
-      const float l = pl[s2];
-      const f32x4 o = po[(int64_t)s2 * DC + dc];
-      const float w = l == -INFINITY ? 0.f : __expf(l - mx);
+#pragma unroll
+    for (int j = 0; j < MAXL; ++j) {
+      if (sg + j * SG < nsplit && l[j] != -INFINITY) {
+        const float w = __expf(l[j] - mx);
+        den += w;
+        acc += w * o[j];
+      }
+    }
+    for (int s2 = sg + MAXL * SG; s2 < nsplit; s2 += SG) {
+      const float ls = pl[s2];
+      if (ls == -INFINITY) continue;
+      const float w = __expf(ls - mx);
       den += w;
-      acc += w * o;
+      acc += w * po[(int64_t)s2 * DC + dc];
     }
   }
   acc_sh[sg][dc] = acc;
-  if (dc == 0) den_sh[sg] = den;
+  if (dc == 0) {
+    den_sh[sg] = den;
+    mx_sh[sg] = mx;
+  }
   __syncthreads();
+  // merge the split groups (each relative to its own max)
   if (threadIdx.x < DC) {
-    f32x4 t = acc_sh[0][threadIdx.x];
-    float d = den_sh[0];
+    float M = -INFINITY;
 #pragma unroll
-    for (int g = 1; g < SG; ++g) {
-      t += acc_sh[g][threadIdx.x];
-      d += den_sh[g];
+    for (int g = 0; g < SG; ++g) M = fmaxf(M, mx_sh[g]);
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    float d = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int g = 0; g < SG; ++g) {
+        if (mx_sh[g] == -INFINITY) continue;
+        const float w = __expf(mx_sh[g] - M);
+        t += w * acc_sh[g][threadIdx.x];
+        d += w * den_sh[g];
+      }
     }
     const float inv = d > 0.f ? 1.f / d : 0.f;
     const int64_t o0 = row * DV + threadIdx.x * 4;
@@ -736,7 +762,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     store_out<OT>(a.out, o0 + 1, t.y * inv);
     store_out<OT>(a.out, o0 + 2, t.z * inv);
     store_out<OT>(a.out, o0 + 3, t.w * inv);
-    if (threadIdx.x == 0 && a.lse) a.lse[row] = d > 0.f ? mx + __logf(d) : -INFINITY;
+    if (threadIdx.x == 0 && a.lse) a.lse[row] = d > 0.f ? M + __logf(d) : -INFINITY;
   }
 }
 

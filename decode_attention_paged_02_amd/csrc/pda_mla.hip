@@ -49,7 +49,8 @@ constexpr int kDv = 512;            // value width
 constexpr int kHeads = 16;          // query heads per workgroup tile
 constexpr int kBlock = 32;          // tokens per LDS block
 constexpr int kThreads = 256;       // 4 waves
-constexpr int kRowBytes = kRec * 2 + 16;  // padded LDS row
+constexpr int kRowBytes = kRec * 2;  // one record per LDS row (16-byte chunks swizzled)
+constexpr int kRowChunks = kRowBytes / 16;
 constexpr int kChunks = kBlock * kRec * 2 / 16 / kThreads;  // 16-byte loads per thread per block
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 8.0f;
@@ -102,6 +103,13 @@ __device__ __forceinline__ float sum_x4(float x) {
   return a + b;
 }
 
+// LDS placement of 16-byte chunk c of row r: the chunk index is XORed with a
+// permutation of r mod 8 inside its aligned group of eight (72 = 9 x 8), so
+// eight consecutive rows read at one chunk hit distinct banks, and so do four
+// consecutive rows reading an aligned chunk pair (the transposing V reads).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kRowBytes + 16 * (c ^ swz(r)); }
+
 // Shared block staging: the workgroup's 256 threads bring one block of 32
 // records (36 KiB) into registers with 16-byte loads, then into LDS.
 struct BlockLoader {
@@ -129,8 +137,8 @@ struct BlockLoader {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int q = tid + i * kThreads;
-      const int row = q / (kRec * 2 / 16), col = q % (kRec * 2 / 16);
-      *(u32x4*)(lds + row * kRowBytes + col * 16) = r[i];
+      const int row = q / kRowChunks, col = q % kRowChunks;
+      *(u32x4*)(lds + lds_off(row, col)) = r[i];
     }
   }
 };
@@ -151,6 +159,7 @@ __device__ __forceinline__ void store_bf16x4(void* out, int64_t i, f32x4 v) {
 
 __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][kBlock * kRowBytes];
+  __shared__ f32x4 spart[kThreads / 64][2][64];  // per-wave partial S^T of a block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,15 +179,20 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
 
   const int h = tile * kHeads + col;
   const bool hvalid = h < a.num_q_heads;
-  // Q^T as the B operand of S^T = K Q^T: lane (col, grp) holds q[h][32c + 8 grp + 0..7]
-  bf16x8 qb[kRec / 32];
+  // The 18 chunks of 32 record values are shared out over the waves (5, 5, 4,
+  // 4): wave w contracts chunks [c_lo, c_lo + n_w) of every key and the four
+  // partial S^T are summed through LDS in a fixed order.
+  const int c_lo = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
+  const int n_w = wave < 2 ? 5 : 4;
+  // Q^T as the B operand: lane (col, grp) holds q[h][32 (c_lo + j) + 8 grp + 0..7]
+  bf16x8 qb[5];
   {
     const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * a.num_q_heads + h) * kRec;
 #pragma unroll
-    for (int c = 0; c < kRec / 32; ++c) {
+    for (int j = 0; j < 5; ++j) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (hvalid) w = *(const u32x4*)(qrow + 32 * c + 8 * grp);
-      qb[c] = __builtin_bit_cast(bf16x8, w);
+      if (hvalid && j < n_w) w = *(const u32x4*)(qrow + 32 * (c_lo + j) + 8 * grp);
+      qb[j] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
@@ -200,21 +214,26 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
     const char* L = lds[blk & 1];
     const int rows = min(kBlock, t1 - (t0 + blk * kBlock));
 
-    // S^T for the two 16-key halves: 18 MFMAs each over the record
-    f32x4 st[2];
+    // this wave's share of S^T for the two 16-key halves, then the sum of the
+    // four shares (every wave adds them in the same order: identical S^T)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      const char* krow = L + (16 * kb + col) * kRowBytes + 16 * grp;
+      f32x4 sp = {0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * kb + col;
 #pragma unroll
-      for (int c = 0; c < kRec / 32; c += 2) {
-        const bf16x8 k0 = *(const bf16x8*)(krow + 64 * c);
-        const bf16x8 k1 = *(const bf16x8*)(krow + 64 * (c + 1));
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[c], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[c + 1], s1, 0, 0, 0);
+      for (int j = 0; j < 5; ++j) {
+        if (j < n_w) {
+          const bf16x8 kv = *(const bf16x8*)(L + lds_off(r, 4 * (c_lo + j) + grp));
+          sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[j], sp, 0, 0, 0);
+        }
       }
-      st[kb] = s0 + s1;
+      spart[wave][kb][lane] = sp;
     }
+    __syncthreads();
+    f32x4 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      st[kb] = ((spart[0][kb][lane] + spart[1][kb][lane]) + spart[2][kb][lane]) + spart[3][kb][lane];
     // scale, mask rows past the context; lane holds keys 16 kb + 4 grp + i of head `col`
     float s[8];
     float tmax = -INFINITY;
@@ -259,8 +278,9 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
         // column 128 wave + 16 mb + 4 (q % 4); it returns V^T rows 16 mb + q
         // (value columns) x keys 16 kb + 4 g + 0..3
         const int q = col;
-        const char* p = L + (16 * kb + 4 * grp + (q >> 2)) * kRowBytes +
-                        (128 * wave + 16 * mb + 4 * (q & 3)) * 2;
+        const int r = 16 * kb + 4 * grp + (q >> 2);
+        const int byte = (128 * wave + 16 * mb + 4 * (q & 3)) * 2;
+        const char* p = L + lds_off(r, byte >> 4) + (byte & 15);
         const s16x4 vt = __builtin_bit_cast(
             s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                        (__attribute__((address_space(3))) ldsv4s*)(p)));
@@ -299,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
 // lane%16): the two dot products over 576 values from LDS (packed bf16 dot2).
 // The block max of a head is a 16-lane row reduction.  P V: thread t owns
 // value columns 8 (t%64) .. +8 of heads 4 (t/64) .. +3 and reads P from LDS.
-__global__ __launch_bounds__(kThreads, 2) void mla_valu_kernel(MlaArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][kBlock * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint32_t q_sh[kHeads][kRec / 2];
   __shared__ __attribute__((aligned(16))) float p_sh[kBlock][kHeads];
@@ -356,13 +376,11 @@ __global__ __launch_bounds__(kThreads, 2) void mla_valu_kernel(MlaArgs a) {
     const int rows = min(kBlock, t1 - (t0 + blk * kBlock));
     // scores of (head sh, keys 2kp, 2kp+1)
     float s0 = 0.f, s1 = 0.f;
-    const char* k0 = L + (2 * kp) * kRowBytes;
-    const char* k1 = k0 + kRowBytes;
 #pragma unroll 4
     for (int c = 0; c < kRec / 8; ++c) {
       const u32x4 qv = *(const u32x4*)&q_sh[sh][4 * c];
-      const u32x4 a0 = *(const u32x4*)(k0 + 16 * c);
-      const u32x4 a1 = *(const u32x4*)(k1 + 16 * c);
+      const u32x4 a0 = *(const u32x4*)(L + lds_off(2 * kp, c));
+      const u32x4 a1 = *(const u32x4*)(L + lds_off(2 * kp + 1, c));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t qj = qv[j], x0 = a0[j], x1 = a1[j];
@@ -396,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_valu_kernel(MlaArgs a) {
       for (int e = 0; e < 8; ++e) acc[j][e] *= al[j];
 #pragma unroll 4
     for (int key = 0; key < kBlock; ++key) {
-      const u32x4 v = *(const u32x4*)(L + key * kRowBytes + 16 * c8);
+      const u32x4 v = *(const u32x4*)(L + lds_off(key, c8));
       const f32x4 p4 = *(const f32x4*)&p_sh[key][4 * hq];
       float vf[8];
 #pragma unroll
