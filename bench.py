@@ -16,11 +16,9 @@ Prints ONE JSON line.  `--gpus N` with N > 1 exits: this library runs on one GPU
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
-import statistics
 import sys
 import time
 
@@ -53,21 +51,13 @@ def make_case(name):
 CALL_KW = {"ragged_fp8": dict(num_splits=4, split_min_tokens=4096)}
 
 
-def source_digest() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "decode_attention_paged_02_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".cpp", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload: str, launches_per_step: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
+    from decode_attention_paged_02_amd.profiling import source_digest
     t = json.load(open(path))
     if t.get("source_digest") != source_digest():
         return None
@@ -118,17 +108,7 @@ def run_gpu(case, workload, steps, warmup, pools):
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    # per-launch device time: events around every call on the same stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record()
-        step(i)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    per = [a.elapsed_time(b) * 1000.0 for a, b in evs]   # us
-    return dict(total_ms=total_ms, kernel_us_mean=statistics.mean(per),
-                kernel_us_median=statistics.median(per), kernel_us_min=min(per),
+    return dict(total_ms=total_ms, kernel_us_mean=total_ms * 1000.0 / steps,
                 kv_bytes=nbytes, n_pools=len(caches), max_splits=plan.max_splits,
                 pages_per_split=plan.pages_per_split, workgroups=plan.workgroups,
                 launches=1 if plan.max_splits == 1 else 2)
@@ -238,9 +218,10 @@ def main():
     traffic = measured_traffic(args.workload, r["launches"])
     roof = {"bound": "hbm", "achieved": round(kgbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "gqa_split_kernel" if not case.mla else "mla kernel",
-            "kernel_us_mean": round(r["kernel_us_mean"], 3),
-            "kernel_us_median": round(r["kernel_us_median"], 3),
+            "kernel": "gqa_split_kernel" if not case.mla else "mla_mfma_kernel",
+            "launch_us_mean": round(r["kernel_us_mean"], 3),
+            "launches_per_step": r["launches"],
+            "timing": "HIP events on the launch stream around the timed region / steps",
             "algorithmic_bytes_per_launch": r["kv_bytes"]}
     others = {}
     for w in [x for x in args.others.split(",") if x and x not in (args.workload, "none")]:
@@ -251,7 +232,6 @@ def main():
         u2, g2, k2 = summarize(r2, st)
         others[w] = {"us_per_step": round(u2, 2), "GB/s": round(g2, 1),
                      "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4),
-                     "kernel_us_mean": round(r2["kernel_us_mean"], 2),
                      "max_splits": r2["max_splits"], "kv_bytes": r2["kv_bytes"]}
         del c2
     if not args.no_bw_probe:

@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 output for the profiles/ directory.
 
     python -m decode_attention_paged_02_amd.profiling stats  DIR [--match SUBSTR]
+    python -m decode_attention_paged_02_amd.profiling counters DIR [--match SUBSTR]
     python -m decode_attention_paged_02_amd.profiling traffic --workload NAME \\
         --fetch DIR --write DIR --kernel SUBSTR --bytes-per-launch N --copy-kernel SUBSTR
 
@@ -106,12 +107,29 @@ def traffic(fetch_dir, write_dir, kernel, copy_kernel, copy_bytes):
     }
 
 
+def counters_text(d, match):
+    """Mean value per dispatch of every counter of the kernels matching `match`."""
+    vals = counter_values(d)
+    out = []
+    for k in vals:
+        if match not in k:
+            continue
+        out.append("kernel: %s  (%d dispatches)" % (short_name(k),
+                                                    len(next(iter(vals[k].values())))))
+        for c in sorted(vals[k]):
+            out.append("  %-28s %18.1f" % (c, statistics.mean(vals[k][c])))
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
     s.add_argument("--match", default="")
+    cn = sub.add_parser("counters")
+    cn.add_argument("dir")
+    cn.add_argument("--match", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--workload", required=True)
     t.add_argument("--fetch", required=True)
@@ -126,6 +144,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_text(a.dir, a.match))
+        return
+    if a.cmd == "counters":
+        print(counters_text(a.dir, a.match))
         return
     r = traffic(a.fetch, a.write, a.kernel, a.copy_kernel, a.copy_bytes)
     r.update({"workload": a.workload, "source_digest": source_digest(),
