@@ -218,7 +218,7 @@ def main():
     traffic = measured_traffic(args.workload, r["launches"])
     roof = {"bound": "hbm", "achieved": round(kgbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "gqa_split_kernel" if not case.mla else "mla_mfma_kernel",
+            "kernel": "mla_mfma_kernel" if case.mla else "gqa_mfma_kernel",
             "launch_us_mean": round(r["kernel_us_mean"], 3),
             "launches_per_step": r["launches"],
             "timing": "HIP events on the launch stream around the timed region / steps",

@@ -30,299 +30,16 @@
 // whose base is the tile's first row in its physical page and whose size
 // covers exactly the tile's valid rows, so rows past the context (stale
 // slots of a last partial page) read as zero and are never fetched, and the
-// per-lane byte offsets are loop invariant.  Block-table entries past the
-// sequence's pages are never read.
-#include "pda_internal.h"
+// per-lane byte offsets are loop invariant.  A wave reads the block-table
+// entries of its next 64 tiles with one vector load (one entry per lane) and
+// takes each tile's entry with a lane read; entries past the sequence's pages
+// may be loaded that way but never address the cache.
+#include "pda_device.h"
 
 #include <type_traits>
 
 namespace pda {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLn2 = 0.6931471805599453f;
-// Growth of a tile's max over the running reference (log2 units) that
-// triggers a rescale; probabilities stay below 2^kLazyMax.
-constexpr float kLazyMax = 8.0f;
-// dword 3 of a gfx9-family buffer resource: 32-bit data format, raw access.
-constexpr int kRsrcFlags = 0x00020000;
-
-struct F32 {};
-struct F16 {};
-struct BF16 {};
-struct E4M3 {};
-
-template <class T> struct Elem;
-template <> struct Elem<F32> { static constexpr int bytes = 4, epl = 4; using frag = u32x4; };
-template <> struct Elem<F16> { static constexpr int bytes = 2, epl = 8; using frag = u32x4; };
-template <> struct Elem<BF16> { static constexpr int bytes = 2, epl = 8; using frag = u32x4; };
-template <> struct Elem<E4M3> { static constexpr int bytes = 1, epl = 8; using frag = u32x2; };
-
-constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
-
-// Reinterpret one 32-bit word as a pair of 16-bit floats.  The word is taken
-// by value: hipcc's __builtin_bit_cast applied directly to an ext_vector
-// element (v[j]) reads element 0 whatever j is, so every vector element goes
-// through a scalar first.
-__device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
-__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
-
-// Cache policy of the K/V stream loads (the buffer instruction's cache-policy
-// field; 2 marks them non-temporal).
-#ifndef PDA_KV_LOAD_POLICY
-#define PDA_KV_LOAD_POLICY 2  // non-temporal: K/V rows are read once
-#endif
-
-__device__ __forceinline__ u32x4 buf_load(__amdgpu_buffer_rsrc_t r, int off, u32x4*) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PDA_KV_LOAD_POLICY);
-}
-__device__ __forceinline__ u32x2 buf_load(__amdgpu_buffer_rsrc_t r, int off, u32x2*) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, PDA_KV_LOAD_POLICY);
-}
-
-// ---------------------------------------------------------------- decoding
-
-__device__ __forceinline__ void to_f32(F32, const u32x4& w, float (&o)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(w[i]);
-}
-__device__ __forceinline__ void to_f32(F16, const u32x4& w, float (&o)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 h = as_f16x2(w[i]);
-    o[2 * i] = (float)h.x;
-    o[2 * i + 1] = (float)h.y;
-  }
-}
-__device__ __forceinline__ void to_f32(BF16, const u32x4& w, float (&o)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[2 * i] = __uint_as_float(w[i] << 16);
-    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void to_f32(E4M3, const u32x2& w, float (&o)[8]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-    o[4 * i] = lo.x;
-    o[4 * i + 1] = lo.y;
-    o[4 * i + 2] = hi.x;
-    o[4 * i + 3] = hi.y;
-  }
-}
-
-// Element pair j (elements 2j, 2j+1) of a K row fragment in q's 16-bit type.
-__device__ __forceinline__ f16x2 k_pair_f16(const u32x4& w, int j) {
-  const uint32_t x = w[j];
-  return as_f16x2(x);
-}
-__device__ __forceinline__ f16x2 k_pair_f16(const u32x2& w, int j) {
-  const uint32_t x = w[j >> 1];
-  return (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true)
-                 : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
-}
-__device__ __forceinline__ bf16x2 k_pair_bf16(const u32x4& w, int j) {
-  const uint32_t x = w[j];
-  return as_bf16x2(x);
-}
-__device__ __forceinline__ bf16x2 k_pair_bf16(const u32x2& w, int j) {
-  const uint32_t x = w[j >> 1];
-  return (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true)
-                 : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
-}
-
-// V of two token rows a, b regrouped into binary16 pairs per element:
-// out[e] = (a[e], b[e]).  v_perm_b32 picks bytes of {b : a} (selector values
-// 0-3 address a, 4-7 address b).
-__device__ __forceinline__ void v_pairs(const u32x4& a, const u32x4& b, uint32_t (&out)[8]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t x = a[j], y = b[j];
-    out[2 * j] = __builtin_amdgcn_perm(y, x, 0x05040100u);      // (a.lo, b.lo)
-    out[2 * j + 1] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // (a.hi, b.hi)
-  }
-}
-__device__ __forceinline__ void v_pairs(const u32x2& a, const u32x2& b, uint32_t (&out)[8]) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t x = a[j], y = b[j];
-    const uint32_t lo = __builtin_amdgcn_perm(y, x, 0x05010400u);  // a0 b0 a1 b1
-    const uint32_t hi = __builtin_amdgcn_perm(y, x, 0x07030602u);  // a2 b2 a3 b3
-    out[4 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
-    out[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
-    out[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
-    out[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
-  }
-}
-
-// q row fragment (EPL elements starting at element `e0` of a q row) as floats.
-template <class QT, int EPL>
-__device__ __forceinline__ void load_q_f32(const void* q, int64_t e0, float (&o)[EPL]) {
-  if constexpr (std::is_same<QT, F32>::value) {
-    const float* p = (const float*)q + e0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) o[i] = p[i];
-  } else if constexpr (std::is_same<QT, F16>::value) {
-    const _Float16* p = (const _Float16*)q + e0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) o[i] = (float)p[i];
-  } else {
-    const uint16_t* p = (const uint16_t*)q + e0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) o[i] = __uint_as_float((uint32_t)p[i] << 16);
-  }
-}
-
-template <class T>
-__device__ __forceinline__ void store_out(void* out, int64_t i, float v) {
-  if constexpr (std::is_same<T, F32>::value) {
-    ((float*)out)[i] = v;
-  } else if constexpr (std::is_same<T, F16>::value) {
-    ((_Float16*)out)[i] = (_Float16)v;
-  } else {
-    ((__bf16*)out)[i] = (__bf16)v;
-  }
-}
-
-// --------------------------------------------------------- lane exchanges
-
-// Cross-row exchanges use the gfx950 lane swaps:
-//   permlane16_swap(a, b): rows 1 and 3 of a trade places with rows 0 and 2 of b;
-//   permlane32_swap(a, b): lanes 32-63 of a trade places with lanes 0-31 of b.
-// With a == b == x every lane ends up holding {x_self, x_partner} (partner =
-// lane ^ 16, resp. lane ^ 32) in the two results, in an order that depends on
-// the row; commutative reductions just combine both.
-__device__ __forceinline__ void swap16(float a, float b, float& ra, float& rb) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  ra = __uint_as_float(r[0]);
-  rb = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void swap32(float a, float b, float& ra, float& rb) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  ra = __uint_as_float(r[0]);
-  rb = __uint_as_float(r[1]);
-}
-
-// DPP lane move (every lane written: rows and banks all enabled).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
-// Value of x held by lane (this lane XOR 2^BIT) for BIT 0..3 (inside a row of
-// 16 lanes, DPP).
-template <int BIT>
-__device__ __forceinline__ float lane_xor(float x) {
-  static_assert(BIT >= 0 && BIT <= 3, "row-local exchange");
-  if constexpr (BIT == 0) {
-    return dpp<0xB1>(x);  // quad_perm 1,0,3,2
-  } else if constexpr (BIT == 1) {
-    return dpp<0x4E>(x);  // quad_perm 2,3,0,1
-  } else if constexpr (BIT == 2) {
-    // row_half_mirror gives lane ^ 7, then quad_perm 3,2,1,0 gives ^ 3: ^ 4
-    return dpp<0x1B>(dpp<0x141>(x));
-  } else {
-    return dpp<0x128>(x);  // row_ror 8
-  }
-}
-
-// Sum of x over the lane pair {lane, lane ^ 2^BIT}, for any BIT 0..5.
-template <int BIT>
-__device__ __forceinline__ float pair_sum(float x) {
-  if constexpr (BIT <= 3) {
-    return x + lane_xor<BIT>(x);
-  } else {
-    float a, b;
-    if constexpr (BIT == 4) swap16(x, x, a, b); else swap32(x, x, a, b);
-    return a + b;
-  }
-}
-
-// Reduce-scatter of N partial sums across the lanes that differ in lane bits
-// BIT, BIT-1, ..., 0 (most significant first).  Each step halves the array:
-// lanes with the bit clear keep the first half, lanes with it set the second,
-// each adding its partner's copy of the half it keeps.  Once one value is
-// left, the remaining bits are summed as an all-reduce (duplicated values).
-template <int N, int BIT>
-__device__ __forceinline__ void reduce_scatter(float* v, int lane) {
-  if constexpr (BIT >= 0) {
-    if constexpr (N > 1) {
-      if constexpr (BIT >= 4) {
-        // the swap hands even rows {first half: self, partner} and odd rows
-        // {second half: partner, self}; adding them is the scatter step
-#pragma unroll
-        for (int k = 0; k < N / 2; ++k) {
-          float a, b;
-          if constexpr (BIT == 4) swap16(v[k], v[k + N / 2], a, b);
-          else swap32(v[k], v[k + N / 2], a, b);
-          v[k] = a + b;
-        }
-      } else {
-        const bool hi = (lane >> BIT) & 1;
-#pragma unroll
-        for (int k = 0; k < N / 2; ++k) {
-          float keep = hi ? v[k + N / 2] : v[k];
-          float send = hi ? v[k] : v[k + N / 2];
-          v[k] = keep + lane_xor<BIT>(send);
-        }
-      }
-      reduce_scatter<N / 2, BIT - 1>(v, lane);
-    } else {
-      v[0] = pair_sum<BIT>(v[0]);
-      reduce_scatter<1, BIT - 1>(v, lane);
-    }
-  }
-}
-
-// Max / sum over the lanes that differ in bits 2..5 (the lanes that hold the
-// same head's scores).  Bits 2 and 3 use row rotations by 4 and 8, which
-// visit all four lanes with equal bits 0-1 in a row of 16.
-__device__ __forceinline__ float wave_max_bits2to5(float x) {
-  float a, b;
-  x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
-  x = fmaxf(x, dpp<0x128>(x));  // row_ror 8
-  swap16(x, x, a, b);
-  x = fmaxf(a, b);
-  swap32(x, x, a, b);
-  return fmaxf(a, b);
-}
-__device__ __forceinline__ float wave_sum_bits2to5(float x) {
-  x += dpp<0x124>(x);
-  x += dpp<0x128>(x);
-  return pair_sum<5>(pair_sum<4>(x));
-}
-
-// Sum over lane bits FROM..5.
-template <int FROM>
-__device__ __forceinline__ float wave_sum_from(float x) {
-  if constexpr (FROM <= 3) x = pair_sum<3>(x);
-  if constexpr (FROM <= 4) x = pair_sum<4>(x);
-  if constexpr (FROM <= 5) x = pair_sum<5>(x);
-  return x;
-}
-
-__device__ __forceinline__ void split_range(const SplitLayout& sp, int n, int P, int split,
-                                            int& nsplit, int& t0, int& t1) {
-  const int pages = (n + P - 1) / P;
-  if (sp.max_splits <= 1 || n <= sp.split_min_tokens) {
-    nsplit = 1;
-    t0 = 0;
-    t1 = n;
-  } else {
-    nsplit = (pages + sp.pages_per_split - 1) / sp.pages_per_split;
-    const int p0 = split * sp.pages_per_split;
-    t0 = p0 * P;
-    t1 = min((p0 + sp.pages_per_split) * P, n);
-  }
-}
 
 // ------------------------------------------------------------ main kernel
 
@@ -361,11 +78,34 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   __shared__ float m_sh[kGqaWaves][GT], l_sh[kGqaWaves][GT];
   __shared__ float acc_sh[kGqaWaves][GT][D];
 
+  // Every kernel argument is fetched in one batch of scalar loads up front
+  // (the empty asm needs them all in registers here), instead of in several
+  // dependent round trips as the code below first touches them.
+  asm volatile("" ::"s"(a.q), "s"(a.k_cache), "s"(a.v_cache), "s"(a.block_tables),
+               "s"(a.context_lens), "s"(a.batch), "s"(a.num_q_heads), "s"(a.num_kv_heads),
+               "s"(a.group), "s"(a.head_tiles), "s"(a.page_size), "s"(a.max_pages),
+               "s"(a.log2_page), "s"(a.tok_stride), "s"(a.page_stride), "s"(a.qk_scale_log2),
+               "s"(a.split.pages_per_split), "s"(a.split.max_splits),
+               "s"(a.split.split_min_tokens));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = lane / LPR;
   const int c = lane % LPR;
   const int seg = c >> DUPBITS;
+  // Per-lane order of the score array for the select-free reduce-scatter:
+  // slot s holds the score of logical value s ^ flip (value v = row ordinal
+  // * GT + head), where flip carries the lane bits that are exchanged with
+  // DPP, each at the index bit its reduction step splits.  A value index
+  // decomposes into (row ordinal, head), so the lane loads its K rows in the
+  // order i ^ flip_row and its q heads in the order g ^ flip_head.
+  constexpr int kLG = ilog2(GT);
+  constexpr int kDppSeg = (4 - DUPBITS) < STEPS ? (4 - DUPBITS) : STEPS;
+  const int flip = (seg & ((1 << kDppSeg) - 1)) * VPL;
+  const int flip_row = kGqaPermuteRows ? flip >> kLG : 0;
+  const int flip_head = flip & (GT - 1);
+  // steps on arrays up to kPerm values use the flipped order (all of them
+  // when the K rows are permuted too, else the head steps only)
+  constexpr int kPerm = kGqaPermuteRows ? NV : GT;
 
   const int wg = blockIdx.x;
   const int tile = wg % a.head_tiles;
@@ -374,45 +114,62 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   const int b = bk / a.num_kv_heads;
   const int split = blockIdx.y;
 
-  const int n = a.context_lens[b];
-  int nsplit, t0, t1;
-  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
-  if (split >= nsplit) return;
-
   const int g0 = tile * GT;                 // first group-local head of the tile
   const int hbase = kvh * a.group + g0;     // first query head of the tile
   const int gvalid = min(GT, a.group - g0); // heads of the tile inside the group
+  const int log2P = a.log2_page;
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
+  // First token of this split when the sequence is split (a split that ends
+  // up unused exits below before anything depends on it).
+  const int t0_hint = a.split.max_splits > 1 ? split * a.split.pages_per_split << log2P : 0;
 
-  // q of the tile's heads, the EPL elements this lane multiplies
+  // The sequence length, this wave's block-table entries and q are requested
+  // together, before anything waits for one of them.  Lane j holds the entry
+  // of the wave's tile ordinal kbase + j; indices are clamped into the
+  // sequence's table row, and entries past its pages are loaded but never
+  // used.
+  auto load_table = [&](int kbase) -> int {
+    const int64_t tok = (int64_t)t0_hint + (int64_t)(wave + (kbase + lane) * kGqaWaves) * kTileTokens;
+    const int64_t pg = tok >> log2P;
+    return table[pg < a.max_pages ? pg : a.max_pages - 1];
+  };
+  const int n = a.context_lens[b];
+  int vtbl = load_table(0);
+
+  // q of the tile's heads (slot g holds head g ^ flip_head), the EPL elements
+  // this lane multiplies.  Heads past the group are loaded from a valid row
+  // (no branch around the load) and zeroed.
   uint32_t qp[GT][EPL / 2];
   float qf[GT][EPL];
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
-    const int64_t e0 = ((int64_t)b * a.num_q_heads + hbase + g) * D + c * EPL;
+    const int gh = g ^ flip_head;
+    const bool hv = gh < gvalid;
+    const int64_t e0 = ((int64_t)b * a.num_q_heads + hbase + (hv ? gh : 0)) * D + c * EPL;
     if constexpr (kPacked) {
-      if (g < gvalid) {
-        u32x4 w = *(const u32x4*)((const char*)a.q + e0 * 2);
+      u32x4 w = *(const u32x4*)((const char*)a.q + e0 * 2);
 #pragma unroll
-        for (int j = 0; j < EPL / 2; ++j) qp[g][j] = w[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < EPL / 2; ++j) qp[g][j] = 0u;
-      }
+      for (int j = 0; j < EPL / 2; ++j) qp[g][j] = hv ? (uint32_t)w[j] : 0u;
     } else {
-      if (g < gvalid) {
-        load_q_f32<QT, EPL>(a.q, e0, qf[g]);
-      } else {
+      load_q_f32<QT, EPL>(a.q, e0, qf[g]);
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) qf[g][j] = 0.f;
-      }
+      for (int j = 0; j < EPL; ++j) qf[g][j] = hv ? qf[g][j] : 0.f;
     }
   }
 
-  // loop-invariant byte offsets of this lane's rows inside a tile
+  int nsplit, t0, t1;
+  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+  if (split >= nsplit) return;
+
+  // loop-invariant byte offsets of this lane's rows inside a tile (K in the
+  // permuted row order of the score array, V in plain order)
   const int tok_bytes = a.tok_stride * ESZ;
-  int voff[NLD];
+  int koff[NLD], voff[NLD];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) voff[i] = (rg + RPL * i) * tok_bytes + (kvh * D + c * EPL) * ESZ;
+  for (int i = 0; i < NLD; ++i) {
+    koff[i] = (rg + RPL * (i ^ flip_row)) * tok_bytes + (kvh * D + c * EPL) * ESZ;
+    voff[i] = (rg + RPL * i) * tok_bytes + (kvh * D + c * EPL) * ESZ;
+  }
 
   float m_run[VPL], l_run[VPL];
   float acc[GT][EPL];
@@ -427,19 +184,15 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
 
   const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
-
-  // Page of a tile: pages hold 2^log2_page tokens (a multiple of the tile).
-  const int log2P = a.log2_page;
-  auto page_of = [&](int T) { return (t0 + T * kTileTokens) >> log2P; };
+  // tile ordinals of this wave: tiles wave, wave + kGqaWaves, ...
+  const int nt_wave = ntiles > wave ? (ntiles - wave + kGqaWaves - 1) / kGqaWaves : 0;
 
   // Buffer resources of tile ordinal k (tile wave + k * kGqaWaves) in physical
-  // page `phys`; empty ones past the range (their loads return zero without
+  // page `phys`; empty ones for dead tiles (their loads return zero without
   // touching memory).
-  auto tile_rsrc = [&](int k, int phys, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv,
-                       int& rows) {
+  auto tile_rsrc = [&](int k, bool live, int phys, __amdgpu_buffer_rsrc_t& rk,
+                       __amdgpu_buffer_rsrc_t& rv, int& rows) {
     const int T = wave + k * kGqaWaves;
-    const bool live = T < ntiles;
     const int tok = t0 + T * kTileTokens;
     rows = live ? min(kTileTokens, t1 - tok) : 0;
     const int slot = tok & ((1 << log2P) - 1);
@@ -449,13 +202,8 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.v_cache + elem * ESZ), 0,
                                            rows * tok_bytes, kRsrcFlags);
   };
-  // Block-table entry of tile ordinal k (a scalar load; entries of tiles past
-  // the range are not read).
-  auto table_entry = [&](int k) {
-    const int T = wave + k * kGqaWaves;
-    return T < ntiles ? table[page_of(T)] : 0;
-  };
 
+  const float pinf = opaque_inf();
   auto compute_tile = [&](const frag_t (&kf)[NLD], const frag_t (&vf)[NLD], int rows) {
     // partial scores of this lane: NLD rows x GT heads over its EPL elements
     float sc[NV];
@@ -488,7 +236,7 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
         }
       }
     }
-    reduce_scatter<NV, LOG_LPR - 1>(sc, lane);
+    reduce_scatter<NV, LOG_LPR - 1, kPerm>(sc, lane);
 
     // this lane now holds the full scores of values seg*VPL + k.
     // Lazy running max: the reference max moves only when the tile's max
@@ -501,12 +249,13 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
     for (int k = 0; k < VPL; ++k) {
       const int v = seg * VPL + k;
       const int row = rg + RPL * (v / GT);
-      const float s = row < rows ? sc[k] * a.qk_scale_log2 : -INFINITY;
-      const float tmax = wave_max_bits2to5(s);
+      // (a min against +-inf masks rows past the context without a branch)
+      const float s = fminf(sc[k] * a.qk_scale_log2, row < rows ? INFINITY : -INFINITY);
+      const float tmax = wave_max_bits2to5(s, pinf);
       const bool move = tmax > m_run[k] + kLazyMax;
       const float m_new = move ? tmax : m_run[k];
-      alpha[k] = exp2f(m_run[k] - m_new);
-      p[k] = exp2f(s - m_new);
+      alpha[k] = __builtin_amdgcn_exp2f(m_run[k] - m_new);
+      p[k] = __builtin_amdgcn_exp2f(s - m_new);
       // P.V runs on binary16 probabilities: round here so that the sum l uses
       // exactly the weights the numerator gets
       if constexpr (kDotPV) p[k] = (float)(_Float16)p[k];
@@ -586,32 +335,43 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   constexpr int NB = kPF + 1;
   frag_t kb[NB][NLD], vb[NB][NLD];
   int rows_b[NB];
-  // The table entry of the next tile to issue is loaded one issue ahead, so
-  // its scalar-load latency hides behind a tile's compute.
-  int phys_next = table_entry(0);
-  auto issue = [&](int k, int u) {
+  // Issue the loads of tile ordinal k into ring buffer u; ordinals at or past
+  // kend (the end of the current 64-tile table chunk) get empty resources.
+  auto issue = [&](int k, int kend, int u) {
     __amdgpu_buffer_rsrc_t rk, rv;
-    const int phys = __builtin_amdgcn_readfirstlane(phys_next);
-    phys_next = table_entry(k + 1);
-    tile_rsrc(k, phys, rk, rv, rows_b[u]);
+    const bool live = k < kend;
+    const int entry = __builtin_amdgcn_readlane(vtbl, k & 63);
+    const int phys = live ? entry : 0;
+    tile_rsrc(k, live, phys, rk, rv, rows_b[u]);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      kb[u][i] = buf_load(rk, voff[i], (frag_t*)nullptr);
+      kb[u][i] = buf_load(rk, koff[i], (frag_t*)nullptr);
       vb[u][i] = buf_load(rv, voff[i], (frag_t*)nullptr);
     }
   };
+  // The wave's tiles in chunks of 64 ordinals, one table entry per lane; the
+  // ring restarts at each chunk (one pipeline drain per 64 tiles of a wave).
+  for (int kbase = 0; kbase < nt_wave;) {
+    const int kend = min(kbase + 64, nt_wave);
+    // (in order: the loop's wait counts assume the oldest tile is issued first)
 #pragma unroll
-  for (int u = 0; u < kPF; ++u) issue(u, u);
-  for (int kc = 0;; kc += NB) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int k = kc + u;
-      if (wave + k * kGqaWaves >= ntiles) goto tiles_done;
-      issue(k + kPF, (u + kPF) % NB);
-      compute_tile(kb[u], vb[u], rows_b[u]);
+    for (int u = 0; u < kPF; ++u) {
+      issue(kbase + u, kend, u);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    for (int kc = kbase;; kc += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int k = kc + u;
+        if (k >= kend) goto chunk_done;
+        issue(k + kPF, kend, (u + kPF) % NB);
+        compute_tile(kb[u], vb[u], rows_b[u]);
+      }
+    }
+  chunk_done:
+    kbase = kend;
+    if (kbase < nt_wave) vtbl = load_table(kbase);
   }
-tiles_done:
 
   // ---- merge the waves' states (the split-combine algebra, in LDS)
 #pragma unroll

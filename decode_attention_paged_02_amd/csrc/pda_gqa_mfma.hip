@@ -1,0 +1,438 @@
+// pda_gqa_mfma.hip -- paged decode attention for the GQA family on the gfx950
+// matrix cores ("From MHA to MLA" sec. 3-5; the drill page sec. 3-5).
+//
+// Same contract as gqa_split_kernel (pda_gqa.hip): a workgroup owns a tile of
+// up to 16 query heads of one KV group of one sequence (one split of its
+// pages), four waves walk 16-token tiles (wave w takes tiles w, w+4, ...),
+// keep an online softmax each, and merge through LDS at the end.  What
+// changes is the arithmetic of a tile:
+//
+//  - scores as S^T = K Q^T with the tile's 16 tokens on the MFMA M dimension
+//    and the 16 heads on N (v_mfma_f32_16x16x32, D/32 of them).  The result
+//    gives lane (head = lane % 16, group g = lane / 16) the scores of tokens
+//    4g..4g+3, which is exactly the B-operand layout of the 16x16x16 MFMA
+//    with the tokens as the contraction, so P^T needs no lane exchange;
+//  - O^T += V^T P^T (v_mfma_f32_16x16x16, D/16 of them; for bfloat16 queries
+//    twice, with p split into two bfloat16 terms), the output rows being
+//    value dimensions and the columns heads, so a lane rescales only its own
+//    head's accumulators when the running max moves.
+//
+// Loads stay row-coalesced: load j of a tile gives lane (g, u) token 4g + j,
+// elements [u D/16, (u+1) D/16) of the row, so every load instruction covers
+// four whole token rows.  That is already the A-operand layout of V^T (lane
+// row u, contraction over the 4 tokens: two v_perm_b32 per operand).  K needs
+// the transposed assignment (lane row = token), so each wave writes its K
+// tile into its own padded LDS tile and reads it back in the MFMA layout
+// (rows padded by 16 bytes: both directions are free of bank conflicts).
+//
+// With fewer than 16 heads in the group the spare MFMA columns are computed
+// on zero queries and never written.
+#include "pda_device.h"
+
+namespace pda {
+namespace {
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMWaves = 4;
+constexpr int kMHeads = 16;  // MFMA N: heads per workgroup tile
+
+// Pieces of a token row held by one lane: D/16 elements.
+template <class KT, int D>
+struct Piece {
+  static constexpr int bytes = D / 16 * Elem<KT>::bytes;
+  static constexpr int words = bytes / 4;
+};
+
+template <int W>
+struct Words {
+  uint32_t w[W];
+};
+
+// Row piece of `W` words at byte `off` of a tile resource (non-temporal).
+template <int W>
+__device__ __forceinline__ Words<W> load_piece(__amdgpu_buffer_rsrc_t r, int off) {
+  Words<W> p;
+  if constexpr (W == 1) {
+    p.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, PDA_KV_LOAD_POLICY);
+  } else if constexpr (W == 2) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, PDA_KV_LOAD_POLICY);
+    p.w[0] = x[0];
+    p.w[1] = x[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < W / 4; ++h) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * h, 0, PDA_KV_LOAD_POLICY);
+      p.w[4 * h] = x[0];
+      p.w[4 * h + 1] = x[1];
+      p.w[4 * h + 2] = x[2];
+      p.w[4 * h + 3] = x[3];
+    }
+  }
+  return p;
+}
+
+// A 16-bit row piece of W words (2 or a multiple of 4) into LDS.
+template <int W>
+__device__ __forceinline__ void store_piece(char* dst, const Words<W>& p) {
+  if constexpr (W == 2) {
+    *(u32x2*)dst = u32x2{p.w[0], p.w[1]};
+  } else {
+    static_assert(W % 4 == 0, "piece width");
+#pragma unroll
+    for (int w = 0; w < W; w += 4) *(u32x4*)(dst + 4 * w) = u32x4{p.w[w], p.w[w + 1], p.w[w + 2], p.w[w + 3]};
+  }
+}
+
+// Four fp8 values (one word) as two 16-bit-float pairs in the query's type.
+template <class QT>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t x, bool hi) {
+  if constexpr (std::is_same<QT, F16>::value) {
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
+  } else {
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+  }
+}
+
+template <class QT>
+__device__ __forceinline__ f32x4 mfma_qk(const u32x4& k, const u32x4& q, f32x4 c) {
+  if constexpr (std::is_same<QT, F16>::value) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                  __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
+  }
+}
+
+template <class QT>
+__device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, f32x4 c) {
+  if constexpr (std::is_same<QT, F16>::value) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v),
+                                                 __builtin_bit_cast(f16x4, p), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v),
+                                                     __builtin_bit_cast(s16x4, p), c, 0, 0, 0);
+  }
+}
+
+template <class QT, class KT, int D>
+__global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
+  constexpr int ESZ = Elem<KT>::bytes;
+  constexpr int PW = Piece<KT, D>::words;       // words of a loaded row piece
+  constexpr int NE = D / 16;                    // elements per piece = PV MFMAs
+  constexpr int NQK = D / 32;                   // QK MFMAs (32 contraction each)
+  constexpr int kRowB = D * 2 + 16;             // LDS bytes per K row (16-bit, padded)
+  constexpr int kTileB = kTileTokens * kRowB;   // one wave's K tile
+  constexpr bool kFp8 = std::is_same<KT, E4M3>::value;
+  constexpr bool kBf16 = std::is_same<QT, BF16>::value;
+  constexpr int kAccStride = D + 4;             // floats per head row of the merge area
+  constexpr int kMergeB = kMWaves * kMHeads * kAccStride * 4;
+  constexpr int kLdsB = kMWaves * kTileB > kMergeB ? kMWaves * kTileB : kMergeB;
+  static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+  static_assert(kFp8 || std::is_same<QT, KT>::value, "q / cache types");
+
+  __shared__ __attribute__((aligned(16))) char lds[kLdsB];
+  __shared__ float m_sh[kMWaves][kMHeads], l_sh[kMWaves][kMHeads];
+
+  // one batch of kernel-argument loads (see gqa_split_kernel)
+  asm volatile("" ::"s"(a.q), "s"(a.k_cache), "s"(a.v_cache), "s"(a.block_tables),
+               "s"(a.context_lens), "s"(a.batch), "s"(a.num_q_heads), "s"(a.num_kv_heads),
+               "s"(a.group), "s"(a.head_tiles), "s"(a.page_size), "s"(a.max_pages),
+               "s"(a.log2_page), "s"(a.tok_stride), "s"(a.page_stride), "s"(a.qk_scale_log2),
+               "s"(a.split.pages_per_split), "s"(a.split.max_splits),
+               "s"(a.split.split_min_tokens));
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;  // MFMA column (head) / V^T row piece / K row token
+  const int grp = lane >> 4;  // lane group
+
+  const int wg = blockIdx.x;
+  const int tile = wg % a.head_tiles;
+  const int bk = wg / a.head_tiles;
+  const int kvh = bk % a.num_kv_heads;
+  const int b = bk / a.num_kv_heads;
+  const int split = blockIdx.y;
+
+  const int g0 = tile * kMHeads;
+  const int hbase = kvh * a.group + g0;
+  const int gvalid = min(kMHeads, a.group - g0);
+  const int log2P = a.log2_page;
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
+  const int t0_hint = a.split.max_splits > 1 ? split * a.split.pages_per_split << log2P : 0;
+
+  // sequence length, block-table entries (lane j: tile ordinal kbase + j,
+  // clamped into the row, unused past the sequence) and q, requested together
+  auto load_table = [&](int kbase) -> int {
+    const int64_t tok = (int64_t)t0_hint + (int64_t)(wave + (kbase + lane) * kMWaves) * kTileTokens;
+    const int64_t pg = tok >> log2P;
+    return table[pg < a.max_pages ? pg : a.max_pages - 1];
+  };
+  const int n = a.context_lens[b];
+  int vtbl = load_table(0);
+
+  // Q^T as the B operand of the QK MFMAs: lane (col, grp) holds
+  // q[head col][32 j + 8 grp .. +8] for MFMA j; heads past the group are zero
+  u32x4 qb[NQK];
+  {
+    const bool hv = col < gvalid;
+    const char* qrow = (const char*)a.q + (((int64_t)b * a.num_q_heads + hbase + (hv ? col : 0)) * D) * 2;
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) {
+      const u32x4 w = *(const u32x4*)(qrow + (32 * j + 8 * grp) * 2);
+      qb[j] = hv ? w : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  int nsplit, t0, t1;
+  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+  if (split >= nsplit) return;
+
+  const int tok_bytes = a.tok_stride * ESZ;
+  // load j of a tile: token 4 grp + j, piece col of the row
+  const int off0 = (4 * grp) * tok_bytes + (kvh * D + col * NE) * ESZ;
+
+  f32x4 acc[NE];  // O^T: rows (4 grp + i) * NE + e of the value, column = head col
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float pinf = opaque_inf();
+
+  const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
+  const int nt_wave = ntiles > wave ? (ntiles - wave + kMWaves - 1) / kMWaves : 0;
+
+  char* ktile = lds + wave * kTileB;
+
+  auto compute_tile = [&](const Words<PW> (&kf)[4], const Words<PW> (&vf)[4], int rows) {
+    // ---- K tile into LDS in 16-bit form: row = token, piece col at 2 NE col bytes
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      char* dst = ktile + (4 * grp + j) * kRowB + col * NE * 2;
+      if constexpr (kFp8) {
+        Words<2 * PW> h;
+#pragma unroll
+        for (int w = 0; w < PW; ++w) {
+          h.w[2 * w] = fp8_pair<QT>(kf[j].w[w], false);
+          h.w[2 * w + 1] = fp8_pair<QT>(kf[j].w[w], true);
+        }
+        store_piece<2 * PW>(dst, h);
+      } else {
+        store_piece<PW>(dst, kf[j]);
+      }
+    }
+    // ---- S^T = K Q^T: lane reads token col, elements 32 j + 8 grp .. +8
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) {
+      const u32x4 kk = *(const u32x4*)(ktile + col * kRowB + (32 * j + 8 * grp) * 2);
+      st = mfma_qk<QT>(kk, qb[j], st);
+    }
+    // ---- online softmax (log2 domain, lazily moved reference max); this lane
+    // holds tokens 4 grp + i of head col
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s[i] = fminf(st[i] * a.qk_scale_log2, 4 * grp + i < rows ? INFINITY : -INFINITY);
+    float tmax = max2(max2(s[0], s[1], pinf), max2(s[2], s[3], pinf), pinf);
+    {
+      float x, y;
+      swap16(tmax, tmax, x, y);
+      tmax = max2(x, y, pinf);
+      swap32(tmax, tmax, x, y);
+      tmax = max2(x, y, pinf);
+    }
+    const bool move = tmax > m_run + kLazyMax;
+    const float m_new = move ? tmax : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
+    u32x2 pb, pb_lo;
+    if constexpr (!kBf16) {
+      // binary16 probabilities (round to nearest even); the denominator sums
+      // the same rounded values
+      const f16x2 p01 = __builtin_convertvector((f32x2{p[0], p[1]}), f16x2);
+      const f16x2 p23 = __builtin_convertvector((f32x2{p[2], p[3]}), f16x2);
+      const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+      l_run = __builtin_amdgcn_fdot2(p23, one, __builtin_amdgcn_fdot2(p01, one, l_run * alpha, false),
+                                     false);
+      pb = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+    } else {
+      // p = p_hi + p_lo, two bfloat16 terms (bfloat16 alone leaves 2^-9
+      // relative error per weight)
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 h = (__bf16)p[i];
+        const __bf16 l = (__bf16)(p[i] - (float)h);
+        hi[i] = __builtin_bit_cast(uint16_t, h);
+        lo[i] = __builtin_bit_cast(uint16_t, l);
+      }
+      l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+      pb = u32x2{(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
+      pb_lo = u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
+    }
+    if (__builtin_amdgcn_read_exec() & __ballot(move)) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e) acc[e] *= alpha;
+    }
+    // ---- O^T += V^T P^T.  A operand of MFMA e: V^T row col (value element
+    // col NE + e) over tokens 4 grp + 0..3 = element e of the four loads.
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      u32x2 va;
+      if constexpr (kFp8) {
+        // bytes e of loads (0, 1) and (2, 3), widened exactly
+        const int w = e >> 2, sh = e & 3;
+        const uint32_t sel = 0x0c0c0000u | ((4u + sh) << 8) | (uint32_t)sh;  // [a.e, b.e, 0, 0]
+        const uint32_t x01 = __builtin_amdgcn_perm(vf[1].w[w], vf[0].w[w], sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(vf[3].w[w], vf[2].w[w], sel);
+        va = u32x2{fp8_pair<QT>(x01, false), fp8_pair<QT>(x23, false)};
+      } else {
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // hi / lo halves of {b : a}
+        va = u32x2{__builtin_amdgcn_perm(vf[1].w[w], vf[0].w[w], sel),
+                   __builtin_amdgcn_perm(vf[3].w[w], vf[2].w[w], sel)};
+      }
+      acc[e] = mfma_pv<QT>(va, pb, acc[e]);
+      if constexpr (kBf16) acc[e] = mfma_pv<QT>(va, pb_lo, acc[e]);
+    }
+  };
+
+  // ring of register buffers, tiles in chunks of 64 ordinals (one table entry
+  // per lane), as in gqa_split_kernel
+  constexpr int kTileRegs = 8 * PW;
+  constexpr int kPF = (96 / kTileRegs - 1) < 1 ? 1
+                      : ((96 / kTileRegs - 1) < kGqaPrefetch ? (96 / kTileRegs - 1) : kGqaPrefetch);
+  constexpr int NB = kPF + 1;
+  Words<PW> kb[NB][4], vb[NB][4];
+  int rows_b[NB];
+  auto issue = [&](int k, int kend, int u) {
+    const bool live = k < kend;
+    const int entry = __builtin_amdgcn_readlane(vtbl, k & 63);
+    const int phys = live ? entry : 0;
+    const int T = wave + k * kMWaves;
+    const int tok = t0 + T * kTileTokens;
+    const int rows = live ? min(kTileTokens, t1 - tok) : 0;
+    rows_b[u] = rows;
+    const int slot = tok & ((1 << log2P) - 1);
+    const int64_t elem = (int64_t)phys * a.page_stride + (int64_t)slot * a.tok_stride;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)a.k_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)a.v_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kb[u][j] = load_piece<PW>(rk, off0 + j * tok_bytes);
+      vb[u][j] = load_piece<PW>(rv, off0 + j * tok_bytes);
+    }
+  };
+  for (int kbase = 0; kbase < nt_wave;) {
+    const int kend = min(kbase + 64, nt_wave);
+    // (in order: the loop's wait counts assume the oldest tile is issued first)
+#pragma unroll
+    for (int u = 0; u < kPF; ++u) {
+      issue(kbase + u, kend, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int kc = kbase;; kc += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int k = kc + u;
+        if (k >= kend) goto chunk_done;
+        issue(k + kPF, kend, (u + kPF) % NB);
+        compute_tile(kb[u], vb[u], rows_b[u]);
+      }
+    }
+  chunk_done:
+    kbase = kend;
+    if (kbase < nt_wave) vtbl = load_table(kbase);
+  }
+
+  // ---- merge the four waves (the split-combine algebra) through LDS; the
+  // merge area overlays the K tiles, so every wave must be done with them
+  l_run = pair_sum<5>(pair_sum<4>(l_run));
+  __syncthreads();
+  float* acc_sh = (float*)lds;  // [wave][head][kAccStride]
+  if (grp == 0) {
+    m_sh[wave][col] = m_run;
+    l_sh[wave][col] = l_run;
+  }
+  {
+    float* dst = acc_sh + (wave * kMHeads + col) * kAccStride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < NE; e += 4)
+        *(f32x4*)(dst + (4 * grp + i) * NE + e) =
+            f32x4{acc[e][i], acc[e + 1][i], acc[e + 2][i], acc[e + 3][i]};
+  }
+  __syncthreads();
+
+  const bool final_out = nsplit == 1;
+  for (int idx = threadIdx.x; idx < kMHeads * D; idx += kMWaves * 64) {
+    const int g = idx / D, d = idx % D;
+    if (g >= gvalid) break;  // idx grows with g
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMWaves; ++w) mx = fmaxf(mx, m_sh[w][g]);
+    float num = 0.f, den = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kMWaves; ++w) {
+        const float wt = exp2f(m_sh[w][g] - mx);
+        num += wt * acc_sh[(w * kMHeads + g) * kAccStride + d];
+        den += wt * l_sh[w][g];
+      }
+    }
+    const float o = den > 0.f ? num / den * a.v_scale : 0.f;
+    const float lse = den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+    const int64_t row = (int64_t)b * a.num_q_heads + hbase + g;
+    if (final_out) {
+      store_out<QT>(a.out, row * D + d, o);
+      if (d == 0 && a.lse) a.lse[row] = lse;
+    } else {
+      a.part_o[(row * a.split.max_splits + split) * D + d] = o;
+      if (d == 0) a.part_lse[row * a.split.max_splits + split] = lse;
+    }
+  }
+}
+
+template <class QT, class KT>
+hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStream_t s) {
+  dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.head_tiles), (unsigned)max_splits);
+  dim3 block(kMWaves * 64);
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 256>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim) {
+  const bool pair_ok = (q_dtype == 1 && (kv_dtype == 1 || kv_dtype == 3)) ||
+                       (q_dtype == 2 && (kv_dtype == 2 || kv_dtype == 3));
+  return pair_ok && (head_dim == 64 || head_dim == 128 || head_dim == 256);
+}
+
+hipError_t launch_gqa_mfma(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
+                           int max_splits, hipStream_t s) {
+  if (q_dtype == 1 && kv_dtype == 1) return launch_mfma_qk<F16, F16>(a, head_dim, max_splits, s);
+  if (q_dtype == 2 && kv_dtype == 2) return launch_mfma_qk<BF16, BF16>(a, head_dim, max_splits, s);
+  if (q_dtype == 1 && kv_dtype == 3) return launch_mfma_qk<F16, E4M3>(a, head_dim, max_splits, s);
+  if (q_dtype == 2 && kv_dtype == 3) return launch_mfma_qk<BF16, E4M3>(a, head_dim, max_splits, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pda

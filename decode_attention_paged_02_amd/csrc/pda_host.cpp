@@ -51,6 +51,9 @@ int check_shape(const pda_shape* s, bool mla) {
   } else {
     if (!pda::gqa_supported(s->q_dtype, s->kv_dtype, s->head_dim, s->head_dim_v))
       return PDA_ERR_UNSUPPORTED;
+    if (s->variant < PDA_GQA_DEFAULT || s->variant > PDA_GQA_VALU) return PDA_ERR_INVALID_ARG;
+    if (s->variant == PDA_GQA_MFMA && !pda::gqa_mfma_supported(s->q_dtype, s->kv_dtype, s->head_dim))
+      return PDA_ERR_UNSUPPORTED;
     if (s->page_size % pda::kTileTokens != 0 || (s->page_size & (s->page_size - 1)) != 0)
       return PDA_ERR_UNSUPPORTED;
     if (s->kv_dtype == PDA_FP8_E4M3 && !(s->k_scale > 0.f && s->v_scale > 0.f))
@@ -63,13 +66,26 @@ int check_shape(const pda_shape* s, bool mla) {
   return PDA_OK;
 }
 
+// Smallest group size for which the default GQA variant takes the matrix-core
+// kernel (its 16 head columns are mostly padding below that).
+constexpr int kMfmaMinGroup = 3;
+
+// Whether a (validated) GQA call runs the matrix-core kernel.
+bool gqa_use_mfma(const pda_shape* s) {
+  if (s->variant == PDA_GQA_VALU) return false;
+  if (s->variant == PDA_GQA_MFMA) return true;
+  return pda::gqa_mfma_supported(s->q_dtype, s->kv_dtype, s->head_dim) &&
+         s->num_q_heads / s->num_kv_heads >= kMfmaMinGroup;
+}
+
 int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_plan_info* p) {
   if (!p || num_splits < 0 || num_cus < 0) return PDA_ERR_INVALID_ARG;
   int rc = check_shape(s, mla);
   if (rc != PDA_OK) return rc;
   const int group = s->num_q_heads / s->num_kv_heads;
-  const int head_tiles = mla ? (int)ceil_div(s->num_q_heads, 16)
-                             : (int)ceil_div(group, pda::gqa_tile_heads(group));
+  const int head_tiles = mla             ? (int)ceil_div(s->num_q_heads, 16)
+                         : gqa_use_mfma(s) ? (int)ceil_div(group, 16)
+                                           : (int)ceil_div(group, pda::gqa_tile_heads(group));
   const int64_t units = (int64_t)s->batch * s->num_kv_heads * head_tiles;
   const int max_pages = s->max_pages_per_seq;
 
@@ -193,9 +209,12 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   a.split.split_min_tokens = s.split_min_tokens;
 
   hipStream_t st = (hipStream_t)stream;
-  if (pda::launch_gqa(a, s.q_dtype, s.kv_dtype, s.head_dim, pda::gqa_tile_heads(group),
-                      p.max_splits, st) != hipSuccess)
-    return PDA_ERR_HIP;
+  const hipError_t le =
+      gqa_use_mfma(shape)
+          ? pda::launch_gqa_mfma(a, s.q_dtype, s.kv_dtype, s.head_dim, p.max_splits, st)
+          : pda::launch_gqa(a, s.q_dtype, s.kv_dtype, s.head_dim, pda::gqa_tile_heads(group),
+                            p.max_splits, st);
+  if (le != hipSuccess) return PDA_ERR_HIP;
   if (p.max_splits > 1) {
     pda::CombineArgs c{};
     c.part_o = a.part_o;

@@ -18,7 +18,14 @@ constexpr int kTileTokens = 16;
 #ifndef PDA_GQA_PREFETCH
 #define PDA_GQA_PREFETCH 2
 #endif
+// 1: each lane loads its K rows of a tile in a lane-dependent order so that
+// every step of the score reduce-scatter is a single DPP add (a load
+// instruction then covers pieces of several rows instead of whole rows).
+#ifndef PDA_GQA_PERMUTE_ROWS
+#define PDA_GQA_PERMUTE_ROWS 0
+#endif
 constexpr int kGqaWaves = PDA_GQA_WAVES;
+constexpr bool kGqaPermuteRows = PDA_GQA_PERMUTE_ROWS != 0;
 constexpr int kGqaPrefetch = PDA_GQA_PREFETCH;
 
 // Split layout shared by the attention kernels and the combine kernel.  For
@@ -82,7 +89,11 @@ struct MlaArgs {
 bool gqa_supported(int q_dtype, int kv_dtype, int head_dim, int head_dim_v);
 int gqa_tile_heads(int group);  // query heads per workgroup tile for a group size
 
+bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim);
+
 // Launchers (return the launch error, hipSuccess otherwise).
+hipError_t launch_gqa_mfma(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
+                           int max_splits, hipStream_t stream);
 hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
                       int tile_heads, int max_splits, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t stream);

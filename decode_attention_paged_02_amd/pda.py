@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpda.so")
 
 PDA_F32, PDA_F16, PDA_BF16, PDA_FP8_E4M3 = 0, 1, 2, 3
 PDA_MLA_DEFAULT, PDA_MLA_MFMA, PDA_MLA_VALU = 0, 1, 2
+PDA_GQA_DEFAULT, PDA_GQA_MFMA, PDA_GQA_VALU = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing or too small", 4: "HIP runtime error"}
 
@@ -128,7 +129,7 @@ def plan(shape: Shape, *, mla: bool = False, num_splits: int = 0, num_cus: int =
 
 
 def gqa_shape(q, k_cache, v_cache, block_tables, *, k_scale=1.0, v_scale=1.0,
-              split_min_tokens=0) -> Shape:
+              split_min_tokens=0, variant=0) -> Shape:
     _need(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4, "bad ranks")
     B, Hq, d = q.shape
     num_pages, P, Hkv, dk = k_cache.shape
@@ -138,7 +139,8 @@ def gqa_shape(q, k_cache, v_cache, block_tables, *, k_scale=1.0, v_scale=1.0,
                       head_dim_v=v_cache.shape[3], page_size=P,
                       max_pages_per_seq=block_tables.shape[1], num_pages=num_pages,
                       q_dtype=_dtype_code(q), kv_dtype=_dtype_code(k_cache, fp8_ok=True),
-                      k_scale=k_scale, v_scale=v_scale, split_min_tokens=split_min_tokens)
+                      k_scale=k_scale, v_scale=v_scale, split_min_tokens=split_min_tokens,
+                      variant=variant)
 
 
 def mla_shape(q, kv_cache, block_tables, *, head_dim_v=512, variant=0,
@@ -171,10 +173,10 @@ def workspace_for(shape: Shape, *, mla: bool, num_splits: int, device) -> Option
 def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, scale: float,
                       num_splits: int = 0, out=None, lse=None, k_scale: float = 1.0,
                       v_scale: float = 1.0, split_min_tokens: int = 0, workspace=None,
-                      stream=None, return_lse: bool = True):
+                      stream=None, return_lse: bool = True, variant: int = 0):
     """GQA/MQA/MHA paged decode attention; returns (out [B, Hq, dv], lse [B, Hq] fp32)."""
     shape = gqa_shape(q, k_cache, v_cache, block_tables, k_scale=k_scale, v_scale=v_scale,
-                      split_min_tokens=split_min_tokens)
+                      split_min_tokens=split_min_tokens, variant=variant)
     _check_device(q, k_cache, v_cache, block_tables, context_lens, out, lse, workspace)
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")

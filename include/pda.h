@@ -47,9 +47,10 @@
  *  - Device-resident values are PRECONDITIONS, not checked: 0 <=
  *    context_lens[b] <= max_pages_per_seq * P, and the first
  *    ceil(context_lens[b] / P) entries of block_tables[b] lie in
- *    [0, num_pages).  Entries past those are never read, nor are cache
- *    slots past context_lens[b] in the last page.  context_lens[b] == 0
- *    gives out = 0 and lse = -inf for that sequence.
+ *    [0, num_pages).  Entries past those may be loaded (the table row
+ *    is read in blocks) but never address the cache, whatever they hold;
+ *    cache slots past context_lens[b] in the last page are never read.
+ *    context_lens[b] == 0 gives out = 0 and lse = -inf for that sequence.
  */
 #ifndef PDA_H
 #define PDA_H
@@ -97,6 +98,12 @@ typedef struct pda_shape {
                              /* never split (0: any sequence may split)    */
   int32_t variant;           /* kernel variant, 0 = default (see below)    */
 } pda_shape;
+
+/* GQA kernel variants (pda_shape.variant for paged_decode_attn). */
+#define PDA_GQA_DEFAULT 0 /* matrix cores when available and the group has   */
+                          /* at least 3 query heads, else vector ALUs       */
+#define PDA_GQA_MFMA 1    /* matrix cores (F16/BF16 queries only)           */
+#define PDA_GQA_VALU 2    /* vector dot products                            */
 
 /* MLA kernel variants (pda_shape.variant for paged_decode_attn_mla). */
 #define PDA_MLA_DEFAULT 0 /* the fastest available                          */

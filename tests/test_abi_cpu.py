@@ -61,9 +61,19 @@ def test_plan_explicit_and_threshold():
 
 
 def test_plan_head_tiles():
-    assert pda.plan(_shape(num_q_heads=64, num_kv_heads=8), num_cus=256).head_tiles == 1
-    assert pda.plan(_shape(num_q_heads=96, num_kv_heads=8), num_cus=256).head_tiles == 2
-    assert pda.plan(_shape(num_q_heads=16, num_kv_heads=1), num_cus=256).head_tiles == 2
+    valu = dict(variant=pda.PDA_GQA_VALU)
+    # vector kernel: tiles of up to 8 heads
+    assert pda.plan(_shape(num_q_heads=64, num_kv_heads=8, **valu), num_cus=256).head_tiles == 1
+    assert pda.plan(_shape(num_q_heads=96, num_kv_heads=8, **valu), num_cus=256).head_tiles == 2
+    assert pda.plan(_shape(num_q_heads=16, num_kv_heads=1, **valu), num_cus=256).head_tiles == 2
+    # matrix-core kernel (the default for f16 / bf16 queries and groups >= 3): 16 heads
+    assert pda.plan(_shape(num_q_heads=96, num_kv_heads=8), num_cus=256).head_tiles == 1
+    assert pda.plan(_shape(num_q_heads=16, num_kv_heads=1), num_cus=256).head_tiles == 1
+    assert pda.plan(_shape(num_q_heads=48, num_kv_heads=1), num_cus=256).head_tiles == 3
+    assert pda.plan(_shape(num_q_heads=8, num_kv_heads=8), num_cus=256).head_tiles == 1
+    mf = dict(variant=pda.PDA_GQA_MFMA)
+    assert pda.plan(_shape(num_q_heads=8, num_kv_heads=8, **mf), num_cus=256).head_tiles == 1
+    assert pda.plan(_shape(num_q_heads=24, num_kv_heads=1, **mf), num_cus=256).head_tiles == 2
     p = pda.plan(_shape(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512,
                         page_size=64, q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16),
                  mla=True, num_cus=256)
@@ -81,6 +91,8 @@ def test_plan_head_tiles():
     (dict(kv_dtype=pda.PDA_FP8_E4M3, k_scale=0.0), 1),          # fp8 needs a positive scale
     (dict(batch=-1), 1),
     (dict(q_dtype=7), 1),
+    (dict(variant=3), 1),                                       # no such GQA variant
+    (dict(q_dtype=pda.PDA_F32, kv_dtype=pda.PDA_F32, variant=pda.PDA_GQA_MFMA), 2),
 ])
 def test_invalid_shapes_rejected_before_device_work(kw, status):
     s = _shape(**kw)

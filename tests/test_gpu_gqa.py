@@ -9,11 +9,18 @@ from decode_attention_paged_02_amd import workloads as W
 from gpu_util import check, need_gpu, oracle_ref, say
 
 pytestmark = pytest.mark.gpu
+# both GQA kernels; the matrix-core one takes f16 / bf16 queries only
+VARIANTS = {"mfma": pda.PDA_GQA_MFMA, "valu": pda.PDA_GQA_VALU}
 
 
 @pytest.fixture(autouse=True)
 def _gpu():
     need_gpu()
+
+
+def _skip_unsupported(variant, q_dtype):
+    if variant == "mfma" and q_dtype == "f32":
+        pytest.skip("matrix-core kernel takes f16 / bf16 queries")
 
 
 def _gqa(seed, B, Hq, Hkv, d, P, lens, q_dtype="f16", kv_dtype="f16", **kw):
@@ -37,9 +44,10 @@ def test_gqa_batch64_full_size():
     dev = pda.to_device(case)
     p = pda.plan(pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables))
     assert p.max_splits == 1
-    out, lse = pda.run_case(case, dev)
     ref_o, ref_l = oracle_ref(case)
-    check(case, out, lse, ref_o, ref_l, label=case.name)
+    for name, v in VARIANTS.items():
+        out, lse = pda.run_case(case, dev, variant=v)
+        check(case, out, lse, ref_o, ref_l, label="%s %s" % (case.name, name))
 
 
 @pytest.mark.parametrize("batch", [1, 4])
@@ -50,9 +58,10 @@ def test_gqa_long_context_split(batch):
     dev = pda.to_device(case)
     p = pda.plan(pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables))
     assert p.max_splits > 1
-    out, lse = pda.run_case(case, dev)
     ref_o, ref_l = oracle_ref(case)
-    check(case, out, lse, ref_o, ref_l, label=case.name)
+    for name, v in VARIANTS.items():
+        out, lse = pda.run_case(case, dev, variant=v)
+        check(case, out, lse, ref_o, ref_l, label="%s %s" % (case.name, name))
 
 
 def test_ragged_fp8_sampled_rows():
@@ -64,29 +73,33 @@ def test_ragged_fp8_sampled_rows():
     rows = rng.random((case.batch, case.num_q_heads)) < 0.25
     rows[:3] = True                                    # the forced lengths 1, 16384, 17
     dev = pda.to_device(case)
-    out, lse = pda.run_case(case, dev, num_splits=4, split_min_tokens=4096)
     ref_o, ref_l = oracle_ref(case, rows=rows)
-    check(case, out, lse, ref_o, ref_l, rows=rows, label=case.name)
+    for name, v in VARIANTS.items():
+        out, lse = pda.run_case(case, dev, num_splits=4, split_min_tokens=4096, variant=v)
+        check(case, out, lse, ref_o, ref_l, rows=rows, label="%s %s" % (case.name, name))
 
 
 @pytest.mark.parametrize("lens", [[1], [15, 16, 17], [31, 32, 33, 47], [100, 1, 64, 129]])
 @pytest.mark.parametrize("dt", [("f16", "f16"), ("bf16", "bf16"), ("f32", "f32"),
                                 ("f16", "e4m3"), ("bf16", "e4m3")])
-def test_page_boundaries_and_dtypes(lens, dt):
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_page_boundaries_and_dtypes(lens, dt, variant):
+    _skip_unsupported(variant, dt[0])
     case = _gqa(len(lens) * 7 + len(dt[1]), len(lens), 8, 2, 128, 16, lens, *dt, extra_pages=3)
-    say("boundaries", lens, dt)
-    out, lse = pda.run_case(case)
+    say("boundaries", lens, dt, variant)
+    out, lse = pda.run_case(case, variant=VARIANTS[variant])
     ref_o, ref_l = oracle_ref(case)
     check(case, out, lse, ref_o, ref_l, label="lens=%s %s" % (lens, dt))
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (16, 1), (12, 4), (24, 4), (48, 4),
                                     (64, 8), (32, 2)])
-def test_group_sizes(Hq, Hkv):
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_group_sizes(Hq, Hkv, variant):
     """G=1 (MHA), MQA (Hkv=1), non-power-of-two groups (padded head tiles), G=16."""
     case = _gqa(Hq * 100 + Hkv, 3, Hq, Hkv, 128, 16, [5, 200, 77], extra_pages=2)
-    say("groups", Hq, Hkv)
-    out, lse = pda.run_case(case)
+    say("groups", Hq, Hkv, variant)
+    out, lse = pda.run_case(case, variant=VARIANTS[variant])
     ref_o, ref_l = oracle_ref(case)
     check(case, out, lse, ref_o, ref_l, label="Hq=%d Hkv=%d" % (Hq, Hkv))
 
@@ -94,44 +107,49 @@ def test_group_sizes(Hq, Hkv):
 @pytest.mark.parametrize("d,P,dt", [(64, 16, "f16"), (64, 32, "bf16"), (256, 16, "f16"),
                                     (128, 64, "f16"), (64, 16, "f32"), (128, 32, "f32"),
                                     (256, 16, "bf16")])
-def test_head_dims_and_page_sizes(d, P, dt):
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_head_dims_and_page_sizes(d, P, dt, variant):
+    _skip_unsupported(variant, dt)
     case = _gqa(d + P, 2, 16, 4, d, P, [333, 70], dt, dt, extra_pages=2)
-    say("d/P", d, P, dt)
+    say("d/P", d, P, dt, variant)
     for s in (1, 3):
-        out, lse = pda.run_case(case, num_splits=s)
+        out, lse = pda.run_case(case, num_splits=s, variant=VARIANTS[variant])
         ref_o, ref_l = oracle_ref(case)
         check(case, out, lse, ref_o, ref_l, label="d=%d P=%d %s S=%d" % (d, P, dt, s))
 
 
-def test_split_counts_agree_and_runs_are_deterministic():
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_split_counts_agree_and_runs_are_deterministic(variant):
     case = _gqa(9, 2, 32, 8, 128, 16, [4000, 2500])
-    say("split invariance")
+    say("split invariance", variant)
     dev = pda.to_device(case)
     ref_o, ref_l = oracle_ref(case)
     outs = {}
     for s in (1, 2, 5, 16, 250):
-        out, lse = pda.run_case(case, dev, num_splits=s)
+        out, lse = pda.run_case(case, dev, num_splits=s, variant=VARIANTS[variant])
         check(case, out, lse, ref_o, ref_l, label="S=%d" % s)
-        out2, lse2 = pda.run_case(case, dev, num_splits=s)
+        out2, lse2 = pda.run_case(case, dev, num_splits=s, variant=VARIANTS[variant])
         assert torch.equal(out, out2) and torch.equal(lse, lse2), "run-to-run differs"
         outs[s] = out.float()
     for s in outs:
         assert (outs[s] - outs[1]).abs().max().item() < 2e-3
 
 
-def test_split_threshold():
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_split_threshold(variant):
     """Sequences at or below split_min_tokens are never split; longer ones are."""
     case = _gqa(10, 4, 16, 4, 128, 16, [4096, 4097, 100, 9000], extra_pages=1)
-    say("split threshold")
+    say("split threshold", variant)
     ref_o, ref_l = oracle_ref(case)
-    out, lse = pda.run_case(case, num_splits=8, split_min_tokens=4096)
+    out, lse = pda.run_case(case, num_splits=8, split_min_tokens=4096, variant=VARIANTS[variant])
     check(case, out, lse, ref_o, ref_l, label="threshold")
 
 
-def test_page_permutation_bit_identical():
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_page_permutation_bit_identical(variant):
     case = _gqa(11, 3, 16, 4, 128, 16, [90, 300, 17], extra_pages=9)
-    say("permutation")
-    out1, lse1 = pda.run_case(case)
+    say("permutation", variant)
+    out1, lse1 = pda.run_case(case, variant=VARIANTS[variant])
     perm = np.random.default_rng(3).permutation(case.num_pages)
     inv = np.argsort(perm)
     case.k_cache = case.k_cache[perm].copy()
@@ -139,35 +157,38 @@ def test_page_permutation_bit_identical():
     bt = case.block_tables.copy()
     bt[bt >= 0] = inv[bt[bt >= 0]]
     case.block_tables = bt
-    out2, lse2 = pda.run_case(case)
+    out2, lse2 = pda.run_case(case, variant=VARIANTS[variant])
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
 
 
-def test_poisoned_slots_and_table_tail_never_read():
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_poisoned_slots_and_table_tail_never_used(variant):
     """Unused pages and stale slots hold NaN, table tails hold -1 (the generator's
     poison); on top, fill every table entry past the context with a huge index."""
     case = _gqa(12, 4, 16, 4, 128, 16, [1, 17, 250, 33], extra_pages=6, max_pages=40)
     case.block_tables[case.block_tables < 0] = 2 ** 30
-    say("poison")
-    out, lse = pda.run_case(case)
+    say("poison", variant)
+    out, lse = pda.run_case(case, variant=VARIANTS[variant])
     assert torch.isfinite(out).all()
     ref_o, ref_l = oracle_ref(case)   # the oracle reports any out-of-range entry it reads
     check(case, out, lse, ref_o, ref_l, label="poison")
 
 
-def test_empty_sequence_and_no_lse():
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_empty_sequence_and_no_lse(variant):
     case = _gqa(13, 3, 8, 2, 128, 16, [0, 5, 40], extra_pages=1)
-    say("empty sequence")
-    out, lse = pda.run_case(case)
+    say("empty sequence", variant)
+    out, lse = pda.run_case(case, variant=VARIANTS[variant])
     o = out.float().cpu()
     assert (o[0] == 0).all() and torch.isinf(lse[0]).all() and (lse[0] < 0).all()
     ref_o, ref_l = oracle_ref(case)
     check(case, out, lse, ref_o, ref_l, label="empty")
-    out2, lse2 = pda.run_case(case, return_lse=False)
+    out2, lse2 = pda.run_case(case, return_lse=False, variant=VARIANTS[variant])
     assert lse2 is None and torch.equal(out, out2)
 
 
-def test_large_pool_64bit_offsets():
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_large_pool_64bit_offsets(variant):
     """Physical pages beyond 4 GiB of the pool (int64 page addressing)."""
     B, Hkv, d, P = 2, 1, 128, 16
     lens = [100, 37]
@@ -183,7 +204,7 @@ def test_large_pool_64bit_offsets():
     bt = torch.from_numpy(small.block_tables + base).cuda()
     q = torch.from_numpy(small.q).cuda()
     cl = torch.from_numpy(small.context_lens).cuda()
-    out, lse = pda.paged_decode_attn(q, k, v, bt, cl, scale=small.scale)
+    out, lse = pda.paged_decode_attn(q, k, v, bt, cl, scale=small.scale, variant=VARIANTS[variant])
     ref_o, ref_l = oracle_ref(small)
     check(small, out, lse, ref_o, ref_l, label="large pool")
     del k, v
