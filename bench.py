@@ -48,7 +48,7 @@ def make_case(name):
     raise SystemExit("unknown workload %s" % name)
 
 
-CALL_KW = {"ragged_fp8": dict(num_splits=4, split_min_tokens=4096)}
+CALL_KW = {"ragged_fp8": dict(num_splits=8, split_min_tokens=4096)}
 
 
 def measured_traffic(workload: str, launches_per_step: int):

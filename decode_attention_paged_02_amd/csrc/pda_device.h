@@ -46,6 +46,13 @@ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
 
+// A 32-bit value the kernel never writes, read with a scalar load (through
+// the constant address space) so that uniform control flow can wait for it
+// where it is first used.
+__device__ __forceinline__ int load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // Cache policy of the K/V stream loads (the buffer instruction's cache-policy
 // field; 2 marks them non-temporal).
 #ifndef PDA_KV_LOAD_POLICY

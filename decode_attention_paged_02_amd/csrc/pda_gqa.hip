@@ -133,8 +133,19 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
     const int64_t pg = tok >> log2P;
     return table[pg < a.max_pages ? pg : a.max_pages - 1];
   };
-  const int n = a.context_lens[b];
+  // With ragged lengths most workgroups past split 0 have no pages to read:
+  // those decide on the length alone and leave without further loads.  Split
+  // 0 always has work (or an empty sequence) and requests its length along
+  // with the table entries and q.
+  int n = 0;
+  if (split > 0) {
+    n = load_uniform(a.context_lens + b);
+    int ns, ta, tb;
+    split_range(a.split, n, a.page_size, split, ns, ta, tb);
+    if (split >= ns) return;
+  }
   int vtbl = load_table(0);
+  if (split == 0) n = load_uniform(a.context_lens + b);
 
   // q of the tile's heads (slot g holds head g ^ flip_head), the EPL elements
   // this lane multiplies.  Heads past the group are loaded from a valid row
@@ -157,6 +168,7 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
     }
   }
 
+  __builtin_amdgcn_sched_barrier(0);  // the loads above go out before waiting for n
   int nsplit, t0, t1;
   split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
   if (split >= nsplit) return;
@@ -330,8 +342,9 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   // Deep rows (d = 256, or fp32 at d = 128) keep one tile in flight, so the
   // ring stays within ~96 registers.
   constexpr int kTileRegs = 2 * NLD * (int)(sizeof(frag_t) / 4);
-  constexpr int kPF = (96 / kTileRegs - 1) < 1 ? 1
-                      : ((96 / kTileRegs - 1) < kGqaPrefetch ? (96 / kTileRegs - 1) : kGqaPrefetch);
+  constexpr int kPF = (kGqaRingRegs / kTileRegs - 1) < 1 ? 1
+                      : ((kGqaRingRegs / kTileRegs - 1) < kGqaPrefetch ? (kGqaRingRegs / kTileRegs - 1)
+                                                                       : kGqaPrefetch);
   constexpr int NB = kPF + 1;
   frag_t kb[NB][NLD], vb[NB][NLD];
   int rows_b[NB];

@@ -99,6 +99,28 @@ __device__ __forceinline__ uint32_t fp8_pair(uint32_t x, bool hi) {
   }
 }
 
+// N consecutive outputs (N = 4, 8 or 16) in the query's 16-bit type, rounded
+// to nearest even, with 8- or 16-byte stores.
+template <class QT, int N>
+__device__ __forceinline__ void store_row(void* out, int64_t i, const float (&o)[N]) {
+  uint32_t w[N / 2];
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    if constexpr (std::is_same<QT, F16>::value) {
+      w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{o[2 * k], o[2 * k + 1]}), f16x2));
+    } else {
+      w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{o[2 * k], o[2 * k + 1]}), bf16x2));
+    }
+  }
+  char* p = (char*)out + i * 2;
+  if constexpr (N == 4) {
+    *(u32x2*)p = u32x2{w[0], w[1]};
+  } else {
+#pragma unroll
+    for (int k = 0; k < N / 2; k += 4) *(u32x4*)(p + 4 * k) = u32x4{w[k], w[k + 1], w[k + 2], w[k + 3]};
+  }
+}
+
 template <class QT>
 __device__ __forceinline__ f32x4 mfma_qk(const u32x4& k, const u32x4& q, f32x4 c) {
   if constexpr (std::is_same<QT, F16>::value) {
@@ -133,7 +155,11 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
   constexpr bool kBf16 = std::is_same<QT, BF16>::value;
   constexpr int kAccStride = D + 4;             // floats per head row of the merge area
   constexpr int kMergeB = kMWaves * kMHeads * kAccStride * 4;
-  constexpr int kLdsB = kMWaves * kTileB > kMergeB ? kMWaves * kTileB : kMergeB;
+  // the merge area gets its own LDS when both fit two workgroups per CU
+  constexpr bool kSeparateMerge = kMWaves * kTileB + kMergeB <= 72 * 1024;
+  constexpr int kMergeOff = kSeparateMerge ? kMWaves * kTileB : 0;
+  constexpr int kLdsB = kSeparateMerge ? kMWaves * kTileB + kMergeB
+                        : (kMWaves * kTileB > kMergeB ? kMWaves * kTileB : kMergeB);
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
   static_assert(kFp8 || std::is_same<QT, KT>::value, "q / cache types");
 
@@ -167,15 +193,31 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
   const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
   const int t0_hint = a.split.max_splits > 1 ? split * a.split.pages_per_split << log2P : 0;
 
-  // sequence length, block-table entries (lane j: tile ordinal kbase + j,
-  // clamped into the row, unused past the sequence) and q, requested together
-  auto load_table = [&](int kbase) -> int {
-    const int64_t tok = (int64_t)t0_hint + (int64_t)(wave + (kbase + lane) * kMWaves) * kTileTokens;
+  // The range is walked in steps of ST consecutive tiles; wave w takes steps
+  // w, w + kMWaves, ...  Sequence length, block-table entries (lane j: tile
+  // j % ST of the wave's step sbase + j / ST, clamped into the row, unused
+  // past the sequence) and q are requested together.
+  constexpr int ST = kGqaStepTiles;
+  constexpr int kStepsPerChunk = 64 / ST;
+  auto load_table = [&](int sbase) -> int {
+    const int T = (wave + (sbase + lane / ST) * kMWaves) * ST + lane % ST;
+    const int64_t tok = (int64_t)t0_hint + (int64_t)T * kTileTokens;
     const int64_t pg = tok >> log2P;
     return table[pg < a.max_pages ? pg : a.max_pages - 1];
   };
-  const int n = a.context_lens[b];
+  // With ragged lengths most workgroups past split 0 have no pages to read:
+  // those decide on the length alone and leave without further loads.  Split
+  // 0 always has work (or an empty sequence) and requests its length along
+  // with the table entries and q.
+  int n = 0;
+  if (split > 0) {
+    n = load_uniform(a.context_lens + b);
+    int ns, ta, tb;
+    split_range(a.split, n, a.page_size, split, ns, ta, tb);
+    if (split >= ns) return;
+  }
   int vtbl = load_table(0);
+  if (split == 0) n = load_uniform(a.context_lens + b);
 
   // Q^T as the B operand of the QK MFMAs: lane (col, grp) holds
   // q[head col][32 j + 8 grp .. +8] for MFMA j; heads past the group are zero
@@ -190,6 +232,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
     }
   }
 
+  __builtin_amdgcn_sched_barrier(0);  // the loads above go out before waiting for n
   int nsplit, t0, t1;
   split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
   if (split >= nsplit) return;
@@ -205,7 +248,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
   const float pinf = opaque_inf();
 
   const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
-  const int nt_wave = ntiles > wave ? (ntiles - wave + kMWaves - 1) / kMWaves : 0;
+  const int nsteps = (ntiles + ST - 1) / ST;
+  const int ns_wave = nsteps > wave ? (nsteps - wave + kMWaves - 1) / kMWaves : 0;
 
   char* ktile = lds + wave * kTileB;
 
@@ -306,61 +350,67 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
     }
   };
 
-  // ring of register buffers, tiles in chunks of 64 ordinals (one table entry
-  // per lane), as in gqa_split_kernel
-  constexpr int kTileRegs = 8 * PW;
-  constexpr int kPF = (96 / kTileRegs - 1) < 1 ? 1
-                      : ((96 / kTileRegs - 1) < kGqaPrefetch ? (96 / kTileRegs - 1) : kGqaPrefetch);
-  constexpr int NB = kPF + 1;
-  Words<PW> kb[NB][4], vb[NB][4];
-  int rows_b[NB];
-  auto issue = [&](int k, int kend, int u) {
-    const bool live = k < kend;
-    const int entry = __builtin_amdgcn_readlane(vtbl, k & 63);
-    const int phys = live ? entry : 0;
-    const int T = wave + k * kMWaves;
-    const int tok = t0 + T * kTileTokens;
-    const int rows = live ? min(kTileTokens, t1 - tok) : 0;
-    rows_b[u] = rows;
-    const int slot = tok & ((1 << log2P) - 1);
-    const int64_t elem = (int64_t)phys * a.page_stride + (int64_t)slot * a.tok_stride;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)a.k_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)a.v_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
+  // Steps in flight per wave: SD (1: a step's loads are issued right before
+  // it is computed; other waves cover the latency).  Each step issues the
+  // loads of its ST tiles back to back.  Steps are grouped in chunks of
+  // kStepsPerChunk (one table entry per lane per tile).
+  constexpr int SD = kGqaStepsInFlight;
+  Words<PW> kb[SD][ST][4], vb[SD][ST][4];
+  int rows_b[SD][ST];
+  auto issue = [&](int sidx, int send, int u) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kb[u][j] = load_piece<PW>(rk, off0 + j * tok_bytes);
-      vb[u][j] = load_piece<PW>(rv, off0 + j * tok_bytes);
+    for (int t = 0; t < ST; ++t) {
+      const int T = (wave + sidx * kMWaves) * ST + t;
+      const bool live = sidx < send && T < ntiles;
+      const int entry = __builtin_amdgcn_readlane(vtbl, ((sidx % kStepsPerChunk) * ST + t) & 63);
+      const int phys = live ? entry : 0;
+      const int tok = t0 + T * kTileTokens;
+      const int rows = live ? min(kTileTokens, t1 - tok) : 0;
+      rows_b[u][t] = rows;
+      const int slot = tok & ((1 << log2P) - 1);
+      const int64_t elem = (int64_t)phys * a.page_stride + (int64_t)slot * a.tok_stride;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const char*)a.k_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const char*)a.v_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kb[u][t][j] = load_piece<PW>(rk, off0 + j * tok_bytes);
+        vb[u][t][j] = load_piece<PW>(rv, off0 + j * tok_bytes);
+      }
     }
   };
-  for (int kbase = 0; kbase < nt_wave;) {
-    const int kend = min(kbase + 64, nt_wave);
-    // (in order: the loop's wait counts assume the oldest tile is issued first)
+  for (int sbase = 0; sbase < ns_wave;) {
+    const int send = min(sbase + kStepsPerChunk, ns_wave);
+    // (in order: the loop's wait counts assume the oldest step is issued first)
 #pragma unroll
-    for (int u = 0; u < kPF; ++u) {
-      issue(kbase + u, kend, u);
+    for (int u = 0; u < SD - 1; ++u) {
+      issue(sbase + u, send, u);
       __builtin_amdgcn_sched_barrier(0);
     }
-    for (int kc = kbase;; kc += NB) {
+    for (int sc = sbase;; sc += SD) {
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int k = kc + u;
-        if (k >= kend) goto chunk_done;
-        issue(k + kPF, kend, (u + kPF) % NB);
-        compute_tile(kb[u], vb[u], rows_b[u]);
+      for (int u = 0; u < SD; ++u) {
+        const int sidx = sc + u;
+        if (sidx >= send) goto chunk_done;
+        issue(sidx + SD - 1, send, (u + SD - 1) % SD);
+        __builtin_amdgcn_sched_barrier(0);  // all of a step's loads go out before any wait
+        // (a step's tiles past the range are computed on zero rows, fully
+        // masked: no branch that would let the compiler sink their loads)
+#pragma unroll
+        for (int t = 0; t < ST; ++t) compute_tile(kb[u][t], vb[u][t], rows_b[u][t]);
       }
     }
   chunk_done:
-    kbase = kend;
-    if (kbase < nt_wave) vtbl = load_table(kbase);
+    sbase = send;
+    if (sbase < ns_wave) vtbl = load_table(sbase);
   }
 
-  // ---- merge the four waves (the split-combine algebra) through LDS; the
-  // merge area overlays the K tiles, so every wave must be done with them
+  // ---- merge the four waves (the split-combine algebra) through LDS.  When
+  // the merge area overlays the K tiles, every wave must be done with them.
   l_run = pair_sum<5>(pair_sum<4>(l_run));
-  __syncthreads();
-  float* acc_sh = (float*)lds;  // [wave][head][kAccStride]
+  if constexpr (!kSeparateMerge) __syncthreads();
+  float* acc_sh = (float*)(lds + kMergeOff);  // [wave][head][kAccStride]
   if (grp == 0) {
     m_sh[wave][col] = m_run;
     l_sh[wave][col] = l_run;
@@ -376,32 +426,47 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
   }
   __syncthreads();
 
-  const bool final_out = nsplit == 1;
-  for (int idx = threadIdx.x; idx < kMHeads * D; idx += kMWaves * 64) {
-    const int g = idx / D, d = idx % D;
-    if (g >= gvalid) break;  // idx grows with g
-    float mx = -INFINITY;
+  // thread t: head t / 16, values [NE (t % 16), NE (t % 16 + 1)); the four
+  // waves' weights exp2(m_w - max) and the normalizer are formed once per head
+  const int g = threadIdx.x >> 4, c16 = threadIdx.x & 15;
+  if (g >= gvalid) return;
+  float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kMWaves; ++w) mx = fmaxf(mx, m_sh[w][g]);
-    float num = 0.f, den = 0.f;
-    if (mx != -INFINITY) {
+  for (int w = 0; w < kMWaves; ++w) mx = fmaxf(mx, m_sh[w][g]);
+  float wt[kMWaves], den = 0.f;
 #pragma unroll
-      for (int w = 0; w < kMWaves; ++w) {
-        const float wt = exp2f(m_sh[w][g] - mx);
-        num += wt * acc_sh[(w * kMHeads + g) * kAccStride + d];
-        den += wt * l_sh[w][g];
-      }
+  for (int w = 0; w < kMWaves; ++w) {
+    wt[w] = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_sh[w][g] - mx);
+    den += wt[w] * l_sh[w][g];
+  }
+  const float inv = den > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(den) : 0.f;
+  float o[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMWaves; ++w) {
+    const float* src = acc_sh + (w * kMHeads + g) * kAccStride + c16 * NE;
+#pragma unroll
+    for (int e = 0; e < NE; e += 4) {
+      const f32x4 x = *(const f32x4*)(src + e);
+      o[e] += wt[w] * x.x;
+      o[e + 1] += wt[w] * x.y;
+      o[e + 2] += wt[w] * x.z;
+      o[e + 3] += wt[w] * x.w;
     }
-    const float o = den > 0.f ? num / den * a.v_scale : 0.f;
-    const float lse = den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
-    const int64_t row = (int64_t)b * a.num_q_heads + hbase + g;
-    if (final_out) {
-      store_out<QT>(a.out, row * D + d, o);
-      if (d == 0 && a.lse) a.lse[row] = lse;
-    } else {
-      a.part_o[(row * a.split.max_splits + split) * D + d] = o;
-      if (d == 0) a.part_lse[row * a.split.max_splits + split] = lse;
-    }
+  }
+#pragma unroll
+  for (int e = 0; e < NE; ++e) o[e] *= inv;
+  const float lse = den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+  const int64_t row = (int64_t)b * a.num_q_heads + hbase + g;
+  if (nsplit == 1) {
+    store_row<QT, NE>(a.out, row * D + c16 * NE, o);
+    if (c16 == 0 && a.lse) a.lse[row] = lse;
+  } else {
+    float* po = a.part_o + (row * a.split.max_splits + split) * D + c16 * NE;
+#pragma unroll
+    for (int e = 0; e < NE; e += 4) *(f32x4*)(po + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+    if (c16 == 0) a.part_lse[row * a.split.max_splits + split] = lse;
   }
 }
 

@@ -18,6 +18,19 @@ constexpr int kTileTokens = 16;
 #ifndef PDA_GQA_PREFETCH
 #define PDA_GQA_PREFETCH 2
 #endif
+// Matrix-core GQA kernel: tiles per step (loads of a step are issued back to
+// back) and steps in flight per wave (1: no prefetch beyond the current step).
+#ifndef PDA_GQA_STEP_TILES
+#define PDA_GQA_STEP_TILES 1
+#endif
+#ifndef PDA_GQA_STEPS_IN_FLIGHT
+#define PDA_GQA_STEPS_IN_FLIGHT 3
+#endif
+// Registers the GQA kernels may spend on the ring of in-flight tiles (caps
+// the prefetch depth for wide rows).
+#ifndef PDA_GQA_RING_REGS
+#define PDA_GQA_RING_REGS 96
+#endif
 // 1: each lane loads its K rows of a tile in a lane-dependent order so that
 // every step of the score reduce-scatter is a single DPP add (a load
 // instruction then covers pieces of several rows instead of whole rows).
@@ -27,6 +40,9 @@ constexpr int kTileTokens = 16;
 constexpr int kGqaWaves = PDA_GQA_WAVES;
 constexpr bool kGqaPermuteRows = PDA_GQA_PERMUTE_ROWS != 0;
 constexpr int kGqaPrefetch = PDA_GQA_PREFETCH;
+constexpr int kGqaRingRegs = PDA_GQA_RING_REGS;
+constexpr int kGqaStepTiles = PDA_GQA_STEP_TILES;
+constexpr int kGqaStepsInFlight = PDA_GQA_STEPS_IN_FLIGHT;
 
 // Split layout shared by the attention kernels and the combine kernel.  For
 // sequence b with n = context_lens[b] tokens and pages = ceil(n / P):

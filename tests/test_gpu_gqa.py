@@ -66,7 +66,7 @@ def test_gqa_long_context_split(batch):
 
 def test_ragged_fp8_sampled_rows():
     """B=128, log-uniform lengths in [1, 16384], Hq=64, Hkv=8, fp8-e4m3 cache with
-    per-tensor scales, fp16 q; sequences longer than 4096 tokens split."""
+    per-tensor scales, fp16 q; sequences longer than 4096 tokens split (up to 8 ways)."""
     case = W.ragged_fp8()
     say(case.name)
     rng = np.random.default_rng(5)
@@ -75,7 +75,7 @@ def test_ragged_fp8_sampled_rows():
     dev = pda.to_device(case)
     ref_o, ref_l = oracle_ref(case, rows=rows)
     for name, v in VARIANTS.items():
-        out, lse = pda.run_case(case, dev, num_splits=4, split_min_tokens=4096, variant=v)
+        out, lse = pda.run_case(case, dev, num_splits=8, split_min_tokens=4096, variant=v)
         check(case, out, lse, ref_o, ref_l, rows=rows, label="%s %s" % (case.name, name))
 
 
