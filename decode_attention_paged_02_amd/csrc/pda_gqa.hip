@@ -443,28 +443,35 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
 
 constexpr int kCombineThreads = 256;
 
-// One workgroup per (sequence, query head) row whose sequence was split:
+// One workgroup per (sequence, query head) row whose sequence was split and
+// per CW-wide column chunk of it (CW = min(DV, 128)):
 // L = M + ln sum_s exp(L_s - M), O = sum_s exp(L_s - M) O_s / sum_s exp(L_s - M)
 // with M = max_s L_s ("From MHA to MLA" sec. 4).  Rows of unsplit sequences
 // were written by the attention kernel and are skipped.  The threads form
-// kCombineThreads / (DV / 4) split groups x (DV / 4) four-float chunks of the
-// row; each group weights its splits against its own maximum, and the groups
-// are merged through LDS with the same algebra.  The sequence length and the
-// first partials are loaded together, so the row costs one memory round trip.
+// kCombineThreads / (CW / 4) split groups x (CW / 4) four-float chunks; each
+// group weights its splits against its own maximum, and the groups are
+// merged through LDS with the same algebra.  The sequence length and the
+// first partials are loaded together, so a chunk costs one memory round trip
+// for up to MAXL splits per group.
 template <class OT, int DV>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
-  constexpr int DC = DV / 4;                    // float4 chunks per row
+  constexpr int CW = DV > 128 ? 128 : DV;       // columns per workgroup
+  constexpr int NCH = DV / CW;                  // column chunks per row
+  constexpr int DC = CW / 4;                    // float4 chunks per workgroup
   constexpr int SG = kCombineThreads / DC;      // split groups
   constexpr int MAXL = 8;                       // splits a thread keeps in flight
-  static_assert(DC * SG == kCombineThreads, "row width");
+  static_assert(DC * SG == kCombineThreads && NCH * CW == DV, "row width");
   __shared__ f32x4 acc_sh[SG][DC];
   __shared__ float den_sh[SG], mx_sh[SG];
 
-  const int64_t row = blockIdx.x;
+  const int64_t row = blockIdx.x / NCH;
+  const int chunk = blockIdx.x % NCH;
   const int b = (int)(row / a.num_q_heads);
   const int S = a.split.max_splits;
   const float* pl = a.part_lse + row * S;
-  const f32x4* po = (const f32x4*)(a.part_o + row * S * DV);
+  // split s of this chunk starts at float4 index s * (DV / 4)
+  const f32x4* po = (const f32x4*)(a.part_o + row * S * DV + chunk * CW);
+  constexpr int SSTR = DV / 4;
   const int sg = threadIdx.x / DC, dc = threadIdx.x % DC;
 
   // Issue the sequence length and this thread's first MAXL partials together
@@ -476,7 +483,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   for (int j = 0; j < MAXL; ++j) {
     const int s2 = sg + j * SG;
     l[j] = s2 < S ? pl[s2] : -INFINITY;
-    o[j] = s2 < S ? po[(int64_t)s2 * DC + dc] : f32x4{0.f, 0.f, 0.f, 0.f};
+    o[j] = s2 < S ? po[(int64_t)s2 * SSTR + dc] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   int nsplit, t0, t1;
   split_range(a.split, n, a.page_size, 0, nsplit, t0, t1);
@@ -504,7 +511,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
       if (ls == -INFINITY) continue;
       const float w = __expf(ls - mx);
       den += w;
-      acc += w * po[(int64_t)s2 * DC + dc];
+      acc += w * po[(int64_t)s2 * SSTR + dc];
     }
   }
   acc_sh[sg][dc] = acc;
@@ -530,12 +537,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
       }
     }
     const float inv = d > 0.f ? 1.f / d : 0.f;
-    const int64_t o0 = row * DV + threadIdx.x * 4;
+    const int64_t o0 = row * DV + chunk * CW + threadIdx.x * 4;
     store_out<OT>(a.out, o0, t.x * inv);
     store_out<OT>(a.out, o0 + 1, t.y * inv);
     store_out<OT>(a.out, o0 + 2, t.z * inv);
     store_out<OT>(a.out, o0 + 3, t.w * inv);
-    if (threadIdx.x == 0 && a.lse) a.lse[row] = d > 0.f ? M + __logf(d) : -INFINITY;
+    if (threadIdx.x == 0 && chunk == 0 && a.lse) a.lse[row] = d > 0.f ? M + __logf(d) : -INFINITY;
   }
 }
 
@@ -597,7 +604,8 @@ hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
 
 template <class OT>
 hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)(a.batch * a.num_q_heads));
+  const int nch = a.head_dim_v > 128 ? a.head_dim_v / 128 : 1;
+  dim3 grid((unsigned)(a.batch * a.num_q_heads * nch));
   dim3 block(kCombineThreads);
   switch (a.head_dim_v) {
     case 64: hipLaunchKernelGGL((combine_kernel<OT, 64>), grid, block, 0, s, a); break;

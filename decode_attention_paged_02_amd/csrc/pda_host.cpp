@@ -263,6 +263,8 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
   a.head_tiles = p.head_tiles;
   a.page_size = s.page_size;
   a.max_pages = s.max_pages_per_seq;
+  a.log2_page = 0;
+  while ((1 << a.log2_page) < s.page_size) ++a.log2_page;
   a.qk_scale_log2 = scale * 1.4426950408889634f;
   a.split.pages_per_split = p.pages_per_split;
   a.split.max_splits = p.max_splits;

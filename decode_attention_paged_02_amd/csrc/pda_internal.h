@@ -97,6 +97,7 @@ struct MlaArgs {
   float* part_lse;
   int32_t batch, num_q_heads, head_tiles;
   int32_t page_size, max_pages;
+  int32_t log2_page;       // page_size == 1 << log2_page
   float qk_scale_log2;     // scale * log2(e)
   SplitLayout split;
 };

@@ -73,6 +73,11 @@ __device__ __forceinline__ void split_range(const SplitLayout& sp, int n, int P,
   }
 }
 
+// A 32-bit value the kernel never writes, read with a scalar load.
+__device__ __forceinline__ int load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
@@ -110,6 +115,25 @@ __device__ __forceinline__ float sum_x4(float x) {
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kRowBytes + 16 * (c ^ swz(r)); }
 
+// Block-table entries of a workgroup's range, one per lane: lane j holds the
+// entry of page base + j (clamped into the table row; entries past the
+// sequence are loaded but never used).  A block's page is then a lane read.
+struct PageTable {
+  const int32_t* row;
+  int max_pages, base, entries;
+
+  __device__ __forceinline__ void load(int page0, int lane) {
+    base = page0;
+    const int p = min(page0 + lane, max_pages - 1);
+    entries = row[p];
+  }
+  // entry of page p (p >= base); moves the window when p is past it
+  __device__ __forceinline__ int entry(int p, int lane) {
+    if (p - base >= 64) load(p, lane);
+    return __builtin_amdgcn_readlane(entries, p - base);
+  }
+};
+
 // Shared block staging: the workgroup's 256 threads bring one block of 32
 // records (36 KiB) into registers with 16-byte loads, then into LDS.
 struct BlockLoader {
@@ -117,13 +141,13 @@ struct BlockLoader {
 
   // Load block `blk` of the range [t0, t1) (tokens t0 + 32 blk ...).  Rows
   // past t1 (and a block past the range) read as zero without memory access.
-  __device__ __forceinline__ void load(const MlaArgs& a, const int32_t* table, int t0, int t1,
-                                       int blk, int log2P, int tid) {
+  __device__ __forceinline__ void load(const MlaArgs& a, PageTable& pt, int t0, int t1, int blk,
+                                       int log2P, int tid) {
     const int tok = t0 + blk * kBlock;
-    const int rows = max(0, min(kBlock, t1 - tok));
-    int phys = 0;
-    if (rows > 0) phys = table[tok >> log2P];
-    phys = __builtin_amdgcn_readfirstlane(phys);
+    // (uniform; read into a scalar register so the resource stays scalar)
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kBlock, t1 - tok)));
+    const int e = pt.entry(tok >> log2P, tid & 63);
+    const int phys = rows > 0 ? e : 0;
     const int slot = tok & ((1 << log2P) - 1);
     const int64_t rec0 = (int64_t)phys * a.page_size + slot;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -170,12 +194,24 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   const int tile = blockIdx.x % a.head_tiles;
   const int b = blockIdx.x / a.head_tiles;
   const int split = blockIdx.y;
-  const int n = a.context_lens[b];
-  int nsplit, t0, t1;
-  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
-  if (split >= nsplit) return;
-  int log2P = 0;
-  while ((1 << log2P) < a.page_size) ++log2P;
+  // One batch of kernel-argument loads; then the sequence length, the
+  // range's block-table entries and q are requested together (workgroups past
+  // split 0 first check on the length alone whether they have pages at all).
+  asm volatile("" ::"s"(a.q), "s"(a.kv_cache), "s"(a.block_tables), "s"(a.context_lens),
+               "s"(a.num_q_heads), "s"(a.head_tiles), "s"(a.page_size), "s"(a.max_pages),
+               "s"(a.log2_page), "s"(a.qk_scale_log2), "s"(a.split.pages_per_split),
+               "s"(a.split.max_splits), "s"(a.split.split_min_tokens));
+  const int log2P = a.log2_page;
+  int n = 0;
+  if (split > 0) {
+    n = load_uniform(a.context_lens + b);
+    int ns, ta, tb;
+    split_range(a.split, n, a.page_size, split, ns, ta, tb);
+    if (split >= ns) return;
+  }
+  PageTable pt{a.block_tables + (int64_t)b * a.max_pages, a.max_pages, 0, 0};
+  pt.load(a.split.max_splits > 1 ? split * a.split.pages_per_split : 0, lane);
+  if (split == 0) n = load_uniform(a.context_lens + b);
 
   const int h = tile * kHeads + col;
   const bool hvalid = h < a.num_q_heads;
@@ -185,18 +221,23 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   const int c_lo = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
   const int n_w = wave < 2 ? 5 : 4;
   // Q^T as the B operand: lane (col, grp) holds q[h][32 (c_lo + j) + 8 grp + 0..7]
+  // (loaded from valid addresses without branches, then zeroed where unused)
   bf16x8 qb[5];
   {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * a.num_q_heads + h) * kRec;
+    const uint16_t* qrow =
+        (const uint16_t*)a.q + ((int64_t)b * a.num_q_heads + (hvalid ? h : 0)) * kRec;
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (hvalid && j < n_w) w = *(const u32x4*)(qrow + 32 * (c_lo + j) + 8 * grp);
-      qb[j] = __builtin_bit_cast(bf16x8, w);
+      const bool use = hvalid && j < n_w;
+      const u32x4 w = *(const u32x4*)(qrow + 32 * (c_lo + (j < n_w ? j : 0)) + 8 * grp);
+      qb[j] = __builtin_bit_cast(bf16x8, use ? w : u32x4{0u, 0u, 0u, 0u});
     }
   }
 
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
+  __builtin_amdgcn_sched_barrier(0);  // the loads above go out before waiting for n
+  int nsplit, t0, t1;
+  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+  if (split >= nsplit) return;
   const int nblocks = (t1 - t0 + kBlock - 1) / kBlock;
 
   f32x4 acc[8];  // O^T rows 128*wave + 16*mb + 4*grp + i, column = head
@@ -205,9 +246,9 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   BlockLoader ld;
-  ld.load(a, table, t0, t1, 0, log2P, tid);
+  ld.load(a, pt, t0, t1, 0, log2P, tid);
   ld.store(lds[0], tid);
-  ld.load(a, table, t0, t1, 1, log2P, tid);
+  ld.load(a, pt, t0, t1, 1, log2P, tid);
   __syncthreads();
 
   for (int blk = 0; blk < nblocks; ++blk) {
@@ -290,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
     }
     // stage the next block, start loading the one after, hand over the buffer
     if (blk + 1 < nblocks) ld.store(lds[(blk + 1) & 1], tid);
-    if (blk + 2 < nblocks) ld.load(a, table, t0, t1, blk + 2, log2P, tid);
+    if (blk + 2 < nblocks) ld.load(a, pt, t0, t1, blk + 2, log2P, tid);
     __syncthreads();
   }
 
@@ -332,12 +373,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
   const int tile = blockIdx.x % a.head_tiles;
   const int b = blockIdx.x / a.head_tiles;
   const int split = blockIdx.y;
-  const int n = a.context_lens[b];
-  int nsplit, t0, t1;
-  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
-  if (split >= nsplit) return;
-  int log2P = 0;
-  while ((1 << log2P) < a.page_size) ++log2P;
+  // One batch of kernel-argument loads; then the sequence length, the
+  // range's block-table entries and q are requested together (workgroups past
+  // split 0 first check on the length alone whether they have pages at all).
+  asm volatile("" ::"s"(a.q), "s"(a.kv_cache), "s"(a.block_tables), "s"(a.context_lens),
+               "s"(a.num_q_heads), "s"(a.head_tiles), "s"(a.page_size), "s"(a.max_pages),
+               "s"(a.log2_page), "s"(a.qk_scale_log2), "s"(a.split.pages_per_split),
+               "s"(a.split.max_splits), "s"(a.split.split_min_tokens));
+  const int log2P = a.log2_page;
+  int n = 0;
+  if (split > 0) {
+    n = load_uniform(a.context_lens + b);
+    int ns, ta, tb;
+    split_range(a.split, n, a.page_size, split, ns, ta, tb);
+    if (split >= ns) return;
+  }
+  PageTable pt{a.block_tables + (int64_t)b * a.max_pages, a.max_pages, 0, 0};
+  pt.load(a.split.max_splits > 1 ? split * a.split.pages_per_split : 0, lane);
+  if (split == 0) n = load_uniform(a.context_lens + b);
   const int hvalid_n = min(kHeads, a.num_q_heads - tile * kHeads);
 
   // q of the tile's heads into LDS (zero for padded heads)
@@ -349,7 +402,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
     q_sh[hh][w] = v;
   }
 
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
+  __builtin_amdgcn_sched_barrier(0);  // the loads above go out before waiting for n
+  int nsplit, t0, t1;
+  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+  if (split >= nsplit) return;
   const int nblocks = (t1 - t0 + kBlock - 1) / kBlock;
 
   // score-phase identity
@@ -366,9 +422,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
 
   BlockLoader ld;
-  ld.load(a, table, t0, t1, 0, log2P, tid);
+  ld.load(a, pt, t0, t1, 0, log2P, tid);
   ld.store(lds[0], tid);
-  ld.load(a, table, t0, t1, 1, log2P, tid);
+  ld.load(a, pt, t0, t1, 1, log2P, tid);
   __syncthreads();
 
   for (int blk = 0; blk < nblocks; ++blk) {
@@ -432,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
       }
     }
     if (blk + 1 < nblocks) ld.store(lds[(blk + 1) & 1], tid);
-    if (blk + 2 < nblocks) ld.load(a, table, t0, t1, blk + 2, log2P, tid);
+    if (blk + 2 < nblocks) ld.load(a, pt, t0, t1, blk + 2, log2P, tid);
     __syncthreads();
   }
 
