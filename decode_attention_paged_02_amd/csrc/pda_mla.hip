@@ -127,9 +127,14 @@ struct PageTable {
     const int p = min(page0 + lane, max_pages - 1);
     entries = row[p];
   }
-  // entry of page p (p >= base); moves the window when p is past it
+  // entry of page p (p >= base); moves the window when p is past it.  The
+  // moved window is waited for inside the branch, so the common path reads
+  // the lane without waiting on the block loads in flight.
   __device__ __forceinline__ int entry(int p, int lane) {
-    if (p - base >= 64) load(p, lane);
+    if (p - base >= 64) {
+      load(p, lane);
+      asm volatile("" ::"v"(entries));
+    }
     return __builtin_amdgcn_readlane(entries, p - base);
   }
 };
@@ -146,7 +151,8 @@ struct BlockLoader {
     const int tok = t0 + blk * kBlock;
     // (uniform; read into a scalar register so the resource stays scalar)
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kBlock, t1 - tok)));
-    const int e = pt.entry(tok >> log2P, tid & 63);
+    // (blocks past the range look up the range's last page and load nothing)
+    const int e = pt.entry(min(tok, t1 - 1) >> log2P, tid & 63);
     const int phys = rows > 0 ? e : 0;
     const int slot = tok & ((1 << log2P) - 1);
     const int64_t rec0 = (int64_t)phys * a.page_size + slot;
@@ -245,13 +251,19 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  BlockLoader ld;
-  ld.load(a, pt, t0, t1, 0, log2P, tid);
-  ld.store(lds[0], tid);
-  ld.load(a, pt, t0, t1, 1, log2P, tid);
+  // Two blocks in flight in registers while one is computed from LDS: block k
+  // sits in ld[k % 2] until it is staged into LDS buffer k % 2, and the loads
+  // of block k + 2 go into the registers it leaves.  Loads of blocks past the
+  // range have empty resources (no memory access), so they need no branch.
+  BlockLoader ld[2];
+  ld[0].load(a, pt, t0, t1, 0, log2P, tid);
+  ld[0].store(lds[0], tid);
+  ld[1].load(a, pt, t0, t1, 1, log2P, tid);
+  ld[0].load(a, pt, t0, t1, 2, log2P, tid);
   __syncthreads();
 
-  for (int blk = 0; blk < nblocks; ++blk) {
+  // block blk from LDS; `nxt` holds block blk + 1 and then receives blk + 3
+  auto body = [&](int blk, BlockLoader& nxt) {
     const char* L = lds[blk & 1];
     const int rows = min(kBlock, t1 - (t0 + blk * kBlock));
 
@@ -329,10 +341,17 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
         acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb_lo[kb], acc[mb], 0, 0, 0);
       }
     }
-    // stage the next block, start loading the one after, hand over the buffer
-    if (blk + 1 < nblocks) ld.store(lds[(blk + 1) & 1], tid);
-    if (blk + 2 < nblocks) ld.load(a, pt, t0, t1, blk + 2, log2P, tid);
+    // stage the next block, start loading the one three ahead, hand over the
+    // buffer.  No branches around loads and stores: the wait counts then
+    // stay exact across iterations, and a block past the range is all zero
+    // rows (an odd block count computes one such block, fully masked).
+    nxt.store(lds[(blk + 1) & 1], tid);
+    nxt.load(a, pt, t0, t1, blk + 3, log2P, tid);
     __syncthreads();
+  };
+  for (int blk = 0; blk < nblocks; blk += 2) {
+    body(blk, ld[1]);
+    body(blk + 1, ld[0]);
   }
 
   // epilogue: l over the four lane groups; lane holds 4 consecutive columns
