@@ -4,7 +4,7 @@
 
 Compiles csrc/*.hip and csrc/*.cpp with hipcc into
 decode_attention_paged_02_amd/libpda.so.  Packed-FP32 instruction selection
-is disabled for the device code.
+is disabled for the device code; kernel-argument preloading is enabled.
 """
 from __future__ import annotations
 
@@ -24,6 +24,8 @@ FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first kernel arguments arrive in scalar registers at wave start
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

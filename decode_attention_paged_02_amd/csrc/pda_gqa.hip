@@ -453,8 +453,13 @@ constexpr int kCombineThreads = 256;
 // merged through LDS with the same algebra.  The sequence length and the
 // first partials are loaded together, so a chunk costs one memory round trip
 // for up to MAXL splits per group.
+// The values needed before the first loads come as separate (preloaded)
+// arguments ahead of CombineArgs, as in the attention kernels.
 template <class OT, int DV>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const float* part_o, const float* part_lse, const int32_t* context_lens, int32_t num_q_heads,
+    int32_t max_splits, int32_t pages_per_split, int32_t split_min_tokens, int32_t page_size,
+    CombineArgs a) {
   constexpr int CW = DV > 128 ? 128 : DV;       // columns per workgroup
   constexpr int NCH = DV / CW;                  // column chunks per row
   constexpr int DC = CW / 4;                    // float4 chunks per workgroup
@@ -466,28 +471,42 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
 
   const int64_t row = blockIdx.x / NCH;
   const int chunk = blockIdx.x % NCH;
-  const int b = (int)(row / a.num_q_heads);
-  const int S = a.split.max_splits;
-  const float* pl = a.part_lse + row * S;
+  const int b = (int)(row / num_q_heads);
+  const int S = max_splits;
+  const SplitLayout sp{pages_per_split, max_splits, split_min_tokens};
+  const float* pl = part_lse + row * S;
   // split s of this chunk starts at float4 index s * (DV / 4)
-  const f32x4* po = (const f32x4*)(a.part_o + row * S * DV + chunk * CW);
+  const f32x4* po = (const f32x4*)(part_o + row * S * DV + chunk * CW);
   constexpr int SSTR = DV / 4;
   const int sg = threadIdx.x / DC, dc = threadIdx.x % DC;
 
-  // Issue the sequence length and this thread's first MAXL partials together
-  // (slots past the split count hold stale data and are ignored below).
-  const int n = a.context_lens[b];
+  // With a split threshold (ragged batches) most rows belong to unsplit
+  // sequences: the length is checked first and only existing partials are
+  // read.  Otherwise the length and this thread's first MAXL partials are
+  // requested together (slots past the split count hold stale data and are
+  // ignored below), so the row costs one memory round trip.
+  const bool guarded = split_min_tokens > 0;
+  int n = 0, nsplit = 0, t0, t1;
+  if (guarded) {
+    n = load_uniform(context_lens + b);
+    split_range(sp, n, page_size, 0, nsplit, t0, t1);
+    if (nsplit <= 1) return;
+  }
+  const int bound = guarded ? nsplit : S;
   float l[MAXL];
   f32x4 o[MAXL];
 #pragma unroll
   for (int j = 0; j < MAXL; ++j) {
     const int s2 = sg + j * SG;
-    l[j] = s2 < S ? pl[s2] : -INFINITY;
-    o[j] = s2 < S ? po[(int64_t)s2 * SSTR + dc] : f32x4{0.f, 0.f, 0.f, 0.f};
+    l[j] = s2 < bound ? pl[s2] : -INFINITY;
+    o[j] = s2 < bound ? po[(int64_t)s2 * SSTR + dc] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  int nsplit, t0, t1;
-  split_range(a.split, n, a.page_size, 0, nsplit, t0, t1);
-  if (nsplit <= 1) return;
+  if (!guarded) {
+    __builtin_amdgcn_sched_barrier(0);  // the partial loads go out before waiting for n
+    n = load_uniform(context_lens + b);
+    split_range(sp, n, page_size, 0, nsplit, t0, t1);
+    if (nsplit <= 1) return;
+  }
 
   // this thread's splits: local max, then weighted sums against it
   float mx = -INFINITY;
@@ -607,13 +626,17 @@ hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
   const int nch = a.head_dim_v > 128 ? a.head_dim_v / 128 : 1;
   dim3 grid((unsigned)(a.batch * a.num_q_heads * nch));
   dim3 block(kCombineThreads);
+#define PDA_COMBINE_ARGS                                                                    \
+  a.part_o, a.part_lse, a.context_lens, a.num_q_heads, a.split.max_splits,                 \
+      a.split.pages_per_split, a.split.split_min_tokens, a.page_size, a
   switch (a.head_dim_v) {
-    case 64: hipLaunchKernelGGL((combine_kernel<OT, 64>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<OT, 128>), grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((combine_kernel<OT, 256>), grid, block, 0, s, a); break;
-    case 512: hipLaunchKernelGGL((combine_kernel<OT, 512>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((combine_kernel<OT, 64>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<OT, 128>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<OT, 256>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
+    case 512: hipLaunchKernelGGL((combine_kernel<OT, 512>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
     default: return hipErrorInvalidValue;
   }
+#undef PDA_COMBINE_ARGS
   return hipGetLastError();
 }
 

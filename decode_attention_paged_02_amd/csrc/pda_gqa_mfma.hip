@@ -143,8 +143,15 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, f32x4 c
   }
 }
 
+// The values the prologue needs come first as separate arguments: with kernel
+// argument preloading (gfx950) they arrive in scalar registers when the wave
+// starts, so the length, table and q requests go out without waiting for a
+// kernel-argument load.  GqaArgs carries everything (the same values too).
 template <class QT, class KT, int D>
-__global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
+__global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
+    const int32_t* context_lens, const int32_t* block_tables, const void* q, int32_t head_tiles,
+    int32_t num_kv_heads, int32_t group, int32_t num_q_heads, int32_t max_pages, int32_t log2_page,
+    int32_t pages_per_split, int32_t max_splits, GqaArgs a) {
   constexpr int ESZ = Elem<KT>::bytes;
   constexpr int PW = Piece<KT, D>::words;       // words of a loaded row piece
   constexpr int NE = D / 16;                    // elements per piece = PV MFMAs
@@ -166,32 +173,24 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsB];
   __shared__ float m_sh[kMWaves][kMHeads], l_sh[kMWaves][kMHeads];
 
-  // one batch of kernel-argument loads (see gqa_split_kernel)
-  asm volatile("" ::"s"(a.q), "s"(a.k_cache), "s"(a.v_cache), "s"(a.block_tables),
-               "s"(a.context_lens), "s"(a.batch), "s"(a.num_q_heads), "s"(a.num_kv_heads),
-               "s"(a.group), "s"(a.head_tiles), "s"(a.page_size), "s"(a.max_pages),
-               "s"(a.log2_page), "s"(a.tok_stride), "s"(a.page_stride), "s"(a.qk_scale_log2),
-               "s"(a.split.pages_per_split), "s"(a.split.max_splits),
-               "s"(a.split.split_min_tokens));
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;  // MFMA column (head) / V^T row piece / K row token
   const int grp = lane >> 4;  // lane group
 
   const int wg = blockIdx.x;
-  const int tile = wg % a.head_tiles;
-  const int bk = wg / a.head_tiles;
-  const int kvh = bk % a.num_kv_heads;
-  const int b = bk / a.num_kv_heads;
+  const int tile = wg % head_tiles;
+  const int bk = wg / head_tiles;
+  const int kvh = bk % num_kv_heads;
+  const int b = bk / num_kv_heads;
   const int split = blockIdx.y;
 
   const int g0 = tile * kMHeads;
-  const int hbase = kvh * a.group + g0;
-  const int gvalid = min(kMHeads, a.group - g0);
-  const int log2P = a.log2_page;
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
-  const int t0_hint = a.split.max_splits > 1 ? split * a.split.pages_per_split << log2P : 0;
+  const int hbase = kvh * group + g0;
+  const int gvalid = min(kMHeads, group - g0);
+  const int log2P = log2_page;
+  const int32_t* table = block_tables + (int64_t)b * max_pages;
+  const int t0_hint = max_splits > 1 ? split * pages_per_split << log2P : 0;
 
   // The range is walked in steps of ST consecutive tiles; wave w takes steps
   // w, w + kMWaves, ...  Sequence length, block-table entries (lane j: tile
@@ -203,7 +202,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
     const int T = (wave + (sbase + lane / ST) * kMWaves) * ST + lane % ST;
     const int64_t tok = (int64_t)t0_hint + (int64_t)T * kTileTokens;
     const int64_t pg = tok >> log2P;
-    return table[pg < a.max_pages ? pg : a.max_pages - 1];
+    return table[pg < max_pages ? pg : max_pages - 1];
   };
   // With ragged lengths most workgroups past split 0 have no pages to read:
   // those decide on the length alone and leave without further loads.  Split
@@ -211,20 +210,20 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(GqaArgs a) {
   // with the table entries and q.
   int n = 0;
   if (split > 0) {
-    n = load_uniform(a.context_lens + b);
+    n = load_uniform(context_lens + b);
     int ns, ta, tb;
     split_range(a.split, n, a.page_size, split, ns, ta, tb);
     if (split >= ns) return;
   }
   int vtbl = load_table(0);
-  if (split == 0) n = load_uniform(a.context_lens + b);
+  if (split == 0) n = load_uniform(context_lens + b);
 
   // Q^T as the B operand of the QK MFMAs: lane (col, grp) holds
   // q[head col][32 j + 8 grp .. +8] for MFMA j; heads past the group are zero
   u32x4 qb[NQK];
   {
     const bool hv = col < gvalid;
-    const char* qrow = (const char*)a.q + (((int64_t)b * a.num_q_heads + hbase + (hv ? col : 0)) * D) * 2;
+    const char* qrow = (const char*)q + (((int64_t)b * num_q_heads + hbase + (hv ? col : 0)) * D) * 2;
 #pragma unroll
     for (int j = 0; j < NQK; ++j) {
       const u32x4 w = *(const u32x4*)(qrow + (32 * j + 8 * grp) * 2);
@@ -475,9 +474,13 @@ hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStr
   dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.head_tiles), (unsigned)max_splits);
   dim3 block(kMWaves * 64);
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128>), grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 256>), grid, block, 0, s, a); break;
+#define PDA_MFMA_ARGS                                                                        \
+  a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.num_q_heads,  \
+      a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a
+    case 64: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64>), grid, block, 0, s, PDA_MFMA_ARGS); break;
+    case 128: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128>), grid, block, 0, s, PDA_MFMA_ARGS); break;
+    case 256: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 256>), grid, block, 0, s, PDA_MFMA_ARGS); break;
+#undef PDA_MFMA_ARGS
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
