@@ -155,23 +155,20 @@ def _oracle_call(case, rows):
 
 
 def bandwidth_probe(nbytes=2 << 30, reps=10):
-    """Device copy (read + write) and read-only (sum) bandwidth over nbytes
-    buffers: the practical HBM ceiling next to the published peak."""
+    """Device-to-device copy bandwidth (bytes read + written) over nbytes
+    buffers: a practical HBM figure next to the published peak."""
     import torch
     a = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda").normal_()
     b = torch.empty_like(a)
-    r = {}
-    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes),
-                            ("read", lambda: a.sum(dtype=torch.float32), nbytes)):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        r[name + "_GBs"] = round(moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    r = {"copy_GBs": round(2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}
     del a, b
     torch.cuda.empty_cache()
     return r
@@ -197,7 +194,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-bw-probe", action="store_true",
-                    help="skip the copy / read bandwidth probe")
+                    help="skip the device copy bandwidth probe")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -2,11 +2,15 @@
 
     python -m decode_attention_paged_02_amd.profiling stats  DIR [--match SUBSTR]
     python -m decode_attention_paged_02_amd.profiling counters DIR [--match SUBSTR]
+    python -m decode_attention_paged_02_amd.profiling summary trace|counters DIR \
+        --workload NAME --command "ROCPROF COMMAND" --out FILE
     python -m decode_attention_paged_02_amd.profiling traffic --workload NAME \\
         --fetch DIR --write DIR --kernel SUBSTR --bytes-per-launch N --copy-kernel SUBSTR
 
 `stats` prints the kernel-time table of a `rocprofv3 --kernel-trace --stats`
-run.  `traffic` reads two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
+run, `counters` the mean per-dispatch value of each counter of a `--pmc` run;
+`summary` writes either table with a header that records the commands and the
+digest of the kernel sources (the files kept under profiles/).  `traffic` reads two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
 runs (KiB per dispatch) and calibrates each counter against the plain device
 copy that bench.py's bandwidth probe performs in the same process: a copy of
 known size must read and write exactly its buffer, so factor = known bytes /
@@ -121,6 +125,26 @@ def counters_text(d, match):
     return "\n".join(out)
 
 
+def summary_text(kind, d, workload, command, match="pda"):
+    """A profiles/ summary: header (commands, source digest) + the table."""
+    if kind == "trace":
+        title = "rocprofv3 kernel trace, workload %s (bench.py; rotating KV pools)" % workload
+        table = stats_text(d, match)
+        tool = "stats"
+    else:
+        title = "rocprofv3 counters, workload %s" % workload
+        table = counters_text(d, match)
+        tool = "counters"
+    head = ["# " + title,
+            "# commands (GPU host, repository root as R; run from /tmp):",
+            "#   " + command,
+            "#   python -m decode_attention_paged_02_amd.profiling %s OUT" % tool,
+            "# source digest " + source_digest()]
+    if kind != "trace":
+        head.append("# counters are summed over the GPU's XCDs/SEs as rocprofv3 reports them")
+    return "\n".join(head) + "\n" + table + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -130,6 +154,13 @@ def main(argv=None):
     cn = sub.add_parser("counters")
     cn.add_argument("dir")
     cn.add_argument("--match", default="")
+    sm = sub.add_parser("summary")
+    sm.add_argument("kind", choices=["trace", "counters"])
+    sm.add_argument("dir")
+    sm.add_argument("--workload", required=True)
+    sm.add_argument("--command", required=True)
+    sm.add_argument("--match", default="pda")
+    sm.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--workload", required=True)
     t.add_argument("--fetch", required=True)
@@ -147,6 +178,12 @@ def main(argv=None):
         return
     if a.cmd == "counters":
         print(counters_text(a.dir, a.match))
+        return
+    if a.cmd == "summary":
+        txt = summary_text(a.kind, a.dir, a.workload, a.command, a.match)
+        with open(a.out, "w") as f:
+            f.write(txt)
+        print(txt)
         return
     r = traffic(a.fetch, a.write, a.kernel, a.copy_kernel, a.copy_bytes)
     r.update({"workload": a.workload, "source_digest": source_digest(),
