@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     m_sh[wave][col] = m_run;
     l_sh[wave][col] = l_run;
   }
-  {
+  if (col < gvalid) {  // only the heads of the group
     float* dst = acc_sh + (wave * kMHeads + col) * kAccStride;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -425,47 +425,44 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   }
   __syncthreads();
 
-  // thread t: head t / 16, values [NE (t % 16), NE (t % 16 + 1)); the four
-  // waves' weights exp2(m_w - max) and the normalizer are formed once per head
-  const int g = threadIdx.x >> 4, c16 = threadIdx.x & 15;
-  if (g >= gvalid) return;
-  float mx = -INFINITY;
+  // Work items: four consecutive values of one valid head, spread over all
+  // threads; each item issues its LDS reads (the four waves' max, sum and
+  // values) before any arithmetic: weights exp2(m_w - max), one reciprocal.
+  constexpr int kQ = D / 4;  // four-value items per head
+  for (int it = threadIdx.x; it < gvalid * kQ; it += kMWaves * 64) {
+    const int g = it / kQ, d0 = 4 * (it % kQ);
+    float mw[kMWaves], lw[kMWaves];
+    f32x4 xw[kMWaves];
 #pragma unroll
-  for (int w = 0; w < kMWaves; ++w) mx = fmaxf(mx, m_sh[w][g]);
-  float wt[kMWaves], den = 0.f;
-#pragma unroll
-  for (int w = 0; w < kMWaves; ++w) {
-    wt[w] = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_sh[w][g] - mx);
-    den += wt[w] * l_sh[w][g];
-  }
-  const float inv = den > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(den) : 0.f;
-  float o[NE];
-#pragma unroll
-  for (int e = 0; e < NE; ++e) o[e] = 0.f;
-#pragma unroll
-  for (int w = 0; w < kMWaves; ++w) {
-    const float* src = acc_sh + (w * kMHeads + g) * kAccStride + c16 * NE;
-#pragma unroll
-    for (int e = 0; e < NE; e += 4) {
-      const f32x4 x = *(const f32x4*)(src + e);
-      o[e] += wt[w] * x.x;
-      o[e + 1] += wt[w] * x.y;
-      o[e + 2] += wt[w] * x.z;
-      o[e + 3] += wt[w] * x.w;
+    for (int w = 0; w < kMWaves; ++w) {
+      mw[w] = m_sh[w][g];
+      lw[w] = l_sh[w][g];
+      xw[w] = *(const f32x4*)(acc_sh + (w * kMHeads + g) * kAccStride + d0);
     }
-  }
+    float mx = mw[0];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) o[e] *= inv;
-  const float lse = den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
-  const int64_t row = (int64_t)b * a.num_q_heads + hbase + g;
-  if (nsplit == 1) {
-    store_row<QT, NE>(a.out, row * D + c16 * NE, o);
-    if (c16 == 0 && a.lse) a.lse[row] = lse;
-  } else {
-    float* po = a.part_o + (row * a.split.max_splits + split) * D + c16 * NE;
+    for (int w = 1; w < kMWaves; ++w) mx = fmaxf(mx, mw[w]);
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
 #pragma unroll
-    for (int e = 0; e < NE; e += 4) *(f32x4*)(po + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
-    if (c16 == 0) a.part_lse[row * a.split.max_splits + split] = lse;
+    for (int w = 0; w < kMWaves; ++w) {
+      const float wt = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mx);
+      den += wt * lw[w];
+      num += wt * xw[w];
+    }
+    const float inv = den > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(den) : 0.f;
+    const float o[4] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv};
+    const int64_t row = (int64_t)b * a.num_q_heads + hbase + g;
+    if (nsplit == 1) {
+      store_row<QT, 4>(a.out, row * D + d0, o);
+      if (d0 == 0 && a.lse) a.lse[row] = den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+    } else {
+      float* po = a.part_o + (row * a.split.max_splits + split) * D + d0;
+      *(f32x4*)po = f32x4{o[0], o[1], o[2], o[3]};
+      if (d0 == 0)
+        a.part_lse[row * a.split.max_splits + split] =
+            den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+    }
   }
 }
 
