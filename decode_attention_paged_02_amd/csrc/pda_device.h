@@ -53,6 +53,9 @@ __device__ __forceinline__ int load_uniform(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
+// The same read where the address differs per lane (a vector load).
+__device__ __forceinline__ int load_uniform_v(const int32_t* p) { return *p; }
+
 // Cache policy of the K/V stream loads (the buffer instruction's cache-policy
 // field; 2 marks them non-temporal).
 #ifndef PDA_KV_LOAD_POLICY

@@ -107,12 +107,25 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   // when the K rows are permuted too, else the head steps only)
   constexpr int kPerm = kGqaPermuteRows ? NV : GT;
 
-  const int wg = blockIdx.x;
-  const int tile = wg % a.head_tiles;
-  const int bk = wg / a.head_tiles;
-  const int kvh = bk % a.num_kv_heads;
-  const int b = bk / a.num_kv_heads;
-  const int split = blockIdx.y;
+  // which (sequence, KV head, head tile, split) this workgroup computes
+  // (ordered: from the unit list, as in gqa_mfma_kernel)
+  int tile, kvh, b, split;
+  if (a.units) {
+    const int nhu = a.num_kv_heads * a.head_tiles;
+    const int hu = blockIdx.x % nhu;
+    const int e = load_uniform(a.units + blockIdx.x / nhu);
+    if (e < 0) return;
+    b = e & 0xffff;
+    split = e >> 16;
+    kvh = hu / a.head_tiles;
+    tile = hu % a.head_tiles;
+  } else {
+    const int bk = blockIdx.x / a.head_tiles;
+    tile = blockIdx.x % a.head_tiles;
+    kvh = bk % a.num_kv_heads;
+    b = bk / a.num_kv_heads;
+    split = blockIdx.y;
+  }
 
   const int g0 = tile * GT;                 // first group-local head of the tile
   const int hbase = kvh * a.group + g0;     // first query head of the tile
@@ -565,9 +578,59 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   }
 }
 
+// ------------------------------------------------------- work ordering
+
+constexpr int kOrderThreads = 1024;
+
+// Longest-processing-time order of the (sequence, split) work units of a
+// mixed-length batch: units are bucketed by the bit length of their token
+// count (a counting sort, buckets taken from the longest down), so that the
+// attention workgroups that start first get the longest ranges.  Split 0 of
+// every sequence is listed even when empty (it writes out = 0, LSE = -inf).
+// Order inside a bucket follows the LDS atomics; each unit's result does not
+// depend on it.  One workgroup.
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(OrderArgs a) {
+  constexpr int NBK = 33;  // bit lengths 0..32
+  __shared__ int cnt[NBK];
+  __shared__ int total_sh;
+  const int S = a.split.max_splits;
+  const int U = a.batch * S;
+  if (threadIdx.x < NBK) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  auto bucket_of = [&](int u) -> int {  // -1: not listed
+    const int b = u / S, s = u % S;
+    int ns, t0, t1;
+    split_range(a.split, load_uniform_v(a.context_lens + b), a.page_size, s, ns, t0, t1);
+    if (s >= ns) return -1;
+    const int tok = t1 - t0;
+    return tok > 0 ? 32 - __clz(tok) : 0;
+  };
+  for (int u = threadIdx.x; u < U; u += kOrderThreads) {
+    const int k = bucket_of(u);
+    if (k >= 0) atomicAdd(&cnt[k], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // bucket offsets, longest bucket first
+    int pos = 0;
+    for (int k = NBK - 1; k >= 0; --k) {
+      const int c = cnt[k];
+      cnt[k] = pos;
+      pos += c;
+    }
+    total_sh = pos;
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < U; u += kOrderThreads) {
+    const int k = bucket_of(u);
+    if (k >= 0) a.units[atomicAdd(&cnt[k], 1)] = (u / S) | ((u % S) << 16);
+  }
+  for (int u = total_sh + threadIdx.x; u < U; u += kOrderThreads) a.units[u] = -1;
+}
+
 template <class QT, class KT, int D>
 hipError_t launch_d(const GqaArgs& a, int tile_heads, int max_splits, hipStream_t s) {
-  dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.head_tiles), (unsigned)max_splits);
+  const unsigned units = (unsigned)(a.batch * a.num_kv_heads * a.head_tiles);
+  dim3 grid(a.units ? units * (unsigned)max_splits : units, a.units ? 1u : (unsigned)max_splits);
   dim3 block(kGqaWaves * 64);
   switch (tile_heads) {
     case 1: hipLaunchKernelGGL((gqa_split_kernel<QT, KT, D, 1>), grid, block, 0, s, a); break;
@@ -637,6 +700,11 @@ hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 #undef PDA_COMBINE_ARGS
+  return hipGetLastError();
+}
+
+hipError_t launch_order(const OrderArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -151,7 +151,7 @@ template <class QT, class KT, int D>
 __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     const int32_t* context_lens, const int32_t* block_tables, const void* q, int32_t head_tiles,
     int32_t num_kv_heads, int32_t group, int32_t num_q_heads, int32_t max_pages, int32_t log2_page,
-    int32_t pages_per_split, int32_t max_splits, GqaArgs a) {
+    int32_t pages_per_split, int32_t max_splits, const int32_t* units, GqaArgs a) {
   constexpr int ESZ = Elem<KT>::bytes;
   constexpr int PW = Piece<KT, D>::words;       // words of a loaded row piece
   constexpr int NE = D / 16;                    // elements per piece = PV MFMAs
@@ -178,12 +178,26 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   const int col = lane & 15;  // MFMA column (head) / V^T row piece / K row token
   const int grp = lane >> 4;  // lane group
 
-  const int wg = blockIdx.x;
-  const int tile = wg % head_tiles;
-  const int bk = wg / head_tiles;
-  const int kvh = bk % num_kv_heads;
-  const int b = bk / num_kv_heads;
-  const int split = blockIdx.y;
+  // which (sequence, KV head, head tile, split) this workgroup computes
+  int tile, kvh, b, split;
+  if (units) {
+    // ordered: the unit list gives (sequence, split) longest first; the
+    // (KV head, head tile) pairs of a unit are consecutive workgroups
+    const int nhu = num_kv_heads * head_tiles;
+    const int hu = blockIdx.x % nhu;
+    const int e = load_uniform(units + blockIdx.x / nhu);
+    if (e < 0) return;
+    b = e & 0xffff;
+    split = e >> 16;
+    kvh = hu / head_tiles;
+    tile = hu % head_tiles;
+  } else {
+    const int bk = blockIdx.x / head_tiles;
+    tile = blockIdx.x % head_tiles;
+    kvh = bk % num_kv_heads;
+    b = bk / num_kv_heads;
+    split = blockIdx.y;
+  }
 
   const int g0 = tile * kMHeads;
   const int hbase = kvh * group + g0;
@@ -468,12 +482,13 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
 
 template <class QT, class KT>
 hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStream_t s) {
-  dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.head_tiles), (unsigned)max_splits);
+  const unsigned units = (unsigned)(a.batch * a.num_kv_heads * a.head_tiles);
+  dim3 grid(a.units ? units * (unsigned)max_splits : units, a.units ? 1u : (unsigned)max_splits);
   dim3 block(kMWaves * 64);
   switch (head_dim) {
 #define PDA_MFMA_ARGS                                                                        \
   a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.num_q_heads,  \
-      a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a
+      a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a.units, a
     case 64: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64>), grid, block, 0, s, PDA_MFMA_ARGS); break;
     case 128: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128>), grid, block, 0, s, PDA_MFMA_ARGS); break;
     case 256: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 256>), grid, block, 0, s, PDA_MFMA_ARGS); break;

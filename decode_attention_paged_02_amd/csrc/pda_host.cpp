@@ -112,23 +112,49 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_pla
   p->head_tiles = head_tiles;
   p->workgroups = (int)std::min<int64_t>(units * splits, INT32_MAX);
   p->num_cus = num_cus;
-  p->reserved = 0;
+  // work ordering for mixed-length batches (the threshold signals them)
+  p->ordered = s->split_min_tokens > 0 && s->batch <= 65535 && units * splits <= INT32_MAX;
   uint64_t ws = 0;
   if (splits > 1) {
     const uint64_t rows = (uint64_t)s->batch * s->num_q_heads;
     const uint64_t o_bytes = rows * splits * s->head_dim_v * sizeof(float);
-    ws = ((o_bytes + 255) / 256) * 256 + rows * splits * sizeof(float);
+    ws = ((o_bytes + 255) / 256) * 256 + ((rows * splits * sizeof(float) + 255) / 256) * 256;
   }
+  if (p->ordered) ws += (uint64_t)s->batch * splits * sizeof(int32_t);
   p->workspace_bytes = ws;
   return PDA_OK;
 }
 
+// Workspace layout: partial outputs [B, Hq, S, dv] fp32, partial LSE
+// [B, Hq, S] fp32 (both only when S > 1, each 256-byte aligned), then the
+// ordered unit list [B * S] int32 (only for ordered calls).
 void workspace_parts(const pda_shape* s, const pda_plan_info& p, void* ws, float** po,
-                     float** pl) {
+                     float** pl, int32_t** un) {
   const uint64_t rows = (uint64_t)s->batch * s->num_q_heads;
-  const uint64_t o_bytes = rows * p.max_splits * s->head_dim_v * sizeof(float);
-  *po = (float*)ws;
-  *pl = (float*)((char*)ws + ((o_bytes + 255) / 256) * 256);
+  char* c = (char*)ws;
+  *po = nullptr;
+  *pl = nullptr;
+  *un = nullptr;
+  if (p.max_splits > 1) {
+    const uint64_t o_bytes = rows * p.max_splits * s->head_dim_v * sizeof(float);
+    *po = (float*)c;
+    c += ((o_bytes + 255) / 256) * 256;
+    *pl = (float*)c;
+    c += ((rows * p.max_splits * sizeof(float) + 255) / 256) * 256;
+  }
+  if (p.ordered) *un = (int32_t*)c;
+}
+
+// The ordering pass of an ordered call (before the attention kernel).
+int run_order(const pda_shape& s, const pda_plan_info& p, const int32_t* context_lens,
+              int32_t* units, const pda::SplitLayout& sp, hipStream_t st) {
+  pda::OrderArgs o{};
+  o.context_lens = context_lens;
+  o.units = units;
+  o.batch = s.batch;
+  o.page_size = s.page_size;
+  o.split = sp;
+  return pda::launch_order(o, st) == hipSuccess ? PDA_OK : PDA_ERR_HIP;
 }
 
 }  // namespace
@@ -187,9 +213,9 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   a.context_lens = context_lens;
   a.out = out;
   a.lse = lse;
-  a.part_o = nullptr;
-  a.part_lse = nullptr;
-  if (p.max_splits > 1) workspace_parts(shape, p, workspace, &a.part_o, &a.part_lse);
+  int32_t* units = nullptr;
+  workspace_parts(shape, p, workspace, &a.part_o, &a.part_lse, &units);
+  a.units = units;
   a.batch = s.batch;
   a.num_q_heads = s.num_q_heads;
   a.num_kv_heads = s.num_kv_heads;
@@ -209,6 +235,10 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   a.split.split_min_tokens = s.split_min_tokens;
 
   hipStream_t st = (hipStream_t)stream;
+  if (units) {
+    rc = run_order(s, p, context_lens, units, a.split, st);
+    if (rc != PDA_OK) return rc;
+  }
   const hipError_t le =
       gqa_use_mfma(shape)
           ? pda::launch_gqa_mfma(a, s.q_dtype, s.kv_dtype, s.head_dim, p.max_splits, st)
@@ -257,7 +287,9 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
   a.context_lens = context_lens;
   a.out = out;
   a.lse = lse;
-  if (p.max_splits > 1) workspace_parts(shape, p, workspace, &a.part_o, &a.part_lse);
+  int32_t* units = nullptr;
+  workspace_parts(shape, p, workspace, &a.part_o, &a.part_lse, &units);
+  a.units = units;
   a.batch = s.batch;
   a.num_q_heads = s.num_q_heads;
   a.head_tiles = p.head_tiles;
@@ -271,6 +303,10 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
   a.split.split_min_tokens = s.split_min_tokens;
 
   hipStream_t st = (hipStream_t)stream;
+  if (units) {
+    rc = run_order(s, p, context_lens, units, a.split, st);
+    if (rc != PDA_OK) return rc;
+  }
   if (pda::launch_mla(a, s.variant, p.max_splits, st) != hipSuccess) return PDA_ERR_HIP;
   if (p.max_splits > 1) {
     pda::CombineArgs c{};

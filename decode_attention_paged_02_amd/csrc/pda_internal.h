@@ -74,6 +74,10 @@ struct GqaArgs {
   float qk_scale_log2;   // scale * k_scale * log2(e)
   float v_scale;
   SplitLayout split;
+  // Ordered work: units[u] = b | split << 16 for u < count, -1 after; the
+  // grid is (kv heads * head tiles) x batch * max_splits in x.  Null: the
+  // grid is (batch, kv head, head tile) in x and the split in y.
+  const int32_t* units;
 };
 
 struct CombineArgs {
@@ -100,6 +104,16 @@ struct MlaArgs {
   int32_t log2_page;       // page_size == 1 << log2_page
   float qk_scale_log2;     // scale * log2(e)
   SplitLayout split;
+  const int32_t* units;    // as in GqaArgs (x = head tiles * batch * max_splits)
+};
+
+// The work-ordering pass: lists every non-empty (sequence, split) unit, and
+// split 0 of every sequence, by decreasing token count.
+struct OrderArgs {
+  const int32_t* context_lens;
+  int32_t* units;          // [batch * max_splits]
+  int32_t batch, page_size;
+  SplitLayout split;
 };
 
 // Host-side support queries (no HIP calls).
@@ -114,6 +128,7 @@ hipError_t launch_gqa_mfma(const GqaArgs& a, int q_dtype, int kv_dtype, int head
 hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
                       int tile_heads, int max_splits, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t stream);
+hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
 hipError_t launch_mla(const MlaArgs& a, int variant, int max_splits, hipStream_t stream);
 
 }  // namespace pda

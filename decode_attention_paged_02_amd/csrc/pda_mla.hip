@@ -197,9 +197,19 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   const int col = lane & 15;      // MFMA column: the head
   const int grp = lane >> 4;      // lane group: rows 4*grp..4*grp+3 of an MFMA tile
 
-  const int tile = blockIdx.x % a.head_tiles;
-  const int b = blockIdx.x / a.head_tiles;
-  const int split = blockIdx.y;
+  // (ordered: the unit list gives (sequence, split), see pda_internal.h)
+  int tile, b, split;
+  if (a.units) {
+    tile = blockIdx.x % a.head_tiles;
+    const int e = load_uniform(a.units + blockIdx.x / a.head_tiles);
+    if (e < 0) return;
+    b = e & 0xffff;
+    split = e >> 16;
+  } else {
+    tile = blockIdx.x % a.head_tiles;
+    b = blockIdx.x / a.head_tiles;
+    split = blockIdx.y;
+  }
   // One batch of kernel-argument loads; then the sequence length, the
   // range's block-table entries and q are requested together (workgroups past
   // split 0 first check on the length alone whether they have pages at all).
@@ -389,9 +399,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  const int tile = blockIdx.x % a.head_tiles;
-  const int b = blockIdx.x / a.head_tiles;
-  const int split = blockIdx.y;
+  // (ordered: the unit list gives (sequence, split), see pda_internal.h)
+  int tile, b, split;
+  if (a.units) {
+    tile = blockIdx.x % a.head_tiles;
+    const int e = load_uniform(a.units + blockIdx.x / a.head_tiles);
+    if (e < 0) return;
+    b = e & 0xffff;
+    split = e >> 16;
+  } else {
+    tile = blockIdx.x % a.head_tiles;
+    b = blockIdx.x / a.head_tiles;
+    split = blockIdx.y;
+  }
   // One batch of kernel-argument loads; then the sequence length, the
   // range's block-table entries and q are requested together (workgroups past
   // split 0 first check on the length alone whether they have pages at all).
@@ -547,7 +567,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
 }  // namespace
 
 hipError_t launch_mla(const MlaArgs& a, int variant, int max_splits, hipStream_t s) {
-  dim3 grid((unsigned)(a.batch * a.head_tiles), (unsigned)max_splits);
+  const unsigned units = (unsigned)(a.batch * a.head_tiles);
+  dim3 grid(a.units ? units * (unsigned)max_splits : units, a.units ? 1u : (unsigned)max_splits);
   dim3 block(kThreads);
   if (variant == 2)
     hipLaunchKernelGGL(mla_valu_kernel, grid, block, 0, s, a);

@@ -43,7 +43,7 @@ class Shape(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("max_splits", ctypes.c_int32), ("pages_per_split", ctypes.c_int32),
                 ("head_tiles", ctypes.c_int32), ("workgroups", ctypes.c_int32),
-                ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("ordered", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64)]
 
 

@@ -117,7 +117,7 @@ typedef struct pda_plan_info {
   int32_t head_tiles;      /* query-head tiles per KV head                   */
   int32_t workgroups;      /* workgroups of the main kernel                  */
   int32_t num_cus;         /* compute units the plan was made for           */
-  int32_t reserved;
+  int32_t ordered;         /* 1: the call orders its work longest first     */
   uint64_t workspace_bytes; /* bytes the call needs in `workspace`          */
 } pda_plan_info;
 
@@ -131,8 +131,16 @@ int pda_plan(const pda_shape* shape, int is_mla, int num_splits, int num_cus,
              pda_plan_info* plan);
 
 /* Workspace bytes a call with these arguments needs (0 when no sequence can
- * split).  Queries the current device's CU count when num_splits == 0.
- * Returns 0 on invalid arguments as well. */
+ * split and the work is not ordered).  Queries the current device's CU count
+ * when num_splits == 0.  Returns 0 on invalid arguments as well.
+ *
+ * Work ordering: when shape->split_min_tokens > 0 (a batch of mixed lengths,
+ * as the threshold signals) and batch <= 65535, each call first runs one
+ * small kernel that lists the (sequence, split) work units by decreasing
+ * token count (in the workspace), and the attention workgroups take units
+ * in that order, so the longest units start first (longest-processing-time
+ * order; the pages do not prescribe a schedule).  The result does not
+ * depend on the order. */
 size_t pda_workspace_bytes(const pda_shape* shape, int is_mla, int num_splits);
 
 /* GQA / MQA / MHA paged decode attention (layouts above).

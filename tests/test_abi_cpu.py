@@ -55,9 +55,25 @@ def test_plan_explicit_and_threshold():
     assert (p.max_splits, p.pages_per_split) == (3, 4)
     p = pda.plan(_shape(max_pages_per_seq=10), num_splits=50, num_cus=256)
     assert (p.max_splits, p.pages_per_split) == (10, 1)
-    # no sequence can exceed the split threshold: never split
+    # no sequence can exceed the split threshold: never split; a threshold
+    # still orders the work, so the workspace holds the unit list (B x S int32)
     p = pda.plan(_shape(max_pages_per_seq=10, split_min_tokens=160), num_splits=4, num_cus=256)
-    assert p.max_splits == 1 and p.workspace_bytes == 0
+    assert p.max_splits == 1 and p.ordered == 1 and p.workspace_bytes == 64 * 4
+    p = pda.plan(_shape(max_pages_per_seq=10), num_splits=4, num_cus=256)
+    assert p.ordered == 0
+
+
+def test_plan_ordered_workspace_layout():
+    """Partials (256-byte aligned), partial LSE (256-byte aligned), unit list."""
+    s = _shape(batch=3, max_pages_per_seq=100, split_min_tokens=64, num_q_heads=8,
+               num_kv_heads=2)
+    p = pda.plan(s, num_splits=5, num_cus=256)
+    assert (p.max_splits, p.pages_per_split, p.ordered) == (5, 20, 1)
+    rows = 3 * 8
+    o = rows * 5 * 128 * 4
+    l = -(-(rows * 5 * 4) // 256) * 256
+    assert p.workspace_bytes == -(-o // 256) * 256 + l + 3 * 5 * 4
+    assert pda.load().pda_workspace_bytes(ctypes.byref(s), 0, 5) == p.workspace_bytes
 
 
 def test_plan_head_tiles():

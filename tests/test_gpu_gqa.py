@@ -209,3 +209,22 @@ def test_large_pool_64bit_offsets(variant):
     check(small, out, lse, ref_o, ref_l, label="large pool")
     del k, v
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_ordered_work_with_empty_and_mixed_lengths(variant):
+    """A split threshold turns on the longest-first ordering pass: empty
+    sequences, sequences at and around the threshold and long split ones."""
+    lens = [0, 4096, 1, 9000, 4097, 17, 0, 2500]
+    case = _gqa(15, len(lens), 16, 4, 128, 16, lens, extra_pages=3)
+    say("ordered", variant)
+    dev = pda.to_device(case)
+    shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, split_min_tokens=4096)
+    assert pda.plan(shape, num_splits=6).ordered == 1
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, dev, num_splits=6, split_min_tokens=4096,
+                            variant=VARIANTS[variant])
+    check(case, out, lse, ref_o, ref_l, label="ordered")
+    # the same call without ordering gives the same values
+    out2, lse2 = pda.run_case(case, dev, num_splits=6, variant=VARIANTS[variant])
+    assert (out.float() - out2.float()).abs().max().item() < 2e-3

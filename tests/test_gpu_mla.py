@@ -112,3 +112,14 @@ def test_mla_b16_full_size_sampled():
         check(case, out, lse, ref_o, ref_l, rows=rows, label="%s %s" % (case.name, name))
     del dev
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_ordered_work_mixed_lengths(variant):
+    """MLA with a split threshold: the longest-first ordering pass, an empty
+    sequence, and sequences on both sides of the threshold."""
+    case = _mla(70, [0, 2000, 64, 5000, 129], extra_pages=2)
+    say("mla ordered", variant)
+    out, lse = pda.run_case(case, variant=VARIANTS[variant], num_splits=5, split_min_tokens=1000)
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label="mla ordered %s" % variant)
