@@ -228,3 +228,42 @@ def test_ordered_work_with_empty_and_mixed_lengths(variant):
     # the same call without ordering gives the same values
     out2, lse2 = pda.run_case(case, dev, num_splits=6, variant=VARIANTS[variant])
     assert (out.float() - out2.float()).abs().max().item() < 2e-3
+
+
+def test_graph_capture_and_replay():
+    """The entry point is capture-safe (no allocation, no memset, no host sync):
+    a call with splits, the combine and the ordering pass is captured into a
+    HIP graph and replayed several times, with eager work and synchronizations
+    between replays; every replay matches the eager result bit for bit."""
+    lens = [3000, 17, 0, 5000]
+    case = _gqa(16, len(lens), 16, 4, 128, 16, lens, extra_pages=2)
+    say("graph capture")
+    dev = pda.to_device(case)
+    kw = dict(scale=case.scale, num_splits=4, split_min_tokens=1024)
+    eager_o, eager_l = pda.paged_decode_attn(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                                             dev.context_lens, **kw)
+    shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, split_min_tokens=1024)
+    ws = pda.workspace_for(shape, mla=False, num_splits=4, device="cuda")
+    out = torch.empty_like(eager_o)
+    lse = torch.empty_like(eager_l)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up on the capture stream
+        pda.paged_decode_attn(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                              dev.context_lens, out=out, lse=lse, workspace=ws, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pda.paged_decode_attn(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                              dev.context_lens, out=out, lse=lse, workspace=ws, **kw)
+    for i in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), "replay %d" % i
+        # unrelated eager work between replays
+        pda.paged_decode_attn(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                              dev.context_lens, **kw)
+        torch.cuda.synchronize()
