@@ -85,14 +85,20 @@ class PagedCase:
     mla: bool = False
     d_latent: int = 0
     name: str = ""
+    causal: bool = True                # several query tokens: bottom-right causal mask
 
     @property
     def batch(self) -> int:
         return self.q.shape[0]
 
     @property
+    def q_len(self) -> int:
+        """Query tokens per sequence: q is [B, Hq, d] (1) or [B, s_q, Hq, d]."""
+        return self.q.shape[1] if self.q.ndim == 4 else 1
+
+    @property
     def num_q_heads(self) -> int:
-        return self.q.shape[1]
+        return self.q.shape[-2]
 
     @property
     def num_kv_heads(self) -> int:
@@ -100,7 +106,7 @@ class PagedCase:
 
     @property
     def head_dim(self) -> int:
-        return self.q.shape[2]
+        return self.q.shape[-1]
 
     @property
     def head_dim_v(self) -> int:
@@ -161,8 +167,12 @@ def make_gqa(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
              page_size: int, context_lens: Sequence[int], q_dtype: str, kv_dtype: str,
              seed: int, head_dim_v: Optional[int] = None, max_pages: Optional[int] = None,
              extra_pages: int = 0, poison: bool = True, std: float = 1.0,
-             scale: Optional[float] = None, name: str = "") -> PagedCase:
+             scale: Optional[float] = None, q_len: int = 1, causal: bool = True,
+             name: str = "") -> PagedCase:
     """GQA/MQA/MHA case: q, K, V ~ N(0, std^2) in fp32, then stored as requested.
+
+    q_len > 1 gives q the shape [B, q_len, Hq, d] (several query tokens per
+    sequence); q_len = 1 keeps [B, Hq, d].
 
     fp8 caches get one fp32 scale per tensor, amax / 448 over the values the
     method reads; the stored byte is e4m3(x / scale) (saturating, RNE)."""
@@ -172,7 +182,8 @@ def make_gqa(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
     rng = _rng(seed)
     P = page_size
     num_pages, tables, used = _layout_pages(rng, lens, P, max_pages, extra_pages)
-    q32 = _normal(rng, (batch, num_q_heads, head_dim), std)
+    qshape = (batch, num_q_heads, head_dim) if q_len == 1 else (batch, q_len, num_q_heads, head_dim)
+    q32 = _normal(rng, qshape, std)
     k32 = _normal(rng, (num_pages, P, num_kv_heads, head_dim), std)
     v32 = _normal(rng, (num_pages, P, num_kv_heads, dv), std)
     k_scale = v_scale = 1.0
@@ -196,21 +207,24 @@ def make_gqa(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
     return PagedCase(q=encode(q32, q_dtype), k_cache=k, v_cache=v, block_tables=tables,
                      context_lens=lens, q_dtype=q_dtype, kv_dtype=kv_dtype, page_size=P,
                      scale=float(1.0 / math.sqrt(head_dim)) if scale is None else scale,
-                     k_scale=k_scale, v_scale=v_scale, name=name)
+                     k_scale=k_scale, v_scale=v_scale, name=name, causal=causal)
 
 
 def make_mla(*, batch: int, num_q_heads: int, d_latent: int, d_rope: int, page_size: int,
              context_lens: Sequence[int], dtype: str, seed: int, scale: float,
              max_pages: Optional[int] = None, extra_pages: int = 0, poison: bool = True,
-             std: float = 1.0, name: str = "") -> PagedCase:
-    """MLA case: one latent record [c (d_latent) | k_R (d_rope)] per token."""
+             std: float = 1.0, q_len: int = 1, causal: bool = True,
+             name: str = "") -> PagedCase:
+    """MLA case: one latent record [c (d_latent) | k_R (d_rope)] per token
+    (q [B, q_len, Hq, rec] when q_len > 1)."""
     lens = np.asarray(context_lens, dtype=np.int32)
     assert lens.shape == (batch,)
     rng = _rng(seed)
     P = page_size
     rec = d_latent + d_rope
     num_pages, tables, used = _layout_pages(rng, lens, P, max_pages, extra_pages)
-    q = encode(_normal(rng, (batch, num_q_heads, rec), std), dtype)
+    qshape = (batch, num_q_heads, rec) if q_len == 1 else (batch, q_len, num_q_heads, rec)
+    q = encode(_normal(rng, qshape, std), dtype)
     kv = encode(_normal(rng, (num_pages, P, rec), std), dtype)
     if poison:
         _poison(kv, tables, lens, used, P, NAN_BITS[dtype])
@@ -218,7 +232,7 @@ def make_mla(*, batch: int, num_q_heads: int, d_latent: int, d_rope: int, page_s
         tables[tables < 0] = 0
     return PagedCase(q=q, k_cache=kv, v_cache=None, block_tables=tables, context_lens=lens,
                      q_dtype=dtype, kv_dtype=dtype, page_size=P, scale=scale, mla=True,
-                     d_latent=d_latent, name=name)
+                     d_latent=d_latent, name=name, causal=causal)
 
 
 def log_uniform_lens(rng: np.random.Generator, n: int, lo: int, hi: int) -> np.ndarray:

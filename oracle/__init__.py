@@ -59,10 +59,10 @@ def _load():
     I64 = ctypes.c_int64
     D = ctypes.c_double
     lib.orc_decode.argtypes = [I, P, I64, I64, P]
-    lib.orc_paged_attention.argtypes = [P, I, P, P, I, P, I, P, P, P, I, I, I, I, I, I, I64,
-                                        D, D, D, P, P, P, I]
-    lib.orc_mla_attention.argtypes = [P, I, P, I, P, I, P, P, P, I, I, I, I, I, I64, D, P, P,
-                                      P, I]
+    lib.orc_paged_attention.argtypes = [P, I, P, P, I, P, I, P, P, P, I, I, I, I, I, I, I,
+                                        I64, D, D, D, I, P, P, P, I]
+    lib.orc_mla_attention.argtypes = [P, I, P, I, P, I, P, P, P, I, I, I, I, I, I, I64, D, I,
+                                      P, P, P, I]
     lib.orc_combine.argtypes = [P, P, I64, I, I, P, P]
     lib.orc_max_threads.argtypes = []
     for f in (lib.orc_decode, lib.orc_paged_attention, lib.orc_mla_attention, lib.orc_combine,
@@ -110,21 +110,43 @@ def _i32(a, n=None):
     return a
 
 
+def _queries(q):
+    """(q as [B, s_q, H, d], s_q, whether the caller passed [B, H, d])."""
+    if q.ndim == 3:
+        return q[:, None], 1, True
+    if q.ndim != 4:
+        raise ValueError("q must be [B, H, d] or [B, s_q, H, d]")
+    return q, q.shape[1], False
+
+
+def _shape_result(out, lse, single):
+    """out [B, s_q, H, dv] and lse [B, H, s_q] back to the caller's rank."""
+    if single:
+        return out[:, 0], lse[:, :, 0]
+    return out, lse
+
+
 def paged_attention(q, k_cache, v_cache, block_tables, context_lens, *, scale,
-                    q_dtype, kv_dtype, k_scale=1.0, v_scale=1.0, tok_begin=None,
-                    tok_end=None, rows=None, num_threads=0):
+                    q_dtype, kv_dtype, k_scale=1.0, v_scale=1.0, causal=True,
+                    tok_begin=None, tok_end=None, rows=None, num_threads=0):
     """GQA/MQA/MHA paged decode attention in fp64.
 
-    q [B, Hq, dk]; k_cache [num_pages, P, Hkv, dk]; v_cache [num_pages, P, Hkv, dv];
-    block_tables [B, max_pages] int32; context_lens [B] int32.
+    q [B, Hq, dk] (one query token) or [B, s_q, Hq, dk] (s_q query tokens,
+    the last s_q positions of the sequence); k_cache [num_pages, P, Hkv, dk];
+    v_cache [num_pages, P, Hkv, dv]; block_tables [B, max_pages] int32;
+    context_lens [B] int32.  causal: query i of s_q sees the first
+    n - (s_q - 1 - i) tokens (bottom-right alignment); else all n.
     tok_begin/tok_end: optional [B] token interval per sequence (a split).
-    rows: optional bool [B, Hq] selecting the rows to compute (others are NaN).
-    Returns (out [B, Hq, dv] float64, lse [B, Hq] float64).
+    rows: optional bool [B, Hq] / [B, s_q, Hq] selecting the rows to compute
+    (others are NaN).
+    Returns (out [B, Hq, dv], lse [B, Hq]) for a 3-D q and
+    (out [B, s_q, Hq, dv], lse [B, Hq, s_q]) for a 4-D q, float64.
     """
     q = _as(q, q_dtype)
     k_cache = _as(k_cache, kv_dtype)
     v_cache = _as(v_cache, kv_dtype)
-    B, Hq, dk = q.shape
+    q, s_q, single = _queries(q)
+    B, _, Hq, dk = q.shape
     num_pages, P, Hkv, dk2 = k_cache.shape
     dv = v_cache.shape[3]
     if dk2 != dk or v_cache.shape[:3] != k_cache.shape[:3]:
@@ -135,28 +157,32 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, *, scale,
     cl = _i32(context_lens, B)
     tb, te = _i32(tok_begin, B), _i32(tok_end, B)
     rm = None if rows is None else np.ascontiguousarray(rows, dtype=np.uint8).reshape(-1)
-    out = np.full((B, Hq, dv), np.nan)
-    lse = np.full((B, Hq), np.nan)
+    out = np.full((B, s_q, Hq, dv), np.nan)
+    lse = np.full((B, Hq, s_q), np.nan)
     rc = _load().orc_paged_attention(
         _ptr(q), _DT[q_dtype], _ptr(k_cache), _ptr(v_cache), _DT[kv_dtype], _ptr(bt),
-        bt.shape[1], _ptr(cl), _ptr(tb), _ptr(te), B, Hq, Hkv, dk, dv, P, num_pages,
-        float(scale), float(k_scale), float(v_scale), _ptr(rm), _ptr(out), _ptr(lse),
-        int(num_threads))
+        bt.shape[1], _ptr(cl), _ptr(tb), _ptr(te), B, s_q, Hq, Hkv, dk, dv, P, num_pages,
+        float(scale), float(k_scale), float(v_scale), int(bool(causal)), _ptr(rm), _ptr(out),
+        _ptr(lse), int(num_threads))
     _check(rc)
-    return out, lse
+    return _shape_result(out, lse, single)
 
 
 def mla_attention(q, kv_cache, block_tables, context_lens, *, scale, d_latent, q_dtype,
-                  kv_dtype, tok_begin=None, tok_end=None, rows=None, num_threads=0):
+                  kv_dtype, causal=True, tok_begin=None, tok_end=None, rows=None,
+                  num_threads=0):
     """MLA paged decode attention in fp64.
 
-    q [B, Hq, d_latent + d_rope]; kv_cache [num_pages, P, d_latent + d_rope].
-    K is the whole record, V its first d_latent values.
-    Returns (out [B, Hq, d_latent] float64, lse [B, Hq] float64).
+    q [B, Hq, d_latent + d_rope] or [B, s_q, Hq, d_latent + d_rope];
+    kv_cache [num_pages, P, d_latent + d_rope].  K is the whole record, V its
+    first d_latent values; s_q and causal as in paged_attention.
+    Returns (out [B, Hq, d_latent], lse [B, Hq]) for a 3-D q and
+    (out [B, s_q, Hq, d_latent], lse [B, Hq, s_q]) for a 4-D q, float64.
     """
     q = _as(q, q_dtype)
     kv_cache = _as(kv_cache, kv_dtype)
-    B, Hq, rec = q.shape
+    q, s_q, single = _queries(q)
+    B, _, Hq, rec = q.shape
     num_pages, P, rec2 = kv_cache.shape
     if rec2 != rec or not (0 < d_latent <= rec):
         raise ValueError("record widths do not match")
@@ -164,14 +190,14 @@ def mla_attention(q, kv_cache, block_tables, context_lens, *, scale, d_latent, q
     cl = _i32(context_lens, B)
     tb, te = _i32(tok_begin, B), _i32(tok_end, B)
     rm = None if rows is None else np.ascontiguousarray(rows, dtype=np.uint8).reshape(-1)
-    out = np.full((B, Hq, d_latent), np.nan)
-    lse = np.full((B, Hq), np.nan)
+    out = np.full((B, s_q, Hq, d_latent), np.nan)
+    lse = np.full((B, Hq, s_q), np.nan)
     rc = _load().orc_mla_attention(
         _ptr(q), _DT[q_dtype], _ptr(kv_cache), _DT[kv_dtype], _ptr(bt), bt.shape[1],
-        _ptr(cl), _ptr(tb), _ptr(te), B, Hq, d_latent, rec - d_latent, P, num_pages,
-        float(scale), _ptr(rm), _ptr(out), _ptr(lse), int(num_threads))
+        _ptr(cl), _ptr(tb), _ptr(te), B, s_q, Hq, d_latent, rec - d_latent, P, num_pages,
+        float(scale), int(bool(causal)), _ptr(rm), _ptr(out), _ptr(lse), int(num_threads))
     _check(rc)
-    return out, lse
+    return _shape_result(out, lse, single)
 
 
 def combine(part_o, part_lse):

@@ -27,6 +27,16 @@
  *     K_j = the whole record, V_j = its first d_latent values (same bytes),
  *     s_j = scale * (q[:d_latent] . c_j + q[d_latent:] . k_R_j).
  *
+ *   Several query tokens per sequence (multi-token decode: FlashMLA-ETAP
+ *   "Supported configurations", query length, and "Usage", the q / o / lse
+ *   shapes): q [B, s_q, Hq, d], out [B, s_q, Hq, dv], lse [B, Hq, s_q].  With
+ *   the causal mask aligned bottom-right ("From MHA to MLA", sec. 2, the
+ *   reference kernel's causal branch) query i of s_q sits at position
+ *   n - s_q + i and sees keys j <= that position, i.e. the first
+ *   n - (s_q - 1 - i) tokens; without the mask every query sees all n.  A
+ *   query that sees no token is empty (out = 0, lse = -inf).  s_q = 1 is
+ *   the single-token case above, where the mask removes nothing.
+ *
  *   Split-KV (Flash-Decoding, "From MHA to MLA", sec. 4): attention over a
  *   token interval gives a normalized partial O_s and L_s; the combine is
  *     L = ln sum_s exp(L_s),  O = sum_s exp(L_s - L) O_s,
@@ -186,30 +196,39 @@ static int gather_rows(const void* cache, int dtype, const int32_t* table_row,
   return ORC_OK;
 }
 
+/* Tokens query i of q_len may see in a sequence of n cached tokens. */
+static int64_t visible_tokens(int64_t n, int q_len, int i, int causal) {
+  int64_t v = causal ? n - (int64_t)(q_len - 1 - i) : n;
+  return v > 0 ? v : 0;
+}
+
 /* ------------------------------------------------------------- GQA / MHA */
 
 /* Paged decode attention, GQA family.
- *   q            [B, Hq, dk] of q_dtype
+ *   q            [B, q_len, Hq, dk] of q_dtype
  *   k_cache      [num_pages, P, Hkv, dk] of kv_dtype
  *   v_cache      [num_pages, P, Hkv, dv] of kv_dtype
  *   block_tables [B, max_pages] int32, context_lens [B] int32
  *   tok_begin/tok_end [B] int32 or NULL: restrict to tokens [begin, end)
- *     of each sequence (a split interval); NULL means [0, n_b).
- *   row_mask [B*Hq] or NULL: compute only rows with a nonzero mask.
- *   out [B, Hq, dv] fp64, lse [B, Hq] fp64 (rows not computed are untouched).
+ *     of each sequence (a split interval); NULL means [0, n_b).  A query
+ *     takes the part of that interval it may see (causal: see the header).
+ *   row_mask [B*q_len*Hq] or NULL: compute only rows with a nonzero mask.
+ *   out [B, q_len, Hq, dv] fp64, lse [B, Hq, q_len] fp64 (rows not computed
+ *   are untouched).
  * Returns ORC_OK, ORC_ERR_ARG or ORC_ERR_TABLE.  num_threads <= 0: default. */
 int orc_paged_attention(const void* q, int q_dtype, const void* k_cache,
                         const void* v_cache, int kv_dtype,
                         const int32_t* block_tables, int max_pages,
                         const int32_t* context_lens, const int32_t* tok_begin,
-                        const int32_t* tok_end, int B, int Hq, int Hkv, int dk,
-                        int dv, int P, int64_t num_pages, double scale,
-                        double k_scale, double v_scale, const uint8_t* row_mask,
-                        double* out, double* lse, int num_threads) {
+                        const int32_t* tok_end, int B, int q_len, int Hq, int Hkv,
+                        int dk, int dv, int P, int64_t num_pages, double scale,
+                        double k_scale, double v_scale, int causal,
+                        const uint8_t* row_mask, double* out, double* lse,
+                        int num_threads) {
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !lse)
     return ORC_ERR_ARG;
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || dk <= 0 || dv <= 0 || P <= 0 ||
-      max_pages < 0 || num_pages < 0)
+  if (B < 0 || q_len <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || dk <= 0 || dv <= 0 ||
+      P <= 0 || max_pages < 0 || num_pages < 0)
     return ORC_ERR_ARG;
   const int G = Hq / Hkv;
   int status = ORC_OK;
@@ -220,10 +239,14 @@ int orc_paged_attention(const void* q, int q_dtype, const void* k_cache,
 #endif
 
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
-    if (row_mask && !row_mask[bh]) continue;
-    int b = (int)(bh / Hq), h = (int)(bh % Hq);
+  for (int64_t r = 0; r < (int64_t)B * q_len * Hq; ++r) {
+    if (row_mask && !row_mask[r]) continue;
+    /* row r = (b, query i, head h) of out [B, q_len, Hq, dv] */
+    int b = (int)(r / ((int64_t)q_len * Hq));
+    int i = (int)((r / Hq) % q_len);
+    int h = (int)(r % Hq);
     int kvh = h / G;
+    int64_t lse_row = ((int64_t)b * Hq + h) * q_len + i;
     int64_t n_b = context_lens[b];
     int64_t t0 = tok_begin ? tok_begin[b] : 0;
     int64_t t1 = tok_end ? tok_end[b] : n_b;
@@ -232,6 +255,8 @@ int orc_paged_attention(const void* q, int q_dtype, const void* k_cache,
       status = ORC_ERR_ARG;
       continue;
     }
+    int64_t vis = visible_tokens(n_b, q_len, i, causal);
+    if (t1 > vis) t1 = vis;
     if (t1 < t0) t1 = t0;
     int64_t n = t1 - t0;
     double* qd = (double*)malloc(sizeof(double) * dk);
@@ -242,7 +267,7 @@ int orc_paged_attention(const void* q, int q_dtype, const void* k_cache,
 #pragma omp atomic write
       status = ORC_ERR_NOMEM;
     } else {
-      for (int i = 0; i < dk; ++i) qd[i] = dec_elem(q_dtype, q, bh * dk + i);
+      for (int e = 0; e < dk; ++e) qd[e] = dec_elem(q_dtype, q, r * dk + e);
       const int32_t* trow = block_tables + (int64_t)b * max_pages;
       int rk = gather_rows(k_cache, kv_dtype, trow, num_pages, P, (int64_t)P * Hkv * dk,
                            (int64_t)Hkv * dk, (int64_t)kvh * dk, dk, k_scale, t0, t1, K);
@@ -252,7 +277,7 @@ int orc_paged_attention(const void* q, int q_dtype, const void* k_cache,
 #pragma omp atomic write
         status = ORC_ERR_TABLE;
       } else {
-        attend_rows(qd, K, V, n, dk, dv, scale, s, out + bh * dv, lse + bh);
+        attend_rows(qd, K, V, n, dk, dv, scale, s, out + r * dv, lse + lse_row);
       }
     }
     free(qd);
@@ -266,19 +291,20 @@ int orc_paged_attention(const void* q, int q_dtype, const void* k_cache,
 /* ------------------------------------------------------------------- MLA */
 
 /* Paged decode attention over an MLA latent cache (one record per token, no
- * head axis).  q [B, Hq, d_latent + d_rope]; kv_cache [num_pages, P,
- * d_latent + d_rope]; out [B, Hq, d_latent] fp64; lse [B, Hq] fp64.
- * K_j is the whole record, V_j its first d_latent values. */
+ * head axis).  q [B, q_len, Hq, d_latent + d_rope]; kv_cache [num_pages, P,
+ * d_latent + d_rope]; out [B, q_len, Hq, d_latent] fp64; lse [B, Hq, q_len]
+ * fp64.  K_j is the whole record, V_j its first d_latent values; queries and
+ * the causal mask as in orc_paged_attention. */
 int orc_mla_attention(const void* q, int q_dtype, const void* kv_cache, int kv_dtype,
                       const int32_t* block_tables, int max_pages,
                       const int32_t* context_lens, const int32_t* tok_begin,
-                      const int32_t* tok_end, int B, int Hq, int d_latent, int d_rope,
-                      int P, int64_t num_pages, double scale,
+                      const int32_t* tok_end, int B, int q_len, int Hq, int d_latent,
+                      int d_rope, int P, int64_t num_pages, double scale, int causal,
                       const uint8_t* row_mask, double* out, double* lse,
                       int num_threads) {
   if (!q || !kv_cache || !block_tables || !context_lens || !out || !lse) return ORC_ERR_ARG;
-  if (B < 0 || Hq <= 0 || d_latent <= 0 || d_rope < 0 || P <= 0 || max_pages < 0 ||
-      num_pages < 0)
+  if (B < 0 || q_len <= 0 || Hq <= 0 || d_latent <= 0 || d_rope < 0 || P <= 0 ||
+      max_pages < 0 || num_pages < 0)
     return ORC_ERR_ARG;
   const int rec = d_latent + d_rope;
   int status = ORC_OK;
@@ -289,9 +315,12 @@ int orc_mla_attention(const void* q, int q_dtype, const void* kv_cache, int kv_d
 #endif
 
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
-    if (row_mask && !row_mask[bh]) continue;
-    int b = (int)(bh / Hq);
+  for (int64_t r = 0; r < (int64_t)B * q_len * Hq; ++r) {
+    if (row_mask && !row_mask[r]) continue;
+    int b = (int)(r / ((int64_t)q_len * Hq));
+    int i = (int)((r / Hq) % q_len);
+    int h = (int)(r % Hq);
+    int64_t lse_row = ((int64_t)b * Hq + h) * q_len + i;
     int64_t n_b = context_lens[b];
     int64_t t0 = tok_begin ? tok_begin[b] : 0;
     int64_t t1 = tok_end ? tok_end[b] : n_b;
@@ -300,6 +329,8 @@ int orc_mla_attention(const void* q, int q_dtype, const void* kv_cache, int kv_d
       status = ORC_ERR_ARG;
       continue;
     }
+    int64_t vis = visible_tokens(n_b, q_len, i, causal);
+    if (t1 > vis) t1 = vis;
     if (t1 < t0) t1 = t0;
     int64_t n = t1 - t0;
     double* qd = (double*)malloc(sizeof(double) * rec);
@@ -310,7 +341,7 @@ int orc_mla_attention(const void* q, int q_dtype, const void* kv_cache, int kv_d
 #pragma omp atomic write
       status = ORC_ERR_NOMEM;
     } else {
-      for (int i = 0; i < rec; ++i) qd[i] = dec_elem(q_dtype, q, bh * rec + i);
+      for (int e = 0; e < rec; ++e) qd[e] = dec_elem(q_dtype, q, r * rec + e);
       const int32_t* trow = block_tables + (int64_t)b * max_pages;
       /* K: the whole record; V: the latent part of the same record. */
       int rk = gather_rows(kv_cache, kv_dtype, trow, num_pages, P, (int64_t)P * rec, rec, 0,
@@ -321,7 +352,7 @@ int orc_mla_attention(const void* q, int q_dtype, const void* kv_cache, int kv_d
 #pragma omp atomic write
         status = ORC_ERR_TABLE;
       } else {
-        attend_rows(qd, K, V, n, rec, d_latent, scale, s, out + bh * d_latent, lse + bh);
+        attend_rows(qd, K, V, n, rec, d_latent, scale, s, out + r * d_latent, lse + lse_row);
       }
     }
     free(qd);

@@ -1,0 +1,231 @@
+"""Pins for the oracle's multi-token decode (s_q query tokens per sequence).
+
+The reading: query i of s_q sits at position n - s_q + i of a sequence of n
+cached tokens (the new tokens are the last s_q of the cache) and, with the
+causal mask aligned bottom-right ("From MHA to MLA", sec. 2, the reference
+kernel's causal branch), sees the keys at positions <= its own; without the
+mask it sees all n.  Shapes follow the FlashMLA-ETAP README, "Usage":
+q [B, s_q, Hq, d], out [B, s_q, Hq, dv], lse [B, Hq, s_q].
+
+Each test ties the oracle to something other than itself:
+ - a pure-Python brute force that compares key and query positions;
+ - torch SDPA (fp64, CPU) with an explicit boolean mask built from positions;
+ - the prefix property: causal query i equals a single-token call over the
+   first n - (s_q - 1 - i) tokens (the single-token path has its own pins);
+ - closed forms (q = 0) and split + combine == unsplit with splits that are
+   empty for some queries only.
+"""
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_paged_02_amd import workloads as W
+from test_oracle_pins import _dense_from_pool, _gather_np
+
+
+def _run(case, **kw):
+    if case.mla:
+        return oracle.mla_attention(case.q, case.k_cache, case.block_tables, case.context_lens,
+                                    scale=case.scale, d_latent=case.d_latent,
+                                    q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
+                                    causal=case.causal, **kw)
+    return oracle.paged_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                  case.context_lens, scale=case.scale, q_dtype=case.q_dtype,
+                                  kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+                                  v_scale=case.v_scale, causal=case.causal, **kw)
+
+
+def _tiny(seed, *, q_len, causal=True, lens=None, dtype="f32"):
+    r = random.Random(seed)
+    B = r.randint(1, 3)
+    Hkv = r.choice([1, 2])
+    G = r.choice([1, 2, 3])
+    lens = lens or [r.randint(1, 30) for _ in range(B)]
+    return W.make_gqa(batch=len(lens), num_q_heads=Hkv * G, num_kv_heads=Hkv,
+                      head_dim=r.choice([2, 4, 8]), page_size=r.choice([1, 2, 4, 16]),
+                      context_lens=lens, q_dtype=dtype, kv_dtype=dtype, seed=seed,
+                      extra_pages=2, q_len=q_len, causal=causal)
+
+
+def _brute(case):
+    """Pure Python, unshifted softmax; key j is visible to query i when its
+    position j is at most the query's position n - s_q + i (causal)."""
+    B, s_q, Hq = case.batch, case.q_len, case.num_q_heads
+    G = Hq // case.num_kv_heads
+    q = W.to_float32(case.q, case.q_dtype).astype(np.float64)
+    out = np.zeros((B, s_q, Hq, case.head_dim_v))
+    lse = np.zeros((B, Hq, s_q))
+    for b in range(B):
+        K, V = _dense_from_pool(case, b)
+        n = len(K)
+        for i in range(s_q):
+            qpos = n - s_q + i
+            keys = [j for j in range(n) if not case.causal or j <= qpos]
+            for h in range(Hq):
+                kvh = h // G
+                e = [math.exp(case.scale * sum(float(a) * float(c)
+                                               for a, c in zip(q[b, i, h], K[j][kvh])))
+                     for j in keys]
+                z = sum(e)
+                if not keys:
+                    lse[b, h, i] = -math.inf
+                    continue
+                for d in range(case.head_dim_v):
+                    out[b, i, h, d] = sum(w * float(V[j][kvh][d]) for w, j in zip(e, keys)) / z
+                lse[b, h, i] = math.log(z)
+    return out, lse
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("q_len", [2, 3, 4])
+def test_multitoken_matches_bruteforce(seed, q_len):
+    case = _tiny(100 * q_len + seed, q_len=q_len, causal=seed % 4 != 3)
+    out, lse = _run(case)
+    bo, bl = _brute(case)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_short_sequences_leave_early_queries_empty():
+    """n < s_q: the first s_q - n queries see no key: out = 0, lse = -inf."""
+    case = _tiny(7, q_len=4, lens=[1, 2, 3, 4, 40])
+    out, lse = _run(case)
+    bo, bl = _brute(case)
+    for b, n in enumerate(case.context_lens):
+        for i in range(4):
+            empty = i < 4 - n
+            assert np.isneginf(lse[b, :, i]).all() == empty
+            if empty:
+                assert (out[b, i] == 0).all()
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(bl))
+    fin = np.isfinite(bl)
+    np.testing.assert_allclose(lse[fin], bl[fin], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_multitoken_matches_torch_sdpa_with_position_mask(causal):
+    case = W.make_gqa(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=16, page_size=16,
+                      context_lens=[3, 45, 130], q_dtype="f16", kv_dtype="f16", seed=9,
+                      extra_pages=3, q_len=3, causal=causal)
+    out, lse = _run(case)
+    G = 4
+    q = torch.from_numpy(W.to_float32(case.q, case.q_dtype).astype(np.float64))
+    for b, n in enumerate(case.context_lens):
+        k, v = _gather_np(case, b)
+        kt = torch.from_numpy(k).transpose(0, 1).repeat_interleave(G, dim=0).contiguous()
+        vt = torch.from_numpy(v).transpose(0, 1).repeat_interleave(G, dim=0).contiguous()
+        qb = q[b].transpose(0, 1).contiguous()                      # [Hq, s_q, d]
+        qpos = torch.arange(3) + (int(n) - 3)
+        mask = torch.arange(int(n))[None, :] <= qpos[:, None] if causal else \
+            torch.ones(3, int(n), dtype=torch.bool)
+        ref = torch.nn.functional.scaled_dot_product_attention(qb, kt, vt, attn_mask=mask,
+                                                               scale=case.scale)
+        np.testing.assert_allclose(out[b].transpose(1, 0, 2), ref.numpy(), rtol=0, atol=1e-12)
+        logits = case.scale * (qb @ kt.transpose(1, 2))
+        ref_lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1)   # [Hq, s_q]
+        np.testing.assert_allclose(lse[b], ref_lse.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "e4m3"])
+def test_causal_query_is_a_single_token_call_on_its_prefix(dtype):
+    q_len = 4
+    case = W.make_gqa(batch=3, num_q_heads=6, num_kv_heads=2, head_dim=8, page_size=4,
+                      context_lens=[5, 17, 33], q_dtype="f16" if dtype == "e4m3" else dtype,
+                      kv_dtype=dtype, seed=51, extra_pages=2, q_len=q_len)
+    out, lse = _run(case)
+    for i in range(q_len):
+        one = W.PagedCase(**{**case.__dict__})
+        one.q = np.ascontiguousarray(case.q[:, i])
+        one.context_lens = (case.context_lens - (q_len - 1 - i)).astype(np.int32)
+        o1, l1 = _run(one)
+        assert np.array_equal(out[:, i], o1) and np.array_equal(lse[:, :, i], l1)
+
+
+def test_non_causal_queries_each_see_the_whole_context():
+    case = _tiny(61, q_len=3, causal=False, lens=[9, 20])
+    out, lse = _run(case)
+    for i in range(3):
+        one = W.PagedCase(**{**case.__dict__})
+        one.q = np.ascontiguousarray(case.q[:, i])
+        o1, l1 = _run(one)
+        assert np.array_equal(out[:, i], o1) and np.array_equal(lse[:, :, i], l1)
+
+
+@pytest.mark.parametrize("n", [3, 16, 17, 37])
+def test_zero_query_gives_mean_of_the_visible_prefix(n):
+    q_len = 3
+    case = W.make_gqa(batch=1, num_q_heads=2, num_kv_heads=1, head_dim=8, page_size=16,
+                      context_lens=[n], q_dtype="f32", kv_dtype="f32", seed=n, extra_pages=2,
+                      q_len=q_len)
+    case.q[:] = 0
+    out, lse = _run(case)
+    _, v = _gather_np(case, 0)
+    for i in range(q_len):
+        vis = n - (q_len - 1 - i)
+        for h in range(2):
+            np.testing.assert_allclose(out[0, i, h], v[:vis, 0].mean(axis=0), rtol=0,
+                                       atol=1e-12)
+            assert abs(lse[0, h, i] - math.log(vis)) < 1e-12
+
+
+@pytest.mark.parametrize("S", [2, 3])
+def test_multitoken_split_then_combine_equals_unsplit(S):
+    """Page-aligned splits; with n = 33, P = 16 the last split holds one
+    token, which queries 0 .. 2 of 4 do not see: their partial is empty."""
+    q_len = 4
+    case = W.make_gqa(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=8, page_size=16,
+                      context_lens=[33, 50], q_dtype="f32", kv_dtype="f32", seed=71,
+                      extra_pages=1, q_len=q_len)
+    out, lse = _run(case)
+    B, Hq, P = 2, 4, 16
+    po = np.zeros((B, q_len, Hq, S, 8))
+    pl = np.zeros((B, Hq, q_len, S))
+    for s in range(S):
+        tb = np.zeros(B, np.int32)
+        te = np.zeros(B, np.int32)
+        for b, n in enumerate(case.context_lens):
+            per = -(-(-(-int(n) // P)) // S)
+            tb[b] = min(s * per * P, n)
+            te[b] = min((s + 1) * per * P, n)
+        o_s, l_s = _run(case, tok_begin=tb, tok_end=te)
+        po[..., s, :], pl[..., s] = o_s, l_s
+    if S == 3:
+        assert np.isneginf(pl[0, :, :3, 2]).all() and np.isfinite(pl[0, :, 3, 2]).all()
+    # the combine merges rows (b, i, h): partial LSEs in the same row order
+    co, cl = oracle.combine(po, np.ascontiguousarray(pl.transpose(0, 2, 1, 3)))
+    np.testing.assert_allclose(co, out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(cl.transpose(0, 2, 1), lse, rtol=0, atol=1e-12)
+
+
+def test_mla_multitoken_matches_gqa_oracle_with_aliased_value():
+    """MLA with s_q = 2 equals the GQA oracle on K = the record, V = its first
+    d_latent values, one KV head, the same causal mask."""
+    case = W.make_mla(batch=2, num_q_heads=4, d_latent=16, d_rope=8, page_size=8,
+                      context_lens=[9, 30], dtype="f32", seed=81, scale=0.2, extra_pages=1,
+                      q_len=2)
+    out, lse = _run(case)
+    k = case.k_cache[:, :, None, :]
+    v = np.ascontiguousarray(case.k_cache[:, :, None, :16])
+    o2, l2 = oracle.paged_attention(case.q, k, v, case.block_tables, case.context_lens,
+                                    scale=0.2, q_dtype="f32", kv_dtype="f32", causal=True)
+    np.testing.assert_allclose(out, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l2, rtol=0, atol=1e-12)
+    assert out.shape == (2, 2, 4, 16) and lse.shape == (2, 4, 2)
+
+
+def test_mla_multitoken_prefix_property():
+    case = W.make_mla(batch=2, num_q_heads=4, d_latent=16, d_rope=8, page_size=8,
+                      context_lens=[3, 30], dtype="bf16", seed=82, scale=0.2, extra_pages=1,
+                      q_len=3)
+    out, lse = _run(case)
+    for i in range(3):
+        one = W.PagedCase(**{**case.__dict__})
+        one.q = np.ascontiguousarray(case.q[:, i])
+        one.context_lens = (case.context_lens - (2 - i)).astype(np.int32)
+        o1, l1 = _run(one)
+        assert np.array_equal(out[:, i], o1) and np.array_equal(lse[:, :, i], l1)
