@@ -23,6 +23,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Growth of a tile's max over the running reference (log2 units) that
 // triggers a rescale; probabilities stay below 2^kLazyMax.
 constexpr float kLazyMax = 8.0f;
+// Start of a running max: the most negative finite float instead of -inf, so
+// that a query row whose tokens are all masked so far (a causal mask can hide
+// a whole tile or range from the early queries) keeps a rescale factor of
+// exp2(0) = 1 and probabilities exp2(-inf) = 0 rather than exp2(-inf + inf).
+constexpr float kMaxStart = -3.40282346638528859812e+38f;
 // dword 3 of a gfx9-family buffer resource: 32-bit data format, raw access.
 constexpr int kRsrcFlags = 0x00020000;
 

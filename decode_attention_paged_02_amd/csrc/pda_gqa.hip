@@ -456,8 +456,8 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
 
 constexpr int kCombineThreads = 256;
 
-// One workgroup per (sequence, query head) row whose sequence was split and
-// per CW-wide column chunk of it (CW = min(DV, 128)):
+// One workgroup per (sequence, query token, query head) row whose sequence
+// was split and per CW-wide column chunk of it (CW = min(DV, 128)):
 // L = M + ln sum_s exp(L_s - M), O = sum_s exp(L_s - M) O_s / sum_s exp(L_s - M)
 // with M = max_s L_s ("From MHA to MLA" sec. 4).  Rows of unsplit sequences
 // were written by the attention kernel and are skipped.  The threads form
@@ -470,7 +470,7 @@ constexpr int kCombineThreads = 256;
 // arguments ahead of CombineArgs, as in the attention kernels.
 template <class OT, int DV>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    const float* part_o, const float* part_lse, const int32_t* context_lens, int32_t num_q_heads,
+    const float* part_o, const float* part_lse, const int32_t* context_lens, int32_t rows_per_seq,
     int32_t max_splits, int32_t pages_per_split, int32_t split_min_tokens, int32_t page_size,
     CombineArgs a) {
   constexpr int CW = DV > 128 ? 128 : DV;       // columns per workgroup
@@ -482,9 +482,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   __shared__ f32x4 acc_sh[SG][DC];
   __shared__ float den_sh[SG], mx_sh[SG];
 
-  const int64_t row = blockIdx.x / NCH;
+  const int64_t row = blockIdx.x / NCH;  // (b, query token i, head h)
   const int chunk = blockIdx.x % NCH;
-  const int b = (int)(row / num_q_heads);
+  const int b = (int)(row / rows_per_seq);
   const int S = max_splits;
   const SplitLayout sp{pages_per_split, max_splits, split_min_tokens};
   const float* pl = part_lse + row * S;
@@ -574,7 +574,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     store_out<OT>(a.out, o0 + 1, t.y * inv);
     store_out<OT>(a.out, o0 + 2, t.z * inv);
     store_out<OT>(a.out, o0 + 3, t.w * inv);
-    if (threadIdx.x == 0 && chunk == 0 && a.lse) a.lse[row] = d > 0.f ? M + __logf(d) : -INFINITY;
+    if (threadIdx.x == 0 && chunk == 0 && a.lse) {
+      // lse is [B, Hq, q_len]
+      const int ih = (int)(row - (int64_t)b * rows_per_seq);
+      const int i = ih / a.num_q_heads, h = ih - i * a.num_q_heads;
+      a.lse[((int64_t)b * a.num_q_heads + h) * a.q_len + i] = d > 0.f ? M + __logf(d) : -INFINITY;
+    }
   }
 }
 
@@ -687,10 +692,10 @@ hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
 template <class OT>
 hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
   const int nch = a.head_dim_v > 128 ? a.head_dim_v / 128 : 1;
-  dim3 grid((unsigned)(a.batch * a.num_q_heads * nch));
+  dim3 grid((unsigned)(a.batch * a.q_len * a.num_q_heads * nch));
   dim3 block(kCombineThreads);
 #define PDA_COMBINE_ARGS                                                                    \
-  a.part_o, a.part_lse, a.context_lens, a.num_q_heads, a.split.max_splits,                 \
+  a.part_o, a.part_lse, a.context_lens, a.q_len * a.num_q_heads, a.split.max_splits,       \
       a.split.pages_per_split, a.split.split_min_tokens, a.page_size, a
   switch (a.head_dim_v) {
     case 64: hipLaunchKernelGGL((combine_kernel<OT, 64>), grid, block, 0, s, PDA_COMBINE_ARGS); break;

@@ -25,8 +25,12 @@
 // tile into its own padded LDS tile and reads it back in the MFMA layout
 // (rows padded by 16 bytes: both directions are free of bank conflicts).
 //
-// With fewer than 16 heads in the group the spare MFMA columns are computed
-// on zero queries and never written.
+// The columns are the (query token, head) rows of the KV group: row
+// i * group + g is query token i of head g (one token per sequence in plain
+// decode, q_len with multi-token decode), so q_len * group rows are tiled by
+// 16.  Spare MFMA columns are computed on zero queries and never written.  A
+// causal mask gives each column its own token limit (query i of q_len sees
+// the first n - (q_len - 1 - i) tokens).
 #include "pda_device.h"
 
 namespace pda {
@@ -150,7 +154,7 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, f32x4 c
 template <class QT, class KT, int D>
 __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     const int32_t* context_lens, const int32_t* block_tables, const void* q, int32_t head_tiles,
-    int32_t num_kv_heads, int32_t group, int32_t num_q_heads, int32_t max_pages, int32_t log2_page,
+    int32_t num_kv_heads, int32_t group, int32_t q_len, int32_t max_pages, int32_t log2_page,
     int32_t pages_per_split, int32_t max_splits, const int32_t* units, GqaArgs a) {
   constexpr int ESZ = Elem<KT>::bytes;
   constexpr int PW = Piece<KT, D>::words;       // words of a loaded row piece
@@ -199,9 +203,9 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     split = blockIdx.y;
   }
 
-  const int g0 = tile * kMHeads;
-  const int hbase = kvh * group + g0;
-  const int gvalid = min(kMHeads, group - g0);
+  const int num_q_heads = group * num_kv_heads;
+  const int g0 = tile * kMHeads;                   // the tile's first row
+  const int gvalid = min(kMHeads, q_len * group - g0);
   const int log2P = log2_page;
   const int32_t* table = block_tables + (int64_t)b * max_pages;
   const int t0_hint = max_splits > 1 ? split * pages_per_split << log2P : 0;
@@ -233,11 +237,20 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   if (split == 0) n = load_uniform(context_lens + b);
 
   // Q^T as the B operand of the QK MFMAs: lane (col, grp) holds
-  // q[head col][32 j + 8 grp .. +8] for MFMA j; heads past the group are zero
+  // q[row col][32 j + 8 grp .. +8] for MFMA j; rows past the group are zero.
+  // Row g0 + col is query token qi of head g of the group.
+  int qi = 0;
   u32x4 qb[NQK];
   {
     const bool hv = col < gvalid;
-    const char* qrow = (const char*)q + (((int64_t)b * num_q_heads + hbase + (hv ? col : 0)) * D) * 2;
+    const int r = g0 + (hv ? col : 0);
+    int g = r;
+    if (q_len > 1) {
+      qi = r / group;
+      g = r - qi * group;
+    }
+    const char* qrow =
+        (const char*)q + ((((int64_t)b * q_len + qi) * num_q_heads + kvh * group + g) * D) * 2;
 #pragma unroll
     for (int j = 0; j < NQK; ++j) {
       const u32x4 w = *(const u32x4*)(qrow + (32 * j + 8 * grp) * 2);
@@ -249,6 +262,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   int nsplit, t0, t1;
   split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
   if (split >= nsplit) return;
+  // end of the tokens this lane's query token may see (t1 without a mask)
+  const int lim = min(t1, a.causal ? n - (q_len - 1 - qi) : n);
 
   const int tok_bytes = a.tok_stride * ESZ;
   // load j of a tile: token 4 grp + j, piece col of the row
@@ -257,7 +272,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   f32x4 acc[NE];  // O^T: rows (4 grp + i) * NE + e of the value, column = head col
 #pragma unroll
   for (int e = 0; e < NE; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = kMaxStart, l_run = 0.f;
   const float pinf = opaque_inf();
 
   const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
@@ -266,7 +281,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
 
   char* ktile = lds + wave * kTileB;
 
-  auto compute_tile = [&](const Words<PW> (&kf)[4], const Words<PW> (&vf)[4], int rows) {
+  // rows: valid token rows of the tile, tok: its first token
+  auto compute_tile = [&](const Words<PW> (&kf)[4], const Words<PW> (&vf)[4], int rows, int tok) {
     // ---- K tile into LDS in 16-bit form: row = token, piece col at 2 NE col bytes
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -291,11 +307,12 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
       st = mfma_qk<QT>(kk, qb[j], st);
     }
     // ---- online softmax (log2 domain, lazily moved reference max); this lane
-    // holds tokens 4 grp + i of head col
+    // holds tokens 4 grp + i of row col
+    const int rl = min(rows, lim - tok);
     float s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      s[i] = fminf(st[i] * a.qk_scale_log2, 4 * grp + i < rows ? INFINITY : -INFINITY);
+      s[i] = fminf(st[i] * a.qk_scale_log2, 4 * grp + i < rl ? INFINITY : -INFINITY);
     float tmax = max2(max2(s[0], s[1], pinf), max2(s[2], s[3], pinf), pinf);
     {
       float x, y;
@@ -369,7 +386,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   // kStepsPerChunk (one table entry per lane per tile).
   constexpr int SD = kGqaStepsInFlight;
   Words<PW> kb[SD][ST][4], vb[SD][ST][4];
-  int rows_b[SD][ST];
+  int rows_b[SD][ST], tok_b[SD][ST];
   auto issue = [&](int sidx, int send, int u) {
 #pragma unroll
     for (int t = 0; t < ST; ++t) {
@@ -380,6 +397,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
       const int tok = t0 + T * kTileTokens;
       const int rows = live ? min(kTileTokens, t1 - tok) : 0;
       rows_b[u][t] = rows;
+      tok_b[u][t] = tok;
       const int slot = tok & ((1 << log2P) - 1);
       const int64_t elem = (int64_t)phys * a.page_stride + (int64_t)slot * a.tok_stride;
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -411,7 +429,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
         // (a step's tiles past the range are computed on zero rows, fully
         // masked: no branch that would let the compiler sink their loads)
 #pragma unroll
-        for (int t = 0; t < ST; ++t) compute_tile(kb[u][t], vb[u][t], rows_b[u][t]);
+        for (int t = 0; t < ST; ++t) compute_tile(kb[u][t], vb[u][t], rows_b[u][t], tok_b[u][t]);
       }
     }
   chunk_done:
@@ -428,7 +446,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     m_sh[wave][col] = m_run;
     l_sh[wave][col] = l_run;
   }
-  if (col < gvalid) {  // only the heads of the group
+  if (col < gvalid) {  // only the rows of the group
     float* dst = acc_sh + (wave * kMHeads + col) * kAccStride;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -439,9 +457,10 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   }
   __syncthreads();
 
-  // Work items: four consecutive values of one valid head, spread over all
+  // Work items: four consecutive values of one valid row, spread over all
   // threads; each item issues its LDS reads (the four waves' max, sum and
   // values) before any arithmetic: weights exp2(m_w - max), one reciprocal.
+  // (A row no wave saw a token of keeps max kMaxStart and sum 0: out 0.)
   constexpr int kQ = D / 4;  // four-value items per head
   for (int it = threadIdx.x; it < gvalid * kQ; it += kMWaves * 64) {
     const int g = it / kQ, d0 = 4 * (it % kQ);
@@ -466,10 +485,20 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     }
     const float inv = den > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(den) : 0.f;
     const float o[4] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv};
-    const int64_t row = (int64_t)b * a.num_q_heads + hbase + g;
+    // row g0 + g of the group: query token i, head h; out row (b, i, h),
+    // lse [B, Hq, q_len]
+    int i = 0, gh = g0 + g;
+    if (q_len > 1) {
+      i = gh / group;
+      gh -= i * group;
+    }
+    const int h = kvh * group + gh;
+    const int64_t row = ((int64_t)b * q_len + i) * num_q_heads + h;
     if (nsplit == 1) {
       store_row<QT, 4>(a.out, row * D + d0, o);
-      if (d0 == 0 && a.lse) a.lse[row] = den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+      if (d0 == 0 && a.lse)
+        a.lse[((int64_t)b * num_q_heads + h) * q_len + i] =
+            den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
     } else {
       float* po = a.part_o + (row * a.split.max_splits + split) * D + d0;
       *(f32x4*)po = f32x4{o[0], o[1], o[2], o[3]};
@@ -487,7 +516,7 @@ hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStr
   dim3 block(kMWaves * 64);
   switch (head_dim) {
 #define PDA_MFMA_ARGS                                                                        \
-  a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.num_q_heads,  \
+  a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.q_len,        \
       a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a.units, a
     case 64: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64>), grid, block, 0, s, PDA_MFMA_ARGS); break;
     case 128: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128>), grid, block, 0, s, PDA_MFMA_ARGS); break;

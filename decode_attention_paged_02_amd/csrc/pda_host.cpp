@@ -30,13 +30,19 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool valid_dtype(int d) { return d >= PDA_F32 && d <= PDA_FP8_E4M3; }
 
+// Query tokens per sequence (q_len 0 stands for 1).
+int query_len(const pda_shape* s) { return s->q_len > 1 ? s->q_len : 1; }
+
 // Shape checks common to both entry points.
 int check_shape(const pda_shape* s, bool mla) {
   if (!s) return PDA_ERR_INVALID_ARG;
   if (s->batch < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->head_dim <= 0 ||
       s->head_dim_v <= 0 || s->page_size <= 0 || s->max_pages_per_seq <= 0 ||
-      s->num_pages <= 0 || s->split_min_tokens < 0)
+      s->num_pages <= 0 || s->split_min_tokens < 0 || s->q_len < 0 ||
+      (s->causal != 0 && s->causal != 1))
     return PDA_ERR_INVALID_ARG;
+  // (query, head) rows of a sequence stay well inside 32-bit indexing
+  if ((int64_t)query_len(s) * s->num_q_heads > (1 << 20)) return PDA_ERR_UNSUPPORTED;
   if (!valid_dtype(s->q_dtype) || !valid_dtype(s->kv_dtype)) return PDA_ERR_INVALID_ARG;
   if (s->num_q_heads % s->num_kv_heads != 0) return PDA_ERR_INVALID_ARG;
   if ((int64_t)s->max_pages_per_seq * s->page_size > INT32_MAX) return PDA_ERR_INVALID_ARG;
@@ -48,11 +54,17 @@ int check_shape(const pda_shape* s, bool mla) {
       return PDA_ERR_UNSUPPORTED;
     if (s->num_q_heads > 16 && s->num_q_heads % 16 != 0) return PDA_ERR_UNSUPPORTED;
     if (s->variant < PDA_MLA_DEFAULT || s->variant > PDA_MLA_VALU) return PDA_ERR_INVALID_ARG;
+    // several query tokens: the matrix-core kernel only
+    if (query_len(s) > 1 && s->variant == PDA_MLA_VALU) return PDA_ERR_UNSUPPORTED;
   } else {
     if (!pda::gqa_supported(s->q_dtype, s->kv_dtype, s->head_dim, s->head_dim_v))
       return PDA_ERR_UNSUPPORTED;
     if (s->variant < PDA_GQA_DEFAULT || s->variant > PDA_GQA_VALU) return PDA_ERR_INVALID_ARG;
     if (s->variant == PDA_GQA_MFMA && !pda::gqa_mfma_supported(s->q_dtype, s->kv_dtype, s->head_dim))
+      return PDA_ERR_UNSUPPORTED;
+    // several query tokens: the matrix-core kernel only
+    if (query_len(s) > 1 &&
+        (s->variant == PDA_GQA_VALU || !pda::gqa_mfma_supported(s->q_dtype, s->kv_dtype, s->head_dim)))
       return PDA_ERR_UNSUPPORTED;
     if (s->page_size % pda::kTileTokens != 0 || (s->page_size & (s->page_size - 1)) != 0)
       return PDA_ERR_UNSUPPORTED;
@@ -70,10 +82,11 @@ int check_shape(const pda_shape* s, bool mla) {
 // kernel (its 16 head columns are mostly padding below that).
 constexpr int kMfmaMinGroup = 3;
 
-// Whether a (validated) GQA call runs the matrix-core kernel.
+// Whether a (validated) GQA call runs the matrix-core kernel (its columns
+// are the q_len * group rows of a KV group).
 bool gqa_use_mfma(const pda_shape* s) {
   if (s->variant == PDA_GQA_VALU) return false;
-  if (s->variant == PDA_GQA_MFMA) return true;
+  if (s->variant == PDA_GQA_MFMA || query_len(s) > 1) return true;
   return pda::gqa_mfma_supported(s->q_dtype, s->kv_dtype, s->head_dim) &&
          s->num_q_heads / s->num_kv_heads >= kMfmaMinGroup;
 }
@@ -83,8 +96,9 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_pla
   int rc = check_shape(s, mla);
   if (rc != PDA_OK) return rc;
   const int group = s->num_q_heads / s->num_kv_heads;
-  const int head_tiles = mla             ? (int)ceil_div(s->num_q_heads, 16)
-                         : gqa_use_mfma(s) ? (int)ceil_div(group, 16)
+  const int ql = query_len(s);
+  const int head_tiles = mla             ? (int)ceil_div(ql * s->num_q_heads, 16)
+                         : gqa_use_mfma(s) ? (int)ceil_div(ql * group, 16)
                                            : (int)ceil_div(group, pda::gqa_tile_heads(group));
   const int64_t units = (int64_t)s->batch * s->num_kv_heads * head_tiles;
   const int max_pages = s->max_pages_per_seq;
@@ -116,7 +130,7 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_pla
   p->ordered = s->split_min_tokens > 0 && s->batch <= 65535 && units * splits <= INT32_MAX;
   uint64_t ws = 0;
   if (splits > 1) {
-    const uint64_t rows = (uint64_t)s->batch * s->num_q_heads;
+    const uint64_t rows = (uint64_t)s->batch * ql * s->num_q_heads;
     const uint64_t o_bytes = rows * splits * s->head_dim_v * sizeof(float);
     ws = ((o_bytes + 255) / 256) * 256 + ((rows * splits * sizeof(float) + 255) / 256) * 256;
   }
@@ -125,12 +139,12 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_pla
   return PDA_OK;
 }
 
-// Workspace layout: partial outputs [B, Hq, S, dv] fp32, partial LSE
-// [B, Hq, S] fp32 (both only when S > 1, each 256-byte aligned), then the
-// ordered unit list [B * S] int32 (only for ordered calls).
+// Workspace layout: partial outputs [B, q_len, Hq, S, dv] fp32, partial LSE
+// [B, q_len, Hq, S] fp32 (both only when S > 1, each 256-byte aligned), then
+// the ordered unit list [B * S] int32 (only for ordered calls).
 void workspace_parts(const pda_shape* s, const pda_plan_info& p, void* ws, float** po,
                      float** pl, int32_t** un) {
-  const uint64_t rows = (uint64_t)s->batch * s->num_q_heads;
+  const uint64_t rows = (uint64_t)s->batch * query_len(s) * s->num_q_heads;
   char* c = (char*)ws;
   *po = nullptr;
   *pl = nullptr;
@@ -221,6 +235,8 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   a.num_kv_heads = s.num_kv_heads;
   a.group = group;
   a.head_tiles = p.head_tiles;
+  a.q_len = query_len(shape);
+  a.causal = shape->causal;
   a.page_size = s.page_size;
   a.max_pages = s.max_pages_per_seq;
   a.log2_page = 0;
@@ -254,6 +270,7 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
     c.lse = lse;
     c.batch = s.batch;
     c.num_q_heads = s.num_q_heads;
+    c.q_len = query_len(shape);
     c.head_dim_v = s.head_dim_v;
     c.page_size = s.page_size;
     c.split = a.split;
@@ -293,6 +310,8 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
   a.batch = s.batch;
   a.num_q_heads = s.num_q_heads;
   a.head_tiles = p.head_tiles;
+  a.q_len = query_len(shape);
+  a.causal = shape->causal;
   a.page_size = s.page_size;
   a.max_pages = s.max_pages_per_seq;
   a.log2_page = 0;
@@ -317,6 +336,7 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
     c.lse = lse;
     c.batch = s.batch;
     c.num_q_heads = s.num_q_heads;
+    c.q_len = query_len(shape);
     c.head_dim_v = s.head_dim_v;
     c.page_size = s.page_size;
     c.split = a.split;

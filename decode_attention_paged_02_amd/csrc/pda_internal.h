@@ -64,9 +64,12 @@ struct GqaArgs {
   const int32_t* context_lens;
   void* out;
   float* lse;       // nullable
-  float* part_o;    // [B, Hq, max_splits, dv] fp32 (when max_splits > 1)
-  float* part_lse;  // [B, Hq, max_splits] fp32
+  float* part_o;    // [B, s_q, Hq, max_splits, dv] fp32 (when max_splits > 1)
+  float* part_lse;  // [B, s_q, Hq, max_splits] fp32
   int32_t batch, num_q_heads, num_kv_heads, group, head_tiles;
+  // query tokens per sequence; the rows of a KV group are (query i, head g)
+  // pairs, row i * group + g; causal: query i sees n - (q_len - 1 - i) tokens
+  int32_t q_len, causal;
   int32_t page_size, max_pages;
   int32_t log2_page;     // page_size == 1 << log2_page
   int32_t tok_stride;    // elements between consecutive tokens of a page (Hkv * d)
@@ -87,19 +90,21 @@ struct CombineArgs {
   void* out;
   float* lse;  // nullable
   int32_t batch, num_q_heads, head_dim_v, page_size;
+  int32_t q_len;  // partial rows are (b, query i, head h); lse is [B, Hq, q_len]
   SplitLayout split;
 };
 
 struct MlaArgs {
-  const void* q;           // [B, Hq, 576] bf16
+  const void* q;           // [B, q_len, Hq, 576] bf16
   const void* kv_cache;    // [num_pages, P, 576] bf16
   const int32_t* block_tables;
   const int32_t* context_lens;
-  void* out;               // [B, Hq, 512] bf16
+  void* out;               // [B, q_len, Hq, 512] bf16
   float* lse;
   float* part_o;
   float* part_lse;
   int32_t batch, num_q_heads, head_tiles;
+  int32_t q_len, causal;   // as in GqaArgs; tile rows are (query i, head h), i * Hq + h
   int32_t page_size, max_pages;
   int32_t log2_page;       // page_size == 1 << log2_page
   float qk_scale_log2;     // scale * log2(e)

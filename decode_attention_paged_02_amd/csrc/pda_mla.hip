@@ -32,15 +32,17 @@
 // Both keep the online softmax in the log2 domain with a lazily moved
 // reference max (see the GQA kernel) and write either the final bf16 output
 // or normalized fp32 partials + LSE for the split combine.
-#include "pda_internal.h"
+//
+// Multi-token decode (mla_mfma_kernel only): the 16 MFMA columns of a tile
+// are (query token, head) rows, row i * Hq + h for query token i of q_len,
+// and each column masks the tokens its query token may not see (causal:
+// query i sees the first n - (q_len - 1 - i) tokens).
+#include "pda_device.h"
 
 namespace pda {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short ldsv4s __attribute__((__vector_size__(4 * sizeof(short))));
 
@@ -52,46 +54,11 @@ constexpr int kThreads = 256;       // 4 waves
 constexpr int kRowBytes = kRec * 2;  // one record per LDS row (16-byte chunks swizzled)
 constexpr int kRowChunks = kRowBytes / 16;
 constexpr int kChunks = kBlock * kRec * 2 / 16 / kThreads;  // 16-byte loads per thread per block
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazyMax = 8.0f;
-constexpr int kRsrcFlags = 0x00020000;
 constexpr int kLoadPolicy = 2;      // non-temporal: each record is read once per head tile
 static_assert(kChunks * kThreads * 16 == kBlock * kRec * 2, "block split over threads");
 
-__device__ __forceinline__ void split_range(const SplitLayout& sp, int n, int P, int split,
-                                            int& nsplit, int& t0, int& t1) {
-  const int pages = (n + P - 1) / P;
-  if (sp.max_splits <= 1 || n <= sp.split_min_tokens) {
-    nsplit = 1;
-    t0 = 0;
-    t1 = n;
-  } else {
-    nsplit = (pages + sp.pages_per_split - 1) / sp.pages_per_split;
-    const int p0 = split * sp.pages_per_split;
-    t0 = p0 * P;
-    t1 = min((p0 + sp.pages_per_split) * P, n);
-  }
-}
-
-// A 32-bit value the kernel never writes, read with a scalar load.
-__device__ __forceinline__ int load_uniform(const int32_t* p) {
-  return *(const __attribute__((address_space(4))) int32_t*)p;
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
-
-__device__ __forceinline__ void swap16(float a, float b, float& ra, float& rb) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  ra = __uint_as_float(r[0]);
-  rb = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void swap32(float a, float b, float& ra, float& rb) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  ra = __uint_as_float(r[0]);
-  rb = __uint_as_float(r[1]);
-}
 // max / sum over the four lanes {l, l^16, l^32, l^48}
 __device__ __forceinline__ float max_x4(float x) {
   float a, b;
@@ -216,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   asm volatile("" ::"s"(a.q), "s"(a.kv_cache), "s"(a.block_tables), "s"(a.context_lens),
                "s"(a.num_q_heads), "s"(a.head_tiles), "s"(a.page_size), "s"(a.max_pages),
                "s"(a.log2_page), "s"(a.qk_scale_log2), "s"(a.split.pages_per_split),
-               "s"(a.split.max_splits), "s"(a.split.split_min_tokens));
+               "s"(a.split.max_splits), "s"(a.split.split_min_tokens), "s"(a.q_len));
   const int log2P = a.log2_page;
   int n = 0;
   if (split > 0) {
@@ -229,8 +196,16 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   pt.load(a.split.max_splits > 1 ? split * a.split.pages_per_split : 0, lane);
   if (split == 0) n = load_uniform(a.context_lens + b);
 
-  const int h = tile * kHeads + col;
-  const bool hvalid = h < a.num_q_heads;
+  // this lane's column: row r = query token qi, head h (rows past the last
+  // one compute on zero queries and are not written)
+  const int q_len = a.q_len;
+  const int r = tile * kHeads + col;
+  const bool hvalid = r < q_len * a.num_q_heads;
+  int qi = 0, h = r;
+  if (q_len > 1) {
+    qi = r / a.num_q_heads;
+    h = r - qi * a.num_q_heads;
+  }
   // The 18 chunks of 32 record values are shared out over the waves (5, 5, 4,
   // 4): wave w contracts chunks [c_lo, c_lo + n_w) of every key and the four
   // partial S^T are summed through LDS in a fixed order.
@@ -241,7 +216,8 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   bf16x8 qb[5];
   {
     const uint16_t* qrow =
-        (const uint16_t*)a.q + ((int64_t)b * a.num_q_heads + (hvalid ? h : 0)) * kRec;
+        (const uint16_t*)a.q +
+        (hvalid ? (((int64_t)b * q_len + qi) * a.num_q_heads + h) * kRec : 0);
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       const bool use = hvalid && j < n_w;
@@ -255,11 +231,13 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
   if (split >= nsplit) return;
   const int nblocks = (t1 - t0 + kBlock - 1) / kBlock;
+  // end of the tokens this column's query token may see (t1 without a mask)
+  const int lim = min(t1, a.causal ? n - (q_len - 1 - qi) : n);
 
   f32x4 acc[8];  // O^T rows 128*wave + 16*mb + 4*grp + i, column = head
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = kMaxStart, l_run = 0.f;
 
   // Two blocks in flight in registers while one is computed from LDS: block k
   // sits in ld[k % 2] until it is staged into LDS buffer k % 2, and the loads
@@ -275,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   // block blk from LDS; `nxt` holds block blk + 1 and then receives blk + 3
   auto body = [&](int blk, BlockLoader& nxt) {
     const char* L = lds[blk & 1];
-    const int rows = min(kBlock, t1 - (t0 + blk * kBlock));
+    const int rows = min(kBlock, lim - (t0 + blk * kBlock));  // per column
 
     // this wave's share of S^T for the two 16-key halves, then the sum of the
     // four shares (every wave adds them in the same order: identical S^T)
@@ -365,16 +343,17 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   }
 
   // epilogue: l over the four lane groups; lane holds 4 consecutive columns
+  // (out row (b, qi, h); lse [B, Hq, q_len])
   const float l = sum_x4(l_run);
   if (!hvalid) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const float lse = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
-  const int64_t row = (int64_t)b * a.num_q_heads + h;
+  const int64_t row = ((int64_t)b * q_len + qi) * a.num_q_heads + h;
   if (nsplit == 1) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
       store_bf16x4<0>(a.out, row * kDv + 128 * wave + 16 * mb + 4 * grp, acc[mb] * inv);
-    if (wave == 0 && grp == 0 && a.lse) a.lse[row] = lse;
+    if (wave == 0 && grp == 0 && a.lse) a.lse[((int64_t)b * a.num_q_heads + h) * q_len + qi] = lse;
   } else {
     float* po = a.part_o + (row * a.split.max_splits + split) * kDv;
 #pragma unroll

@@ -37,7 +37,8 @@ class Shape(ctypes.Structure):
                 ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
-                ("split_min_tokens", ctypes.c_int32), ("variant", ctypes.c_int32)]
+                ("split_min_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -112,10 +113,28 @@ def _need(cond, msg):
 
 def make_shape(*, batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, page_size,
                max_pages_per_seq, num_pages, q_dtype, kv_dtype, k_scale=1.0, v_scale=1.0,
-               split_min_tokens=0, variant=0) -> Shape:
+               split_min_tokens=0, variant=0, q_len=1, causal=True) -> Shape:
     return Shape(batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, page_size,
                  max_pages_per_seq, num_pages, q_dtype, kv_dtype, k_scale, v_scale,
-                 split_min_tokens, variant)
+                 split_min_tokens, variant, q_len, int(causal))
+
+
+def _query_dims(q):
+    """(B, s_q, Hq, d) of q [B, Hq, d] (s_q = 1) or [B, s_q, Hq, d]."""
+    _need(q.dim() in (3, 4), "q must be [B, Hq, d] or [B, s_q, Hq, d]")
+    if q.dim() == 3:
+        B, Hq, d = q.shape
+        return B, 1, Hq, d
+    return tuple(q.shape)
+
+
+def _result_shapes(q, dv):
+    """out and lse shapes for q: [B, Hq, dv] / [B, Hq], or [B, s_q, Hq, dv] /
+    [B, Hq, s_q] for several query tokens."""
+    B, s_q, Hq, _ = _query_dims(q)
+    if q.dim() == 3:
+        return (B, Hq, dv), (B, Hq)
+    return (B, s_q, Hq, dv), (B, Hq, s_q)
 
 
 def plan(shape: Shape, *, mla: bool = False, num_splits: int = 0, num_cus: int = 0) -> PlanInfo:
@@ -129,9 +148,9 @@ def plan(shape: Shape, *, mla: bool = False, num_splits: int = 0, num_cus: int =
 
 
 def gqa_shape(q, k_cache, v_cache, block_tables, *, k_scale=1.0, v_scale=1.0,
-              split_min_tokens=0, variant=0) -> Shape:
-    _need(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4, "bad ranks")
-    B, Hq, d = q.shape
+              split_min_tokens=0, variant=0, causal=True) -> Shape:
+    _need(k_cache.dim() == 4 and v_cache.dim() == 4, "bad ranks")
+    B, s_q, Hq, d = _query_dims(q)
     num_pages, P, Hkv, dk = k_cache.shape
     _need(dk == d and v_cache.shape[:3] == k_cache.shape[:3], "cache shapes do not match q")
     _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, *]")
@@ -140,13 +159,13 @@ def gqa_shape(q, k_cache, v_cache, block_tables, *, k_scale=1.0, v_scale=1.0,
                       max_pages_per_seq=block_tables.shape[1], num_pages=num_pages,
                       q_dtype=_dtype_code(q), kv_dtype=_dtype_code(k_cache, fp8_ok=True),
                       k_scale=k_scale, v_scale=v_scale, split_min_tokens=split_min_tokens,
-                      variant=variant)
+                      variant=variant, q_len=s_q, causal=causal)
 
 
 def mla_shape(q, kv_cache, block_tables, *, head_dim_v=512, variant=0,
-              split_min_tokens=0) -> Shape:
-    _need(q.dim() == 3 and kv_cache.dim() == 3, "bad ranks")
-    B, Hq, d = q.shape
+              split_min_tokens=0, causal=True) -> Shape:
+    _need(kv_cache.dim() == 3, "bad ranks")
+    B, s_q, Hq, d = _query_dims(q)
     num_pages, P, dk = kv_cache.shape
     _need(dk == d, "latent width of q and cache differ")
     _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, *]")
@@ -154,7 +173,8 @@ def mla_shape(q, kv_cache, block_tables, *, head_dim_v=512, variant=0,
                       head_dim_v=head_dim_v, page_size=P,
                       max_pages_per_seq=block_tables.shape[1], num_pages=num_pages,
                       q_dtype=_dtype_code(q), kv_dtype=_dtype_code(kv_cache),
-                      split_min_tokens=split_min_tokens, variant=variant)
+                      split_min_tokens=split_min_tokens, variant=variant, q_len=s_q,
+                      causal=causal)
 
 
 def _check_device(*ts):
@@ -173,18 +193,26 @@ def workspace_for(shape: Shape, *, mla: bool, num_splits: int, device) -> Option
 def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, scale: float,
                       num_splits: int = 0, out=None, lse=None, k_scale: float = 1.0,
                       v_scale: float = 1.0, split_min_tokens: int = 0, workspace=None,
-                      stream=None, return_lse: bool = True, variant: int = 0):
-    """GQA/MQA/MHA paged decode attention; returns (out [B, Hq, dv], lse [B, Hq] fp32)."""
+                      stream=None, return_lse: bool = True, variant: int = 0,
+                      causal: bool = True):
+    """GQA/MQA/MHA paged decode attention.
+
+    q [B, Hq, d] returns (out [B, Hq, dv], lse [B, Hq] fp32); q [B, s_q, Hq, d]
+    (s_q query tokens per sequence, the last s_q positions; causal: bottom-right
+    mask) returns (out [B, s_q, Hq, dv], lse [B, Hq, s_q] fp32)."""
     shape = gqa_shape(q, k_cache, v_cache, block_tables, k_scale=k_scale, v_scale=v_scale,
-                      split_min_tokens=split_min_tokens, variant=variant)
+                      split_min_tokens=split_min_tokens, variant=variant, causal=causal)
     _check_device(q, k_cache, v_cache, block_tables, context_lens, out, lse, workspace)
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
-    B, Hq, _ = q.shape
+    Hq = shape.num_q_heads
+    o_shape, l_shape = _result_shapes(q, shape.head_dim_v)
     if out is None:
-        out = torch.empty((B, Hq, shape.head_dim_v), dtype=q.dtype, device=q.device)
+        out = torch.empty(o_shape, dtype=q.dtype, device=q.device)
     if lse is None and return_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = torch.empty(l_shape, dtype=torch.float32, device=q.device)
+    _need(tuple(out.shape) == o_shape and (lse is None or tuple(lse.shape) == l_shape),
+          "out / lse shapes do not match q")
     if workspace is None:
         workspace = workspace_for(shape, mla=False, num_splits=num_splits, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -201,18 +229,21 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, scale:
 def paged_decode_attn_mla(q, kv_cache, block_tables, context_lens, *, scale: float,
                           num_splits: int = 0, out=None, lse=None, variant: int = 0,
                           head_dim_v: int = 512, split_min_tokens: int = 0, workspace=None,
-                          stream=None, return_lse: bool = True):
-    """MLA paged decode attention; returns (out [B, Hq, 512], lse [B, Hq] fp32)."""
+                          stream=None, return_lse: bool = True, causal: bool = True):
+    """MLA paged decode attention; returns (out [B, Hq, 512], lse [B, Hq] fp32),
+    or (out [B, s_q, Hq, 512], lse [B, Hq, s_q]) for q [B, s_q, Hq, 576]."""
     shape = mla_shape(q, kv_cache, block_tables, head_dim_v=head_dim_v, variant=variant,
-                      split_min_tokens=split_min_tokens)
+                      split_min_tokens=split_min_tokens, causal=causal)
     _check_device(q, kv_cache, block_tables, context_lens, out, lse, workspace)
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
-    B, Hq, _ = q.shape
+    o_shape, l_shape = _result_shapes(q, head_dim_v)
     if out is None:
-        out = torch.empty((B, Hq, head_dim_v), dtype=q.dtype, device=q.device)
+        out = torch.empty(o_shape, dtype=q.dtype, device=q.device)
     if lse is None and return_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = torch.empty(l_shape, dtype=torch.float32, device=q.device)
+    _need(tuple(out.shape) == o_shape and (lse is None or tuple(lse.shape) == l_shape),
+          "out / lse shapes do not match q")
     if workspace is None:
         workspace = workspace_for(shape, mla=True, num_splits=num_splits, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -262,6 +293,7 @@ def to_device(case, device="cuda") -> DeviceCase:
 def run_case(case, dev: Optional[DeviceCase] = None, **kw):
     """Run the HIP path on a workloads.PagedCase; returns (out, lse) device tensors."""
     dev = dev or to_device(case)
+    kw.setdefault("causal", case.causal)
     if case.mla:
         return paged_decode_attn_mla(dev.q, dev.k_cache, dev.block_tables, dev.context_lens,
                                      scale=case.scale, head_dim_v=case.d_latent, **kw)

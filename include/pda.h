@@ -18,6 +18,15 @@
  *   one latent record per token [c (512) | k_R (64)] shared by all query
  *   heads; K_j = the 576-wide record, V_j = its first 512 values.
  *
+ *   Several query tokens per sequence (multi-token decode, e.g. speculative
+ *   or MTP drafts: FlashMLA-ETAP README, "Supported configurations" and
+ *   "Usage"): with shape->q_len = s_q > 1 the s_q queries of sequence b are
+ *   its last s_q tokens, query i at position n - s_q + i.  With the causal
+ *   mask aligned bottom-right ("From MHA to MLA" sec. 2, the reference
+ *   kernel's causal branch) query i attends to the first n - (s_q - 1 - i)
+ *   tokens; without it every query attends to all n.  A query that sees no
+ *   token gets out = 0 and lse = -inf.
+ *
  * Long sequences may be cut into page-aligned splits (Flash-Decoding,
  * "From MHA to MLA" sec. 4); each split writes a normalized partial output
  * and its LSE to the workspace and a combine pass merges them with weights
@@ -28,15 +37,16 @@
  *  - Pointers named *_cache, q, out, lse, block_tables, context_lens and
  *    workspace are DEVICE pointers owned by the caller; the library neither
  *    allocates nor retains memory.  `shape` and `plan` are HOST pointers.
- *  - All arrays are dense row-major with the last dimension contiguous:
- *      q            [B, Hq, head_dim]          of shape->q_dtype
+ *  - All arrays are dense row-major with the last dimension contiguous
+ *    (s_q = shape->q_len; for s_q = 1 the layouts below are [B, Hq, ...]):
+ *      q            [B, s_q, Hq, head_dim]     of shape->q_dtype
  *      k_cache      [num_pages, P, Hkv, head_dim]   of shape->kv_dtype
  *      v_cache      [num_pages, P, Hkv, head_dim_v] of shape->kv_dtype
  *      kv_cache     [num_pages, P, head_dim]   (MLA, K and V share it)
  *      block_tables [B, max_pages_per_seq] int32 (logical -> physical page)
  *      context_lens [B] int32, the number of cached tokens of each sequence
- *      out          [B, Hq, head_dim_v]        of shape->q_dtype
- *      lse          [B, Hq] float32, may be NULL
+ *      out          [B, s_q, Hq, head_dim_v]   of shape->q_dtype
+ *      lse          [B, Hq, s_q] float32, may be NULL
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *    asynchronous on that stream and never synchronize.  Calls that share a
  *    workspace must be ordered on one stream.
@@ -97,6 +107,10 @@ typedef struct pda_shape {
   int32_t split_min_tokens;  /* sequences with context_lens[b] <= this are */
                              /* never split (0: any sequence may split)    */
   int32_t variant;           /* kernel variant, 0 = default (see below)    */
+  int32_t q_len;             /* s_q, query tokens per sequence (0 means 1;  */
+                             /* q_len * num_q_heads at most 2^20)          */
+  int32_t causal;            /* s_q > 1: 1 = bottom-right causal mask,      */
+                             /* 0 = every query sees all n tokens           */
 } pda_shape;
 
 /* GQA kernel variants (pda_shape.variant for paged_decode_attn). */
@@ -148,7 +162,9 @@ size_t pda_workspace_bytes(const pda_shape* shape, int is_mla, int num_splits);
  * the softmax (k_scale/v_scale are applied on top for FP8 caches).
  * Supported: (q, kv) dtypes (F32,F32), (F16,F16), (BF16,BF16), (F16,FP8),
  * (BF16,FP8); head_dim == head_dim_v in {64, 128, 256} (256 not for F32);
- * page_size a power of two, at least 16.
+ * page_size a power of two, at least 16.  q_len > 1 needs F16 or BF16
+ * queries and a variant other than PDA_GQA_VALU (the matrix-core kernel,
+ * whose columns are the q_len * group (query, head) rows of a KV group).
  * workspace: at least pda_workspace_bytes(shape, 0, num_splits) bytes, may
  * be NULL when that is 0. */
 int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -161,7 +177,8 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
  * "From MHA to MLA" sec. 6).  shape->num_kv_heads must be 1, head_dim 576,
  * head_dim_v 512, q_dtype == kv_dtype == PDA_BF16, page_size a power of two,
  * at least 64, num_q_heads a multiple of 16 or at most 16.  k_scale/v_scale are
- * ignored.  The variant field picks the kernel (PDA_MLA_*). */
+ * ignored.  The variant field picks the kernel (PDA_MLA_*); q_len > 1 needs
+ * PDA_MLA_DEFAULT or PDA_MLA_MFMA. */
 int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* block_tables,
                           const int32_t* context_lens, float scale, int num_splits,
                           void* out, float* lse, const pda_shape* shape, void* workspace,

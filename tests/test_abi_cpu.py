@@ -96,6 +96,30 @@ def test_plan_head_tiles():
     assert p.head_tiles == 1
 
 
+def test_plan_multi_token_rows():
+    """With q_len query tokens the matrix-core tiles hold q_len * group rows
+    (query token, head), and the partials cover every (b, token, head) row."""
+    assert pda.plan(_shape(q_len=4), num_cus=256).head_tiles == 1          # 4 x 4 rows
+    assert pda.plan(_shape(q_len=5), num_cus=256).head_tiles == 2          # 20 rows
+    assert pda.plan(_shape(num_q_heads=64, q_len=3), num_cus=256).head_tiles == 2
+    # a group of 1 or 2 takes the matrix-core kernel once q_len > 1
+    assert pda.plan(_shape(num_q_heads=8, q_len=2), num_cus=256).head_tiles == 1
+    assert pda.plan(_shape(num_q_heads=8, q_len=0), num_cus=256).head_tiles == 1
+    s = _shape(batch=1, max_pages_per_seq=2048, q_len=3)
+    p = pda.plan(s, num_splits=8, num_cus=256)
+    rows = 3 * 32
+    assert p.workspace_bytes == rows * 8 * 128 * 4 + -(-(rows * 8 * 4) // 256) * 256
+    mla = dict(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512, page_size=64,
+               q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16)
+    assert pda.plan(_shape(q_len=2, **mla), mla=True, num_cus=256).head_tiles == 2
+    assert pda.plan(_shape(q_len=3, **{**mla, "num_q_heads": 8}), mla=True,
+                    num_cus=256).head_tiles == 2
+    fake = ctypes.c_void_p(0x1000)
+    bad = _shape(q_len=2, variant=pda.PDA_MLA_VALU, **mla)
+    assert pda.load().paged_decode_attn_mla(fake, fake, fake, fake, 0.1, 1, fake, None,
+                                            ctypes.byref(bad), None, 0, None) == 2
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(num_q_heads=30), 1),                                  # Hq % Hkv != 0
     (dict(page_size=8), 2),                                     # not a multiple of 16
@@ -109,6 +133,11 @@ def test_plan_head_tiles():
     (dict(q_dtype=7), 1),
     (dict(variant=3), 1),                                       # no such GQA variant
     (dict(q_dtype=pda.PDA_F32, kv_dtype=pda.PDA_F32, variant=pda.PDA_GQA_MFMA), 2),
+    (dict(q_len=-1), 1),                                        # negative query count
+    (dict(q_len=2, causal=2), 1),                               # causal is 0 or 1
+    (dict(q_len=2, variant=pda.PDA_GQA_VALU), 2),               # several tokens: MFMA only
+    (dict(q_len=2, q_dtype=pda.PDA_F32, kv_dtype=pda.PDA_F32), 2),
+    (dict(q_len=1 << 16), 2),                                   # q_len * Hq > 2^20
 ])
 def test_invalid_shapes_rejected_before_device_work(kw, status):
     s = _shape(**kw)
