@@ -45,6 +45,10 @@ def make_case(name):
         return W.mla_b16()
     if name == "ragged_fp8":
         return W.ragged_fp8()
+    if name == "gqa_b64_q2":
+        return W.gqa_batch64_mtp(2)
+    if name == "mla_b16_q2":
+        return W.mla_b16_mtp(2)
     raise SystemExit("unknown workload %s" % name)
 
 
@@ -77,16 +81,18 @@ def run_gpu(case, workload, steps, warmup, pools):
     caches = [(dev.k_cache, dev.v_cache)]
     for _ in range(n_pools - 1):
         caches.append((dev.k_cache.clone(), None if dev.v_cache is None else dev.v_cache.clone()))
-    B, Hq = case.batch, case.num_q_heads
-    out = torch.empty((B, Hq, case.head_dim_v), dtype=dev.q.dtype, device="cuda")
-    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    o_shape, l_shape = pda._result_shapes(dev.q, case.head_dim_v)
+    out = torch.empty(o_shape, dtype=dev.q.dtype, device="cuda")
+    lse = torch.empty(l_shape, dtype=torch.float32, device="cuda")
     if case.mla:
         shape = pda.mla_shape(dev.q, dev.k_cache, dev.block_tables, head_dim_v=case.d_latent,
-                              split_min_tokens=kw.get("split_min_tokens", 0))
+                              split_min_tokens=kw.get("split_min_tokens", 0),
+                              causal=case.causal)
     else:
         shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
                               k_scale=case.k_scale, v_scale=case.v_scale,
-                              split_min_tokens=kw.get("split_min_tokens", 0))
+                              split_min_tokens=kw.get("split_min_tokens", 0),
+                              causal=case.causal)
     nsplit = kw.get("num_splits", 0)
     plan = pda.plan(shape, mla=case.mla, num_splits=nsplit)
     ws = pda.workspace_for(shape, mla=case.mla, num_splits=nsplit, device="cuda")
@@ -122,7 +128,7 @@ def cpu_baseline(case, budget_s=20.0):
     import oracle
     from decode_attention_paged_02_amd import accounting as A
     threads = oracle.max_threads()
-    rows = np.zeros((case.batch, case.num_q_heads), dtype=bool)
+    rows = np.zeros(case.q.shape[:-1], dtype=bool)     # [B, Hq] or [B, s_q, Hq]
     # time one sequence to size the sample
     rows[0] = True
     t = time.perf_counter()
@@ -152,11 +158,12 @@ def _oracle_call(case, rows):
     if case.mla:
         return oracle.mla_attention(case.q, case.k_cache, case.block_tables, case.context_lens,
                                     scale=case.scale, d_latent=case.d_latent,
-                                    q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, rows=rows)
+                                    q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
+                                    causal=case.causal, rows=rows)
     return oracle.paged_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
                                   case.context_lens, scale=case.scale, q_dtype=case.q_dtype,
                                   kv_dtype=case.kv_dtype, k_scale=case.k_scale,
-                                  v_scale=case.v_scale, rows=rows)
+                                  v_scale=case.v_scale, causal=case.causal, rows=rows)
 
 
 def bandwidth_probe(nbytes=2 << 30, reps=10):
@@ -192,7 +199,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa_b64",
-                    choices=["gqa_b64", "gqa_b1_split", "gqa_b4_split", "mla_b16", "ragged_fp8"])
+                    choices=["gqa_b64", "gqa_b1_split", "gqa_b4_split", "mla_b16", "ragged_fp8",
+                             "gqa_b64_q2", "mla_b16_q2"])
     ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
     ap.add_argument("--others", default="gqa_b1_split,gqa_b4_split",
                     help="extra workloads measured into 'other_workloads' ('' for none)")
@@ -257,6 +265,7 @@ def main():
                    "head_dim": case.head_dim, "page_size": case.page_size,
                    "context_lens": "uniform %d" % int(case.context_lens[0])
                    if len(set(case.context_lens.tolist())) == 1 else "ragged",
+                   "q_len": case.q_len,
                    "max_splits": r["max_splits"], "kv_bytes_per_step": r["kv_bytes"],
                    "rotating_pools": r["n_pools"]},
         "roofline": roof, "cpu_baseline": cpu, "other_workloads": others,

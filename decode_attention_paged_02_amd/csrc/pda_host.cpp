@@ -97,7 +97,11 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_pla
   if (rc != PDA_OK) return rc;
   const int group = s->num_q_heads / s->num_kv_heads;
   const int ql = query_len(s);
-  const int head_tiles = mla             ? (int)ceil_div(ql * s->num_q_heads, 16)
+  // MLA matrix-core tiles hold 16 rows per column group (two groups in a
+  // 512-thread workgroup, which then runs one per compute unit)
+  const int mla_groups =
+      mla && s->variant != PDA_MLA_VALU ? pda::mla_column_groups(ql * s->num_q_heads) : 1;
+  const int head_tiles = mla             ? (int)ceil_div(ql * s->num_q_heads, 16 * mla_groups)
                          : gqa_use_mfma(s) ? (int)ceil_div(ql * group, 16)
                                            : (int)ceil_div(group, pda::gqa_tile_heads(group));
   const int64_t units = (int64_t)s->batch * s->num_kv_heads * head_tiles;
@@ -109,9 +113,10 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_pla
   } else {
     if (num_cus == 0) num_cus = device_cus();
     if (num_cus <= 0) return PDA_ERR_HIP;
-    // Two workgroups per compute unit; split only when the (sequence, head
-    // tile) units alone cannot reach that.
-    const int64_t target = 2 * (int64_t)num_cus;
+    // Eight waves per compute unit (two four-wave workgroups, or one of
+    // eight); split only when the (sequence, head tile) units alone cannot
+    // reach that.
+    const int64_t target = (mla_groups == 2 ? 1 : 2) * (int64_t)num_cus;
     if (units > 0 && units < target)
       splits = (int)std::min<int64_t>(ceil_div(target, units), max_pages);
   }

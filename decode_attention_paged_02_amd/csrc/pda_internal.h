@@ -121,6 +121,11 @@ struct OrderArgs {
   SplitLayout split;
 };
 
+// Column groups of 16 rows in a workgroup of the MLA matrix-core kernel for
+// `rows` (query token, head) rows per sequence: two (512 threads) once there
+// are more than 16, so that one staged block serves 32 rows.
+inline int mla_column_groups(int rows) { return rows > 16 ? 2 : 1; }
+
 // Host-side support queries (no HIP calls).
 bool gqa_supported(int q_dtype, int kv_dtype, int head_dim, int head_dim_v);
 int gqa_tile_heads(int group);  // query heads per workgroup tile for a group size

@@ -36,7 +36,11 @@
 // Multi-token decode (mla_mfma_kernel only): the 16 MFMA columns of a tile
 // are (query token, head) rows, row i * Hq + h for query token i of q_len,
 // and each column masks the tokens its query token may not see (causal:
-// query i sees the first n - (q_len - 1 - i) tokens).
+// query i sees the first n - (q_len - 1 - i) tokens).  When a sequence has
+// more than 16 rows (q_len * Hq > 16), a workgroup of two four-wave groups
+// carries 32 rows over every staged block: each group computes its own 16
+// columns from the shared LDS block, so the cache is read once per 32 rows
+// rather than once per 16.
 #include "pda_device.h"
 
 namespace pda {
@@ -50,12 +54,11 @@ constexpr int kRec = 576;           // record width (latent 512 + rope 64)
 constexpr int kDv = 512;            // value width
 constexpr int kHeads = 16;          // query heads per workgroup tile
 constexpr int kBlock = 32;          // tokens per LDS block
-constexpr int kThreads = 256;       // 4 waves
+constexpr int kThreads = 256;       // 4 waves: one column group of 16 rows
 constexpr int kRowBytes = kRec * 2;  // one record per LDS row (16-byte chunks swizzled)
 constexpr int kRowChunks = kRowBytes / 16;
-constexpr int kChunks = kBlock * kRec * 2 / 16 / kThreads;  // 16-byte loads per thread per block
-constexpr int kLoadPolicy = 2;      // non-temporal: each record is read once per head tile
-static_assert(kChunks * kThreads * 16 == kBlock * kRec * 2, "block split over threads");
+constexpr int kBlockChunks = kBlock * kRowChunks;  // 16-byte chunks of a staged block
+constexpr int kLoadPolicy = 2;      // non-temporal: each record is read once per row tile
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -106,10 +109,14 @@ struct PageTable {
   }
 };
 
-// Shared block staging: the workgroup's 256 threads bring one block of 32
-// records (36 KiB) into registers with 16-byte loads, then into LDS.
+// Shared block staging: the workgroup's T threads bring one block of 32
+// records (36 KiB) into registers with 16-byte loads, then into LDS.  With
+// T = 512 the last load of a thread may lie past the block: its offset is
+// outside the buffer resource (zero, no memory access) and it is not stored.
+template <int T>
 struct BlockLoader {
-  u32x4 r[kChunks];
+  static constexpr int kN = (kBlockChunks + T - 1) / T;  // loads per thread
+  u32x4 r[kN];
 
   // Load block `blk` of the range [t0, t1) (tokens t0 + 32 blk ...).  Rows
   // past t1 (and a block past the range) read as zero without memory access.
@@ -126,16 +133,18 @@ struct BlockLoader {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const char*)a.kv_cache + rec0 * (kRec * 2)), 0, rows * kRec * 2, kRsrcFlags);
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i)
-      r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + i * kThreads) * 16, 0, kLoadPolicy);
+    for (int i = 0; i < kN; ++i)
+      r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + i * T) * 16, 0, kLoadPolicy);
   }
 
   __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int q = tid + i * kThreads;
-      const int row = q / kRowChunks, col = q % kRowChunks;
-      *(u32x4*)(lds + lds_off(row, col)) = r[i];
+    for (int i = 0; i < kN; ++i) {
+      const int q = tid + i * T;
+      if (kN * T == kBlockChunks || q < kBlockChunks) {
+        const int row = q / kRowChunks, col = q % kRowChunks;
+        *(u32x4*)(lds + lds_off(row, col)) = r[i];
+      }
     }
   }
 };
@@ -154,14 +163,19 @@ __device__ __forceinline__ void store_bf16x4(void* out, int64_t i, f32x4 v) {
 
 // ------------------------------------------------------------ MFMA kernel
 
-__global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
+// NG column groups of four waves; a workgroup owns 16 NG rows.
+template <int NG>
+__global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs a) {
+  constexpr int T = kThreads * NG;
   __shared__ __attribute__((aligned(16))) char lds[2][kBlock * kRowBytes];
-  __shared__ f32x4 spart[kThreads / 64][2][64];  // per-wave partial S^T of a block
+  __shared__ f32x4 spart[4 * NG][2][64];  // per-wave partial S^T of a block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15;      // MFMA column: the head
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = wid >> 2;        // column group: rows 16 cg .. 16 cg + 15 of the tile
+  const int wave = wid & 3;       // wave within the group
+  const int col = lane & 15;      // MFMA column: the row
   const int grp = lane >> 4;      // lane group: rows 4*grp..4*grp+3 of an MFMA tile
 
   // (ordered: the unit list gives (sequence, split), see pda_internal.h)
@@ -199,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   // this lane's column: row r = query token qi, head h (rows past the last
   // one compute on zero queries and are not written)
   const int q_len = a.q_len;
-  const int r = tile * kHeads + col;
+  const int r = tile * (kHeads * NG) + kHeads * cg + col;
   const bool hvalid = r < q_len * a.num_q_heads;
   int qi = 0, h = r;
   if (q_len > 1) {
@@ -243,15 +257,16 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
   // sits in ld[k % 2] until it is staged into LDS buffer k % 2, and the loads
   // of block k + 2 go into the registers it leaves.  Loads of blocks past the
   // range have empty resources (no memory access), so they need no branch.
-  BlockLoader ld[2];
+  // (A deeper ring for the 512-thread workgroups measured no gain.)
+  BlockLoader<T> ld[2];
   ld[0].load(a, pt, t0, t1, 0, log2P, tid);
   ld[0].store(lds[0], tid);
   ld[1].load(a, pt, t0, t1, 1, log2P, tid);
   ld[0].load(a, pt, t0, t1, 2, log2P, tid);
   __syncthreads();
 
-  // block blk from LDS; `nxt` holds block blk + 1 and then receives blk + 3
-  auto body = [&](int blk, BlockLoader& nxt) {
+  // block blk from LDS
+  auto compute = [&](int blk) {
     const char* L = lds[blk & 1];
     const int rows = min(kBlock, lim - (t0 + blk * kBlock));  // per column
 
@@ -268,13 +283,15 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
           sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[j], sp, 0, 0, 0);
         }
       }
-      spart[wave][kb][lane] = sp;
+      spart[wid][kb][lane] = sp;
     }
     __syncthreads();
     f32x4 st[2];
+    const int w0 = 4 * cg;  // the group's four shares
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      st[kb] = ((spart[0][kb][lane] + spart[1][kb][lane]) + spart[2][kb][lane]) + spart[3][kb][lane];
+      st[kb] = ((spart[w0][kb][lane] + spart[w0 + 1][kb][lane]) + spart[w0 + 2][kb][lane]) +
+               spart[w0 + 3][kb][lane];
     // scale, mask rows past the context; lane holds keys 16 kb + 4 grp + i of head `col`
     float s[8];
     float tmax = -INFINITY;
@@ -295,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
     }
-    // P^T as the B operand of the 16x16x16 MFMA, split into two bf16 terms
+    // P^T as the B operand of the PV MFMA, split into two bf16 terms
     // p = p_hi + p_lo (bf16 alone would leave a 2^-9 relative error per
     // weight); both terms multiply the same V^T operand.
     s16x4 pb_hi[2], pb_lo[2];
@@ -310,9 +327,20 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
         pb_hi[kb][i] = __builtin_bit_cast(short, hi);
         pb_lo[kb][i] = __builtin_bit_cast(short, lo);
       }
-    // O^T += V^T P^T over this wave's 128 value columns
+    // O^T += V^T P^T over this wave's 128 value columns, one 16x16x32 MFMA
+    // per term over all 32 keys of the block.  The contraction index k of
+    // lane group g covers keys 4 g + 0..3 (k = 8 g + 0..3) and 16 + 4 g + 0..3
+    // (k = 8 g + 4..7): that is where the S^T layout left this lane's
+    // probabilities, and the two transposing reads below give the V^T
+    // operand the same key order (a sum over k does not depend on it).
+    const bf16x8 pk_hi = __builtin_bit_cast(bf16x8, __builtin_shufflevector(
+                                                        pb_hi[0], pb_hi[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    const bf16x8 pk_lo = __builtin_bit_cast(bf16x8, __builtin_shufflevector(
+                                                        pb_lo[0], pb_lo[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    bf16x8 va[8];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
+      s16x4 vt[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // transposing read: lane q of group g points at key 16 kb + 4 g + q/4,
@@ -322,17 +350,27 @@ __global__ __launch_bounds__(kThreads, 2) void mla_mfma_kernel(MlaArgs a) {
         const int r = 16 * kb + 4 * grp + (q >> 2);
         const int byte = (128 * wave + 16 * mb + 4 * (q & 3)) * 2;
         const char* p = L + lds_off(r, byte >> 4) + (byte & 15);
-        const s16x4 vt = __builtin_bit_cast(
-            s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                       (__attribute__((address_space(3))) ldsv4s*)(p)));
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb_hi[kb], acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb_lo[kb], acc[mb], 0, 0, 0);
+        vt[kb] = __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                               (__attribute__((address_space(3))) ldsv4s*)(p)));
       }
+      va[mb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vt[0], vt[1], 0, 1, 2, 3, 4, 5,
+                                                                  6, 7));
     }
-    // stage the next block, start loading the one three ahead, hand over the
-    // buffer.  No branches around loads and stores: the wait counts then
-    // stay exact across iterations, and a block past the range is all zero
-    // rows (an odd block count computes one such block, fully masked).
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mb], pk_hi, acc[mb], 0, 0, 0);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mb], pk_lo, acc[mb], 0, 0, 0);
+  };
+  // block blk, then: stage the next block, start loading the one three
+  // ahead, hand over the buffer (`nxt` holds block blk + 1 and then receives
+  // blk + 3).  No branches around loads and stores (nor exits from the
+  // unrolled pair): the wait counts then stay exact across iterations, and a
+  // block past the range is all zero rows (an odd block count computes one
+  // such block, fully masked).
+  auto body = [&](int blk, BlockLoader<T>& nxt) {
+    compute(blk);
     nxt.store(lds[(blk + 1) & 1], tid);
     nxt.load(a, pt, t0, t1, blk + 3, log2P, tid);
     __syncthreads();
@@ -439,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
 
-  BlockLoader ld;
+  BlockLoader<kThreads> ld;
   ld.load(a, pt, t0, t1, 0, log2P, tid);
   ld.store(lds[0], tid);
   ld.load(a, pt, t0, t1, 1, log2P, tid);
@@ -548,11 +586,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
 hipError_t launch_mla(const MlaArgs& a, int variant, int max_splits, hipStream_t s) {
   const unsigned units = (unsigned)(a.batch * a.head_tiles);
   dim3 grid(a.units ? units * (unsigned)max_splits : units, a.units ? 1u : (unsigned)max_splits);
-  dim3 block(kThreads);
-  if (variant == 2)
-    hipLaunchKernelGGL(mla_valu_kernel, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(mla_mfma_kernel, grid, block, 0, s, a);
+  if (variant == 2) {
+    hipLaunchKernelGGL(mla_valu_kernel, grid, dim3(kThreads), 0, s, a);
+  } else if (mla_column_groups(a.q_len * a.num_q_heads) == 2) {
+    hipLaunchKernelGGL(mla_mfma_kernel<2>, grid, dim3(2 * kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(mla_mfma_kernel<1>, grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -258,6 +258,14 @@ def gqa_batch64(seed_offset: int = 0) -> PagedCase:
                     seed=1001 + seed_offset, poison=False, name="gqa_b64_ctx1024_fp16")
 
 
+def gqa_batch64_mtp(q_len: int = 2) -> PagedCase:
+    """The B=64 / ctx 1024 GQA step with q_len query tokens per sequence (the
+    last q_len positions, bottom-right causal mask): multi-token decode."""
+    return make_gqa(batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                    context_lens=[1024] * 64, q_dtype="f16", kv_dtype="f16", seed=1101,
+                    poison=False, q_len=q_len, name="gqa_b64_ctx1024_fp16_q%d" % q_len)
+
+
 def gqa_long(batch: int) -> PagedCase:
     """B in {1, 4}, Hq=32, Hkv=8, d=128, ctx 32768, P=16, fp16 (split-KV)."""
     return make_gqa(batch=batch, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
@@ -272,6 +280,14 @@ def mla_b16(ctx: int = 65536) -> PagedCase:
                     context_lens=[ctx] * 16, dtype="bf16", seed=1003, std=0.5,
                     scale=1.0 / math.sqrt(192.0), poison=False,
                     name="mla_b16_ctx%d_bf16" % ctx)
+
+
+def mla_b16_mtp(q_len: int = 2, ctx: int = 65536) -> PagedCase:
+    """The MLA B=16 step with q_len query tokens per sequence (causal)."""
+    return make_mla(batch=16, num_q_heads=16, d_latent=512, d_rope=64, page_size=64,
+                    context_lens=[ctx] * 16, dtype="bf16", seed=1103, std=0.5,
+                    scale=1.0 / math.sqrt(192.0), poison=False, q_len=q_len,
+                    name="mla_b16_ctx%d_bf16_q%d" % (ctx, q_len))
 
 
 def ragged_fp8_lens(batch: int = 128, seed: int = 1004) -> np.ndarray:

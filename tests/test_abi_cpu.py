@@ -111,9 +111,20 @@ def test_plan_multi_token_rows():
     assert p.workspace_bytes == rows * 8 * 128 * 4 + -(-(rows * 8 * 4) // 256) * 256
     mla = dict(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512, page_size=64,
                q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16)
-    assert pda.plan(_shape(q_len=2, **mla), mla=True, num_cus=256).head_tiles == 2
+    # MLA: more than 16 rows take 512-thread workgroups of 32 rows, one per CU
+    p = pda.plan(_shape(batch=16, max_pages_per_seq=1024, q_len=2, **mla), mla=True,
+                 num_cus=256)
+    assert (p.head_tiles, p.max_splits) == (1, 16)
+    p = pda.plan(_shape(batch=16, max_pages_per_seq=1024, **mla), mla=True, num_cus=256)
+    assert (p.head_tiles, p.max_splits) == (1, 32)
     assert pda.plan(_shape(q_len=3, **{**mla, "num_q_heads": 8}), mla=True,
+                    num_cus=256).head_tiles == 1
+    assert pda.plan(_shape(q_len=2, **{**mla, "num_q_heads": 32}), mla=True,
                     num_cus=256).head_tiles == 2
+    assert pda.plan(_shape(**{**mla, "num_q_heads": 48}), mla=True, num_cus=256).head_tiles == 2
+    # the vector-ALU MLA kernel keeps 16-head tiles
+    assert pda.plan(_shape(**{**mla, "num_q_heads": 48, "variant": pda.PDA_MLA_VALU}), mla=True,
+                    num_cus=256).head_tiles == 3
     fake = ctypes.c_void_p(0x1000)
     bad = _shape(q_len=2, variant=pda.PDA_MLA_VALU, **mla)
     assert pda.load().paged_decode_attn_mla(fake, fake, fake, fake, 0.1, 1, fake, None,
