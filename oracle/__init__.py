@@ -64,9 +64,10 @@ def _load():
     lib.orc_mla_attention.argtypes = [P, I, P, I, P, I, P, P, P, I, I, I, I, I, I, I64, D, I,
                                       P, P, P, I]
     lib.orc_combine.argtypes = [P, P, I64, I, I, P, P]
+    lib.orc_kv_append.argtypes = [P, I, P, I, P, I, P, I, I, I, I, I, I64, ctypes.c_float]
     lib.orc_max_threads.argtypes = []
     for f in (lib.orc_decode, lib.orc_paged_attention, lib.orc_mla_attention, lib.orc_combine,
-              lib.orc_max_threads):
+              lib.orc_kv_append, lib.orc_max_threads):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -212,3 +213,29 @@ def combine(part_o, part_lse):
     lse = np.empty(tuple(lead))
     _check(_load().orc_combine(_ptr(part_o), _ptr(part_lse), R, S, dv, _ptr(out), _ptr(lse)))
     return out, lse
+
+
+def kv_append(src, cache, block_tables, positions, *, src_dtype, cache_dtype, scale=1.0):
+    """Write s_new new tokens per sequence into a copy of one paged cache tensor.
+
+    src [B, s_new, H, width] (or [B, s_new, width] for a headless MLA cache);
+    cache [num_pages, P, H, width] (or [num_pages, P, width]); positions [B]
+    int32, the position of each sequence's first new token (< 0: skipped).
+    E4M3 caches store the nearest E4M3FN byte to the fp32 quotient x / scale
+    (ties to even, saturated at 448).  Returns the updated copy of cache."""
+    src = _as(src, src_dtype)
+    out = _as(cache, cache_dtype).copy()
+    if src.ndim == 3:
+        src, out4 = src[:, :, None], out[:, :, None]
+    else:
+        out4 = out
+    B, s_new, H, width = src.shape
+    num_pages, P, H2, width2 = out4.shape
+    if (H2, width2) != (H, width):
+        raise ValueError("cache rows do not match src")
+    bt = _i32(block_tables)
+    pos = _i32(positions, B)
+    _check(_load().orc_kv_append(_ptr(src), _DT[src_dtype], _ptr(out), _DT[cache_dtype],
+                                 _ptr(bt), bt.shape[1], _ptr(pos), B, s_new, H, width, P,
+                                 num_pages, float(scale)))
+    return out

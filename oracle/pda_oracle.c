@@ -363,6 +363,94 @@ int orc_mla_attention(const void* q, int q_dtype, const void* kv_cache, int kv_d
   return status;
 }
 
+/* ------------------------------------------------------------- KV append */
+
+static size_t elem_size(int dtype) {
+  switch (dtype) {
+    case ORC_F32: return 4;
+    case ORC_F16: return 2;
+    case ORC_BF16: return 2;
+    case ORC_E4M3: return 1;
+    case ORC_F64: return 8;
+    default: return 0;
+  }
+}
+
+/* The E4M3FN byte nearest to x (already a float value), by search over every
+ * finite code: ties go to the code with an even mantissa; magnitudes beyond
+ * 448, infinities included, saturate to 448; NaN gives 0x7F. */
+static uint8_t enc_e4m3(double x) {
+  if (x != x) return 0x7F;
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs(x);
+  if (a > 448.0) a = 448.0;
+  uint8_t best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(dec_e4m3((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+      best = (uint8_t)c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* Write s_new new tokens per sequence into one paged cache tensor (the blog,
+ * sec. 2: the new token's key and value join the cache before attention;
+ * sec. 5 and the drill page sec. 4: block-table addressing).
+ *   src   [B, s_new, H, width] of src_dtype
+ *   cache [num_pages, P, H, width] of cache_dtype
+ *   token t of sequence b, at position p = positions[b] + t, goes to
+ *   cache[block_tables[b][p / P], p % P, :, :]; positions[b] < 0 skips b.
+ * Same dtype: the elements are copied.  E4M3 cache (src f32/f16/bf16): the
+ * byte is the E4M3FN value nearest to the fp32 quotient x / scale, ties to
+ * even, saturated at +-448.  Other pairs: ORC_ERR_ARG.  Every table entry
+ * and position is bounds-checked (ORC_ERR_TABLE / ORC_ERR_ARG, nothing
+ * written for that token). */
+int orc_kv_append(const void* src, int src_dtype, void* cache, int cache_dtype,
+                  const int32_t* block_tables, int max_pages, const int32_t* positions, int B,
+                  int s_new, int H, int width, int P, int64_t num_pages, float scale) {
+  if (!src || !cache || !block_tables || !positions || B < 0 || s_new < 0 || H <= 0 ||
+      width <= 0 || P <= 0 || max_pages < 0 || num_pages < 0)
+    return ORC_ERR_ARG;
+  const int quant = cache_dtype == ORC_E4M3;
+  if (quant ? !(src_dtype == ORC_F32 || src_dtype == ORC_F16 || src_dtype == ORC_BF16)
+            : src_dtype != cache_dtype)
+    return ORC_ERR_ARG;
+  if (quant && !(scale > 0.0f)) return ORC_ERR_ARG;
+  const size_t es = elem_size(cache_dtype);
+  const int64_t row = (int64_t)H * width; /* elements of one token */
+  int status = ORC_OK;
+  for (int b = 0; b < B; ++b) {
+    if (positions[b] < 0) continue;
+    for (int t = 0; t < s_new; ++t) {
+      int64_t p = (int64_t)positions[b] + t;
+      if (p >= (int64_t)max_pages * P) {
+        status = ORC_ERR_ARG;
+        continue;
+      }
+      int32_t page = block_tables[(int64_t)b * max_pages + p / P];
+      if (page < 0 || (int64_t)page >= num_pages) {
+        status = ORC_ERR_TABLE;
+        continue;
+      }
+      int64_t dst0 = ((int64_t)page * P + p % P) * row;
+      int64_t src0 = ((int64_t)b * s_new + t) * row;
+      for (int64_t i = 0; i < row; ++i) {
+        if (quant) {
+          float x = (float)dec_elem(src_dtype, src, src0 + i); /* exact: f32/f16/bf16 */
+          float q = x / scale;                                 /* one fp32 division */
+          ((uint8_t*)cache)[dst0 + i] = enc_e4m3((double)q);
+        } else {
+          memcpy((char*)cache + (dst0 + i) * es, (const char*)src + (src0 + i) * es, es);
+        }
+      }
+    }
+  }
+  return status;
+}
+
 /* --------------------------------------------------------------- combine */
 
 /* LSE-weighted merge of S split partials ("From MHA to MLA", sec. 4).

@@ -15,7 +15,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "pda_oracle.c")
 PIN_FILES = ["tests/test_oracle_pins.py", "tests/test_oracle_mla.py",
-             "tests/test_oracle_multitoken.py"]
+             "tests/test_oracle_multitoken.py", "tests/test_oracle_append.py"]
 
 MUTATIONS = [
     ("interleaved head grouping", "int kvh = h / G;", "int kvh = h % Hkv;"),
@@ -53,6 +53,16 @@ MUTATIONS = [
      "int64_t lse_row = ((int64_t)b * q_len + i) * Hq + h;"),
     ("query index from the wrong axis", "int i = (int)((r / Hq) % q_len);",
      "int i = (int)(r % q_len);"),
+    ("append slot off by one", "int64_t dst0 = ((int64_t)page * P + p % P) * row;",
+     "int64_t dst0 = ((int64_t)page * P + (p + 1) % P) * row;"),
+    ("append source token ignored", "int64_t src0 = ((int64_t)b * s_new + t) * row;",
+     "int64_t src0 = ((int64_t)b * s_new) * row;"),
+    ("append quantizes x * scale", "float q = x / scale;", "float q = x * scale;"),
+    ("append rounds ties toward zero",
+     "d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)", "d < best_d"),
+    ("append page from the next table entry",
+     "block_tables[(int64_t)b * max_pages + p / P];",
+     "block_tables[(int64_t)b * max_pages + (p + P) / P];"),
 ]
 
 
