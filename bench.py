@@ -120,6 +120,58 @@ def run_gpu(case, workload, steps, warmup, pools):
                 launches=1 if plan.max_splits == 1 else 2)
 
 
+APPEND_WORKLOADS = {"kv_append_b64": "gqa_b64", "kv_append_ragged_fp8": "ragged_fp8"}
+
+
+def run_append(base: str, steps: int, warmup: int):
+    """Time the KV append of one new token per sequence into the cache of an
+    attention workload (f16 rows, or fp16 rows quantized into an fp8 cache):
+    bytes = new rows read + cache rows written."""
+    import numpy as np
+    import torch
+    from decode_attention_paged_02_amd import pda
+    case = make_case(base)
+    dev = pda.to_device(case)
+    B, Hkv, d = case.batch, case.num_kv_heads, case.head_dim
+    rng = np.random.default_rng(7)
+    k_new = torch.from_numpy(rng.standard_normal((B, 1, Hkv, d)).astype(np.float16)).cuda()
+    v_new = torch.from_numpy(rng.standard_normal((B, 1, Hkv, d)).astype(np.float16)).cuda()
+    pos = (dev.context_lens - 1).contiguous()
+    pda.paged_kv_append(k_new, v_new, dev.block_tables, pos, dev.k_cache, dev.v_cache,
+                        k_scale=case.k_scale, v_scale=case.v_scale)   # validates the shapes
+    # then the bare C call with marshalled arguments, so the host keeps ahead
+    import ctypes
+    shape = pda.make_shape(batch=B, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=d, head_dim_v=d,
+                           page_size=case.page_size, max_pages_per_seq=case.max_pages,
+                           num_pages=case.num_pages, q_dtype=pda.PDA_F16,
+                           kv_dtype=pda._dtype_code(dev.k_cache, fp8_ok=True),
+                           k_scale=case.k_scale, v_scale=case.v_scale, q_len=1)
+    args = [pda._ptr(t) for t in (k_new, v_new, dev.block_tables, pos, dev.k_cache, dev.v_cache)]
+    args += [ctypes.byref(shape), pda._stream_handle(None)]
+    lib = pda.load()
+
+    def call():
+        rc = lib.paged_kv_append(*args)
+        if rc:
+            raise pda.PdaError(rc, "paged_kv_append")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    elem = {"f16": 2, "bf16": 2, "f32": 4, "e4m3": 1}[case.kv_dtype]
+    nbytes = B * Hkv * 2 * d * (2 + elem)
+    return {"us_per_step": round(us, 3), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "bytes": nbytes, "cache_dtype": case.kv_dtype,
+            "note": "HIP events around back-to-back calls; one token per sequence per step"}
+
+
 def cpu_baseline(case, budget_s=20.0):
     """The fp64 oracle on the host cores over a bounded sample of the workload:
     whole sequences in order, repeated as whole passes, until about budget_s
@@ -202,7 +254,7 @@ def main():
                     choices=["gqa_b64", "gqa_b1_split", "gqa_b4_split", "mla_b16", "ragged_fp8",
                              "gqa_b64_q2", "mla_b16_q2"])
     ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
-    ap.add_argument("--others", default="gqa_b1_split,gqa_b4_split",
+    ap.add_argument("--others", default="gqa_b1_split,gqa_b4_split,kv_append_b64",
                     help="extra workloads measured into 'other_workloads' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -236,6 +288,9 @@ def main():
     others = {}
     for w in [x for x in args.others.split(",") if x and x not in (args.workload, "none")]:
         _log("other workload", w)
+        if w in APPEND_WORKLOADS:
+            others[w] = run_append(APPEND_WORKLOADS[w], max(20, args.steps // 4), 5)
+            continue
         c2 = make_case(w)
         st = max(20, args.steps // 4)
         r2 = run_gpu(c2, w, st, 5, args.pools)

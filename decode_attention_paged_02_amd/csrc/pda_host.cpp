@@ -350,4 +350,47 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
   return PDA_OK;
 }
 
+int paged_kv_append(const void* k_new, const void* v_new, const int32_t* block_tables,
+                    const int32_t* positions, void* k_cache, void* v_cache,
+                    const pda_shape* shape, void* stream) {
+  if (!shape || !k_new || !k_cache || !block_tables || !positions) return PDA_ERR_INVALID_ARG;
+  const bool has_v = v_cache != nullptr;
+  if ((v_new != nullptr) != has_v) return PDA_ERR_INVALID_ARG;
+  const pda_shape& s = *shape;
+  if (s.batch < 0 || s.num_kv_heads <= 0 || s.head_dim <= 0 || s.page_size <= 0 ||
+      s.max_pages_per_seq <= 0 || s.num_pages <= 0 || s.q_len < 0 ||
+      (has_v && s.head_dim_v <= 0))
+    return PDA_ERR_INVALID_ARG;
+  if (!valid_dtype(s.q_dtype) || !valid_dtype(s.kv_dtype)) return PDA_ERR_INVALID_ARG;
+  if ((int64_t)s.max_pages_per_seq * s.page_size > INT32_MAX) return PDA_ERR_INVALID_ARG;
+  if (!pda::append_supported(s.q_dtype, s.kv_dtype)) return PDA_ERR_UNSUPPORTED;
+  if (s.head_dim % 8 != 0 || (has_v && s.head_dim_v % 8 != 0)) return PDA_ERR_UNSUPPORTED;
+  if (s.kv_dtype == PDA_FP8_E4M3 && !(s.k_scale > 0.f && (!has_v || s.v_scale > 0.f)))
+    return PDA_ERR_INVALID_ARG;
+  // rows move in 16-byte pieces
+  for (const void* ptr : {k_new, v_new, (const void*)k_cache, (const void*)v_cache})
+    if ((uintptr_t)ptr % 16 != 0) return PDA_ERR_INVALID_ARG;
+  if (s.batch == 0) return PDA_OK;
+
+  pda::AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.positions = positions;
+  a.batch = s.batch;
+  a.s_new = query_len(shape);
+  a.num_kv_heads = s.num_kv_heads;
+  a.head_dim = s.head_dim;
+  a.head_dim_v = has_v ? s.head_dim_v : 0;
+  a.page_size = s.page_size;
+  a.max_pages = s.max_pages_per_seq;
+  a.k_scale = s.k_scale;
+  a.v_scale = s.v_scale;
+  return pda::launch_append(a, s.q_dtype, s.kv_dtype, (hipStream_t)stream) == hipSuccess
+             ? PDA_OK
+             : PDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -121,6 +121,18 @@ struct OrderArgs {
   SplitLayout split;
 };
 
+// KV append: s_new new tokens per sequence into the paged K (and V) cache.
+struct AppendArgs {
+  const void* k_new;             // [B, s_new, Hkv, head_dim]
+  const void* v_new;             // [B, s_new, Hkv, head_dim_v] (null with v_cache)
+  void* k_cache;                 // [num_pages, P, Hkv, head_dim]
+  void* v_cache;                 // [num_pages, P, Hkv, head_dim_v] or null
+  const int32_t* block_tables;   // [B, max_pages]
+  const int32_t* positions;      // [B]: first new token's position, < 0 skips b
+  int32_t batch, s_new, num_kv_heads, head_dim, head_dim_v, page_size, max_pages;
+  float k_scale, v_scale;        // E4M3 caches: stored byte = e4m3(x / scale)
+};
+
 // Column groups of 16 rows in a workgroup of the MLA matrix-core kernel for
 // `rows` (query token, head) rows per sequence: two (512 threads) once there
 // are more than 16, so that one staged block serves 32 rows.
@@ -131,6 +143,7 @@ bool gqa_supported(int q_dtype, int kv_dtype, int head_dim, int head_dim_v);
 int gqa_tile_heads(int group);  // query heads per workgroup tile for a group size
 
 bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim);
+bool append_supported(int src_dtype, int cache_dtype);
 
 // Launchers (return the launch error, hipSuccess otherwise).
 hipError_t launch_gqa_mfma(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
@@ -140,5 +153,6 @@ hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t stream);
 hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
 hipError_t launch_mla(const MlaArgs& a, int variant, int max_splits, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, int src_dtype, int cache_dtype, hipStream_t stream);
 
 }  // namespace pda

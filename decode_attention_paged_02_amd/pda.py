@@ -49,7 +49,7 @@ class PlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("pda_plan", "pda_workspace_bytes", "paged_decode_attn", "paged_decode_attn_mla",
-           "pda_status_string", "pda_version")
+           "paged_kv_append", "pda_status_string", "pda_version")
 
 _lib = None
 
@@ -73,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.paged_decode_attn.restype = i32
     lib.paged_decode_attn_mla.argtypes = [vp, vp, vp, vp, f32, i32, vp, vp, sp, vp, sz, vp]
     lib.paged_decode_attn_mla.restype = i32
+    lib.paged_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, sp, vp]
+    lib.paged_kv_append.restype = i32
     lib.pda_status_string.argtypes = [i32]
     lib.pda_status_string.restype = ctypes.c_char_p
     lib.pda_version.argtypes = []
@@ -254,6 +256,44 @@ def paged_decode_attn_mla(q, kv_cache, block_tables, context_lens, *, scale: flo
     if rc:
         raise PdaError(rc, "paged_decode_attn_mla")
     return out, lse
+
+
+def paged_kv_append(k_new, v_new, block_tables, positions, k_cache, v_cache=None, *,
+                    k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """Write new tokens' K (and V) rows into the paged cache, in place.
+
+    k_new [B, s_new, Hkv, d] (or [B, s_new, 576] for an MLA latent cache
+    [pages, P, 576], with v_new = v_cache = None); v_new [B, s_new, Hkv, dv];
+    positions [B] int32, the position of each sequence's first new token
+    (< 0: skipped).  fp8 caches (uint8 storage) store e4m3(x / scale)."""
+    _need((v_new is None) == (v_cache is None), "v_new and v_cache go together")
+    kn = k_new if k_new.dim() == 4 else k_new.unsqueeze(2)
+    kc = k_cache if k_cache.dim() == 4 else k_cache.unsqueeze(2)
+    _need(kn.dim() == 4 and kc.dim() == 4, "bad ranks")
+    B, s_new, Hkv, d = kn.shape
+    num_pages, P, Hkv2, d2 = kc.shape
+    _need((Hkv2, d2) == (Hkv, d), "k_new rows do not match k_cache")
+    dv = 0
+    if v_cache is not None:
+        _need(v_new.dim() == 4 and v_cache.dim() == 4 and v_new.shape[:3] == kn.shape[:3] and
+              v_cache.shape[:3] == kc.shape[:3] and v_new.shape[3] == v_cache.shape[3],
+              "v_new / v_cache shapes")
+        dv = v_new.shape[3]
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, *]")
+    _need(positions.dim() == 1 and positions.shape[0] == B, "positions must be [B]")
+    _check_device(k_new, v_new, block_tables, positions, k_cache, v_cache)
+    _need(block_tables.dtype == torch.int32 and positions.dtype == torch.int32,
+          "block_tables and positions must be int32")
+    shape = make_shape(batch=B, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=d,
+                       head_dim_v=dv, page_size=P, max_pages_per_seq=block_tables.shape[1],
+                       num_pages=num_pages, q_dtype=_dtype_code(k_new),
+                       kv_dtype=_dtype_code(k_cache, fp8_ok=True), k_scale=k_scale,
+                       v_scale=v_scale, q_len=s_new)
+    rc = load().paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(block_tables), _ptr(positions),
+                                _ptr(k_cache), _ptr(v_cache), ctypes.byref(shape),
+                                _stream_handle(stream))
+    if rc:
+        raise PdaError(rc, "paged_kv_append")
 
 
 # ----------------------------------------------------------------------------

@@ -184,6 +184,35 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
                           void* out, float* lse, const pda_shape* shape, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Append the new tokens' K and V rows to the paged cache, the step before
+ * attention ("From MHA to MLA" sec. 2: the new token's key and value join the
+ * cache first; sec. 5 and the drill page sec. 4: a token's page is
+ * block_tables[b][position / P], its slot position % P).
+ *   k_new      [B, s_new, Hkv, head_dim]   of shape->q_dtype (s_new = q_len,
+ *   v_new      [B, s_new, Hkv, head_dim_v]  0 meaning 1), device
+ *   positions  [B] int32, device: position of sequence b's first new token;
+ *              token t goes to position positions[b] + t; a negative entry
+ *              skips the sequence (nothing is written for it)
+ *   k_cache, v_cache: the caches of paged_decode_attn (updated in place)
+ * v_new and v_cache are both NULL for a cache with K only (an MLA latent
+ * cache: num_kv_heads 1, head_dim 576; V is the start of each record).
+ * Same-type caches receive the elements unchanged.  A PDA_FP8_E4M3 cache
+ * receives the E4M3FN code nearest to the fp32 quotient x / k_scale (v_scale
+ * for V): ties to even, magnitudes at or beyond 448 saturate to 448, NaN
+ * gives 0x7F.
+ * Supported: (q_dtype, kv_dtype) = (F32, F32), (F16, F16), (BF16, BF16), or
+ * any of F32/F16/BF16 with FP8_E4M3; head_dim and head_dim_v multiples of 8;
+ * any page_size.  The four data pointers must be 16-byte aligned.  Only
+ * batch, num_kv_heads, head_dim, head_dim_v, page_size, max_pages_per_seq,
+ * num_pages, q_dtype, kv_dtype, k_scale, v_scale and q_len are read from
+ * shape.  Preconditions (not checked): positions[b] + s_new <=
+ * max_pages_per_seq * P, and the table entries of the pages written lie in
+ * [0, num_pages).  Calls whose positions overlap write the same slots in an
+ * unspecified order.  No workspace; asynchronous on `stream`. */
+int paged_kv_append(const void* k_new, const void* v_new, const int32_t* block_tables,
+                    const int32_t* positions, void* k_cache, void* v_cache,
+                    const pda_shape* shape, void* stream);
+
 /* Static description of a status code. */
 const char* pda_status_string(int status);
 

@@ -204,6 +204,31 @@ def test_mla_validation():
                                      ctypes.byref(s), None, 0, None) == 1
 
 
+def test_append_validation():
+    lib = pda.load()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1008)                     # not 16-byte aligned
+
+    def call(kw, v=True, k_new=fake):
+        s = _shape(**kw)
+        return lib.paged_kv_append(k_new, fake if v else None, fake, fake, fake,
+                                   fake if v else None, ctypes.byref(s), None)
+
+    assert call(dict(batch=0)) == 0                                     # nothing to do
+    assert call(dict(head_dim=36, head_dim_v=36)) == 2                  # not a multiple of 8
+    assert call(dict(q_dtype=pda.PDA_F16, kv_dtype=pda.PDA_BF16)) == 2  # no conversion rule
+    assert call(dict(q_dtype=pda.PDA_FP8_E4M3, kv_dtype=pda.PDA_FP8_E4M3)) == 2
+    assert call(dict(kv_dtype=pda.PDA_FP8_E4M3, k_scale=0.0)) == 1      # fp8 needs scales
+    assert call(dict(kv_dtype=pda.PDA_FP8_E4M3, v_scale=-1.0)) == 1
+    assert call(dict(batch=-1)) == 1
+    assert call(dict(q_len=-2)) == 1
+    assert call(dict(), k_new=odd) == 1
+    assert call(dict(batch=0, head_dim=576), v=False) == 0              # K-only (MLA) form
+    s = _shape()
+    assert lib.paged_kv_append(fake, None, fake, fake, fake, fake, ctypes.byref(s), None) == 1
+    assert lib.paged_kv_append(fake, fake, fake, fake, fake, fake, None, None) == 1
+
+
 def test_empty_batch_is_a_no_op():
     s = _shape(batch=0)
     fake = ctypes.c_void_p(0x1000)
