@@ -43,7 +43,7 @@ def make_case(name):
         return W.gqa_long(4)
     if name == "mla_b16":
         return W.mla_b16()
-    if name == "ragged_fp8":
+    if name in ("ragged_fp8", "ragged_fp8_balanced"):
         return W.ragged_fp8()
     if name == "gqa_b64_q2":
         return W.gqa_batch64_mtp(2)
@@ -52,7 +52,9 @@ def make_case(name):
     raise SystemExit("unknown workload %s" % name)
 
 
-CALL_KW = {"ragged_fp8": dict(num_splits=8, split_min_tokens=4096)}
+CALL_KW = {"ragged_fp8": dict(num_splits=8, split_min_tokens=4096),
+           # the balanced schedule (device-side chunking) on the same batch
+           "ragged_fp8_balanced": dict(num_splits=8, schedule=1)}
 
 
 def measured_traffic(workload: str, launches_per_step: int):
@@ -87,12 +89,12 @@ def run_gpu(case, workload, steps, warmup, pools):
     if case.mla:
         shape = pda.mla_shape(dev.q, dev.k_cache, dev.block_tables, head_dim_v=case.d_latent,
                               split_min_tokens=kw.get("split_min_tokens", 0),
-                              causal=case.causal)
+                              causal=case.causal, schedule=kw.get("schedule", 0))
     else:
         shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
                               k_scale=case.k_scale, v_scale=case.v_scale,
                               split_min_tokens=kw.get("split_min_tokens", 0),
-                              causal=case.causal)
+                              causal=case.causal, schedule=kw.get("schedule", 0))
     nsplit = kw.get("num_splits", 0)
     plan = pda.plan(shape, mla=case.mla, num_splits=nsplit)
     ws = pda.workspace_for(shape, mla=case.mla, num_splits=nsplit, device="cuda")
@@ -117,7 +119,7 @@ def run_gpu(case, workload, steps, warmup, pools):
     return dict(total_ms=total_ms, kernel_us_mean=total_ms * 1000.0 / steps,
                 kv_bytes=nbytes, n_pools=len(caches), max_splits=plan.max_splits,
                 pages_per_split=plan.pages_per_split, workgroups=plan.workgroups,
-                launches=1 if plan.max_splits == 1 else 2)
+                launches=(1 if plan.max_splits == 1 else 2) + (1 if plan.ordered else 0))
 
 
 APPEND_WORKLOADS = {"kv_append_b64": "gqa_b64", "kv_append_ragged_fp8": "ragged_fp8"}
@@ -252,7 +254,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa_b64",
                     choices=["gqa_b64", "gqa_b1_split", "gqa_b4_split", "mla_b16", "ragged_fp8",
-                             "gqa_b64_q2", "mla_b16_q2"])
+                             "ragged_fp8_balanced", "gqa_b64_q2", "mla_b16_q2"])
     ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
     ap.add_argument("--others", default="gqa_b1_split,gqa_b4_split,kv_append_b64",
                     help="extra workloads measured into 'other_workloads' ('' for none)")

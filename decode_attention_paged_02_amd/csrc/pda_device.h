@@ -61,6 +61,19 @@ __device__ __forceinline__ int load_uniform(const int32_t* p) {
 // The same read where the address differs per lane (a vector load).
 __device__ __forceinline__ int load_uniform_v(const int32_t* p) { return *p; }
 
+// A work unit of an ordered call (written by the planning kernel): sequence
+// b (negative: no unit, the workgroup exits), split index (-1: the
+// sequence's only split, whose result is the final output) and the token
+// range [t0, t1).  Read with one scalar load.
+struct WorkUnit {
+  int b, split, t0, t1;
+};
+__device__ __forceinline__ WorkUnit load_unit(const int32_t* units, int idx) {
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 w = *(const __attribute__((address_space(4))) i32x4*)(units + 4 * idx);
+  return WorkUnit{w[0], w[1], w[2], w[3]};
+}
+
 // Cache policy of the K/V stream loads (the buffer instruction's cache-policy
 // field; 2 marks them non-temporal).
 #ifndef PDA_KV_LOAD_POLICY

@@ -109,14 +109,17 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
 
   // which (sequence, KV head, head tile, split) this workgroup computes
   // (ordered: from the unit list, as in gqa_mfma_kernel)
-  int tile, kvh, b, split;
-  if (a.units) {
+  const bool ordered = a.units != nullptr;
+  int tile, kvh, b, split, ut0 = 0, ut1 = 0;
+  if (ordered) {
     const int nhu = a.num_kv_heads * a.head_tiles;
     const int hu = blockIdx.x % nhu;
-    const int e = load_uniform(a.units + blockIdx.x / nhu);
-    if (e < 0) return;
-    b = e & 0xffff;
-    split = e >> 16;
+    const WorkUnit w = load_unit(a.units, blockIdx.x / nhu);
+    if (w.b < 0) return;
+    b = w.b;
+    split = w.split;
+    ut0 = w.t0;
+    ut1 = w.t1;
     kvh = hu / a.head_tiles;
     tile = hu % a.head_tiles;
   } else {
@@ -134,7 +137,9 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
   // First token of this split when the sequence is split (a split that ends
   // up unused exits below before anything depends on it).
-  const int t0_hint = a.split.max_splits > 1 ? split * a.split.pages_per_split << log2P : 0;
+  const int t0_hint = ordered                  ? ut0
+                      : a.split.max_splits > 1 ? split * a.split.pages_per_split << log2P
+                                               : 0;
 
   // The sequence length, this wave's block-table entries and q are requested
   // together, before anything waits for one of them.  Lane j holds the entry
@@ -151,14 +156,14 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   // 0 always has work (or an empty sequence) and requests its length along
   // with the table entries and q.
   int n = 0;
-  if (split > 0) {
+  if (!ordered && split > 0) {
     n = load_uniform(a.context_lens + b);
     int ns, ta, tb;
     split_range(a.split, n, a.page_size, split, ns, ta, tb);
     if (split >= ns) return;
   }
   int vtbl = load_table(0);
-  if (split == 0) n = load_uniform(a.context_lens + b);
+  if (!ordered && split == 0) n = load_uniform(a.context_lens + b);
 
   // q of the tile's heads (slot g holds head g ^ flip_head), the EPL elements
   // this lane multiplies.  Heads past the group are loaded from a valid row
@@ -183,8 +188,14 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
 
   __builtin_amdgcn_sched_barrier(0);  // the loads above go out before waiting for n
   int nsplit, t0, t1;
-  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
-  if (split >= nsplit) return;
+  if (ordered) {  // the unit's range; split -1: the sequence's only split
+    nsplit = split < 0 ? 1 : 2;
+    t0 = ut0;
+    t1 = ut1;
+  } else {
+    split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+    if (split >= nsplit) return;
+  }
 
   // loop-invariant byte offsets of this lane's rows inside a tile (K in the
   // permuted row order of the score array, V in plain order)
@@ -493,14 +504,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   constexpr int SSTR = DV / 4;
   const int sg = threadIdx.x / DC, dc = threadIdx.x % DC;
 
-  // With a split threshold (ragged batches) most rows belong to unsplit
-  // sequences: the length is checked first and only existing partials are
-  // read.  Otherwise the length and this thread's first MAXL partials are
-  // requested together (slots past the split count hold stale data and are
-  // ignored below), so the row costs one memory round trip.
-  const bool guarded = split_min_tokens > 0;
+  // In ordered calls (ragged batches) many rows belong to unsplit sequences:
+  // the split count is read first and only existing partials are read.
+  // Otherwise the length and this thread's first MAXL partials are requested
+  // together (slots past the split count hold stale data and are ignored
+  // below), so the row costs one memory round trip.
+  const bool guarded = split_min_tokens > 0 || a.seq_splits;
   int n = 0, nsplit = 0, t0, t1;
-  if (guarded) {
+  if (a.seq_splits) {  // ordered call: the planning pass recorded the count
+    nsplit = load_uniform(a.seq_splits + b);
+    if (nsplit <= 1) return;
+  } else if (guarded) {
     n = load_uniform(context_lens + b);
     split_range(sp, n, page_size, 0, nsplit, t0, t1);
     if (nsplit <= 1) return;
@@ -587,32 +601,78 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
 constexpr int kOrderThreads = 1024;
 
-// Longest-processing-time order of the (sequence, split) work units of a
-// mixed-length batch: units are bucketed by the bit length of their token
-// count (a counting sort, buckets taken from the longest down), so that the
-// attention workgroups that start first get the longest ranges.  Split 0 of
-// every sequence is listed even when empty (it writes out = 0, LSE = -inf).
-// Order inside a bucket follows the LDS atomics; each unit's result does not
-// depend on it.  One workgroup.
+// The planning pass of an ordered call (one workgroup).  Each sequence is cut
+// into splits -- by the SplitLayout (grid schedule), or into near-equal
+// chunks of the batch's total pages (balanced schedule) -- and the resulting
+// (sequence, split) work units are listed in longest-processing-time order:
+// bucketed by the bit length of their token count (a counting sort, buckets
+// taken from the longest down), so that the attention workgroups that start
+// first get the longest ranges.  A sequence's only split is listed even when
+// empty (it writes out = 0, LSE = -inf).  Order inside a bucket follows the
+// LDS atomics; each unit's result does not depend on it.  The pages do not
+// prescribe a schedule (FlashMLA-ETAP "Usage" shows only that one is
+// computed from the sequence lengths, once per decoding step).
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(OrderArgs a) {
   constexpr int NBK = 33;  // bit lengths 0..32
   __shared__ int cnt[NBK];
   __shared__ int total_sh;
+  __shared__ long long pages_sh;
   const int S = a.split.max_splits;
   const int U = a.batch * S;
+  const int P = a.page_size;
   if (threadIdx.x < NBK) cnt[threadIdx.x] = 0;
+  if (threadIdx.x == 0) pages_sh = 0;
   __syncthreads();
-  auto bucket_of = [&](int u) -> int {  // -1: not listed
+  // balanced schedule: the chunk size from the batch's total pages
+  int chunk = 0;
+  if (a.balanced) {
+    long long part = 0;
+    for (int b = threadIdx.x; b < a.batch; b += kOrderThreads)
+      part += (load_uniform_v(a.context_lens + b) + P - 1) / P;
+    atomicAdd((unsigned long long*)&pages_sh, (unsigned long long)part);
+    __syncthreads();
+    const long long c = (pages_sh + a.target_units - 1) / a.target_units;
+    chunk = (int)(c > a.min_chunk_pages ? c : a.min_chunk_pages);
+  }
+  // splits of sequence b (n tokens) and the pages each one covers
+  auto layout = [&](int n, int& ns, int& pps) {
+    const int pages = (n + P - 1) / P;
+    if (S <= 1 || n <= a.split.split_min_tokens || (a.balanced && pages <= chunk)) {
+      ns = 1;
+      pps = pages > 0 ? pages : 1;
+    } else if (!a.balanced) {
+      pps = a.split.pages_per_split;
+      ns = (pages + pps - 1) / pps;
+    } else {
+      ns = min(S, (pages + chunk - 1) / chunk);
+      pps = (pages + ns - 1) / ns;
+      ns = (pages + pps - 1) / pps;
+    }
+  };
+  // unit u = (b, s): its token range, or false past the sequence's splits
+  auto unit_of = [&](int u, WorkUnit& w, int& ns) -> bool {
     const int b = u / S, s = u % S;
-    int ns, t0, t1;
-    split_range(a.split, load_uniform_v(a.context_lens + b), a.page_size, s, ns, t0, t1);
-    if (s >= ns) return -1;
-    const int tok = t1 - t0;
+    const int n = load_uniform_v(a.context_lens + b);
+    int pps;
+    layout(n, ns, pps);
+    if (s >= ns) return false;
+    w.b = b;
+    w.split = ns == 1 ? -1 : s;
+    w.t0 = s * pps * P;
+    w.t1 = (int)min((int64_t)(s + 1) * pps * P, (int64_t)n);
+    return true;
+  };
+  auto bucket = [](const WorkUnit& w) {
+    const int tok = w.t1 - w.t0;
     return tok > 0 ? 32 - __clz(tok) : 0;
   };
   for (int u = threadIdx.x; u < U; u += kOrderThreads) {
-    const int k = bucket_of(u);
-    if (k >= 0) atomicAdd(&cnt[k], 1);
+    WorkUnit w;
+    int ns;
+    if (unit_of(u, w, ns)) {
+      atomicAdd(&cnt[bucket(w)], 1);
+      if (u % S == 0) a.seq_splits[u / S] = ns;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {  // bucket offsets, longest bucket first
@@ -625,17 +685,24 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(OrderArgs a) {
     total_sh = pos;
   }
   __syncthreads();
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
   for (int u = threadIdx.x; u < U; u += kOrderThreads) {
-    const int k = bucket_of(u);
-    if (k >= 0) a.units[atomicAdd(&cnt[k], 1)] = (u / S) | ((u % S) << 16);
+    WorkUnit w;
+    int ns;
+    if (unit_of(u, w, ns)) {
+      const int slot = atomicAdd(&cnt[bucket(w)], 1);
+      if (slot < a.capacity) *(i32x4*)(a.units + 4 * slot) = i32x4{w.b, w.split, w.t0, w.t1};
+    }
   }
-  for (int u = total_sh + threadIdx.x; u < U; u += kOrderThreads) a.units[u] = -1;
+  for (int u = total_sh + threadIdx.x; u < a.capacity; u += kOrderThreads)
+    *(i32x4*)(a.units + 4 * u) = i32x4{-1, -1, 0, 0};
 }
 
 template <class QT, class KT, int D>
 hipError_t launch_d(const GqaArgs& a, int tile_heads, int max_splits, hipStream_t s) {
   const unsigned units = (unsigned)(a.batch * a.num_kv_heads * a.head_tiles);
-  dim3 grid(a.units ? units * (unsigned)max_splits : units, a.units ? 1u : (unsigned)max_splits);
+  const unsigned nhu = (unsigned)(a.num_kv_heads * a.head_tiles);
+  dim3 grid(a.units ? nhu * (unsigned)a.unit_count : units, a.units ? 1u : (unsigned)max_splits);
   dim3 block(kGqaWaves * 64);
   switch (tile_heads) {
     case 1: hipLaunchKernelGGL((gqa_split_kernel<QT, KT, D, 1>), grid, block, 0, s, a); break;

@@ -183,16 +183,20 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   const int grp = lane >> 4;  // lane group
 
   // which (sequence, KV head, head tile, split) this workgroup computes
-  int tile, kvh, b, split;
-  if (units) {
-    // ordered: the unit list gives (sequence, split) longest first; the
-    // (KV head, head tile) pairs of a unit are consecutive workgroups
+  const bool ordered = units != nullptr;
+  int tile, kvh, b, split, ut0 = 0, ut1 = 0;
+  if (ordered) {
+    // ordered: the unit list gives (sequence, split, token range) longest
+    // first; the (KV head, head tile) pairs of a unit are consecutive
+    // workgroups
     const int nhu = num_kv_heads * head_tiles;
     const int hu = blockIdx.x % nhu;
-    const int e = load_uniform(units + blockIdx.x / nhu);
-    if (e < 0) return;
-    b = e & 0xffff;
-    split = e >> 16;
+    const WorkUnit w = load_unit(units, blockIdx.x / nhu);
+    if (w.b < 0) return;
+    b = w.b;
+    split = w.split;
+    ut0 = w.t0;
+    ut1 = w.t1;
     kvh = hu / head_tiles;
     tile = hu % head_tiles;
   } else {
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   const int gvalid = min(kMHeads, q_len * group - g0);
   const int log2P = log2_page;
   const int32_t* table = block_tables + (int64_t)b * max_pages;
-  const int t0_hint = max_splits > 1 ? split * pages_per_split << log2P : 0;
+  const int t0_hint = ordered ? ut0 : max_splits > 1 ? split * pages_per_split << log2P : 0;
 
   // The range is walked in steps of ST consecutive tiles; wave w takes steps
   // w, w + kMWaves, ...  Sequence length, block-table entries (lane j: tile
@@ -225,16 +229,17 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   // With ragged lengths most workgroups past split 0 have no pages to read:
   // those decide on the length alone and leave without further loads.  Split
   // 0 always has work (or an empty sequence) and requests its length along
-  // with the table entries and q.
+  // with the table entries and q; so does every ordered unit (its range is
+  // known, the length only bounds the causal windows).
   int n = 0;
-  if (split > 0) {
+  if (!ordered && split > 0) {
     n = load_uniform(context_lens + b);
     int ns, ta, tb;
     split_range(a.split, n, a.page_size, split, ns, ta, tb);
     if (split >= ns) return;
   }
   int vtbl = load_table(0);
-  if (split == 0) n = load_uniform(context_lens + b);
+  if (ordered || split == 0) n = load_uniform(context_lens + b);
 
   // Q^T as the B operand of the QK MFMAs: lane (col, grp) holds
   // q[row col][32 j + 8 grp .. +8] for MFMA j; rows past the group are zero.
@@ -260,8 +265,14 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
 
   __builtin_amdgcn_sched_barrier(0);  // the loads above go out before waiting for n
   int nsplit, t0, t1;
-  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
-  if (split >= nsplit) return;
+  if (ordered) {  // the unit's range; split -1: the sequence's only split
+    nsplit = split < 0 ? 1 : 2;
+    t0 = ut0;
+    t1 = ut1;
+  } else {
+    split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+    if (split >= nsplit) return;
+  }
   // end of the tokens this lane's query token may see (t1 without a mask)
   const int lim = min(t1, a.causal ? n - (q_len - 1 - qi) : n);
 
@@ -512,7 +523,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
 template <class QT, class KT>
 hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStream_t s) {
   const unsigned units = (unsigned)(a.batch * a.num_kv_heads * a.head_tiles);
-  dim3 grid(a.units ? units * (unsigned)max_splits : units, a.units ? 1u : (unsigned)max_splits);
+  const unsigned nhu = (unsigned)(a.num_kv_heads * a.head_tiles);
+  dim3 grid(a.units ? nhu * (unsigned)a.unit_count : units, a.units ? 1u : (unsigned)max_splits);
   dim3 block(kMWaves * 64);
   switch (head_dim) {
 #define PDA_MFMA_ARGS                                                                        \

@@ -39,7 +39,8 @@ int check_shape(const pda_shape* s, bool mla) {
   if (s->batch < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->head_dim <= 0 ||
       s->head_dim_v <= 0 || s->page_size <= 0 || s->max_pages_per_seq <= 0 ||
       s->num_pages <= 0 || s->split_min_tokens < 0 || s->q_len < 0 ||
-      (s->causal != 0 && s->causal != 1))
+      (s->causal != 0 && s->causal != 1) ||
+      (s->schedule != PDA_SCHEDULE_GRID && s->schedule != PDA_SCHEDULE_BALANCED))
     return PDA_ERR_INVALID_ARG;
   // (query, head) rows of a sequence stay well inside 32-bit indexing
   if ((int64_t)query_len(s) * s->num_q_heads > (1 << 20)) return PDA_ERR_UNSUPPORTED;
@@ -78,6 +79,9 @@ int check_shape(const pda_shape* s, bool mla) {
   return PDA_OK;
 }
 
+// Smallest chunk of the balanced schedule, in pages.
+constexpr int kMinChunkPages = 16;
+
 // Smallest group size for which the default GQA variant takes the matrix-core
 // kernel (its 16 head columns are mostly padding below that).
 constexpr int kMfmaMinGroup = 3;
@@ -91,8 +95,16 @@ bool gqa_use_mfma(const pda_shape* s) {
          s->num_q_heads / s->num_kv_heads >= kMfmaMinGroup;
 }
 
-int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_plan_info* p) {
-  if (!p || num_splits < 0 || num_cus < 0) return PDA_ERR_INVALID_ARG;
+// The plan of a call: the public summary plus what only the library uses.
+struct Plan {
+  pda_plan_info info;
+  int32_t unit_capacity;  // ordered calls: length of the work-unit list
+  int32_t target_units;   // balanced schedule: chunks per KV head and head tile
+};
+
+int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* plan) {
+  if (!plan || num_splits < 0 || num_cus < 0) return PDA_ERR_INVALID_ARG;
+  pda_plan_info* p = &plan->info;
   int rc = check_shape(s, mla);
   if (rc != PDA_OK) return rc;
   const int group = s->num_q_heads / s->num_kv_heads;
@@ -106,17 +118,27 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_pla
                                            : (int)ceil_div(group, pda::gqa_tile_heads(group));
   const int64_t units = (int64_t)s->batch * s->num_kv_heads * head_tiles;
   const int max_pages = s->max_pages_per_seq;
+  const bool balanced = s->schedule == PDA_SCHEDULE_BALANCED;
+  // Eight waves per compute unit (two four-wave workgroups, or one of eight)
+  const int wg_per_cu = mla_groups == 2 ? 1 : 2;
 
+  if ((num_splits == 0 || balanced) && num_cus == 0) {
+    num_cus = device_cus();
+    if (num_cus <= 0) return PDA_ERR_HIP;
+  }
   int splits = 1;
   if (num_splits > 0) {
     splits = std::min(num_splits, max_pages);
+  } else if (balanced) {
+    // at most as many splits as units per KV head and head tile fill the
+    // GPU, and no more than chunks of the smallest size fit a table row
+    splits = (int)std::min<int64_t>(
+        std::max<int64_t>(1, (int64_t)wg_per_cu * num_cus / (s->num_kv_heads * head_tiles)),
+        std::min<int64_t>(ceil_div(max_pages, kMinChunkPages), 64));
   } else {
-    if (num_cus == 0) num_cus = device_cus();
-    if (num_cus <= 0) return PDA_ERR_HIP;
-    // Eight waves per compute unit (two four-wave workgroups, or one of
-    // eight); split only when the (sequence, head tile) units alone cannot
-    // reach that.
-    const int64_t target = (mla_groups == 2 ? 1 : 2) * (int64_t)num_cus;
+    // split only when the (sequence, head tile) units alone cannot fill the
+    // compute units
+    const int64_t target = wg_per_cu * (int64_t)num_cus;
     if (units > 0 && units < target)
       splits = (int)std::min<int64_t>(ceil_div(target, units), max_pages);
   }
@@ -127,33 +149,52 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, pda_pla
   splits = (int)ceil_div(max_pages, pps);
 
   p->max_splits = splits;
-  p->pages_per_split = pps;
+  p->pages_per_split = balanced ? 0 : pps;
   p->head_tiles = head_tiles;
-  p->workgroups = (int)std::min<int64_t>(units * splits, INT32_MAX);
   p->num_cus = num_cus;
-  // work ordering for mixed-length batches (the threshold signals them)
-  p->ordered = s->split_min_tokens > 0 && s->batch <= 65535 && units * splits <= INT32_MAX;
+  // The balanced schedule aims at twice the (sequence, split) units that fill
+  // the compute units (per KV head and head tile), so that the longest-first
+  // order can even out the units' different sizes; its units number at most
+  // B + target (each sequence adds at most pages / chunk splits beyond its
+  // first, and the chunk is at least total pages / target).
+  const int64_t fill = std::max<int64_t>(1, (int64_t)wg_per_cu * num_cus /
+                                                (s->num_kv_heads * head_tiles));
+  plan->target_units = (int)std::min<int64_t>(2 * fill, 1 << 20);
+  int64_t ucap = (int64_t)s->batch * splits;
+  if (balanced) ucap = std::min<int64_t>(ucap, (int64_t)s->batch + plan->target_units);
+  // work ordering for mixed-length batches (the threshold signals them) and
+  // for the balanced schedule
+  p->ordered = (s->split_min_tokens > 0 || balanced) &&
+               ucap * s->num_kv_heads * head_tiles <= INT32_MAX;
+  plan->unit_capacity = p->ordered ? (int32_t)ucap : 0;
+  p->workgroups = (int)std::min<int64_t>(
+      p->ordered ? ucap * s->num_kv_heads * head_tiles : units * splits, INT32_MAX);
   uint64_t ws = 0;
   if (splits > 1) {
     const uint64_t rows = (uint64_t)s->batch * ql * s->num_q_heads;
     const uint64_t o_bytes = rows * splits * s->head_dim_v * sizeof(float);
     ws = ((o_bytes + 255) / 256) * 256 + ((rows * splits * sizeof(float) + 255) / 256) * 256;
   }
-  if (p->ordered) ws += (uint64_t)s->batch * splits * sizeof(int32_t);
+  if (p->ordered)
+    ws += (((uint64_t)ucap * 4 * sizeof(int32_t) + 255) / 256) * 256 +
+          (uint64_t)s->batch * sizeof(int32_t);
   p->workspace_bytes = ws;
   return PDA_OK;
 }
 
 // Workspace layout: partial outputs [B, q_len, Hq, S, dv] fp32, partial LSE
 // [B, q_len, Hq, S] fp32 (both only when S > 1, each 256-byte aligned), then
-// the ordered unit list [B * S] int32 (only for ordered calls).
-void workspace_parts(const pda_shape* s, const pda_plan_info& p, void* ws, float** po,
-                     float** pl, int32_t** un) {
+// for ordered calls the work units [B * S][4] int32 (256-byte aligned) and
+// the split count of each sequence [B] int32.
+void workspace_parts(const pda_shape* s, const Plan& plan, void* ws, float** po, float** pl,
+                     int32_t** un, int32_t** ss) {
+  const pda_plan_info& p = plan.info;
   const uint64_t rows = (uint64_t)s->batch * query_len(s) * s->num_q_heads;
   char* c = (char*)ws;
   *po = nullptr;
   *pl = nullptr;
   *un = nullptr;
+  *ss = nullptr;
   if (p.max_splits > 1) {
     const uint64_t o_bytes = rows * p.max_splits * s->head_dim_v * sizeof(float);
     *po = (float*)c;
@@ -161,17 +202,26 @@ void workspace_parts(const pda_shape* s, const pda_plan_info& p, void* ws, float
     *pl = (float*)c;
     c += ((rows * p.max_splits * sizeof(float) + 255) / 256) * 256;
   }
-  if (p.ordered) *un = (int32_t*)c;
+  if (p.ordered) {
+    *un = (int32_t*)c;
+    c += (((uint64_t)plan.unit_capacity * 4 * sizeof(int32_t) + 255) / 256) * 256;
+    *ss = (int32_t*)c;
+  }
 }
 
-// The ordering pass of an ordered call (before the attention kernel).
-int run_order(const pda_shape& s, const pda_plan_info& p, const int32_t* context_lens,
-              int32_t* units, const pda::SplitLayout& sp, hipStream_t st) {
+// The planning pass of an ordered call (before the attention kernel).
+int run_order(const pda_shape& s, const Plan& plan, const int32_t* context_lens, int32_t* units,
+              int32_t* seq_splits, const pda::SplitLayout& sp, hipStream_t st) {
   pda::OrderArgs o{};
   o.context_lens = context_lens;
   o.units = units;
+  o.seq_splits = seq_splits;
+  o.capacity = plan.unit_capacity;
   o.batch = s.batch;
   o.page_size = s.page_size;
+  o.balanced = s.schedule == PDA_SCHEDULE_BALANCED;
+  o.target_units = plan.target_units;
+  o.min_chunk_pages = kMinChunkPages;
   o.split = sp;
   return pda::launch_order(o, st) == hipSuccess ? PDA_OK : PDA_ERR_HIP;
 }
@@ -195,13 +245,17 @@ const char* pda_status_string(int status) {
 
 int pda_plan(const pda_shape* shape, int is_mla, int num_splits, int num_cus,
              pda_plan_info* plan) {
-  return plan_impl(shape, is_mla != 0, num_splits, num_cus, plan);
+  if (!plan) return PDA_ERR_INVALID_ARG;
+  Plan p;
+  const int rc = plan_impl(shape, is_mla != 0, num_splits, num_cus, &p);
+  if (rc == PDA_OK) *plan = p.info;
+  return rc;
 }
 
 size_t pda_workspace_bytes(const pda_shape* shape, int is_mla, int num_splits) {
-  pda_plan_info p;
+  Plan p;
   if (plan_impl(shape, is_mla != 0, num_splits, 0, &p) != PDA_OK) return 0;
-  return (size_t)p.workspace_bytes;
+  return (size_t)p.info.workspace_bytes;
 }
 
 int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -217,9 +271,10 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   if (!(scale == scale) || num_splits < 0) return PDA_ERR_INVALID_ARG;
   if (shape->batch == 0) return PDA_OK;
 
-  pda_plan_info p;
-  rc = plan_impl(shape, false, num_splits, 0, &p);
+  Plan plan;
+  rc = plan_impl(shape, false, num_splits, 0, &plan);
   if (rc != PDA_OK) return rc;
+  const pda_plan_info& p = plan.info;
   if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
     return PDA_ERR_WORKSPACE;
 
@@ -233,8 +288,10 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   a.out = out;
   a.lse = lse;
   int32_t* units = nullptr;
-  workspace_parts(shape, p, workspace, &a.part_o, &a.part_lse, &units);
+  int32_t* seq_splits = nullptr;
+  workspace_parts(shape, plan, workspace, &a.part_o, &a.part_lse, &units, &seq_splits);
   a.units = units;
+  a.unit_count = plan.unit_capacity;
   a.batch = s.batch;
   a.num_q_heads = s.num_q_heads;
   a.num_kv_heads = s.num_kv_heads;
@@ -257,7 +314,7 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
 
   hipStream_t st = (hipStream_t)stream;
   if (units) {
-    rc = run_order(s, p, context_lens, units, a.split, st);
+    rc = run_order(s, plan, context_lens, units, seq_splits, a.split, st);
     if (rc != PDA_OK) return rc;
   }
   const hipError_t le =
@@ -279,6 +336,7 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
     c.head_dim_v = s.head_dim_v;
     c.page_size = s.page_size;
     c.split = a.split;
+    c.seq_splits = seq_splits;
     if (pda::launch_combine(c, s.q_dtype, st) != hipSuccess) return PDA_ERR_HIP;
   }
   return PDA_OK;
@@ -295,9 +353,10 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
   if (!(scale == scale) || num_splits < 0) return PDA_ERR_INVALID_ARG;
   if (shape->batch == 0) return PDA_OK;
 
-  pda_plan_info p;
-  rc = plan_impl(shape, true, num_splits, 0, &p);
+  Plan plan;
+  rc = plan_impl(shape, true, num_splits, 0, &plan);
   if (rc != PDA_OK) return rc;
+  const pda_plan_info& p = plan.info;
   if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
     return PDA_ERR_WORKSPACE;
 
@@ -310,8 +369,10 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
   a.out = out;
   a.lse = lse;
   int32_t* units = nullptr;
-  workspace_parts(shape, p, workspace, &a.part_o, &a.part_lse, &units);
+  int32_t* seq_splits = nullptr;
+  workspace_parts(shape, plan, workspace, &a.part_o, &a.part_lse, &units, &seq_splits);
   a.units = units;
+  a.unit_count = plan.unit_capacity;
   a.batch = s.batch;
   a.num_q_heads = s.num_q_heads;
   a.head_tiles = p.head_tiles;
@@ -328,7 +389,7 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
 
   hipStream_t st = (hipStream_t)stream;
   if (units) {
-    rc = run_order(s, p, context_lens, units, a.split, st);
+    rc = run_order(s, plan, context_lens, units, seq_splits, a.split, st);
     if (rc != PDA_OK) return rc;
   }
   if (pda::launch_mla(a, s.variant, p.max_splits, st) != hipSuccess) return PDA_ERR_HIP;
@@ -345,6 +406,7 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
     c.head_dim_v = s.head_dim_v;
     c.page_size = s.page_size;
     c.split = a.split;
+    c.seq_splits = seq_splits;
     if (pda::launch_combine(c, s.q_dtype, st) != hipSuccess) return PDA_ERR_HIP;
   }
   return PDA_OK;

@@ -77,10 +77,12 @@ struct GqaArgs {
   float qk_scale_log2;   // scale * k_scale * log2(e)
   float v_scale;
   SplitLayout split;
-  // Ordered work: units[u] = b | split << 16 for u < count, -1 after; the
-  // grid is (kv heads * head tiles) x batch * max_splits in x.  Null: the
-  // grid is (batch, kv head, head tile) in x and the split in y.
+  // Ordered work: units[4u .. 4u + 3] = {b, split (-1: only split), t0, t1}
+  // for the listed units, b = -1 after (see WorkUnit); the grid is (kv heads
+  // * head tiles) x unit_count in x.  Null: the grid is (batch, kv head, head
+  // tile) in x and the split in y, ranges from SplitLayout.
   const int32_t* units;
+  int32_t unit_count;
 };
 
 struct CombineArgs {
@@ -92,6 +94,9 @@ struct CombineArgs {
   int32_t batch, num_q_heads, head_dim_v, page_size;
   int32_t q_len;  // partial rows are (b, query i, head h); lse is [B, Hq, q_len]
   SplitLayout split;
+  // ordered calls: the number of splits of each sequence, written by the
+  // planning kernel (null: from SplitLayout)
+  const int32_t* seq_splits;
 };
 
 struct MlaArgs {
@@ -109,15 +114,25 @@ struct MlaArgs {
   int32_t log2_page;       // page_size == 1 << log2_page
   float qk_scale_log2;     // scale * log2(e)
   SplitLayout split;
-  const int32_t* units;    // as in GqaArgs (x = head tiles * batch * max_splits)
+  const int32_t* units;    // as in GqaArgs (x = head tiles * unit_count)
+  int32_t unit_count;
 };
 
-// The work-ordering pass: lists every non-empty (sequence, split) unit, and
-// split 0 of every sequence, by decreasing token count.
+// The planning pass of ordered calls: splits every sequence, lists every
+// (sequence, split) work unit by decreasing token count (WorkUnit layout,
+// [batch * max_splits] units) and records each sequence's split count.
+//   grid schedule: the SplitLayout (pages_per_split, split threshold);
+//   balanced schedule: a chunk of max(min_chunk_pages, ceil(total pages /
+//   target_units)) pages; sequences longer than a chunk (and than the split
+//   threshold) take ceil(pages / chunk) splits, at most max_splits, of
+//   ceil(pages / splits) pages each.
 struct OrderArgs {
   const int32_t* context_lens;
-  int32_t* units;          // [batch * max_splits]
+  int32_t* units;          // [capacity * 4]
+  int32_t* seq_splits;     // [batch]
+  int32_t capacity;        // listed units never exceed it (see the planner)
   int32_t batch, page_size;
+  int32_t balanced, target_units, min_chunk_pages;
   SplitLayout split;
 };
 

@@ -178,14 +178,18 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   const int col = lane & 15;      // MFMA column: the row
   const int grp = lane >> 4;      // lane group: rows 4*grp..4*grp+3 of an MFMA tile
 
-  // (ordered: the unit list gives (sequence, split), see pda_internal.h)
-  int tile, b, split;
-  if (a.units) {
+  // (ordered: the unit list gives (sequence, split, token range), see
+  // WorkUnit)
+  const bool ordered = a.units != nullptr;
+  int tile, b, split, ut0 = 0, ut1 = 0;
+  if (ordered) {
     tile = blockIdx.x % a.head_tiles;
-    const int e = load_uniform(a.units + blockIdx.x / a.head_tiles);
-    if (e < 0) return;
-    b = e & 0xffff;
-    split = e >> 16;
+    const WorkUnit w = load_unit(a.units, blockIdx.x / a.head_tiles);
+    if (w.b < 0) return;
+    b = w.b;
+    split = w.split;
+    ut0 = w.t0;
+    ut1 = w.t1;
   } else {
     tile = blockIdx.x % a.head_tiles;
     b = blockIdx.x / a.head_tiles;
@@ -200,15 +204,18 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
                "s"(a.split.max_splits), "s"(a.split.split_min_tokens), "s"(a.q_len));
   const int log2P = a.log2_page;
   int n = 0;
-  if (split > 0) {
+  if (!ordered && split > 0) {
     n = load_uniform(a.context_lens + b);
     int ns, ta, tb;
     split_range(a.split, n, a.page_size, split, ns, ta, tb);
     if (split >= ns) return;
   }
   PageTable pt{a.block_tables + (int64_t)b * a.max_pages, a.max_pages, 0, 0};
-  pt.load(a.split.max_splits > 1 ? split * a.split.pages_per_split : 0, lane);
-  if (split == 0) n = load_uniform(a.context_lens + b);
+  pt.load(ordered                  ? ut0 >> log2P
+          : a.split.max_splits > 1 ? split * a.split.pages_per_split
+                                   : 0,
+          lane);
+  if (ordered || split == 0) n = load_uniform(a.context_lens + b);
 
   // this lane's column: row r = query token qi, head h (rows past the last
   // one compute on zero queries and are not written)
@@ -242,8 +249,14 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
 
   __builtin_amdgcn_sched_barrier(0);  // the loads above go out before waiting for n
   int nsplit, t0, t1;
-  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
-  if (split >= nsplit) return;
+  if (ordered) {  // the unit's range; split -1: the sequence's only split
+    nsplit = split < 0 ? 1 : 2;
+    t0 = ut0;
+    t1 = ut1;
+  } else {
+    split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+    if (split >= nsplit) return;
+  }
   const int nblocks = (t1 - t0 + kBlock - 1) / kBlock;
   // end of the tokens this column's query token may see (t1 without a mask)
   const int lim = min(t1, a.causal ? n - (q_len - 1 - qi) : n);
@@ -416,14 +429,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // (ordered: the unit list gives (sequence, split), see pda_internal.h)
-  int tile, b, split;
-  if (a.units) {
+  // (ordered: the unit list gives (sequence, split, token range), see
+  // WorkUnit)
+  const bool ordered = a.units != nullptr;
+  int tile, b, split, ut0 = 0, ut1 = 0;
+  if (ordered) {
     tile = blockIdx.x % a.head_tiles;
-    const int e = load_uniform(a.units + blockIdx.x / a.head_tiles);
-    if (e < 0) return;
-    b = e & 0xffff;
-    split = e >> 16;
+    const WorkUnit w = load_unit(a.units, blockIdx.x / a.head_tiles);
+    if (w.b < 0) return;
+    b = w.b;
+    split = w.split;
+    ut0 = w.t0;
+    ut1 = w.t1;
   } else {
     tile = blockIdx.x % a.head_tiles;
     b = blockIdx.x / a.head_tiles;
@@ -438,15 +455,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
                "s"(a.split.max_splits), "s"(a.split.split_min_tokens));
   const int log2P = a.log2_page;
   int n = 0;
-  if (split > 0) {
+  if (!ordered && split > 0) {
     n = load_uniform(a.context_lens + b);
     int ns, ta, tb;
     split_range(a.split, n, a.page_size, split, ns, ta, tb);
     if (split >= ns) return;
   }
   PageTable pt{a.block_tables + (int64_t)b * a.max_pages, a.max_pages, 0, 0};
-  pt.load(a.split.max_splits > 1 ? split * a.split.pages_per_split : 0, lane);
-  if (split == 0) n = load_uniform(a.context_lens + b);
+  pt.load(ordered                  ? ut0 >> log2P
+          : a.split.max_splits > 1 ? split * a.split.pages_per_split
+                                   : 0,
+          lane);
+  if (ordered || split == 0) n = load_uniform(a.context_lens + b);
   const int hvalid_n = min(kHeads, a.num_q_heads - tile * kHeads);
 
   // q of the tile's heads into LDS (zero for padded heads)
@@ -460,8 +480,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
 
   __builtin_amdgcn_sched_barrier(0);  // the loads above go out before waiting for n
   int nsplit, t0, t1;
-  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
-  if (split >= nsplit) return;
+  if (ordered) {  // the unit's range; split -1: the sequence's only split
+    nsplit = split < 0 ? 1 : 2;
+    t0 = ut0;
+    t1 = ut1;
+  } else {
+    split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+    if (split >= nsplit) return;
+  }
   const int nblocks = (t1 - t0 + kBlock - 1) / kBlock;
 
   // score-phase identity
@@ -585,7 +611,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
 
 hipError_t launch_mla(const MlaArgs& a, int variant, int max_splits, hipStream_t s) {
   const unsigned units = (unsigned)(a.batch * a.head_tiles);
-  dim3 grid(a.units ? units * (unsigned)max_splits : units, a.units ? 1u : (unsigned)max_splits);
+  dim3 grid(a.units ? (unsigned)(a.head_tiles * a.unit_count) : units,
+            a.units ? 1u : (unsigned)max_splits);
   if (variant == 2) {
     hipLaunchKernelGGL(mla_valu_kernel, grid, dim3(kThreads), 0, s, a);
   } else if (mla_column_groups(a.q_len * a.num_q_heads) == 2) {

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libpda.so")
 PDA_F32, PDA_F16, PDA_BF16, PDA_FP8_E4M3 = 0, 1, 2, 3
 PDA_MLA_DEFAULT, PDA_MLA_MFMA, PDA_MLA_VALU = 0, 1, 2
 PDA_GQA_DEFAULT, PDA_GQA_MFMA, PDA_GQA_VALU = 0, 1, 2
+PDA_SCHEDULE_GRID, PDA_SCHEDULE_BALANCED = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing or too small", 4: "HIP runtime error"}
 
@@ -38,7 +39,8 @@ class Shape(ctypes.Structure):
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("split_min_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
-                ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32)]
+                ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("schedule", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -115,10 +117,10 @@ def _need(cond, msg):
 
 def make_shape(*, batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, page_size,
                max_pages_per_seq, num_pages, q_dtype, kv_dtype, k_scale=1.0, v_scale=1.0,
-               split_min_tokens=0, variant=0, q_len=1, causal=True) -> Shape:
+               split_min_tokens=0, variant=0, q_len=1, causal=True, schedule=0) -> Shape:
     return Shape(batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, page_size,
                  max_pages_per_seq, num_pages, q_dtype, kv_dtype, k_scale, v_scale,
-                 split_min_tokens, variant, q_len, int(causal))
+                 split_min_tokens, variant, q_len, int(causal), int(schedule))
 
 
 def _query_dims(q):
@@ -150,7 +152,7 @@ def plan(shape: Shape, *, mla: bool = False, num_splits: int = 0, num_cus: int =
 
 
 def gqa_shape(q, k_cache, v_cache, block_tables, *, k_scale=1.0, v_scale=1.0,
-              split_min_tokens=0, variant=0, causal=True) -> Shape:
+              split_min_tokens=0, variant=0, causal=True, schedule=0) -> Shape:
     _need(k_cache.dim() == 4 and v_cache.dim() == 4, "bad ranks")
     B, s_q, Hq, d = _query_dims(q)
     num_pages, P, Hkv, dk = k_cache.shape
@@ -161,11 +163,11 @@ def gqa_shape(q, k_cache, v_cache, block_tables, *, k_scale=1.0, v_scale=1.0,
                       max_pages_per_seq=block_tables.shape[1], num_pages=num_pages,
                       q_dtype=_dtype_code(q), kv_dtype=_dtype_code(k_cache, fp8_ok=True),
                       k_scale=k_scale, v_scale=v_scale, split_min_tokens=split_min_tokens,
-                      variant=variant, q_len=s_q, causal=causal)
+                      variant=variant, q_len=s_q, causal=causal, schedule=schedule)
 
 
 def mla_shape(q, kv_cache, block_tables, *, head_dim_v=512, variant=0,
-              split_min_tokens=0, causal=True) -> Shape:
+              split_min_tokens=0, causal=True, schedule=0) -> Shape:
     _need(kv_cache.dim() == 3, "bad ranks")
     B, s_q, Hq, d = _query_dims(q)
     num_pages, P, dk = kv_cache.shape
@@ -176,7 +178,7 @@ def mla_shape(q, kv_cache, block_tables, *, head_dim_v=512, variant=0,
                       max_pages_per_seq=block_tables.shape[1], num_pages=num_pages,
                       q_dtype=_dtype_code(q), kv_dtype=_dtype_code(kv_cache),
                       split_min_tokens=split_min_tokens, variant=variant, q_len=s_q,
-                      causal=causal)
+                      causal=causal, schedule=schedule)
 
 
 def _check_device(*ts):
@@ -196,14 +198,15 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, scale:
                       num_splits: int = 0, out=None, lse=None, k_scale: float = 1.0,
                       v_scale: float = 1.0, split_min_tokens: int = 0, workspace=None,
                       stream=None, return_lse: bool = True, variant: int = 0,
-                      causal: bool = True):
+                      causal: bool = True, schedule: int = PDA_SCHEDULE_GRID):
     """GQA/MQA/MHA paged decode attention.
 
     q [B, Hq, d] returns (out [B, Hq, dv], lse [B, Hq] fp32); q [B, s_q, Hq, d]
     (s_q query tokens per sequence, the last s_q positions; causal: bottom-right
     mask) returns (out [B, s_q, Hq, dv], lse [B, Hq, s_q] fp32)."""
     shape = gqa_shape(q, k_cache, v_cache, block_tables, k_scale=k_scale, v_scale=v_scale,
-                      split_min_tokens=split_min_tokens, variant=variant, causal=causal)
+                      split_min_tokens=split_min_tokens, variant=variant, causal=causal,
+                      schedule=schedule)
     _check_device(q, k_cache, v_cache, block_tables, context_lens, out, lse, workspace)
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
@@ -231,11 +234,12 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, scale:
 def paged_decode_attn_mla(q, kv_cache, block_tables, context_lens, *, scale: float,
                           num_splits: int = 0, out=None, lse=None, variant: int = 0,
                           head_dim_v: int = 512, split_min_tokens: int = 0, workspace=None,
-                          stream=None, return_lse: bool = True, causal: bool = True):
+                          stream=None, return_lse: bool = True, causal: bool = True,
+                          schedule: int = PDA_SCHEDULE_GRID):
     """MLA paged decode attention; returns (out [B, Hq, 512], lse [B, Hq] fp32),
     or (out [B, s_q, Hq, 512], lse [B, Hq, s_q]) for q [B, s_q, Hq, 576]."""
     shape = mla_shape(q, kv_cache, block_tables, head_dim_v=head_dim_v, variant=variant,
-                      split_min_tokens=split_min_tokens, causal=causal)
+                      split_min_tokens=split_min_tokens, causal=causal, schedule=schedule)
     _check_device(q, kv_cache, block_tables, context_lens, out, lse, workspace)
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")

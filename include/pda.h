@@ -111,7 +111,24 @@ typedef struct pda_shape {
                              /* q_len * num_q_heads at most 2^20)          */
   int32_t causal;            /* s_q > 1: 1 = bottom-right causal mask,      */
                              /* 0 = every query sees all n tokens           */
+  int32_t schedule;          /* PDA_SCHEDULE_* (below)                       */
 } pda_shape;
+
+/* How a call cuts sequences into splits (pda_shape.schedule).
+ * GRID: every sequence longer than split_min_tokens takes ceil(pages /
+ *   pages_per_split) splits of one common size (pda_plan_info); with
+ *   split_min_tokens > 0 the work units are listed longest first.
+ * BALANCED: a device-side planning pass, run at the start of each call
+ *   from context_lens, cuts the batch's total pages into near-equal chunks
+ *   of max(16, ceil(total pages / units)) pages, where units is the number
+ *   of (sequence, split) units per KV head and head tile that fill the
+ *   compute units (two workgroups per CU).  A sequence longer than a chunk
+ *   and than split_min_tokens takes ceil(pages / chunk) splits (at most the
+ *   planned max_splits) of equal size; the units are listed longest first.
+ *   Short sequences stay whole, so a batch of mixed lengths becomes units of
+ *   at most one chunk each (load balance across the compute units). */
+#define PDA_SCHEDULE_GRID 0
+#define PDA_SCHEDULE_BALANCED 1
 
 /* GQA kernel variants (pda_shape.variant for paged_decode_attn). */
 #define PDA_GQA_DEFAULT 0 /* matrix cores when available and the group has   */
@@ -128,6 +145,7 @@ typedef struct pda_shape {
 typedef struct pda_plan_info {
   int32_t max_splits;      /* split-axis extent of the launch grid          */
   int32_t pages_per_split; /* pages per split for sequences that split      */
+                           /* (GRID; 0 with BALANCED: chosen on the device) */
   int32_t head_tiles;      /* query-head tiles per KV head                   */
   int32_t workgroups;      /* workgroups of the main kernel                  */
   int32_t num_cus;         /* compute units the plan was made for           */
@@ -146,15 +164,16 @@ int pda_plan(const pda_shape* shape, int is_mla, int num_splits, int num_cus,
 
 /* Workspace bytes a call with these arguments needs (0 when no sequence can
  * split and the work is not ordered).  Queries the current device's CU count
- * when num_splits == 0.  Returns 0 on invalid arguments as well.
+ * when num_splits == 0 or the schedule is BALANCED.  Returns 0 on invalid
+ * arguments as well.
  *
  * Work ordering: when shape->split_min_tokens > 0 (a batch of mixed lengths,
- * as the threshold signals) and batch <= 65535, each call first runs one
- * small kernel that lists the (sequence, split) work units by decreasing
- * token count (in the workspace), and the attention workgroups take units
- * in that order, so the longest units start first (longest-processing-time
- * order; the pages do not prescribe a schedule).  The result does not
- * depend on the order. */
+ * as the threshold signals) or the schedule is BALANCED, each call first
+ * runs one small planning kernel that lists the (sequence, split) work
+ * units, with their token ranges, by decreasing token count (in the
+ * workspace), and the attention workgroups take units in that order, so the
+ * longest units start first (longest-processing-time order; the pages do not
+ * prescribe a schedule).  The result does not depend on the order. */
 size_t pda_workspace_bytes(const pda_shape* shape, int is_mla, int num_splits);
 
 /* GQA / MQA / MHA paged decode attention (layouts above).

@@ -58,13 +58,15 @@ def test_plan_explicit_and_threshold():
     # no sequence can exceed the split threshold: never split; a threshold
     # still orders the work, so the workspace holds the unit list (B x S int32)
     p = pda.plan(_shape(max_pages_per_seq=10, split_min_tokens=160), num_splits=4, num_cus=256)
-    assert p.max_splits == 1 and p.ordered == 1 and p.workspace_bytes == 64 * 4
+    assert p.max_splits == 1 and p.ordered == 1
+    assert p.workspace_bytes == 64 * 16 + 64 * 4       # units [B][4] int32, split counts [B]
     p = pda.plan(_shape(max_pages_per_seq=10), num_splits=4, num_cus=256)
     assert p.ordered == 0
 
 
 def test_plan_ordered_workspace_layout():
-    """Partials (256-byte aligned), partial LSE (256-byte aligned), unit list."""
+    """Partials (256-byte aligned), partial LSE (256-byte aligned), work units
+    [B * S][4] int32 (256-byte aligned), split count per sequence [B]."""
     s = _shape(batch=3, max_pages_per_seq=100, split_min_tokens=64, num_q_heads=8,
                num_kv_heads=2)
     p = pda.plan(s, num_splits=5, num_cus=256)
@@ -72,8 +74,37 @@ def test_plan_ordered_workspace_layout():
     rows = 3 * 8
     o = rows * 5 * 128 * 4
     l = -(-(rows * 5 * 4) // 256) * 256
-    assert p.workspace_bytes == -(-o // 256) * 256 + l + 3 * 5 * 4
+    u = -(-(3 * 5 * 16) // 256) * 256
+    assert p.workspace_bytes == -(-o // 256) * 256 + l + u + 3 * 4
     assert pda.load().pda_workspace_bytes(ctypes.byref(s), 0, 5) == p.workspace_bytes
+
+
+def test_plan_balanced_schedule():
+    """BALANCED: always ordered; the split cap fills the CUs per (KV head,
+    head tile) unless num_splits caps it; pages per split are chosen on the
+    device (0 in the plan)."""
+    bal = dict(schedule=pda.PDA_SCHEDULE_BALANCED)
+    p = pda.plan(_shape(batch=128, num_q_heads=64, max_pages_per_seq=1024, **bal), num_cus=256)
+    assert (p.max_splits, p.pages_per_split, p.ordered) == (64, 0, 1)   # 512 / 8 units
+    p = pda.plan(_shape(batch=128, num_q_heads=64, max_pages_per_seq=1024, **bal),
+                 num_splits=8, num_cus=256)
+    assert (p.max_splits, p.ordered) == (8, 1)
+    rows = 128 * 64
+    # the unit list holds at most B + target units (target = 2 x 512 / 8 chunks)
+    assert p.workspace_bytes == (rows * 8 * 128 * 4 + -(-(rows * 8 * 4) // 256) * 256 +
+                                 (128 + 128) * 16 + 128 * 4)
+    assert p.workgroups == (128 + 128) * 8
+    p = pda.plan(_shape(batch=1, max_pages_per_seq=2048, **bal), num_cus=256)
+    assert (p.max_splits, p.ordered) == (64, 1)
+    # no more splits than 16-page chunks fit a table row
+    p = pda.plan(_shape(max_pages_per_seq=10, **bal), num_cus=256)
+    assert (p.max_splits, p.ordered) == (1, 1)
+    p = pda.plan(_shape(batch=1, max_pages_per_seq=100, **bal), num_cus=256)
+    assert p.max_splits == 7
+    fake = ctypes.c_void_p(0x1000)
+    bad = _shape(schedule=2)
+    assert pda.load().paged_decode_attn(fake, fake, fake, fake, fake, 4, 0.1, 1, fake, None,
+                                        ctypes.byref(bad), None, 0, None) == 1
 
 
 def test_plan_head_tiles():

@@ -267,3 +267,63 @@ def test_graph_capture_and_replay():
         pda.paged_decode_attn(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
                               dev.context_lens, **kw)
         torch.cuda.synchronize()
+
+
+BAL = pda.PDA_SCHEDULE_BALANCED
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("num_splits,thr", [(0, 0), (8, 0), (8, 4096)])
+def test_balanced_schedule_mixed_lengths(variant, num_splits, thr):
+    """The balanced schedule: the device-side planning pass cuts the batch's
+    pages into near-equal chunks; empty, tiny, threshold-length and long
+    sequences."""
+    lens = [0, 4096, 1, 9000, 4097, 17, 0, 2500, 16384, 700]
+    case = _gqa(17, len(lens), 16, 4, 128, 16, lens, extra_pages=3)
+    say("balanced", variant, num_splits, thr)
+    dev = pda.to_device(case)
+    shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, schedule=BAL,
+                          split_min_tokens=thr, variant=VARIANTS[variant])
+    p = pda.plan(shape, num_splits=num_splits)
+    assert p.ordered == 1 and p.pages_per_split == 0
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, dev, num_splits=num_splits, split_min_tokens=thr,
+                            variant=VARIANTS[variant], schedule=BAL)
+    check(case, out, lse, ref_o, ref_l, label="balanced")
+    out2, lse2 = pda.run_case(case, dev, num_splits=num_splits, split_min_tokens=thr,
+                              variant=VARIANTS[variant], schedule=BAL)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "run-to-run differs"
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_balanced_schedule_long_context(batch):
+    case = W.gqa_long(batch)
+    say("balanced", case.name)
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, dev, schedule=BAL)
+    check(case, out, lse, ref_o, ref_l, label="balanced %s" % case.name)
+
+
+def test_balanced_schedule_ragged_fp8_sampled_rows():
+    """The ragged fp8 workload (B=128, log-uniform lengths up to 16384) under
+    the balanced schedule with no split threshold, up to 8 splits."""
+    case = W.ragged_fp8()
+    say("balanced", case.name)
+    rng = np.random.default_rng(6)
+    rows = rng.random((case.batch, case.num_q_heads)) < 0.25
+    rows[:3] = True
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case, rows=rows)
+    out, lse = pda.run_case(case, dev, num_splits=8, schedule=BAL)
+    check(case, out, lse, ref_o, ref_l, rows=rows, label="balanced ragged")
+
+
+def test_balanced_schedule_multi_token():
+    case = W.make_gqa(batch=5, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                      context_lens=[3, 5000, 100, 1, 2048], q_dtype="bf16", kv_dtype="bf16",
+                      seed=18, q_len=3, extra_pages=2)
+    say("balanced multi-token")
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, schedule=BAL)
+    check(case, out, lse, ref_o, ref_l, label="balanced q_len=3")

@@ -123,3 +123,15 @@ def test_ordered_work_mixed_lengths(variant):
     out, lse = pda.run_case(case, variant=VARIANTS[variant], num_splits=5, split_min_tokens=1000)
     ref_o, ref_l = oracle_ref(case)
     check(case, out, lse, ref_o, ref_l, label="mla ordered %s" % variant)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("Hq", [16, 32])
+def test_balanced_schedule_mixed_lengths(variant, Hq):
+    """MLA under the balanced schedule (device-side chunking of the batch's
+    pages), 16- and 32-row workgroups."""
+    case = _mla(71 + Hq, [0, 2000, 64, 9000, 129, 1], Hq=Hq, extra_pages=2)
+    say("mla balanced", variant, Hq)
+    out, lse = pda.run_case(case, variant=VARIANTS[variant], schedule=pda.PDA_SCHEDULE_BALANCED)
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label="mla balanced %s Hq=%d" % (variant, Hq))
