@@ -213,7 +213,7 @@ def _oracle_call(case, rows):
         return oracle.mla_attention(case.q, case.k_cache, case.block_tables, case.context_lens,
                                     scale=case.scale, d_latent=case.d_latent,
                                     q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
-                                    causal=case.causal, rows=rows)
+                                    kv_scale=case.k_scale, causal=case.causal, rows=rows)
     return oracle.paged_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
                                   case.context_lens, scale=case.scale, q_dtype=case.q_dtype,
                                   kv_dtype=case.kv_dtype, k_scale=case.k_scale,

@@ -214,9 +214,12 @@ def make_mla(*, batch: int, num_q_heads: int, d_latent: int, d_rope: int, page_s
              context_lens: Sequence[int], dtype: str, seed: int, scale: float,
              max_pages: Optional[int] = None, extra_pages: int = 0, poison: bool = True,
              std: float = 1.0, q_len: int = 1, causal: bool = True,
-             name: str = "") -> PagedCase:
+             kv_dtype: Optional[str] = None, name: str = "") -> PagedCase:
     """MLA case: one latent record [c (d_latent) | k_R (d_rope)] per token
-    (q [B, q_len, Hq, rec] when q_len > 1)."""
+    (q [B, q_len, Hq, rec] when q_len > 1).  kv_dtype "e4m3" stores the
+    latent as fp8 with one fp32 scale (amax / 448 over the records read),
+    kept in k_scale (and v_scale: V is part of the same record)."""
+    kvd = dtype if kv_dtype is None else kv_dtype
     lens = np.asarray(context_lens, dtype=np.int32)
     assert lens.shape == (batch,)
     rng = _rng(seed)
@@ -225,14 +228,22 @@ def make_mla(*, batch: int, num_q_heads: int, d_latent: int, d_rope: int, page_s
     num_pages, tables, used = _layout_pages(rng, lens, P, max_pages, extra_pages)
     qshape = (batch, num_q_heads, rec) if q_len == 1 else (batch, q_len, num_q_heads, rec)
     q = encode(_normal(rng, qshape, std), dtype)
-    kv = encode(_normal(rng, (num_pages, P, rec), std), dtype)
+    kv32 = _normal(rng, (num_pages, P, rec), std)
+    kv_scale = 1.0
+    if kvd == "e4m3":
+        amax = float(np.abs(kv32[used]).max()) if used.any() else 1.0
+        kv_scale = float(np.float32(amax / E4M3_MAX))
+        kv32 /= np.float32(kv_scale)
+    kv = encode(kv32, kvd)
+    del kv32
     if poison:
-        _poison(kv, tables, lens, used, P, NAN_BITS[dtype])
+        _poison(kv, tables, lens, used, P, NAN_BITS[kvd])
     else:
         tables[tables < 0] = 0
     return PagedCase(q=q, k_cache=kv, v_cache=None, block_tables=tables, context_lens=lens,
-                     q_dtype=dtype, kv_dtype=dtype, page_size=P, scale=scale, mla=True,
-                     d_latent=d_latent, name=name, causal=causal)
+                     q_dtype=dtype, kv_dtype=kvd, page_size=P, scale=scale,
+                     k_scale=kv_scale, v_scale=kv_scale, mla=True, d_latent=d_latent,
+                     name=name, causal=causal)
 
 
 def log_uniform_lens(rng: np.random.Generator, n: int, lo: int, hi: int) -> np.ndarray:

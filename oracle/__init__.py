@@ -61,8 +61,8 @@ def _load():
     lib.orc_decode.argtypes = [I, P, I64, I64, P]
     lib.orc_paged_attention.argtypes = [P, I, P, P, I, P, I, P, P, P, I, I, I, I, I, I, I,
                                         I64, D, D, D, I, P, P, P, I]
-    lib.orc_mla_attention.argtypes = [P, I, P, I, P, I, P, P, P, I, I, I, I, I, I, I64, D, I,
-                                      P, P, P, I]
+    lib.orc_mla_attention.argtypes = [P, I, P, I, P, I, P, P, P, I, I, I, I, I, I, I64, D, D,
+                                      I, P, P, P, I]
     lib.orc_combine.argtypes = [P, P, I64, I, I, P, P]
     lib.orc_kv_append.argtypes = [P, I, P, I, P, I, P, I, I, I, I, I, I64, ctypes.c_float]
     lib.orc_max_threads.argtypes = []
@@ -170,13 +170,14 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, *, scale,
 
 
 def mla_attention(q, kv_cache, block_tables, context_lens, *, scale, d_latent, q_dtype,
-                  kv_dtype, causal=True, tok_begin=None, tok_end=None, rows=None,
-                  num_threads=0):
+                  kv_dtype, kv_scale=1.0, causal=True, tok_begin=None, tok_end=None,
+                  rows=None, num_threads=0):
     """MLA paged decode attention in fp64.
 
     q [B, Hq, d_latent + d_rope] or [B, s_q, Hq, d_latent + d_rope];
     kv_cache [num_pages, P, d_latent + d_rope].  K is the whole record, V its
-    first d_latent values; s_q and causal as in paged_attention.
+    first d_latent values, both times kv_scale (an fp8 latent's dequantization
+    scale); s_q and causal as in paged_attention.
     Returns (out [B, Hq, d_latent], lse [B, Hq]) for a 3-D q and
     (out [B, s_q, Hq, d_latent], lse [B, Hq, s_q]) for a 4-D q, float64.
     """
@@ -196,7 +197,8 @@ def mla_attention(q, kv_cache, block_tables, context_lens, *, scale, d_latent, q
     rc = _load().orc_mla_attention(
         _ptr(q), _DT[q_dtype], _ptr(kv_cache), _DT[kv_dtype], _ptr(bt), bt.shape[1],
         _ptr(cl), _ptr(tb), _ptr(te), B, s_q, Hq, d_latent, rec - d_latent, P, num_pages,
-        float(scale), int(bool(causal)), _ptr(rm), _ptr(out), _ptr(lse), int(num_threads))
+        float(scale), float(kv_scale), int(bool(causal)), _ptr(rm), _ptr(out), _ptr(lse),
+        int(num_threads))
     _check(rc)
     return _shape_result(out, lse, single)
 

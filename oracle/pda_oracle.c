@@ -293,14 +293,15 @@ int orc_paged_attention(const void* q, int q_dtype, const void* k_cache,
 /* Paged decode attention over an MLA latent cache (one record per token, no
  * head axis).  q [B, q_len, Hq, d_latent + d_rope]; kv_cache [num_pages, P,
  * d_latent + d_rope]; out [B, q_len, Hq, d_latent] fp64; lse [B, Hq, q_len]
- * fp64.  K_j is the whole record, V_j its first d_latent values; queries and
- * the causal mask as in orc_paged_attention. */
+ * fp64.  K_j is the whole record times kv_scale (the dequantization scale of
+ * an fp8 latent, 1 otherwise), V_j its first d_latent values (the same
+ * scaled values); queries and the causal mask as in orc_paged_attention. */
 int orc_mla_attention(const void* q, int q_dtype, const void* kv_cache, int kv_dtype,
                       const int32_t* block_tables, int max_pages,
                       const int32_t* context_lens, const int32_t* tok_begin,
                       const int32_t* tok_end, int B, int q_len, int Hq, int d_latent,
-                      int d_rope, int P, int64_t num_pages, double scale, int causal,
-                      const uint8_t* row_mask, double* out, double* lse,
+                      int d_rope, int P, int64_t num_pages, double scale, double kv_scale,
+                      int causal, const uint8_t* row_mask, double* out, double* lse,
                       int num_threads) {
   if (!q || !kv_cache || !block_tables || !context_lens || !out || !lse) return ORC_ERR_ARG;
   if (B < 0 || q_len <= 0 || Hq <= 0 || d_latent <= 0 || d_rope < 0 || P <= 0 ||
@@ -345,9 +346,9 @@ int orc_mla_attention(const void* q, int q_dtype, const void* kv_cache, int kv_d
       const int32_t* trow = block_tables + (int64_t)b * max_pages;
       /* K: the whole record; V: the latent part of the same record. */
       int rk = gather_rows(kv_cache, kv_dtype, trow, num_pages, P, (int64_t)P * rec, rec, 0,
-                           rec, 1.0, t0, t1, K);
+                           rec, kv_scale, t0, t1, K);
       int rv = gather_rows(kv_cache, kv_dtype, trow, num_pages, P, (int64_t)P * rec, rec, 0,
-                           d_latent, 1.0, t0, t1, V);
+                           d_latent, kv_scale, t0, t1, V);
       if (rk != ORC_OK || rv != ORC_OK) {
 #pragma omp atomic write
         status = ORC_ERR_TABLE;

@@ -20,17 +20,18 @@ from decode_attention_paged_02_amd import workloads as W
 DL, DR = 32, 8          # small latent / rope widths for fast fp64 checks
 
 
-def _case(seed, lens, Hq=4, P=8, dtype="f32"):
+def _case(seed, lens, Hq=4, P=8, dtype="f32", kv_dtype=None):
     return W.make_mla(batch=len(lens), num_q_heads=Hq, d_latent=DL, d_rope=DR, page_size=P,
                       context_lens=lens, dtype=dtype, seed=seed, scale=1 / math.sqrt(24.0),
-                      extra_pages=2)
+                      extra_pages=2, kv_dtype=kv_dtype)
 
 
 def _mla(case, q=None, kv=None, qd=None, kd=None):
     return oracle.mla_attention(case.q if q is None else q,
                                 case.k_cache if kv is None else kv, case.block_tables,
                                 case.context_lens, scale=case.scale, d_latent=case.d_latent,
-                                q_dtype=qd or case.q_dtype, kv_dtype=kd or case.kv_dtype)
+                                q_dtype=qd or case.q_dtype, kv_dtype=kd or case.kv_dtype,
+                                kv_scale=case.k_scale)
 
 
 def test_absorbed_equals_materialized_per_head():
@@ -118,6 +119,40 @@ def test_mla_matches_torch_sdpa():
     for b in range(case.batch):
         j = np.arange(int(case.context_lens[b]))
         rec = torch.from_numpy(kv[case.block_tables[b, j // P], j % P])   # [n, DL + DR]
+        k = rec.unsqueeze(0).expand(case.num_q_heads, -1, -1).contiguous()
+        v = rec[:, :DL].unsqueeze(0).expand(case.num_q_heads, -1, -1).contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(q[b].unsqueeze(1), k, v,
+                                                               scale=case.scale)
+        np.testing.assert_allclose(out[b], ref[:, 0].numpy(), rtol=0, atol=1e-12)
+
+
+def test_fp8_latent_matches_gqa_oracle_with_aliased_value_and_scales():
+    """An fp8 latent with one dequantization scale: MLA == the GQA oracle on the
+    same stored bytes with K = the record, V = its first DL columns and
+    k_scale = v_scale = the latent scale (whose fp8 handling is pinned on its
+    own)."""
+    case = _case(12, [5, 50, 21], Hq=5, dtype="bf16", kv_dtype="e4m3")
+    assert case.kv_dtype == "e4m3" and case.k_scale != 1.0
+    out, lse = _mla(case)
+    k = case.k_cache[:, :, None, :]
+    v = np.ascontiguousarray(case.k_cache[:, :, None, :DL])
+    o2, l2 = oracle.paged_attention(case.q, k, v, case.block_tables, case.context_lens,
+                                    scale=case.scale, q_dtype="bf16", kv_dtype="e4m3",
+                                    k_scale=case.k_scale, v_scale=case.k_scale)
+    np.testing.assert_allclose(out, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l2, rtol=0, atol=1e-12)
+
+
+def test_fp8_latent_matches_torch_sdpa_on_decoded_values():
+    import torch
+    case = _case(13, [3, 70], Hq=4, dtype="bf16", kv_dtype="e4m3")
+    out, lse = _mla(case)
+    kv = torch.from_numpy(case.k_cache).view(torch.float8_e4m3fn).double().numpy() * case.k_scale
+    q = torch.from_numpy(W.to_float32(case.q, "bf16").astype(np.float64))
+    P = case.page_size
+    for b in range(case.batch):
+        j = np.arange(int(case.context_lens[b]))
+        rec = torch.from_numpy(kv[case.block_tables[b, j // P], j % P])
         k = rec.unsqueeze(0).expand(case.num_q_heads, -1, -1).contiguous()
         v = rec[:, :DL].unsqueeze(0).expand(case.num_q_heads, -1, -1).contiguous()
         ref = torch.nn.functional.scaled_dot_product_attention(q[b].unsqueeze(1), k, v,

@@ -35,8 +35,10 @@ MUTATIONS = [
      "ldexp(1.0 + (double)m / 128.0, e - 126)"),
     ("V read from the K cache", "int rv = gather_rows(v_cache,", "int rv = gather_rows(k_cache,"),
     ("MLA value taken from the record's tail",
-     "P, (int64_t)P * rec, rec, 0,\n                           d_latent, 1.0,",
-     "P, (int64_t)P * rec, rec, d_rope,\n                           d_latent, 1.0,"),
+     "P, (int64_t)P * rec, rec, 0,\n                           d_latent, kv_scale,",
+     "P, (int64_t)P * rec, rec, d_rope,\n                           d_latent, kv_scale,"),
+    ("MLA value missing the latent scale",
+     "d_latent, kv_scale, t0, t1, V);", "d_latent, 1.0, t0, t1, V);"),
     ("MLA rope block dropped from the score",
      "attend_rows(qd, K, V, n, rec, d_latent,", "attend_rows(qd, K, V, n, d_latent, d_latent,"),
     ("combine: plain average of splits", "double w = exp(l - mx);", "double w = 1.0;"),
