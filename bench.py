@@ -49,6 +49,8 @@ def make_case(name):
         return W.gqa_batch64_mtp(2)
     if name == "mla_b16_q2":
         return W.mla_b16_mtp(2)
+    if name == "mla_b16_fp8":
+        return W.mla_b16(kv_dtype="e4m3")
     raise SystemExit("unknown workload %s" % name)
 
 
@@ -89,7 +91,8 @@ def run_gpu(case, workload, steps, warmup, pools):
     if case.mla:
         shape = pda.mla_shape(dev.q, dev.k_cache, dev.block_tables, head_dim_v=case.d_latent,
                               split_min_tokens=kw.get("split_min_tokens", 0),
-                              causal=case.causal, schedule=kw.get("schedule", 0))
+                              causal=case.causal, schedule=kw.get("schedule", 0),
+                              kv_scale=case.k_scale)
     else:
         shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
                               k_scale=case.k_scale, v_scale=case.v_scale,
@@ -254,7 +257,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa_b64",
                     choices=["gqa_b64", "gqa_b1_split", "gqa_b4_split", "mla_b16", "ragged_fp8",
-                             "ragged_fp8_balanced", "gqa_b64_q2", "mla_b16_q2"])
+                             "ragged_fp8_balanced", "gqa_b64_q2", "mla_b16_q2", "mla_b16_fp8"])
     ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
     ap.add_argument("--others", default="gqa_b1_split,gqa_b4_split,kv_append_b64",
                     help="extra workloads measured into 'other_workloads' ('' for none)")

@@ -50,7 +50,9 @@ int check_shape(const pda_shape* s, bool mla) {
   if (mla) {
     if (s->num_kv_heads != 1) return PDA_ERR_INVALID_ARG;
     if (s->head_dim != 576 || s->head_dim_v != 512) return PDA_ERR_UNSUPPORTED;
-    if (s->q_dtype != PDA_BF16 || s->kv_dtype != PDA_BF16) return PDA_ERR_UNSUPPORTED;
+    if (s->q_dtype != PDA_BF16 || (s->kv_dtype != PDA_BF16 && s->kv_dtype != PDA_FP8_E4M3))
+      return PDA_ERR_UNSUPPORTED;
+    if (s->kv_dtype == PDA_FP8_E4M3 && !(s->k_scale > 0.f)) return PDA_ERR_INVALID_ARG;
     if (s->page_size % 64 != 0 || (s->page_size & (s->page_size - 1)) != 0)
       return PDA_ERR_UNSUPPORTED;
     if (s->num_q_heads > 16 && s->num_q_heads % 16 != 0) return PDA_ERR_UNSUPPORTED;
@@ -382,7 +384,10 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
   a.max_pages = s.max_pages_per_seq;
   a.log2_page = 0;
   while ((1 << a.log2_page) < s.page_size) ++a.log2_page;
-  a.qk_scale_log2 = scale * 1.4426950408889634f;
+  // an fp8 latent: K and V are the same dequantized values (one scale)
+  const float kvs = s.kv_dtype == PDA_FP8_E4M3 ? s.k_scale : 1.0f;
+  a.qk_scale_log2 = scale * kvs * 1.4426950408889634f;
+  a.v_scale = kvs;
   a.split.pages_per_split = p.pages_per_split;
   a.split.max_splits = p.max_splits;
   a.split.split_min_tokens = s.split_min_tokens;
@@ -392,7 +397,8 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
     rc = run_order(s, plan, context_lens, units, seq_splits, a.split, st);
     if (rc != PDA_OK) return rc;
   }
-  if (pda::launch_mla(a, s.variant, p.max_splits, st) != hipSuccess) return PDA_ERR_HIP;
+  if (pda::launch_mla(a, s.variant, s.kv_dtype, p.max_splits, st) != hipSuccess)
+    return PDA_ERR_HIP;
   if (p.max_splits > 1) {
     pda::CombineArgs c{};
     c.part_o = a.part_o;

@@ -101,7 +101,7 @@ struct CombineArgs {
 
 struct MlaArgs {
   const void* q;           // [B, q_len, Hq, 576] bf16
-  const void* kv_cache;    // [num_pages, P, 576] bf16
+  const void* kv_cache;    // [num_pages, P, 576] bf16 or fp8 (E4M3)
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;               // [B, q_len, Hq, 512] bf16
@@ -112,7 +112,8 @@ struct MlaArgs {
   int32_t q_len, causal;   // as in GqaArgs; tile rows are (query i, head h), i * Hq + h
   int32_t page_size, max_pages;
   int32_t log2_page;       // page_size == 1 << log2_page
-  float qk_scale_log2;     // scale * log2(e)
+  float qk_scale_log2;     // scale * kv_scale * log2(e)
+  float v_scale;           // the latent's dequantization scale (1 for bf16)
   SplitLayout split;
   const int32_t* units;    // as in GqaArgs (x = head tiles * unit_count)
   int32_t unit_count;
@@ -167,7 +168,8 @@ hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
                       int tile_heads, int max_splits, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t stream);
 hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
-hipError_t launch_mla(const MlaArgs& a, int variant, int max_splits, hipStream_t stream);
+hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int max_splits,
+                      hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int src_dtype, int cache_dtype, hipStream_t stream);
 
 }  // namespace pda

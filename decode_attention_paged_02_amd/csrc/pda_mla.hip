@@ -110,13 +110,18 @@ struct PageTable {
 };
 
 // Shared block staging: the workgroup's T threads bring one block of 32
-// records (36 KiB) into registers with 16-byte loads, then into LDS.  With
-// T = 512 the last load of a thread may lie past the block: its offset is
-// outside the buffer resource (zero, no memory access) and it is not stored.
-template <int T>
+// records into registers, then into LDS as bf16 rows: 16-byte loads of a
+// bf16 latent (36 KiB per block), or 8-byte loads of an fp8 latent (18 KiB),
+// each widened exactly to the same 16-byte bf16 LDS chunk.  With T = 512 the
+// last load of a thread may lie past the block: its offset is outside the
+// buffer resource (zero, no memory access) and it is not stored.
+template <int T, class KT>
 struct BlockLoader {
-  static constexpr int kN = (kBlockChunks + T - 1) / T;  // loads per thread
-  u32x4 r[kN];
+  static constexpr bool kFp8 = std::is_same<KT, E4M3>::value;
+  static constexpr int kRecBytes = kFp8 ? kRec : 2 * kRec;  // bytes of a record in memory
+  static constexpr int kN = (kBlockChunks + T - 1) / T;      // loads per thread
+  typedef typename std::conditional<kFp8, u32x2, u32x4>::type piece_t;
+  piece_t r[kN];
 
   // Load block `blk` of the range [t0, t1) (tokens t0 + 32 blk ...).  Rows
   // past t1 (and a block past the range) read as zero without memory access.
@@ -131,10 +136,14 @@ struct BlockLoader {
     const int slot = tok & ((1 << log2P) - 1);
     const int64_t rec0 = (int64_t)phys * a.page_size + slot;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)a.kv_cache + rec0 * (kRec * 2)), 0, rows * kRec * 2, kRsrcFlags);
+        (void*)((const char*)a.kv_cache + rec0 * kRecBytes), 0, rows * kRecBytes, kRsrcFlags);
 #pragma unroll
-    for (int i = 0; i < kN; ++i)
-      r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + i * T) * 16, 0, kLoadPolicy);
+    for (int i = 0; i < kN; ++i) {
+      if constexpr (kFp8)
+        r[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, (tid + i * T) * 8, 0, kLoadPolicy);
+      else
+        r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + i * T) * 16, 0, kLoadPolicy);
+    }
   }
 
   __device__ __forceinline__ void store(char* lds, int tid) const {
@@ -143,7 +152,21 @@ struct BlockLoader {
       const int q = tid + i * T;
       if (kN * T == kBlockChunks || q < kBlockChunks) {
         const int row = q / kRowChunks, col = q % kRowChunks;
-        *(u32x4*)(lds + lds_off(row, col)) = r[i];
+        u32x4 w;
+        if constexpr (kFp8) {
+          // bytes 0..7 -> bf16 pairs (0, 1), (2, 3), (4, 5), (6, 7); every
+          // E4M3 value is a bf16 value, the conversion is exact
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            w[2 * h] = __builtin_bit_cast(uint32_t,
+                                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[i][h], 1.0f, false));
+            w[2 * h + 1] = __builtin_bit_cast(uint32_t,
+                                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[i][h], 1.0f, true));
+          }
+        } else {
+          w = r[i];
+        }
+        *(u32x4*)(lds + lds_off(row, col)) = w;
       }
     }
   }
@@ -163,8 +186,9 @@ __device__ __forceinline__ void store_bf16x4(void* out, int64_t i, f32x4 v) {
 
 // ------------------------------------------------------------ MFMA kernel
 
-// NG column groups of four waves; a workgroup owns 16 NG rows.
-template <int NG>
+// NG column groups of four waves; a workgroup owns 16 NG rows.  KT: the
+// latent's storage type (BF16, or E4M3 with a dequantization scale).
+template <int NG, class KT>
 __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs a) {
   constexpr int T = kThreads * NG;
   __shared__ __attribute__((aligned(16))) char lds[2][kBlock * kRowBytes];
@@ -271,7 +295,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   // of block k + 2 go into the registers it leaves.  Loads of blocks past the
   // range have empty resources (no memory access), so they need no branch.
   // (A deeper ring for the 512-thread workgroups measured no gain.)
-  BlockLoader<T> ld[2];
+  BlockLoader<T, KT> ld[2];
   ld[0].load(a, pt, t0, t1, 0, log2P, tid);
   ld[0].store(lds[0], tid);
   ld[1].load(a, pt, t0, t1, 1, log2P, tid);
@@ -382,7 +406,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   // unrolled pair): the wait counts then stay exact across iterations, and a
   // block past the range is all zero rows (an odd block count computes one
   // such block, fully masked).
-  auto body = [&](int blk, BlockLoader<T>& nxt) {
+  auto body = [&](int blk, BlockLoader<T, KT>& nxt) {
     compute(blk);
     nxt.store(lds[(blk + 1) & 1], tid);
     nxt.load(a, pt, t0, t1, blk + 3, log2P, tid);
@@ -397,7 +421,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   // (out row (b, qi, h); lse [B, Hq, q_len])
   const float l = sum_x4(l_run);
   if (!hvalid) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = l > 0.f ? a.v_scale / l : 0.f;
   const float lse = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
   const int64_t row = ((int64_t)b * q_len + qi) * a.num_q_heads + h;
   if (nsplit == 1) {
@@ -419,6 +443,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
 // lane%16): the two dot products over 576 values from LDS (packed bf16 dot2).
 // The block max of a head is a 16-lane row reduction.  P V: thread t owns
 // value columns 8 (t%64) .. +8 of heads 4 (t/64) .. +3 and reads P from LDS.
+template <class KT>
 __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][kBlock * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint32_t q_sh[kHeads][kRec / 2];
@@ -503,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
 
-  BlockLoader<kThreads> ld;
+  BlockLoader<kThreads, KT> ld;
   ld.load(a, pt, t0, t1, 0, log2P, tid);
   ld.store(lds[0], tid);
   ld.load(a, pt, t0, t1, 1, log2P, tid);
@@ -589,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
     const int hh = 4 * hq + j;
     if (hh >= hvalid_n) continue;
     const float l = l_sh[hh];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? a.v_scale / l : 0.f;
     const int64_t row = (int64_t)b * a.num_q_heads + tile * kHeads + hh;
     const f32x4 o0 = {acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv};
     const f32x4 o1 = {acc[j][4] * inv, acc[j][5] * inv, acc[j][6] * inv, acc[j][7] * inv};
@@ -609,16 +634,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
 
 }  // namespace
 
-hipError_t launch_mla(const MlaArgs& a, int variant, int max_splits, hipStream_t s) {
+hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int max_splits, hipStream_t s) {
   const unsigned units = (unsigned)(a.batch * a.head_tiles);
   dim3 grid(a.units ? (unsigned)(a.head_tiles * a.unit_count) : units,
             a.units ? 1u : (unsigned)max_splits);
+  const bool fp8 = kv_dtype == 3;
+  const bool two = mla_column_groups(a.q_len * a.num_q_heads) == 2;
   if (variant == 2) {
-    hipLaunchKernelGGL(mla_valu_kernel, grid, dim3(kThreads), 0, s, a);
-  } else if (mla_column_groups(a.q_len * a.num_q_heads) == 2) {
-    hipLaunchKernelGGL(mla_mfma_kernel<2>, grid, dim3(2 * kThreads), 0, s, a);
+    if (fp8) hipLaunchKernelGGL(mla_valu_kernel<E4M3>, grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(mla_valu_kernel<BF16>, grid, dim3(kThreads), 0, s, a);
+  } else if (two) {
+    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<2, E4M3>), grid, dim3(2 * kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mla_mfma_kernel<2, BF16>), grid, dim3(2 * kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(mla_mfma_kernel<1>, grid, dim3(kThreads), 0, s, a);
+    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<1, E4M3>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mla_mfma_kernel<1, BF16>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

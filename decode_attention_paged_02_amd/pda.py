@@ -167,7 +167,7 @@ def gqa_shape(q, k_cache, v_cache, block_tables, *, k_scale=1.0, v_scale=1.0,
 
 
 def mla_shape(q, kv_cache, block_tables, *, head_dim_v=512, variant=0,
-              split_min_tokens=0, causal=True, schedule=0) -> Shape:
+              split_min_tokens=0, causal=True, schedule=0, kv_scale=1.0) -> Shape:
     _need(kv_cache.dim() == 3, "bad ranks")
     B, s_q, Hq, d = _query_dims(q)
     num_pages, P, dk = kv_cache.shape
@@ -176,9 +176,9 @@ def mla_shape(q, kv_cache, block_tables, *, head_dim_v=512, variant=0,
     return make_shape(batch=B, num_q_heads=Hq, num_kv_heads=1, head_dim=d,
                       head_dim_v=head_dim_v, page_size=P,
                       max_pages_per_seq=block_tables.shape[1], num_pages=num_pages,
-                      q_dtype=_dtype_code(q), kv_dtype=_dtype_code(kv_cache),
-                      split_min_tokens=split_min_tokens, variant=variant, q_len=s_q,
-                      causal=causal, schedule=schedule)
+                      q_dtype=_dtype_code(q), kv_dtype=_dtype_code(kv_cache, fp8_ok=True),
+                      k_scale=kv_scale, v_scale=kv_scale, split_min_tokens=split_min_tokens,
+                      variant=variant, q_len=s_q, causal=causal, schedule=schedule)
 
 
 def _check_device(*ts):
@@ -235,11 +235,13 @@ def paged_decode_attn_mla(q, kv_cache, block_tables, context_lens, *, scale: flo
                           num_splits: int = 0, out=None, lse=None, variant: int = 0,
                           head_dim_v: int = 512, split_min_tokens: int = 0, workspace=None,
                           stream=None, return_lse: bool = True, causal: bool = True,
-                          schedule: int = PDA_SCHEDULE_GRID):
+                          schedule: int = PDA_SCHEDULE_GRID, kv_scale: float = 1.0):
     """MLA paged decode attention; returns (out [B, Hq, 512], lse [B, Hq] fp32),
-    or (out [B, s_q, Hq, 512], lse [B, Hq, s_q]) for q [B, s_q, Hq, 576]."""
+    or (out [B, s_q, Hq, 512], lse [B, Hq, s_q]) for q [B, s_q, Hq, 576].  An
+    fp8 latent (uint8 storage, E4M3) takes its dequantization scale kv_scale."""
     shape = mla_shape(q, kv_cache, block_tables, head_dim_v=head_dim_v, variant=variant,
-                      split_min_tokens=split_min_tokens, causal=causal, schedule=schedule)
+                      split_min_tokens=split_min_tokens, causal=causal, schedule=schedule,
+                      kv_scale=kv_scale)
     _check_device(q, kv_cache, block_tables, context_lens, out, lse, workspace)
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
@@ -340,7 +342,8 @@ def run_case(case, dev: Optional[DeviceCase] = None, **kw):
     kw.setdefault("causal", case.causal)
     if case.mla:
         return paged_decode_attn_mla(dev.q, dev.k_cache, dev.block_tables, dev.context_lens,
-                                     scale=case.scale, head_dim_v=case.d_latent, **kw)
+                                     scale=case.scale, head_dim_v=case.d_latent,
+                                     kv_scale=case.k_scale, **kw)
     return paged_decode_attn(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
                              dev.context_lens, scale=case.scale, k_scale=case.k_scale,
                              v_scale=case.v_scale, **kw)

@@ -194,10 +194,13 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
 
 /* MLA paged decode attention over a latent cache (FlashMLA-ETAP "Usage";
  * "From MHA to MLA" sec. 6).  shape->num_kv_heads must be 1, head_dim 576,
- * head_dim_v 512, q_dtype == kv_dtype == PDA_BF16, page_size a power of two,
- * at least 64, num_q_heads a multiple of 16 or at most 16.  k_scale/v_scale are
- * ignored.  The variant field picks the kernel (PDA_MLA_*); q_len > 1 needs
- * PDA_MLA_DEFAULT or PDA_MLA_MFMA. */
+ * head_dim_v 512, q_dtype PDA_BF16, page_size a power of two, at least 64,
+ * num_q_heads a multiple of 16 or at most 16.  kv_dtype PDA_BF16, or
+ * PDA_FP8_E4M3 for an fp8 latent (the variants page's halved MLA record)
+ * dequantized as e4m3(byte) * k_scale -- K and V are the same values, so
+ * v_scale is ignored; k_scale is ignored for a bf16 latent.  The variant
+ * field picks the kernel (PDA_MLA_*); q_len > 1 needs PDA_MLA_DEFAULT or
+ * PDA_MLA_MFMA. */
 int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* block_tables,
                           const int32_t* context_lens, float scale, int num_splits,
                           void* out, float* lse, const pda_shape* shape, void* workspace,

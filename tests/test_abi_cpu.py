@@ -233,6 +233,14 @@ def test_mla_validation():
     s.variant = 9
     assert lib.paged_decode_attn_mla(fake, fake, fake, fake, 0.1, 1, fake, None,
                                      ctypes.byref(s), None, 0, None) == 1
+    # an fp8 latent needs a positive dequantization scale (k_scale)
+    f8 = _shape(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512, page_size=64,
+                q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_FP8_E4M3, k_scale=0.0, batch=0)
+    assert lib.paged_decode_attn_mla(fake, fake, fake, fake, 0.1, 1, fake, None,
+                                     ctypes.byref(f8), None, 0, None) == 1
+    f8.k_scale = 0.02
+    assert lib.paged_decode_attn_mla(fake, fake, fake, fake, 0.1, 1, fake, None,
+                                     ctypes.byref(f8), None, 0, None) == 0   # B = 0: no-op
 
 
 def test_append_validation():

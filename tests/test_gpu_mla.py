@@ -135,3 +135,32 @@ def test_balanced_schedule_mixed_lengths(variant, Hq):
     out, lse = pda.run_case(case, variant=VARIANTS[variant], schedule=pda.PDA_SCHEDULE_BALANCED)
     ref_o, ref_l = oracle_ref(case)
     check(case, out, lse, ref_o, ref_l, label="mla balanced %s Hq=%d" % (variant, Hq))
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("Hq,q_len", [(16, 1), (32, 1), (16, 2), (8, 1)])
+def test_fp8_latent(variant, Hq, q_len):
+    """An fp8 (E4M3) latent with one dequantization scale: staged into LDS as
+    exact bf16, the scale folded into the score and the output."""
+    if variant == "valu" and q_len > 1:
+        pytest.skip("several query tokens take the matrix-core kernel")
+    case = _mla(80 + Hq + q_len, [1, 33, 700, 2000], Hq=Hq, extra_pages=2, kv_dtype="e4m3",
+                q_len=q_len)
+    say("mla fp8 latent", variant, Hq, q_len)
+    ref_o, ref_l = oracle_ref(case)
+    for s in (1, 4):
+        out, lse = pda.run_case(case, variant=VARIANTS[variant], num_splits=s)
+        check(case, out, lse, ref_o, ref_l, label="mla fp8 %s Hq=%d q=%d S=%d" % (variant, Hq,
+                                                                                q_len, s))
+
+
+def test_fp8_latent_b16_sampled():
+    """The MLA decode shape with an fp8 latent: B=16, Hq=16, ctx 65536, sampled rows."""
+    case = W.mla_b16(kv_dtype="e4m3")
+    rng = np.random.default_rng(9)
+    rows = rng.random((16, 16)) < 0.05
+    rows[0, :2] = True
+    say(case.name)
+    ref_o, ref_l = oracle_ref(case, rows=rows)
+    out, lse = pda.run_case(case)
+    check(case, out, lse, ref_o, ref_l, rows=rows, label=case.name)
