@@ -51,6 +51,8 @@ def make_case(name):
         return W.mla_b16_mtp(2)
     if name == "mla_b16_fp8":
         return W.mla_b16(kv_dtype="e4m3")
+    if name == "mla_b16_320":
+        return W.mla_b16(d_latent=256)
     raise SystemExit("unknown workload %s" % name)
 
 
@@ -257,7 +259,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa_b64",
                     choices=["gqa_b64", "gqa_b1_split", "gqa_b4_split", "mla_b16", "ragged_fp8",
-                             "ragged_fp8_balanced", "gqa_b64_q2", "mla_b16_q2", "mla_b16_fp8"])
+                             "ragged_fp8_balanced", "gqa_b64_q2", "mla_b16_q2", "mla_b16_fp8",
+                             "mla_b16_320"])
     ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
     ap.add_argument("--others", default="gqa_b1_split,gqa_b4_split,kv_append_b64",
                     help="extra workloads measured into 'other_workloads' ('' for none)")

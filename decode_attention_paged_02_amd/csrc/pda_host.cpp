@@ -49,7 +49,11 @@ int check_shape(const pda_shape* s, bool mla) {
   if ((int64_t)s->max_pages_per_seq * s->page_size > INT32_MAX) return PDA_ERR_INVALID_ARG;
   if (mla) {
     if (s->num_kv_heads != 1) return PDA_ERR_INVALID_ARG;
-    if (s->head_dim != 576 || s->head_dim_v != 512) return PDA_ERR_UNSUPPORTED;
+    // (576, 512) and (320, 256): latent 512 or 256 + rope 64
+    if (!((s->head_dim == 576 && s->head_dim_v == 512) ||
+          (s->head_dim == 320 && s->head_dim_v == 256)))
+      return PDA_ERR_UNSUPPORTED;
+    if (s->head_dim != 576 && s->variant == PDA_MLA_VALU) return PDA_ERR_UNSUPPORTED;
     if (s->q_dtype != PDA_BF16 || (s->kv_dtype != PDA_BF16 && s->kv_dtype != PDA_FP8_E4M3))
       return PDA_ERR_UNSUPPORTED;
     if (s->kv_dtype == PDA_FP8_E4M3 && !(s->k_scale > 0.f)) return PDA_ERR_INVALID_ARG;
@@ -397,7 +401,7 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
     rc = run_order(s, plan, context_lens, units, seq_splits, a.split, st);
     if (rc != PDA_OK) return rc;
   }
-  if (pda::launch_mla(a, s.variant, s.kv_dtype, p.max_splits, st) != hipSuccess)
+  if (pda::launch_mla(a, s.variant, s.kv_dtype, s.head_dim, p.max_splits, st) != hipSuccess)
     return PDA_ERR_HIP;
   if (p.max_splits > 1) {
     pda::CombineArgs c{};

@@ -100,11 +100,11 @@ struct CombineArgs {
 };
 
 struct MlaArgs {
-  const void* q;           // [B, q_len, Hq, 576] bf16
-  const void* kv_cache;    // [num_pages, P, 576] bf16 or fp8 (E4M3)
+  const void* q;           // [B, q_len, Hq, 576 or 320] bf16
+  const void* kv_cache;    // [num_pages, P, 576 or 320] bf16 or fp8 (E4M3)
   const int32_t* block_tables;
   const int32_t* context_lens;
-  void* out;               // [B, q_len, Hq, 512] bf16
+  void* out;               // [B, q_len, Hq, 512 or 256] bf16
   float* lse;
   float* part_o;
   float* part_lse;
@@ -168,7 +168,7 @@ hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
                       int tile_heads, int max_splits, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t stream);
 hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
-hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int max_splits,
+hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int head_dim, int max_splits,
                       hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int src_dtype, int cache_dtype, hipStream_t stream);
 

@@ -50,15 +50,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short ldsv4s __attribute__((__vector_size__(4 * sizeof(short))));
 
-constexpr int kRec = 576;           // record width (latent 512 + rope 64)
-constexpr int kDv = 512;            // value width
 constexpr int kHeads = 16;          // query heads per workgroup tile
 constexpr int kBlock = 32;          // tokens per LDS block
 constexpr int kThreads = 256;       // 4 waves: one column group of 16 rows
-constexpr int kRowBytes = kRec * 2;  // one record per LDS row (16-byte chunks swizzled)
-constexpr int kRowChunks = kRowBytes / 16;
-constexpr int kBlockChunks = kBlock * kRowChunks;  // 16-byte chunks of a staged block
 constexpr int kLoadPolicy = 2;      // non-temporal: each record is read once per row tile
+
+// Widths of the cached record (K: latent + rope) and of its value prefix (V):
+// (576, 512) for a 512-wide latent, (320, 256) for a 256-wide one (FlashMLA-
+// ETAP "Supported configurations", head dimensions).
+template <int REC, int DV>
+struct Dims {
+  static constexpr int kRec = REC, kDv = DV;
+  static constexpr int kRowBytes = REC * 2;          // one record per LDS row (bf16)
+  static constexpr int kRowChunks = kRowBytes / 16;  // 16-byte chunks, swizzled
+  static constexpr int kBlockChunks = kBlock * kRowChunks;
+  static constexpr int kQkChunks = REC / 32;         // 32-wide contraction chunks of a score
+  static constexpr int kColsPerWave = DV / 4;        // value columns a wave owns
+  static constexpr int kMB = kColsPerWave / 16;      // 16-row MFMA tiles of them
+  static_assert(kRowChunks % 8 == 0 && REC % 32 == 0 && DV % 64 == 0, "record widths");
+};
+typedef Dims<576, 512> Dims576;
+typedef Dims<320, 256> Dims320;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -79,11 +91,15 @@ __device__ __forceinline__ float sum_x4(float x) {
 }
 
 // LDS placement of 16-byte chunk c of row r: the chunk index is XORed with a
-// permutation of r mod 8 inside its aligned group of eight (72 = 9 x 8), so
-// eight consecutive rows read at one chunk hit distinct banks, and so do four
-// consecutive rows reading an aligned chunk pair (the transposing V reads).
+// permutation of r mod 8 inside its aligned group of eight (rows hold 72 or
+// 40 chunks, multiples of 8), so eight consecutive rows read at one chunk hit
+// distinct banks, and so do four consecutive rows reading an aligned chunk
+// pair (the transposing V reads).
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ int lds_off(int r, int c) { return r * kRowBytes + 16 * (c ^ swz(r)); }
+template <class DM>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return r * DM::kRowBytes + 16 * (c ^ swz(r));
+}
 
 // Block-table entries of a workgroup's range, one per lane: lane j holds the
 // entry of page base + j (clamped into the table row; entries past the
@@ -115,11 +131,12 @@ struct PageTable {
 // each widened exactly to the same 16-byte bf16 LDS chunk.  With T = 512 the
 // last load of a thread may lie past the block: its offset is outside the
 // buffer resource (zero, no memory access) and it is not stored.
-template <int T, class KT>
+template <int T, class KT, class DM>
 struct BlockLoader {
   static constexpr bool kFp8 = std::is_same<KT, E4M3>::value;
-  static constexpr int kRecBytes = kFp8 ? kRec : 2 * kRec;  // bytes of a record in memory
-  static constexpr int kN = (kBlockChunks + T - 1) / T;      // loads per thread
+  static constexpr int kBlockChunks = DM::kBlockChunks, kRowChunks = DM::kRowChunks;
+  static constexpr int kRecBytes = kFp8 ? DM::kRec : 2 * DM::kRec;  // a record in memory
+  static constexpr int kN = (kBlockChunks + T - 1) / T;              // loads per thread
   typedef typename std::conditional<kFp8, u32x2, u32x4>::type piece_t;
   piece_t r[kN];
 
@@ -166,7 +183,7 @@ struct BlockLoader {
         } else {
           w = r[i];
         }
-        *(u32x4*)(lds + lds_off(row, col)) = w;
+        *(u32x4*)(lds + lds_off<DM>(row, col)) = w;
       }
     }
   }
@@ -187,11 +204,17 @@ __device__ __forceinline__ void store_bf16x4(void* out, int64_t i, f32x4 v) {
 // ------------------------------------------------------------ MFMA kernel
 
 // NG column groups of four waves; a workgroup owns 16 NG rows.  KT: the
-// latent's storage type (BF16, or E4M3 with a dequantization scale).
-template <int NG, class KT>
+// latent's storage type (BF16, or E4M3 with a dequantization scale); DM: the
+// record widths.
+template <int NG, class KT, class DM>
 __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs a) {
   constexpr int T = kThreads * NG;
-  __shared__ __attribute__((aligned(16))) char lds[2][kBlock * kRowBytes];
+  constexpr int kRec = DM::kRec, kDv = DM::kDv;
+  constexpr int QC = DM::kQkChunks;      // contraction chunks of a score
+  constexpr int NWMAX = (QC + 3) / 4;    // most chunks a wave contracts
+  constexpr int MB = DM::kMB;            // 16-column MFMA tiles of a wave's values
+  constexpr int CPW = DM::kColsPerWave;  // value columns a wave owns
+  __shared__ __attribute__((aligned(16))) char lds[2][kBlock * DM::kRowBytes];
   __shared__ f32x4 spart[4 * NG][2][64];  // per-wave partial S^T of a block
 
   const int tid = threadIdx.x;
@@ -251,20 +274,21 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
     qi = r / a.num_q_heads;
     h = r - qi * a.num_q_heads;
   }
-  // The 18 chunks of 32 record values are shared out over the waves (5, 5, 4,
-  // 4): wave w contracts chunks [c_lo, c_lo + n_w) of every key and the four
-  // partial S^T are summed through LDS in a fixed order.
-  const int c_lo = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
-  const int n_w = wave < 2 ? 5 : 4;
+  // The QC chunks of 32 record values are shared out over the waves (18:
+  // 5, 5, 4, 4; 10: 3, 3, 2, 2): wave w contracts chunks [c_lo, c_lo + n_w)
+  // of every key and the four partial S^T are summed through LDS in a fixed
+  // order.
+  const int n_w = QC / 4 + (wave < QC % 4 ? 1 : 0);
+  const int c_lo = wave * (QC / 4) + min(wave, QC % 4);
   // Q^T as the B operand: lane (col, grp) holds q[h][32 (c_lo + j) + 8 grp + 0..7]
   // (loaded from valid addresses without branches, then zeroed where unused)
-  bf16x8 qb[5];
+  bf16x8 qb[NWMAX];
   {
     const uint16_t* qrow =
         (const uint16_t*)a.q +
         (hvalid ? (((int64_t)b * q_len + qi) * a.num_q_heads + h) * kRec : 0);
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
+    for (int j = 0; j < NWMAX; ++j) {
       const bool use = hvalid && j < n_w;
       const u32x4 w = *(const u32x4*)(qrow + 32 * (c_lo + (j < n_w ? j : 0)) + 8 * grp);
       qb[j] = __builtin_bit_cast(bf16x8, use ? w : u32x4{0u, 0u, 0u, 0u});
@@ -285,9 +309,9 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   // end of the tokens this column's query token may see (t1 without a mask)
   const int lim = min(t1, a.causal ? n - (q_len - 1 - qi) : n);
 
-  f32x4 acc[8];  // O^T rows 128*wave + 16*mb + 4*grp + i, column = head
+  f32x4 acc[MB];  // O^T rows CPW*wave + 16*mb + 4*grp + i, column = head
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kMaxStart, l_run = 0.f;
 
   // Two blocks in flight in registers while one is computed from LDS: block k
@@ -295,7 +319,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   // of block k + 2 go into the registers it leaves.  Loads of blocks past the
   // range have empty resources (no memory access), so they need no branch.
   // (A deeper ring for the 512-thread workgroups measured no gain.)
-  BlockLoader<T, KT> ld[2];
+  BlockLoader<T, KT, DM> ld[2];
   ld[0].load(a, pt, t0, t1, 0, log2P, tid);
   ld[0].store(lds[0], tid);
   ld[1].load(a, pt, t0, t1, 1, log2P, tid);
@@ -314,9 +338,9 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
       f32x4 sp = {0.f, 0.f, 0.f, 0.f};
       const int r = 16 * kb + col;
 #pragma unroll
-      for (int j = 0; j < 5; ++j) {
+      for (int j = 0; j < NWMAX; ++j) {
         if (j < n_w) {
-          const bf16x8 kv = *(const bf16x8*)(L + lds_off(r, 4 * (c_lo + j) + grp));
+          const bf16x8 kv = *(const bf16x8*)(L + lds_off<DM>(r, 4 * (c_lo + j) + grp));
           sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[j], sp, 0, 0, 0);
         }
       }
@@ -347,7 +371,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
       m_run = tmax;
       l_run *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
     }
     // P^T as the B operand of the PV MFMA, split into two bf16 terms
     // p = p_hi + p_lo (bf16 alone would leave a 2^-9 relative error per
@@ -364,7 +388,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
         pb_hi[kb][i] = __builtin_bit_cast(short, hi);
         pb_lo[kb][i] = __builtin_bit_cast(short, lo);
       }
-    // O^T += V^T P^T over this wave's 128 value columns, one 16x16x32 MFMA
+    // O^T += V^T P^T over this wave's CPW value columns, one 16x16x32 MFMA
     // per term over all 32 keys of the block.  The contraction index k of
     // lane group g covers keys 4 g + 0..3 (k = 8 g + 0..3) and 16 + 4 g + 0..3
     // (k = 8 g + 4..7): that is where the S^T layout left this lane's
@@ -374,19 +398,19 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
                                                         pb_hi[0], pb_hi[1], 0, 1, 2, 3, 4, 5, 6, 7));
     const bf16x8 pk_lo = __builtin_bit_cast(bf16x8, __builtin_shufflevector(
                                                         pb_lo[0], pb_lo[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    bf16x8 va[8];
+    bf16x8 va[MB];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       s16x4 vt[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // transposing read: lane q of group g points at key 16 kb + 4 g + q/4,
-        // column 128 wave + 16 mb + 4 (q % 4); it returns V^T rows 16 mb + q
+        // column CPW wave + 16 mb + 4 (q % 4); it returns V^T rows 16 mb + q
         // (value columns) x keys 16 kb + 4 g + 0..3
         const int q = col;
         const int r = 16 * kb + 4 * grp + (q >> 2);
-        const int byte = (128 * wave + 16 * mb + 4 * (q & 3)) * 2;
-        const char* p = L + lds_off(r, byte >> 4) + (byte & 15);
+        const int byte = (CPW * wave + 16 * mb + 4 * (q & 3)) * 2;
+        const char* p = L + lds_off<DM>(r, byte >> 4) + (byte & 15);
         vt[kb] = __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                (__attribute__((address_space(3))) ldsv4s*)(p)));
       }
@@ -394,10 +418,10 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
                                                                   6, 7));
     }
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mb], pk_hi, acc[mb], 0, 0, 0);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mb], pk_lo, acc[mb], 0, 0, 0);
   };
   // block blk, then: stage the next block, start loading the one three
@@ -406,7 +430,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   // unrolled pair): the wait counts then stay exact across iterations, and a
   // block past the range is all zero rows (an odd block count computes one
   // such block, fully masked).
-  auto body = [&](int blk, BlockLoader<T, KT>& nxt) {
+  auto body = [&](int blk, BlockLoader<T, KT, DM>& nxt) {
     compute(blk);
     nxt.store(lds[(blk + 1) & 1], tid);
     nxt.load(a, pt, t0, t1, blk + 3, log2P, tid);
@@ -426,13 +450,13 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   const int64_t row = ((int64_t)b * q_len + qi) * a.num_q_heads + h;
   if (nsplit == 1) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-      store_bf16x4<0>(a.out, row * kDv + 128 * wave + 16 * mb + 4 * grp, acc[mb] * inv);
+    for (int mb = 0; mb < MB; ++mb)
+      store_bf16x4<0>(a.out, row * kDv + CPW * wave + 16 * mb + 4 * grp, acc[mb] * inv);
     if (wave == 0 && grp == 0 && a.lse) a.lse[((int64_t)b * a.num_q_heads + h) * q_len + qi] = lse;
   } else {
     float* po = a.part_o + (row * a.split.max_splits + split) * kDv;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) *(f32x4*)(po + 128 * wave + 16 * mb + 4 * grp) = acc[mb] * inv;
+    for (int mb = 0; mb < MB; ++mb) *(f32x4*)(po + CPW * wave + 16 * mb + 4 * grp) = acc[mb] * inv;
     if (wave == 0 && grp == 0) a.part_lse[row * a.split.max_splits + split] = lse;
   }
 }
@@ -445,6 +469,9 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
 // value columns 8 (t%64) .. +8 of heads 4 (t/64) .. +3 and reads P from LDS.
 template <class KT>
 __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
+  // (the 576 / 512 record only: 64 threads cover a 512-wide value row)
+  using DM = Dims576;
+  constexpr int kRec = DM::kRec, kDv = DM::kDv, kRowBytes = DM::kRowBytes;
   __shared__ __attribute__((aligned(16))) char lds[2][kBlock * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint32_t q_sh[kHeads][kRec / 2];
   __shared__ __attribute__((aligned(16))) float p_sh[kBlock][kHeads];
@@ -528,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
 
-  BlockLoader<kThreads, KT> ld;
+  BlockLoader<kThreads, KT, DM> ld;
   ld.load(a, pt, t0, t1, 0, log2P, tid);
   ld.store(lds[0], tid);
   ld.load(a, pt, t0, t1, 1, log2P, tid);
@@ -542,8 +569,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
 #pragma unroll 4
     for (int c = 0; c < kRec / 8; ++c) {
       const u32x4 qv = *(const u32x4*)&q_sh[sh][4 * c];
-      const u32x4 a0 = *(const u32x4*)(L + lds_off(2 * kp, c));
-      const u32x4 a1 = *(const u32x4*)(L + lds_off(2 * kp + 1, c));
+      const u32x4 a0 = *(const u32x4*)(L + lds_off<DM>(2 * kp, c));
+      const u32x4 a1 = *(const u32x4*)(L + lds_off<DM>(2 * kp + 1, c));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t qj = qv[j], x0 = a0[j], x1 = a1[j];
@@ -577,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
       for (int e = 0; e < 8; ++e) acc[j][e] *= al[j];
 #pragma unroll 4
     for (int key = 0; key < kBlock; ++key) {
-      const u32x4 v = *(const u32x4*)(L + lds_off(key, c8));
+      const u32x4 v = *(const u32x4*)(L + lds_off<DM>(key, c8));
       const f32x4 p4 = *(const f32x4*)&p_sh[key][4 * hq];
       float vf[8];
 #pragma unroll
@@ -632,23 +659,36 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
   }
 }
 
+template <class DM>
+void launch_mfma(const MlaArgs& a, bool two, bool fp8, dim3 grid, hipStream_t s) {
+  if (two) {
+    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<2, E4M3, DM>), grid, dim3(2 * kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mla_mfma_kernel<2, BF16, DM>), grid, dim3(2 * kThreads), 0, s, a);
+  } else {
+    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<1, E4M3, DM>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mla_mfma_kernel<1, BF16, DM>), grid, dim3(kThreads), 0, s, a);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int max_splits, hipStream_t s) {
+hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int head_dim, int max_splits,
+                      hipStream_t s) {
   const unsigned units = (unsigned)(a.batch * a.head_tiles);
   dim3 grid(a.units ? (unsigned)(a.head_tiles * a.unit_count) : units,
             a.units ? 1u : (unsigned)max_splits);
   const bool fp8 = kv_dtype == 3;
   const bool two = mla_column_groups(a.q_len * a.num_q_heads) == 2;
   if (variant == 2) {
+    if (head_dim != 576) return hipErrorInvalidValue;
     if (fp8) hipLaunchKernelGGL(mla_valu_kernel<E4M3>, grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(mla_valu_kernel<BF16>, grid, dim3(kThreads), 0, s, a);
-  } else if (two) {
-    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<2, E4M3>), grid, dim3(2 * kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mla_mfma_kernel<2, BF16>), grid, dim3(2 * kThreads), 0, s, a);
+  } else if (head_dim == 576) {
+    launch_mfma<Dims576>(a, two, fp8, grid, s);
+  } else if (head_dim == 320) {
+    launch_mfma<Dims320>(a, two, fp8, grid, s);
   } else {
-    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<1, E4M3>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mla_mfma_kernel<1, BF16>), grid, dim3(kThreads), 0, s, a);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

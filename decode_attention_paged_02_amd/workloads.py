@@ -285,14 +285,16 @@ def gqa_long(batch: int) -> PagedCase:
                     name="gqa_b%d_ctx32768_fp16_split" % batch)
 
 
-def mla_b16(ctx: int = 65536, kv_dtype: str = "bf16") -> PagedCase:
+def mla_b16(ctx: int = 65536, kv_dtype: str = "bf16", d_latent: int = 512) -> PagedCase:
     """B=16, 16 heads, latent 512 + rope 64, P=64, bf16 ~ N(0, 0.5^2), scale 1/sqrt(192)
-    (kv_dtype "e4m3": the latent stored as fp8 with one scale, q in bf16)."""
-    return make_mla(batch=16, num_q_heads=16, d_latent=512, d_rope=64, page_size=64,
+    (kv_dtype "e4m3": the latent stored as fp8 with one scale, q in bf16;
+    d_latent 256: the (320, 256) record)."""
+    tag = ("bf16" if kv_dtype == "bf16" else "fp8_latent") + ("" if d_latent == 512 else
+                                                             "_rec%d" % (d_latent + 64))
+    return make_mla(batch=16, num_q_heads=16, d_latent=d_latent, d_rope=64, page_size=64,
                     context_lens=[ctx] * 16, dtype="bf16", seed=1003, std=0.5,
                     scale=1.0 / math.sqrt(192.0), poison=False, kv_dtype=kv_dtype,
-                    name="mla_b16_ctx%d_%s" % (ctx, "bf16" if kv_dtype == "bf16" else
-                                                 "fp8_latent"))
+                    name="mla_b16_ctx%d_%s" % (ctx, tag))
 
 
 def mla_b16_mtp(q_len: int = 2, ctx: int = 65536) -> PagedCase:

@@ -193,8 +193,10 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                       void* stream);
 
 /* MLA paged decode attention over a latent cache (FlashMLA-ETAP "Usage";
- * "From MHA to MLA" sec. 6).  shape->num_kv_heads must be 1, head_dim 576,
- * head_dim_v 512, q_dtype PDA_BF16, page_size a power of two, at least 64,
+ * "From MHA to MLA" sec. 6).  shape->num_kv_heads must be 1, (head_dim,
+ * head_dim_v) (576, 512) or (320, 256) (a 512- or 256-wide latent + 64 rope
+ * values; FlashMLA-ETAP "Supported configurations"; 320 with the matrix-core
+ * variant only), q_dtype PDA_BF16, page_size a power of two, at least 64,
  * num_q_heads a multiple of 16 or at most 16.  kv_dtype PDA_BF16, or
  * PDA_FP8_E4M3 for an fp8 latent (the variants page's halved MLA record)
  * dequantized as e4m3(byte) * k_scale -- K and V are the same values, so

@@ -241,6 +241,14 @@ def test_mla_validation():
     f8.k_scale = 0.02
     assert lib.paged_decode_attn_mla(fake, fake, fake, fake, 0.1, 1, fake, None,
                                      ctypes.byref(f8), None, 0, None) == 0   # B = 0: no-op
+    # record widths: (576, 512) and (320, 256); 320 only on the matrix cores
+    for dk, dv, variant, want in [(320, 256, pda.PDA_MLA_DEFAULT, 0), (320, 256, pda.PDA_MLA_MFMA, 0),
+                                  (320, 256, pda.PDA_MLA_VALU, 2), (320, 512, 0, 2),
+                                  (576, 256, 0, 2), (448, 384, 0, 2)]:
+        w = _shape(num_q_heads=16, num_kv_heads=1, head_dim=dk, head_dim_v=dv, page_size=64,
+                   q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16, batch=0, variant=variant)
+        assert lib.paged_decode_attn_mla(fake, fake, fake, fake, 0.1, 1, fake, None,
+                                         ctypes.byref(w), None, 0, None) == want, (dk, dv)
 
 
 def test_append_validation():

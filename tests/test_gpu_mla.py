@@ -164,3 +164,22 @@ def test_fp8_latent_b16_sampled():
     ref_o, ref_l = oracle_ref(case, rows=rows)
     out, lse = pda.run_case(case)
     check(case, out, lse, ref_o, ref_l, rows=rows, label=case.name)
+
+
+@pytest.mark.parametrize("Hq,q_len,kv", [(16, 1, "bf16"), (32, 1, "bf16"), (16, 2, "bf16"),
+                                         (8, 1, "e4m3"), (16, 1, "e4m3")])
+def test_record_320_value_256(Hq, q_len, kv):
+    """The (320, 256) record: a 256-wide latent + 64 rope values (FlashMLA-ETAP's
+    second head-dimension pair), matrix-core kernel."""
+    case = W.make_mla(batch=4, num_q_heads=Hq, d_latent=256, d_rope=64, page_size=64,
+                      context_lens=[1, 65, 700, 3000], dtype="bf16", seed=90 + Hq + q_len,
+                      std=0.5, scale=1.0 / math.sqrt(192.0), extra_pages=2, q_len=q_len,
+                      kv_dtype=kv)
+    say("mla 320/256", Hq, q_len, kv)
+    ref_o, ref_l = oracle_ref(case)
+    for s in (1, 5):
+        out, lse = pda.run_case(case, num_splits=s)
+        assert out.shape[-1] == 256
+        check(case, out, lse, ref_o, ref_l, label="mla320 Hq=%d q=%d %s S=%d" % (Hq, q_len, kv, s))
+    out, lse = pda.run_case(case, schedule=pda.PDA_SCHEDULE_BALANCED)
+    check(case, out, lse, ref_o, ref_l, label="mla320 balanced")
