@@ -600,6 +600,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 // ------------------------------------------------------- work ordering
 
 constexpr int kOrderThreads = 1024;
+constexpr int kOrderStagedLens = 8192;  // sequence lengths the planning pass keeps in LDS
 
 // The planning pass of an ordered call (one workgroup).  Each sequence is cut
 // into splits -- by the SplitLayout (grid schedule), or into near-equal
@@ -616,23 +617,35 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(OrderArgs a) {
   constexpr int NBK = 33;  // bit lengths 0..32
   __shared__ int cnt[NBK];
   __shared__ int total_sh;
-  __shared__ long long pages_sh;
+  __shared__ unsigned long long pages_sh;
+  __shared__ int lens_sh[kOrderStagedLens];
   const int S = a.split.max_splits;
   const int U = a.batch * S;
   const int P = a.page_size;
+  // the lengths are read from memory once (staged in LDS up to
+  // kOrderStagedLens sequences), together with the batch's page count
+  const bool staged = a.batch <= kOrderStagedLens;
   if (threadIdx.x < NBK) cnt[threadIdx.x] = 0;
   if (threadIdx.x == 0) pages_sh = 0;
   __syncthreads();
+  unsigned long long part = 0;
+  for (int b = threadIdx.x; b < a.batch; b += kOrderThreads) {
+    const int n = load_uniform_v(a.context_lens + b);
+    if (staged) lens_sh[b] = n;
+    part += (unsigned)((n + P - 1) / P);
+  }
+  if (a.balanced) {  // a wave sums its part, then one LDS atomic per wave
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    if ((threadIdx.x & 63) == 0 && part) atomicAdd(&pages_sh, part);
+  }
+  __syncthreads();
+  auto len_of = [&](int b) { return staged ? lens_sh[b] : load_uniform_v(a.context_lens + b); };
   // balanced schedule: the chunk size from the batch's total pages
   int chunk = 0;
   if (a.balanced) {
-    long long part = 0;
-    for (int b = threadIdx.x; b < a.batch; b += kOrderThreads)
-      part += (load_uniform_v(a.context_lens + b) + P - 1) / P;
-    atomicAdd((unsigned long long*)&pages_sh, (unsigned long long)part);
-    __syncthreads();
-    const long long c = (pages_sh + a.target_units - 1) / a.target_units;
-    chunk = (int)(c > a.min_chunk_pages ? c : a.min_chunk_pages);
+    const unsigned long long c = (pages_sh + a.target_units - 1) / a.target_units;
+    chunk = (int)(c > (unsigned long long)a.min_chunk_pages ? c : a.min_chunk_pages);
   }
   // splits of sequence b (n tokens) and the pages each one covers
   auto layout = [&](int n, int& ns, int& pps) {
@@ -652,7 +665,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(OrderArgs a) {
   // unit u = (b, s): its token range, or false past the sequence's splits
   auto unit_of = [&](int u, WorkUnit& w, int& ns) -> bool {
     const int b = u / S, s = u % S;
-    const int n = load_uniform_v(a.context_lens + b);
+    const int n = len_of(b);
     int pps;
     layout(n, ns, pps);
     if (s >= ns) return false;
