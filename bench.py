@@ -34,19 +34,24 @@ def _log(*a):
 
 
 def make_case(name):
+    """The named workload; a "_hm" suffix on a GQA workload stores the same
+    cache with head-major pages [pages, Hkv, P, d]."""
     from decode_attention_paged_02_amd import workloads as W
+    hm = 0
+    if name.endswith("_hm") and name.startswith(("gqa", "ragged")):
+        name, hm = name[:-3], 1
     if name == "gqa_b64":
-        return W.gqa_batch64()
+        return W.gqa_batch64(kv_layout=hm)
     if name == "gqa_b1_split":
-        return W.gqa_long(1)
+        return W.gqa_long(1, kv_layout=hm)
     if name == "gqa_b4_split":
-        return W.gqa_long(4)
+        return W.gqa_long(4, kv_layout=hm)
     if name == "mla_b16":
         return W.mla_b16()
     if name in ("ragged_fp8", "ragged_fp8_balanced"):
-        return W.ragged_fp8()
+        return W.ragged_fp8(kv_layout=hm)
     if name == "gqa_b64_q2":
-        return W.gqa_batch64_mtp(2)
+        return W.gqa_batch64_mtp(2, kv_layout=hm)
     if name == "mla_b16_q2":
         return W.mla_b16_mtp(2)
     if name == "mla_b16_fp8":
@@ -59,6 +64,14 @@ def make_case(name):
 CALL_KW = {"ragged_fp8": dict(num_splits=8, split_min_tokens=4096),
            # the balanced schedule (device-side chunking) on the same batch
            "ragged_fp8_balanced": dict(num_splits=8, schedule=1)}
+GQA_WORKLOADS = ["gqa_b64", "gqa_b1_split", "gqa_b4_split", "ragged_fp8", "ragged_fp8_balanced",
+                 "gqa_b64_q2"]
+WORKLOADS = GQA_WORKLOADS + [w + "_hm" for w in GQA_WORKLOADS] + [
+    "mla_b16", "mla_b16_q2", "mla_b16_fp8", "mla_b16_320"]
+
+
+def call_kw(workload):
+    return dict(CALL_KW.get(workload[:-3] if workload.endswith("_hm") else workload, {}))
 
 
 def measured_traffic(workload: str, launches_per_step: int):
@@ -80,7 +93,7 @@ def run_gpu(case, workload, steps, warmup, pools):
     from decode_attention_paged_02_amd import pda
 
     dev = pda.to_device(case)
-    kw = dict(CALL_KW.get(workload, {}))
+    kw = call_kw(workload)
     nbytes = A.case_kv_bytes(case)
     pool_bytes = dev.k_cache.numel() * dev.k_cache.element_size() * (1 if case.mla else 2)
     n_pools = max(pools, math.ceil((1 << 30) / max(pool_bytes, 1))) if pools > 0 else 1
@@ -99,7 +112,8 @@ def run_gpu(case, workload, steps, warmup, pools):
         shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
                               k_scale=case.k_scale, v_scale=case.v_scale,
                               split_min_tokens=kw.get("split_min_tokens", 0),
-                              causal=case.causal, schedule=kw.get("schedule", 0))
+                              causal=case.causal, schedule=kw.get("schedule", 0),
+                              kv_layout=case.kv_layout)
     nsplit = kw.get("num_splits", 0)
     plan = pda.plan(shape, mla=case.mla, num_splits=nsplit)
     ws = pda.workspace_for(shape, mla=case.mla, num_splits=nsplit, device="cuda")
@@ -127,7 +141,8 @@ def run_gpu(case, workload, steps, warmup, pools):
                 launches=(1 if plan.max_splits == 1 else 2) + (1 if plan.ordered else 0))
 
 
-APPEND_WORKLOADS = {"kv_append_b64": "gqa_b64", "kv_append_ragged_fp8": "ragged_fp8"}
+APPEND_WORKLOADS = {"kv_append_b64": "gqa_b64", "kv_append_ragged_fp8": "ragged_fp8",
+                    "kv_append_b64_hm": "gqa_b64_hm"}
 
 
 def run_append(base: str, steps: int, warmup: int):
@@ -145,14 +160,16 @@ def run_append(base: str, steps: int, warmup: int):
     v_new = torch.from_numpy(rng.standard_normal((B, 1, Hkv, d)).astype(np.float16)).cuda()
     pos = (dev.context_lens - 1).contiguous()
     pda.paged_kv_append(k_new, v_new, dev.block_tables, pos, dev.k_cache, dev.v_cache,
-                        k_scale=case.k_scale, v_scale=case.v_scale)   # validates the shapes
+                        k_scale=case.k_scale, v_scale=case.v_scale,
+                        kv_layout=case.kv_layout)                       # validates the shapes
     # then the bare C call with marshalled arguments, so the host keeps ahead
     import ctypes
     shape = pda.make_shape(batch=B, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=d, head_dim_v=d,
                            page_size=case.page_size, max_pages_per_seq=case.max_pages,
                            num_pages=case.num_pages, q_dtype=pda.PDA_F16,
                            kv_dtype=pda._dtype_code(dev.k_cache, fp8_ok=True),
-                           k_scale=case.k_scale, v_scale=case.v_scale, q_len=1)
+                           k_scale=case.k_scale, v_scale=case.v_scale, q_len=1,
+                           kv_layout=case.kv_layout)
     args = [pda._ptr(t) for t in (k_new, v_new, dev.block_tables, pos, dev.k_cache, dev.v_cache)]
     args += [ctypes.byref(shape), pda._stream_handle(None)]
     lib = pda.load()
@@ -222,7 +239,8 @@ def _oracle_call(case, rows):
     return oracle.paged_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
                                   case.context_lens, scale=case.scale, q_dtype=case.q_dtype,
                                   kv_dtype=case.kv_dtype, k_scale=case.k_scale,
-                                  v_scale=case.v_scale, causal=case.causal, rows=rows)
+                                  v_scale=case.v_scale, causal=case.causal, rows=rows,
+                                  kv_layout=case.kv_layout)
 
 
 def bandwidth_probe(nbytes=2 << 30, reps=10):
@@ -257,10 +275,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gqa_b64",
-                    choices=["gqa_b64", "gqa_b1_split", "gqa_b4_split", "mla_b16", "ragged_fp8",
-                             "ragged_fp8_balanced", "gqa_b64_q2", "mla_b16_q2", "mla_b16_fp8",
-                             "mla_b16_320"])
+    ap.add_argument("--workload", default="gqa_b64", choices=WORKLOADS)
     ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
     ap.add_argument("--others", default="gqa_b1_split,gqa_b4_split,kv_append_b64",
                     help="extra workloads measured into 'other_workloads' ('' for none)")
@@ -329,6 +344,8 @@ def main():
                    "context_lens": "uniform %d" % int(case.context_lens[0])
                    if len(set(case.context_lens.tolist())) == 1 else "ragged",
                    "q_len": case.q_len,
+                   "kv_layout": "head-major pages [pages, Hkv, P, d]" if case.kv_layout
+                   else "token-major pages [pages, P, Hkv, d]",
                    "max_splits": r["max_splits"], "kv_bytes_per_step": r["kv_bytes"],
                    "rotating_pools": r["n_pools"]},
         "roofline": roof, "cpu_baseline": cpu, "other_workloads": others,

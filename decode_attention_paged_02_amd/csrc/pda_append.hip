@@ -5,9 +5,11 @@
 //
 // One thread moves eight consecutive elements of one token row (a 16-byte
 // load for 16-bit sources, two for fp32): the rows of all KV heads of a
-// token are contiguous in both the source [B, s_new, Hkv, d] and the cache
+// token are contiguous in the source [B, s_new, Hkv, d] and in a token-major
 // page [P, Hkv, d], so consecutive threads write consecutive bytes of one
-// slot.  Same-type caches get the elements copied; an E4M3 cache gets the
+// slot; in a head-major page [Hkv, P, d] they write the token's d-wide row
+// of each head (a head width is a multiple of 8, so no piece straddles two
+// heads).  Same-type caches get the elements copied; an E4M3 cache gets the
 // nearest E4M3FN code of the fp32 quotient x / scale (ties to even,
 // saturated at +-448), from the format's definition (bias 7, 3 mantissa
 // bits, subnormal step 2^-9, no infinities).
@@ -75,7 +77,16 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   if (pos < 0) return;
   const int p = pos + t;
   const int page = a.block_tables[(int64_t)b * a.max_pages + p / a.page_size];
-  const int64_t dst = ((int64_t)page * a.page_size + p % a.page_size) * row + off;
+  const int slot = p % a.page_size;
+  // token-major pages [P, Hkv, width]: the token's row is contiguous;
+  // head-major pages [Hkv, P, width]: head h's piece sits at h * P * width
+  int64_t dst;
+  if (a.head_major) {
+    const int h = (int)(off / width), e = (int)(off - (int64_t)h * width);
+    dst = (int64_t)page * a.page_size * row + ((int64_t)h * a.page_size + slot) * width + e;
+  } else {
+    dst = ((int64_t)page * a.page_size + slot) * row + off;
+  }
   const int64_t src = tok * row + off;
   const void* from = is_v ? a.v_new : a.k_new;
   void* to = is_v ? a.v_cache : a.k_cache;

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   asm volatile("" ::"s"(a.q), "s"(a.k_cache), "s"(a.v_cache), "s"(a.block_tables),
                "s"(a.context_lens), "s"(a.batch), "s"(a.num_q_heads), "s"(a.num_kv_heads),
                "s"(a.group), "s"(a.head_tiles), "s"(a.page_size), "s"(a.max_pages),
-               "s"(a.log2_page), "s"(a.tok_stride), "s"(a.page_stride), "s"(a.qk_scale_log2),
+               "s"(a.log2_page), "s"(a.tok_stride), "s"(a.head_stride), "s"(a.page_stride), "s"(a.qk_scale_log2),
                "s"(a.split.pages_per_split), "s"(a.split.max_splits),
                "s"(a.split.split_min_tokens));
   const int lane = threadIdx.x & 63;
@@ -203,8 +203,8 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   int koff[NLD], voff[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    koff[i] = (rg + RPL * (i ^ flip_row)) * tok_bytes + (kvh * D + c * EPL) * ESZ;
-    voff[i] = (rg + RPL * i) * tok_bytes + (kvh * D + c * EPL) * ESZ;
+    koff[i] = (rg + RPL * (i ^ flip_row)) * tok_bytes + (c * EPL) * ESZ;
+    voff[i] = (rg + RPL * i) * tok_bytes + (c * EPL) * ESZ;
   }
 
   float m_run[VPL], l_run[VPL];
@@ -232,7 +232,8 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
     const int tok = t0 + T * kTileTokens;
     rows = live ? min(kTileTokens, t1 - tok) : 0;
     const int slot = tok & ((1 << log2P) - 1);
-    const int64_t elem = (int64_t)(live ? phys : 0) * a.page_stride + (int64_t)slot * a.tok_stride;
+    const int64_t elem = (int64_t)(live ? phys : 0) * a.page_stride + (int64_t)slot * a.tok_stride +
+                         (int64_t)kvh * a.head_stride;
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.k_cache + elem * ESZ), 0,
                                            rows * tok_bytes, kRsrcFlags);
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.v_cache + elem * ESZ), 0,

@@ -277,8 +277,10 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   const int lim = min(t1, a.causal ? n - (q_len - 1 - qi) : n);
 
   const int tok_bytes = a.tok_stride * ESZ;
-  // load j of a tile: token 4 grp + j, piece col of the row
-  const int off0 = (4 * grp) * tok_bytes + (kvh * D + col * NE) * ESZ;
+  // load j of a tile: token 4 grp + j, piece col of the row (relative to the
+  // tile's first token row of this KV head)
+  const int off0 = (4 * grp) * tok_bytes + (col * NE) * ESZ;
+  const int64_t head_elem = (int64_t)kvh * a.head_stride;
 
   f32x4 acc[NE];  // O^T: rows (4 grp + i) * NE + e of the value, column = head col
 #pragma unroll
@@ -410,7 +412,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
       rows_b[u][t] = rows;
       tok_b[u][t] = tok;
       const int slot = tok & ((1 << log2P) - 1);
-      const int64_t elem = (int64_t)phys * a.page_stride + (int64_t)slot * a.tok_stride;
+      const int64_t elem = (int64_t)phys * a.page_stride + (int64_t)slot * a.tok_stride + head_elem;
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
           (void*)((const char*)a.k_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(

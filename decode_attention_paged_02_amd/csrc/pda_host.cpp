@@ -40,7 +40,8 @@ int check_shape(const pda_shape* s, bool mla) {
       s->head_dim_v <= 0 || s->page_size <= 0 || s->max_pages_per_seq <= 0 ||
       s->num_pages <= 0 || s->split_min_tokens < 0 || s->q_len < 0 ||
       (s->causal != 0 && s->causal != 1) ||
-      (s->schedule != PDA_SCHEDULE_GRID && s->schedule != PDA_SCHEDULE_BALANCED))
+      (s->schedule != PDA_SCHEDULE_GRID && s->schedule != PDA_SCHEDULE_BALANCED) ||
+      (s->kv_layout != PDA_KV_TOKEN_MAJOR && s->kv_layout != PDA_KV_HEAD_MAJOR))
     return PDA_ERR_INVALID_ARG;
   // (query, head) rows of a sequence stay well inside 32-bit indexing
   if ((int64_t)query_len(s) * s->num_q_heads > (1 << 20)) return PDA_ERR_UNSUPPORTED;
@@ -81,6 +82,8 @@ int check_shape(const pda_shape* s, bool mla) {
     const int64_t elem = s->kv_dtype == PDA_F32 ? 4 : s->kv_dtype == PDA_FP8_E4M3 ? 1 : 2;
     if ((int64_t)pda::kTileTokens * s->num_kv_heads * s->head_dim * elem > INT32_MAX)
       return PDA_ERR_UNSUPPORTED;
+    // the head stride of head-major pages (P * d elements) is 32-bit
+    if ((int64_t)s->page_size * s->head_dim > INT32_MAX) return PDA_ERR_UNSUPPORTED;
   }
   return PDA_OK;
 }
@@ -309,7 +312,9 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   a.max_pages = s.max_pages_per_seq;
   a.log2_page = 0;
   while ((1 << a.log2_page) < s.page_size) ++a.log2_page;
-  a.tok_stride = s.num_kv_heads * s.head_dim;
+  const bool head_major = s.kv_layout == PDA_KV_HEAD_MAJOR;
+  a.tok_stride = head_major ? s.head_dim : s.num_kv_heads * s.head_dim;
+  a.head_stride = head_major ? s.page_size * s.head_dim : s.head_dim;
   a.page_stride = (int64_t)s.page_size * s.num_kv_heads * s.head_dim;
   const float ks = s.kv_dtype == PDA_FP8_E4M3 ? s.k_scale : 1.0f;
   a.qk_scale_log2 = scale * ks * 1.4426950408889634f;
@@ -431,7 +436,8 @@ int paged_kv_append(const void* k_new, const void* v_new, const int32_t* block_t
   const pda_shape& s = *shape;
   if (s.batch < 0 || s.num_kv_heads <= 0 || s.head_dim <= 0 || s.page_size <= 0 ||
       s.max_pages_per_seq <= 0 || s.num_pages <= 0 || s.q_len < 0 ||
-      (has_v && s.head_dim_v <= 0))
+      (has_v && s.head_dim_v <= 0) ||
+      (s.kv_layout != PDA_KV_TOKEN_MAJOR && s.kv_layout != PDA_KV_HEAD_MAJOR))
     return PDA_ERR_INVALID_ARG;
   if (!valid_dtype(s.q_dtype) || !valid_dtype(s.kv_dtype)) return PDA_ERR_INVALID_ARG;
   if ((int64_t)s.max_pages_per_seq * s.page_size > INT32_MAX) return PDA_ERR_INVALID_ARG;
@@ -458,6 +464,7 @@ int paged_kv_append(const void* k_new, const void* v_new, const int32_t* block_t
   a.head_dim_v = has_v ? s.head_dim_v : 0;
   a.page_size = s.page_size;
   a.max_pages = s.max_pages_per_seq;
+  a.head_major = s.kv_layout == PDA_KV_HEAD_MAJOR && s.num_kv_heads > 1;
   a.k_scale = s.k_scale;
   a.v_scale = s.v_scale;
   return pda::launch_append(a, s.q_dtype, s.kv_dtype, (hipStream_t)stream) == hipSuccess

@@ -72,8 +72,12 @@ struct GqaArgs {
   int32_t q_len, causal;
   int32_t page_size, max_pages;
   int32_t log2_page;     // page_size == 1 << log2_page
-  int32_t tok_stride;    // elements between consecutive tokens of a page (Hkv * d)
-  int64_t page_stride;   // elements between consecutive pages (P * Hkv * d)
+  // cache strides in elements: token-major pages [P, Hkv, d] have tok_stride
+  // Hkv * d and head_stride d, head-major pages [Hkv, P, d] tok_stride d and
+  // head_stride P * d; page_stride is P * Hkv * d either way
+  int32_t tok_stride;
+  int32_t head_stride;
+  int64_t page_stride;
   float qk_scale_log2;   // scale * k_scale * log2(e)
   float v_scale;
   SplitLayout split;
@@ -141,8 +145,9 @@ struct OrderArgs {
 struct AppendArgs {
   const void* k_new;             // [B, s_new, Hkv, head_dim]
   const void* v_new;             // [B, s_new, Hkv, head_dim_v] (null with v_cache)
-  void* k_cache;                 // [num_pages, P, Hkv, head_dim]
-  void* v_cache;                 // [num_pages, P, Hkv, head_dim_v] or null
+  void* k_cache;                 // [num_pages, P, Hkv, head_dim] or [num_pages, Hkv, P, head_dim]
+  void* v_cache;                 // the same with head_dim_v, or null
+  int32_t head_major;            // 1: pages are [Hkv, P, width]
   const int32_t* block_tables;   // [B, max_pages]
   const int32_t* positions;      // [B]: first new token's position, < 0 skips b
   int32_t batch, s_new, num_kv_heads, head_dim, head_dim_v, page_size, max_pages;

@@ -21,6 +21,7 @@ PDA_F32, PDA_F16, PDA_BF16, PDA_FP8_E4M3 = 0, 1, 2, 3
 PDA_MLA_DEFAULT, PDA_MLA_MFMA, PDA_MLA_VALU = 0, 1, 2
 PDA_GQA_DEFAULT, PDA_GQA_MFMA, PDA_GQA_VALU = 0, 1, 2
 PDA_SCHEDULE_GRID, PDA_SCHEDULE_BALANCED = 0, 1
+PDA_KV_TOKEN_MAJOR, PDA_KV_HEAD_MAJOR = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing or too small", 4: "HIP runtime error"}
 
@@ -40,7 +41,7 @@ class Shape(ctypes.Structure):
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("split_min_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("q_len", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("schedule", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("kv_layout", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -117,10 +118,11 @@ def _need(cond, msg):
 
 def make_shape(*, batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, page_size,
                max_pages_per_seq, num_pages, q_dtype, kv_dtype, k_scale=1.0, v_scale=1.0,
-               split_min_tokens=0, variant=0, q_len=1, causal=True, schedule=0) -> Shape:
+               split_min_tokens=0, variant=0, q_len=1, causal=True, schedule=0,
+               kv_layout=PDA_KV_TOKEN_MAJOR) -> Shape:
     return Shape(batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, page_size,
                  max_pages_per_seq, num_pages, q_dtype, kv_dtype, k_scale, v_scale,
-                 split_min_tokens, variant, q_len, int(causal), int(schedule))
+                 split_min_tokens, variant, q_len, int(causal), int(schedule), int(kv_layout))
 
 
 def _query_dims(q):
@@ -152,10 +154,16 @@ def plan(shape: Shape, *, mla: bool = False, num_splits: int = 0, num_cus: int =
 
 
 def gqa_shape(q, k_cache, v_cache, block_tables, *, k_scale=1.0, v_scale=1.0,
-              split_min_tokens=0, variant=0, causal=True, schedule=0) -> Shape:
+              split_min_tokens=0, variant=0, causal=True, schedule=0,
+              kv_layout=PDA_KV_TOKEN_MAJOR) -> Shape:
+    """Caches are [pages, P, Hkv, d] (token-major) or [pages, Hkv, P, d]
+    (kv_layout = PDA_KV_HEAD_MAJOR)."""
     _need(k_cache.dim() == 4 and v_cache.dim() == 4, "bad ranks")
     B, s_q, Hq, d = _query_dims(q)
-    num_pages, P, Hkv, dk = k_cache.shape
+    if kv_layout == PDA_KV_HEAD_MAJOR:
+        num_pages, Hkv, P, dk = k_cache.shape
+    else:
+        num_pages, P, Hkv, dk = k_cache.shape
     _need(dk == d and v_cache.shape[:3] == k_cache.shape[:3], "cache shapes do not match q")
     _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, *]")
     return make_shape(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
@@ -163,7 +171,8 @@ def gqa_shape(q, k_cache, v_cache, block_tables, *, k_scale=1.0, v_scale=1.0,
                       max_pages_per_seq=block_tables.shape[1], num_pages=num_pages,
                       q_dtype=_dtype_code(q), kv_dtype=_dtype_code(k_cache, fp8_ok=True),
                       k_scale=k_scale, v_scale=v_scale, split_min_tokens=split_min_tokens,
-                      variant=variant, q_len=s_q, causal=causal, schedule=schedule)
+                      variant=variant, q_len=s_q, causal=causal, schedule=schedule,
+                      kv_layout=kv_layout)
 
 
 def mla_shape(q, kv_cache, block_tables, *, head_dim_v=512, variant=0,
@@ -198,15 +207,19 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, scale:
                       num_splits: int = 0, out=None, lse=None, k_scale: float = 1.0,
                       v_scale: float = 1.0, split_min_tokens: int = 0, workspace=None,
                       stream=None, return_lse: bool = True, variant: int = 0,
-                      causal: bool = True, schedule: int = PDA_SCHEDULE_GRID):
+                      causal: bool = True, schedule: int = PDA_SCHEDULE_GRID,
+                      kv_layout: int = PDA_KV_TOKEN_MAJOR):
     """GQA/MQA/MHA paged decode attention.
+
+    Caches are [pages, P, Hkv, d] (token-major), or [pages, Hkv, P, d] with
+    kv_layout = PDA_KV_HEAD_MAJOR.
 
     q [B, Hq, d] returns (out [B, Hq, dv], lse [B, Hq] fp32); q [B, s_q, Hq, d]
     (s_q query tokens per sequence, the last s_q positions; causal: bottom-right
     mask) returns (out [B, s_q, Hq, dv], lse [B, Hq, s_q] fp32)."""
     shape = gqa_shape(q, k_cache, v_cache, block_tables, k_scale=k_scale, v_scale=v_scale,
                       split_min_tokens=split_min_tokens, variant=variant, causal=causal,
-                      schedule=schedule)
+                      schedule=schedule, kv_layout=kv_layout)
     _check_device(q, k_cache, v_cache, block_tables, context_lens, out, lse, workspace)
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
@@ -265,19 +278,24 @@ def paged_decode_attn_mla(q, kv_cache, block_tables, context_lens, *, scale: flo
 
 
 def paged_kv_append(k_new, v_new, block_tables, positions, k_cache, v_cache=None, *,
-                    k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+                    k_scale: float = 1.0, v_scale: float = 1.0, stream=None,
+                    kv_layout: int = PDA_KV_TOKEN_MAJOR):
     """Write new tokens' K (and V) rows into the paged cache, in place.
 
     k_new [B, s_new, Hkv, d] (or [B, s_new, 576] for an MLA latent cache
     [pages, P, 576], with v_new = v_cache = None); v_new [B, s_new, Hkv, dv];
     positions [B] int32, the position of each sequence's first new token
-    (< 0: skipped).  fp8 caches (uint8 storage) store e4m3(x / scale)."""
+    (< 0: skipped).  fp8 caches (uint8 storage) store e4m3(x / scale).
+    Head-major caches (kv_layout = PDA_KV_HEAD_MAJOR) are [pages, Hkv, P, d]."""
     _need((v_new is None) == (v_cache is None), "v_new and v_cache go together")
     kn = k_new if k_new.dim() == 4 else k_new.unsqueeze(2)
     kc = k_cache if k_cache.dim() == 4 else k_cache.unsqueeze(2)
     _need(kn.dim() == 4 and kc.dim() == 4, "bad ranks")
     B, s_new, Hkv, d = kn.shape
-    num_pages, P, Hkv2, d2 = kc.shape
+    if kv_layout == PDA_KV_HEAD_MAJOR and k_cache.dim() == 4:
+        num_pages, Hkv2, P, d2 = kc.shape
+    else:
+        num_pages, P, Hkv2, d2 = kc.shape
     _need((Hkv2, d2) == (Hkv, d), "k_new rows do not match k_cache")
     dv = 0
     if v_cache is not None:
@@ -294,7 +312,7 @@ def paged_kv_append(k_new, v_new, block_tables, positions, k_cache, v_cache=None
                        head_dim_v=dv, page_size=P, max_pages_per_seq=block_tables.shape[1],
                        num_pages=num_pages, q_dtype=_dtype_code(k_new),
                        kv_dtype=_dtype_code(k_cache, fp8_ok=True), k_scale=k_scale,
-                       v_scale=v_scale, q_len=s_new)
+                       v_scale=v_scale, q_len=s_new, kv_layout=kv_layout)
     rc = load().paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(block_tables), _ptr(positions),
                                 _ptr(k_cache), _ptr(v_cache), ctypes.byref(shape),
                                 _stream_handle(stream))
@@ -344,6 +362,7 @@ def run_case(case, dev: Optional[DeviceCase] = None, **kw):
         return paged_decode_attn_mla(dev.q, dev.k_cache, dev.block_tables, dev.context_lens,
                                      scale=case.scale, head_dim_v=case.d_latent,
                                      kv_scale=case.k_scale, **kw)
+    kw.setdefault("kv_layout", case.kv_layout)
     return paged_decode_attn(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
                              dev.context_lens, scale=case.scale, k_scale=case.k_scale,
                              v_scale=case.v_scale, **kw)

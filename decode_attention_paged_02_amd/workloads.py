@@ -13,7 +13,8 @@ by library casts (numpy for fp16, torch for bf16 and fp8), round-to-nearest-even
 Layouts follow the pages ("From MHA to MLA" sec. 5 paged addressing; the drill
 page sec. 4 cache strides; FlashMLA-ETAP "Usage" for the latent cache):
   q            [B, Hq, d]
-  k/v cache    [num_pages, P, Hkv, d]      (GQA family)
+  k/v cache    [num_pages, P, Hkv, d]      (GQA family, token-major pages)
+               [num_pages, Hkv, P, d]      (kv_layout=1, head-major pages)
   latent cache [num_pages, P, d_latent + d_rope]   (MLA, one record per token)
   block_tables [B, max_pages] int32, context_lens [B] int32.
 
@@ -86,6 +87,7 @@ class PagedCase:
     d_latent: int = 0
     name: str = ""
     causal: bool = True                # several query tokens: bottom-right causal mask
+    kv_layout: int = 0                 # 0: pages [P, Hkv, d]; 1: pages [Hkv, P, d]
 
     @property
     def batch(self) -> int:
@@ -102,7 +104,7 @@ class PagedCase:
 
     @property
     def num_kv_heads(self) -> int:
-        return 1 if self.mla else self.k_cache.shape[2]
+        return 1 if self.mla else self.k_cache.shape[1 if self.kv_layout else 2]
 
     @property
     def head_dim(self) -> int:
@@ -168,14 +170,17 @@ def make_gqa(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
              seed: int, head_dim_v: Optional[int] = None, max_pages: Optional[int] = None,
              extra_pages: int = 0, poison: bool = True, std: float = 1.0,
              scale: Optional[float] = None, q_len: int = 1, causal: bool = True,
-             name: str = "") -> PagedCase:
+             kv_layout: int = 0, name: str = "") -> PagedCase:
     """GQA/MQA/MHA case: q, K, V ~ N(0, std^2) in fp32, then stored as requested.
 
     q_len > 1 gives q the shape [B, q_len, Hq, d] (several query tokens per
     sequence); q_len = 1 keeps [B, Hq, d].
 
     fp8 caches get one fp32 scale per tensor, amax / 448 over the values the
-    method reads; the stored byte is e4m3(x / scale) (saturating, RNE)."""
+    method reads; the stored byte is e4m3(x / scale) (saturating, RNE).
+
+    kv_layout=1 stores the same values with head-major pages [Hkv, P, d]
+    (the random draws do not depend on the layout)."""
     dv = head_dim if head_dim_v is None else head_dim_v
     lens = np.asarray(context_lens, dtype=np.int32)
     assert lens.shape == (batch,)
@@ -204,10 +209,14 @@ def make_gqa(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
         _poison(v, tables, lens, used, P, NAN_BITS[kv_dtype])
     else:
         tables[tables < 0] = 0
+    if kv_layout:
+        k = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+        v = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
     return PagedCase(q=encode(q32, q_dtype), k_cache=k, v_cache=v, block_tables=tables,
                      context_lens=lens, q_dtype=q_dtype, kv_dtype=kv_dtype, page_size=P,
                      scale=float(1.0 / math.sqrt(head_dim)) if scale is None else scale,
-                     k_scale=k_scale, v_scale=v_scale, name=name, causal=causal)
+                     k_scale=k_scale, v_scale=v_scale, name=name, causal=causal,
+                     kv_layout=int(kv_layout))
 
 
 def make_mla(*, batch: int, num_q_heads: int, d_latent: int, d_rope: int, page_size: int,
@@ -262,27 +271,34 @@ def tiny_gqa(poison: bool = True) -> PagedCase:
                     max_pages=8, extra_pages=16 - 10, poison=poison, name="tiny_gqa_fp32")
 
 
-def gqa_batch64(seed_offset: int = 0) -> PagedCase:
-    """B=64, Hq=32, Hkv=8, d=128, ctx 1024, P=16, fp16, a permuted 4096-page pool."""
+def _layout_tag(kv_layout: int) -> str:
+    return "_headmajor" if kv_layout else ""
+
+
+def gqa_batch64(seed_offset: int = 0, kv_layout: int = 0) -> PagedCase:
+    """B=64, Hq=32, Hkv=8, d=128, ctx 1024, P=16, fp16, a permuted 4096-page pool
+    (kv_layout 1: head-major pages)."""
     return make_gqa(batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
                     context_lens=[1024] * 64, q_dtype="f16", kv_dtype="f16",
-                    seed=1001 + seed_offset, poison=False, name="gqa_b64_ctx1024_fp16")
+                    seed=1001 + seed_offset, poison=False, kv_layout=kv_layout,
+                    name="gqa_b64_ctx1024_fp16" + _layout_tag(kv_layout))
 
 
-def gqa_batch64_mtp(q_len: int = 2) -> PagedCase:
+def gqa_batch64_mtp(q_len: int = 2, kv_layout: int = 0) -> PagedCase:
     """The B=64 / ctx 1024 GQA step with q_len query tokens per sequence (the
     last q_len positions, bottom-right causal mask): multi-token decode."""
     return make_gqa(batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
                     context_lens=[1024] * 64, q_dtype="f16", kv_dtype="f16", seed=1101,
-                    poison=False, q_len=q_len, name="gqa_b64_ctx1024_fp16_q%d" % q_len)
+                    poison=False, q_len=q_len, kv_layout=kv_layout,
+                    name="gqa_b64_ctx1024_fp16_q%d" % q_len + _layout_tag(kv_layout))
 
 
-def gqa_long(batch: int) -> PagedCase:
+def gqa_long(batch: int, kv_layout: int = 0) -> PagedCase:
     """B in {1, 4}, Hq=32, Hkv=8, d=128, ctx 32768, P=16, fp16 (split-KV)."""
     return make_gqa(batch=batch, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
                     context_lens=[32768] * batch, q_dtype="f16", kv_dtype="f16",
-                    seed=1002 * 10 + batch, poison=False,
-                    name="gqa_b%d_ctx32768_fp16_split" % batch)
+                    seed=1002 * 10 + batch, poison=False, kv_layout=kv_layout,
+                    name="gqa_b%d_ctx32768_fp16_split" % batch + _layout_tag(kv_layout))
 
 
 def mla_b16(ctx: int = 65536, kv_dtype: str = "bf16", d_latent: int = 512) -> PagedCase:
@@ -312,9 +328,10 @@ def ragged_fp8_lens(batch: int = 128, seed: int = 1004) -> np.ndarray:
     return lens
 
 
-def ragged_fp8() -> PagedCase:
+def ragged_fp8(kv_layout: int = 0) -> PagedCase:
     """B=128, lens log-uniform in [1, 16384] (1, 16384, 17 forced), Hq=64, Hkv=8,
     d=128, P=16, fp8-e4m3 cache with per-tensor scales, fp16 queries."""
     return make_gqa(batch=128, num_q_heads=64, num_kv_heads=8, head_dim=128, page_size=16,
                     context_lens=ragged_fp8_lens(), q_dtype="f16", kv_dtype="e4m3",
-                    seed=1004, max_pages=1024, poison=True, name="ragged_b128_fp8")
+                    seed=1004, max_pages=1024, poison=True, kv_layout=kv_layout,
+                    name="ragged_b128_fp8" + _layout_tag(kv_layout))

@@ -41,7 +41,9 @@
  *    (s_q = shape->q_len; for s_q = 1 the layouts below are [B, Hq, ...]):
  *      q            [B, s_q, Hq, head_dim]     of shape->q_dtype
  *      k_cache      [num_pages, P, Hkv, head_dim]   of shape->kv_dtype
+ *                   ([num_pages, Hkv, P, head_dim] with PDA_KV_HEAD_MAJOR)
  *      v_cache      [num_pages, P, Hkv, head_dim_v] of shape->kv_dtype
+ *                   ([num_pages, Hkv, P, head_dim_v] with PDA_KV_HEAD_MAJOR)
  *      kv_cache     [num_pages, P, head_dim]   (MLA, K and V share it)
  *      block_tables [B, max_pages_per_seq] int32 (logical -> physical page)
  *      context_lens [B] int32, the number of cached tokens of each sequence
@@ -112,7 +114,21 @@ typedef struct pda_shape {
   int32_t causal;            /* s_q > 1: 1 = bottom-right causal mask,      */
                              /* 0 = every query sees all n tokens           */
   int32_t schedule;          /* PDA_SCHEDULE_* (below)                       */
+  int32_t kv_layout;         /* PDA_KV_* (below): axis order inside a page   */
 } pda_shape;
+
+/* Order of a cache page's axes (pda_shape.kv_layout).  The pages address a
+ * cached element through separate page, slot and head strides ("From MHA
+ * to MLA" sec. 5, paged loads; the drill page sec. 4, the page loop), so
+ * both orders describe the same cache:
+ * TOKEN_MAJOR: k_cache [num_pages, P, Hkv, head_dim] (a token's KV heads are
+ *   adjacent);
+ * HEAD_MAJOR:  k_cache [num_pages, Hkv, P, head_dim] (one KV head's P rows
+ *   of a page are one contiguous block, so a workgroup that serves one KV
+ *   head reads whole blocks); likewise v_cache with head_dim_v.
+ * With Hkv = 1 (MLA) the two orders coincide. */
+#define PDA_KV_TOKEN_MAJOR 0
+#define PDA_KV_HEAD_MAJOR 1
 
 /* How a call cuts sequences into splits (pda_shape.schedule).
  * GRID: every sequence longer than split_min_tokens takes ceil(pages /

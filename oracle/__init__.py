@@ -127,9 +127,19 @@ def _shape_result(out, lse, single):
     return out, lse
 
 
+def _token_major(cache, kv_layout):
+    """A head-major cache [num_pages, H, P, w] as the token-major array
+    [num_pages, P, H, w] that holds the same elements: element (page, slot,
+    head) is addressed by its own stride in either order ("From MHA to MLA"
+    sec. 5, paged loads; the drill page sec. 4)."""
+    if kv_layout not in (0, 1):
+        raise ValueError("kv_layout must be 0 (token-major) or 1 (head-major)")
+    return np.ascontiguousarray(cache.transpose(0, 2, 1, 3)) if kv_layout else cache
+
+
 def paged_attention(q, k_cache, v_cache, block_tables, context_lens, *, scale,
                     q_dtype, kv_dtype, k_scale=1.0, v_scale=1.0, causal=True,
-                    tok_begin=None, tok_end=None, rows=None, num_threads=0):
+                    tok_begin=None, tok_end=None, rows=None, num_threads=0, kv_layout=0):
     """GQA/MQA/MHA paged decode attention in fp64.
 
     q [B, Hq, dk] (one query token) or [B, s_q, Hq, dk] (s_q query tokens,
@@ -142,10 +152,11 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, *, scale,
     (others are NaN).
     Returns (out [B, Hq, dv], lse [B, Hq]) for a 3-D q and
     (out [B, s_q, Hq, dv], lse [B, Hq, s_q]) for a 4-D q, float64.
+    kv_layout=1: the caches are head-major, [num_pages, Hkv, P, d].
     """
     q = _as(q, q_dtype)
-    k_cache = _as(k_cache, kv_dtype)
-    v_cache = _as(v_cache, kv_dtype)
+    k_cache = _as(_token_major(np.asarray(k_cache), kv_layout), kv_dtype)
+    v_cache = _as(_token_major(np.asarray(v_cache), kv_layout), kv_dtype)
     q, s_q, single = _queries(q)
     B, _, Hq, dk = q.shape
     num_pages, P, Hkv, dk2 = k_cache.shape
@@ -217,14 +228,20 @@ def combine(part_o, part_lse):
     return out, lse
 
 
-def kv_append(src, cache, block_tables, positions, *, src_dtype, cache_dtype, scale=1.0):
+def kv_append(src, cache, block_tables, positions, *, src_dtype, cache_dtype, scale=1.0,
+              kv_layout=0):
     """Write s_new new tokens per sequence into a copy of one paged cache tensor.
 
     src [B, s_new, H, width] (or [B, s_new, width] for a headless MLA cache);
     cache [num_pages, P, H, width] (or [num_pages, P, width]); positions [B]
     int32, the position of each sequence's first new token (< 0: skipped).
     E4M3 caches store the nearest E4M3FN byte to the fp32 quotient x / scale
-    (ties to even, saturated at 448).  Returns the updated copy of cache."""
+    (ties to even, saturated at 448).  Returns the updated copy of cache.
+    kv_layout=1: cache is head-major, [num_pages, H, P, width] (returned so)."""
+    if kv_layout and np.asarray(cache).ndim == 4:
+        tm = kv_append(src, _token_major(np.asarray(cache), 1), block_tables, positions,
+                       src_dtype=src_dtype, cache_dtype=cache_dtype, scale=scale)
+        return np.ascontiguousarray(tm.transpose(0, 2, 1, 3))
     src = _as(src, src_dtype)
     out = _as(cache, cache_dtype).copy()
     if src.ndim == 3:

@@ -38,7 +38,8 @@ def oracle_ref(case, rows=None, **kw):
     return oracle.paged_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
                                   case.context_lens, scale=case.scale, q_dtype=case.q_dtype,
                                   kv_dtype=case.kv_dtype, k_scale=case.k_scale,
-                                  v_scale=case.v_scale, causal=case.causal, rows=rows, **kw)
+                                  v_scale=case.v_scale, causal=case.causal, rows=rows,
+                                  kv_layout=case.kv_layout, **kw)
 
 
 def round_to(ref, dtype):

@@ -180,6 +180,8 @@ def test_plan_multi_token_rows():
     (dict(q_len=2, variant=pda.PDA_GQA_VALU), 2),               # several tokens: MFMA only
     (dict(q_len=2, q_dtype=pda.PDA_F32, kv_dtype=pda.PDA_F32), 2),
     (dict(q_len=1 << 16), 2),                                   # q_len * Hq > 2^20
+    (dict(kv_layout=2), 1),                                     # no such page layout
+    (dict(kv_layout=-1), 1),
 ])
 def test_invalid_shapes_rejected_before_device_work(kw, status):
     s = _shape(**kw)
@@ -271,6 +273,8 @@ def test_append_validation():
     assert call(dict(q_len=-2)) == 1
     assert call(dict(), k_new=odd) == 1
     assert call(dict(batch=0, head_dim=576), v=False) == 0              # K-only (MLA) form
+    assert call(dict(kv_layout=3)) == 1                                 # no such page layout
+    assert call(dict(batch=0, kv_layout=pda.PDA_KV_HEAD_MAJOR)) == 0
     s = _shape()
     assert lib.paged_kv_append(fake, None, fake, fake, fake, fake, ctypes.byref(s), None) == 1
     assert lib.paged_kv_append(fake, fake, fake, fake, fake, fake, None, None) == 1

@@ -1,0 +1,109 @@
+"""GPU parity with head-major cache pages ([num_pages, Hkv, P, d]) against
+the fp64 oracle: both GQA kernels, every cache type, splits, several query
+tokens, the balanced schedule, the full-size workloads, and the KV append
+(bit-exact) into a head-major cache."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_paged_02_amd import pda
+from decode_attention_paged_02_amd import workloads as W
+from gpu_util import check, need_gpu, oracle_ref, say
+
+pytestmark = pytest.mark.gpu
+HEAD_MAJOR = pda.PDA_KV_HEAD_MAJOR
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype,d,variant", [
+    ("f16", "f16", 128, pda.PDA_GQA_MFMA), ("bf16", "bf16", 64, pda.PDA_GQA_MFMA),
+    ("f16", "e4m3", 256, pda.PDA_GQA_MFMA), ("bf16", "e4m3", 128, pda.PDA_GQA_MFMA),
+    ("f32", "f32", 128, pda.PDA_GQA_VALU), ("f16", "f16", 64, pda.PDA_GQA_VALU),
+    ("bf16", "e4m3", 128, pda.PDA_GQA_VALU)])
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_head_major_parity(q_dtype, kv_dtype, d, variant, num_splits):
+    case = W.make_gqa(batch=4, num_q_heads=16, num_kv_heads=4, head_dim=d, page_size=32,
+                      context_lens=[1, 33, 700, 2049], q_dtype=q_dtype, kv_dtype=kv_dtype,
+                      seed=61 + d, extra_pages=3, kv_layout=HEAD_MAJOR)
+    say("head-major", q_dtype, kv_dtype, d, variant, num_splits)
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, num_splits=num_splits, variant=variant)
+    check(case, out, lse, ref_o, ref_l, label="head-major %s %s d%d v%d S%d" % (
+        q_dtype, kv_dtype, d, variant, num_splits))
+
+
+@pytest.mark.parametrize("q_len,schedule", [(3, pda.PDA_SCHEDULE_GRID),
+                                            (1, pda.PDA_SCHEDULE_BALANCED),
+                                            (2, pda.PDA_SCHEDULE_BALANCED)])
+def test_head_major_multi_token_and_balanced(q_len, schedule):
+    case = W.make_gqa(batch=5, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                      context_lens=[5, 16, 3000, 129, 1000], q_dtype="f16", kv_dtype="f16",
+                      seed=71 + q_len, extra_pages=2, q_len=q_len, kv_layout=HEAD_MAJOR)
+    say("head-major q_len", q_len, "schedule", schedule)
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, num_splits=4, schedule=schedule)
+    check(case, out, lse, ref_o, ref_l, label="head-major q%d sched %d" % (q_len, schedule))
+
+
+def test_head_major_full_size_batch64():
+    case = W.gqa_batch64(kv_layout=HEAD_MAJOR)
+    say(case.name)
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case)
+    check(case, out, lse, ref_o, ref_l, label=case.name)
+
+
+def test_head_major_full_size_long_split():
+    case = W.gqa_long(1, kv_layout=HEAD_MAJOR)
+    say(case.name)
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case)
+    check(case, out, lse, ref_o, ref_l, label=case.name)
+
+
+def test_head_major_equals_token_major_bitwise():
+    """The two layouts of one case read the same elements in the same order:
+    the kernels' outputs are bit-identical."""
+    kw = dict(batch=6, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+              context_lens=[1, 17, 100, 640, 1024, 33], q_dtype="bf16", kv_dtype="bf16",
+              seed=81, extra_pages=2)
+    t = W.make_gqa(kv_layout=0, **kw)
+    h = W.make_gqa(kv_layout=HEAD_MAJOR, **kw)
+    say("layouts bitwise")
+    for v in (pda.PDA_GQA_MFMA, pda.PDA_GQA_VALU):
+        ot, lt = pda.run_case(t, num_splits=2, variant=v)
+        oh, lh = pda.run_case(h, num_splits=2, variant=v)
+        assert torch.equal(ot.view(torch.int16), oh.view(torch.int16))
+        assert torch.equal(lt, lh)
+
+
+@pytest.mark.parametrize("src,cache", [("f16", "f16"), ("bf16", "e4m3"), ("f32", "f32")])
+def test_append_head_major_bit_exact(src, cache):
+    case = W.make_gqa(batch=5, num_q_heads=4, num_kv_heads=4, head_dim=128, page_size=16,
+                      context_lens=[7, 16, 17, 40, 100],
+                      q_dtype=src if cache == "e4m3" else cache, kv_dtype=cache, seed=91,
+                      extra_pages=2, kv_layout=HEAD_MAJOR)
+    rng = np.random.default_rng(91)
+    k_new = W.encode((rng.standard_normal((5, 2, 4, 128)) * 2).astype(np.float32), src)
+    v_new = W.encode((rng.standard_normal((5, 2, 4, 128)) * 2).astype(np.float32), src)
+    pos = (case.context_lens - 2).astype(np.int32)
+    pos[1] = -1
+    say("append head-major", src, cache)
+    kc = pda._storage_to_torch(case.k_cache, cache, "cuda")
+    vc = pda._storage_to_torch(case.v_cache, cache, "cuda")
+    pda.paged_kv_append(pda._storage_to_torch(k_new, src, "cuda"),
+                        pda._storage_to_torch(v_new, src, "cuda"),
+                        torch.from_numpy(case.block_tables).cuda(), torch.from_numpy(pos).cuda(),
+                        kc, vc, k_scale=case.k_scale, v_scale=case.v_scale, kv_layout=HEAD_MAJOR)
+    torch.cuda.synchronize()
+    for new, dev, host, sc in ((k_new, kc, case.k_cache, case.k_scale),
+                               (v_new, vc, case.v_cache, case.v_scale)):
+        want = oracle.kv_append(new, host, case.block_tables, pos, src_dtype=src,
+                                cache_dtype=cache, scale=sc, kv_layout=HEAD_MAJOR)
+        got = dev.cpu().view(torch.uint8).numpy() if dev.dtype != torch.uint8 else dev.cpu().numpy()
+        assert np.array_equal(got.reshape(-1), want.view(np.uint8).reshape(-1))
