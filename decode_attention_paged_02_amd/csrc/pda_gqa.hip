@@ -151,19 +151,12 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
     const int64_t pg = tok >> log2P;
     return table[pg < a.max_pages ? pg : a.max_pages - 1];
   };
-  // With ragged lengths most workgroups past split 0 have no pages to read:
-  // those decide on the length alone and leave without further loads.  Split
-  // 0 always has work (or an empty sequence) and requests its length along
-  // with the table entries and q.
+  // A split past the end of a short sequence finds out from the length,
+  // requested together with its first table entries and q (entries in the
+  // table row, never used then), and leaves after that one round trip.
   int n = 0;
-  if (!ordered && split > 0) {
-    n = load_uniform(a.context_lens + b);
-    int ns, ta, tb;
-    split_range(a.split, n, a.page_size, split, ns, ta, tb);
-    if (split >= ns) return;
-  }
   int vtbl = load_table(0);
-  if (!ordered && split == 0) n = load_uniform(a.context_lens + b);
+  if (!ordered) n = load_uniform(a.context_lens + b);
 
   // q of the tile's heads (slot g holds head g ^ flip_head), the EPL elements
   // this lane multiplies.  Heads past the group are loaded from a valid row

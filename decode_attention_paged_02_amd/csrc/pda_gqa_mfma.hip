@@ -226,20 +226,12 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     const int64_t pg = tok >> log2P;
     return table[pg < max_pages ? pg : max_pages - 1];
   };
-  // With ragged lengths most workgroups past split 0 have no pages to read:
-  // those decide on the length alone and leave without further loads.  Split
-  // 0 always has work (or an empty sequence) and requests its length along
-  // with the table entries and q; so does every ordered unit (its range is
-  // known, the length only bounds the causal windows).
-  int n = 0;
-  if (!ordered && split > 0) {
-    n = load_uniform(context_lens + b);
-    int ns, ta, tb;
-    split_range(a.split, n, a.page_size, split, ns, ta, tb);
-    if (split >= ns) return;
-  }
+  // Every workgroup requests its length, its first table entries and q
+  // together, and only then decides whether its split has pages at all (a
+  // split past the end of a short sequence leaves after that one round trip;
+  // the entries it loaded lie in the table row and are never used).
   int vtbl = load_table(0);
-  if (ordered || split == 0) n = load_uniform(context_lens + b);
+  int n = load_uniform(context_lens + b);
 
   // Q^T as the B operand of the QK MFMAs: lane (col, grp) holds
   // q[row col][32 j + 8 grp .. +8] for MFMA j; rows past the group are zero.

@@ -24,7 +24,7 @@ constexpr int kTileTokens = 16;
 #define PDA_GQA_STEP_TILES 1
 #endif
 #ifndef PDA_GQA_STEPS_IN_FLIGHT
-#define PDA_GQA_STEPS_IN_FLIGHT 3
+#define PDA_GQA_STEPS_IN_FLIGHT 2
 #endif
 // Registers the GQA kernels may spend on the ring of in-flight tiles (caps
 // the prefetch depth for wide rows).

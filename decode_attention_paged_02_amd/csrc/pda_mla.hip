@@ -243,26 +243,20 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
     split = blockIdx.y;
   }
   // One batch of kernel-argument loads; then the sequence length, the
-  // range's block-table entries and q are requested together (workgroups past
-  // split 0 first check on the length alone whether they have pages at all).
+  // range's block-table entries and q are requested together (a split past
+  // the end of a short sequence finds out from the length and leaves after
+  // that one round trip; the entries it loaded lie in the table row).
   asm volatile("" ::"s"(a.q), "s"(a.kv_cache), "s"(a.block_tables), "s"(a.context_lens),
                "s"(a.num_q_heads), "s"(a.head_tiles), "s"(a.page_size), "s"(a.max_pages),
                "s"(a.log2_page), "s"(a.qk_scale_log2), "s"(a.split.pages_per_split),
                "s"(a.split.max_splits), "s"(a.split.split_min_tokens), "s"(a.q_len));
   const int log2P = a.log2_page;
-  int n = 0;
-  if (!ordered && split > 0) {
-    n = load_uniform(a.context_lens + b);
-    int ns, ta, tb;
-    split_range(a.split, n, a.page_size, split, ns, ta, tb);
-    if (split >= ns) return;
-  }
   PageTable pt{a.block_tables + (int64_t)b * a.max_pages, a.max_pages, 0, 0};
   pt.load(ordered                  ? ut0 >> log2P
           : a.split.max_splits > 1 ? split * a.split.pages_per_split
                                    : 0,
           lane);
-  if (ordered || split == 0) n = load_uniform(a.context_lens + b);
+  int n = load_uniform(a.context_lens + b);
 
   // this lane's column: row r = query token qi, head h (rows past the last
   // one compute on zero queries and are not written)
@@ -499,26 +493,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
     split = blockIdx.y;
   }
   // One batch of kernel-argument loads; then the sequence length, the
-  // range's block-table entries and q are requested together (workgroups past
-  // split 0 first check on the length alone whether they have pages at all).
+  // range's block-table entries and q are requested together (a split past
+  // the end of a short sequence finds out from the length and leaves after
+  // that one round trip; the entries it loaded lie in the table row).
   asm volatile("" ::"s"(a.q), "s"(a.kv_cache), "s"(a.block_tables), "s"(a.context_lens),
                "s"(a.num_q_heads), "s"(a.head_tiles), "s"(a.page_size), "s"(a.max_pages),
                "s"(a.log2_page), "s"(a.qk_scale_log2), "s"(a.split.pages_per_split),
                "s"(a.split.max_splits), "s"(a.split.split_min_tokens));
   const int log2P = a.log2_page;
-  int n = 0;
-  if (!ordered && split > 0) {
-    n = load_uniform(a.context_lens + b);
-    int ns, ta, tb;
-    split_range(a.split, n, a.page_size, split, ns, ta, tb);
-    if (split >= ns) return;
-  }
   PageTable pt{a.block_tables + (int64_t)b * a.max_pages, a.max_pages, 0, 0};
   pt.load(ordered                  ? ut0 >> log2P
           : a.split.max_splits > 1 ? split * a.split.pages_per_split
                                    : 0,
           lane);
-  if (ordered || split == 0) n = load_uniform(a.context_lens + b);
+  int n = load_uniform(a.context_lens + b);
   const int hvalid_n = min(kHeads, a.num_q_heads - tile * kHeads);
 
   // q of the tile's heads into LDS (zero for padded heads)
