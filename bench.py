@@ -4,7 +4,10 @@ us per decode step of paged decode attention on one GPU.
 
 Default workload: GQA decode at batch, B=64, Hq=32, Hkv=8, d=128, every context
 1024 tokens, page 16, fp16 cache and queries ~ N(0, 1), block tables a random
-permutation of a 4096-page pool, no split-KV.
+permutation of a 4096-page pool, no split-KV; the cache pages are head-major
+([pages, Hkv, P, d], one KV head's 16 rows of a page contiguous).  The same
+cache with token-major pages ([pages, P, Hkv, d]) is measured as "gqa_b64"
+among the other workloads.
 
 A step is one call of the C-ABI entry point (planner + attention kernel +
 combine when splitting) over resident device inputs.  Cold-HBM timing: the
@@ -275,9 +278,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gqa_b64", choices=WORKLOADS)
+    ap.add_argument("--workload", default="gqa_b64_hm", choices=WORKLOADS,
+                    help="the timed workload (default: B=64 / ctx 1024 with head-major pages; "
+                         "gqa_b64 is the same cache with token-major pages)")
     ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
-    ap.add_argument("--others", default="gqa_b1_split,gqa_b4_split,kv_append_b64",
+    ap.add_argument("--others", default="gqa_b64,gqa_b1_split_hm,gqa_b4_split_hm,kv_append_b64_hm",
                     help="extra workloads measured into 'other_workloads' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
