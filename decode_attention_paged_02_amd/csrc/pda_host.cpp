@@ -239,6 +239,29 @@ int run_order(const pda_shape& s, const Plan& plan, const int32_t* context_lens,
 
 extern "C" {
 
+int pda_check_inputs(const pda_shape* shape, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* positions, int32_t* result,
+                     void* stream) {
+  if (!shape || !result) return PDA_ERR_INVALID_ARG;
+  const pda_shape& s = *shape;
+  if (s.batch < 0 || s.page_size <= 0 || s.max_pages_per_seq <= 0 || s.num_pages <= 0 ||
+      s.q_len < 0)
+    return PDA_ERR_INVALID_ARG;
+  if (s.batch > 0 && (!block_tables || !context_lens)) return PDA_ERR_INVALID_ARG;
+  if ((int64_t)s.max_pages_per_seq * s.page_size > INT32_MAX) return PDA_ERR_INVALID_ARG;
+  pda::CheckArgs a{};
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.positions = s.batch > 0 ? positions : nullptr;
+  a.result = result;
+  a.batch = s.batch;
+  a.max_pages = s.max_pages_per_seq;
+  a.page_size = s.page_size;
+  a.num_pages = s.num_pages;
+  a.s_new = query_len(shape);
+  return pda::launch_check(a, (hipStream_t)stream) == hipSuccess ? PDA_OK : PDA_ERR_HIP;
+}
+
 int pda_version(void) { return 100; }
 
 const char* pda_status_string(int status) {

@@ -154,6 +154,15 @@ struct AppendArgs {
   float k_scale, v_scale;        // E4M3 caches: stored byte = e4m3(x / scale)
 };
 
+// Precondition check of device-resident inputs (see pda_check_inputs).
+struct CheckArgs {
+  const int32_t* block_tables;  // [batch, max_pages]
+  const int32_t* context_lens;  // [batch]
+  const int32_t* positions;     // [batch] or null (append positions)
+  int32_t* result;              // [3]: bad lengths, bad table entries, bad positions
+  int32_t batch, max_pages, page_size, num_pages, s_new;
+};
+
 // Column groups of 16 rows in a workgroup of the MLA matrix-core kernel for
 // `rows` (query token, head) rows per sequence: two (512 threads) once there
 // are more than 16, so that one staged block serves 32 rows.
@@ -176,5 +185,6 @@ hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
 hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int head_dim, int max_splits,
                       hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int src_dtype, int cache_dtype, hipStream_t stream);
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 
 }  // namespace pda

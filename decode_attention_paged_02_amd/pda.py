@@ -52,7 +52,7 @@ class PlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("pda_plan", "pda_workspace_bytes", "paged_decode_attn", "paged_decode_attn_mla",
-           "paged_kv_append", "pda_status_string", "pda_version")
+           "paged_kv_append", "pda_check_inputs", "pda_status_string", "pda_version")
 
 _lib = None
 
@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.paged_decode_attn_mla.restype = i32
     lib.paged_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, sp, vp]
     lib.paged_kv_append.restype = i32
+    lib.pda_check_inputs.argtypes = [sp, vp, vp, vp, vp, vp]
+    lib.pda_check_inputs.restype = i32
     lib.pda_status_string.argtypes = [i32]
     lib.pda_status_string.restype = ctypes.c_char_p
     lib.pda_version.argtypes = []
@@ -318,6 +320,30 @@ def paged_kv_append(k_new, v_new, block_tables, positions, k_cache, v_cache=None
                                 _stream_handle(stream))
     if rc:
         raise PdaError(rc, "paged_kv_append")
+
+
+def check_inputs(block_tables, context_lens, *, page_size: int, num_pages: int,
+                 positions=None, s_new: int = 1, stream=None):
+    """Count violations of the device-resident preconditions (pda_check_inputs):
+    returns (bad lengths, bad table entries, bad append positions).  Synchronizes."""
+    _need(block_tables.dim() == 2 and context_lens.dim() == 1 and
+          context_lens.shape[0] == block_tables.shape[0], "block_tables [B, *], context_lens [B]")
+    _check_device(block_tables, context_lens, positions)
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32 and
+          (positions is None or (positions.dtype == torch.int32 and
+                                 positions.shape == context_lens.shape)),
+          "int32 [B] lengths and positions")
+    B, max_pages = block_tables.shape
+    shape = make_shape(batch=B, num_q_heads=1, num_kv_heads=1, head_dim=8, head_dim_v=8,
+                       page_size=page_size, max_pages_per_seq=max(1, max_pages),
+                       num_pages=num_pages, q_dtype=PDA_F16, kv_dtype=PDA_F16, q_len=s_new)
+    result = torch.zeros(3, dtype=torch.int32, device=block_tables.device)
+    rc = load().pda_check_inputs(ctypes.byref(shape), _ptr(block_tables), _ptr(context_lens),
+                                 _ptr(positions), _ptr(result), _stream_handle(stream))
+    if rc:
+        raise PdaError(rc, "pda_check_inputs")
+    torch.cuda.synchronize(block_tables.device)
+    return tuple(int(x) for x in result.cpu())
 
 
 # ----------------------------------------------------------------------------

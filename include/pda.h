@@ -253,6 +253,29 @@ int paged_kv_append(const void* k_new, const void* v_new, const int32_t* block_t
                     const int32_t* positions, void* k_cache, void* v_cache,
                     const pda_shape* shape, void* stream);
 
+/* Check, on the device, the preconditions the calls above take on trust
+ * (the drill page sec. 4 and 8: lengths bound the pages read, and each
+ * table entry a call follows is a page index into the pool).  Writes three
+ * int32 counts to the DEVICE pointer `result`:
+ *   result[0]  sequences with context_lens[b] outside [0, max_pages_per_seq * P];
+ *   result[1]  table entries outside [0, num_pages) among those a call would
+ *              follow: the first ceil(context_lens[b] / P) of row b (rows of
+ *              sequences counted in result[0] are skipped), and, when
+ *              `positions` is not NULL, the pages an append of q_len tokens at
+ *              positions[b] writes;
+ *   result[2]  sequences (positions not NULL, positions[b] >= 0) with
+ *              positions[b] + q_len > max_pages_per_seq * P.
+ * Reads batch, page_size, max_pages_per_seq, num_pages and q_len (the
+ * append's s_new; 0 means 1) from shape.  `positions` may be NULL.  The
+ * values read are only compared, never followed, so any contents are safe.
+ * One workgroup reads every length and table entry: a debugging aid, not
+ * for the decode loop.  Asynchronous on `stream`; read `result` after
+ * synchronizing.  Errors: PDA_ERR_INVALID_ARG for a NULL shape or result, a
+ * NULL table or length array with batch > 0, or non-positive sizes. */
+int pda_check_inputs(const pda_shape* shape, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* positions, int32_t* result,
+                     void* stream);
+
 /* Static description of a status code. */
 const char* pda_status_string(int status);
 

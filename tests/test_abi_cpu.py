@@ -285,3 +285,16 @@ def test_empty_batch_is_a_no_op():
     fake = ctypes.c_void_p(0x1000)
     assert pda.load().paged_decode_attn(fake, fake, fake, fake, fake, 4, 0.1, 1, fake, None,
                                         ctypes.byref(s), None, 0, None) == 0
+
+
+def test_check_inputs_validation():
+    """pda_check_inputs rejects bad host arguments before any device work."""
+    lib = pda.load()
+    fake = ctypes.c_void_p(0x1000)
+    s = _shape()
+    assert lib.pda_check_inputs(None, fake, fake, None, fake, None) == 1     # no shape
+    assert lib.pda_check_inputs(ctypes.byref(s), fake, fake, None, None, None) == 1  # no result
+    assert lib.pda_check_inputs(ctypes.byref(s), None, fake, None, fake, None) == 1  # no table
+    for kw in (dict(page_size=0), dict(num_pages=0), dict(batch=-1), dict(q_len=-1)):
+        assert lib.pda_check_inputs(ctypes.byref(_shape(**kw)), fake, fake, None, fake,
+                                    None) == 1, kw
