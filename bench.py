@@ -77,15 +77,16 @@ def call_kw(workload):
     return dict(CALL_KW.get(workload[:-3] if workload.endswith("_hm") else workload, {}))
 
 
-def measured_traffic(workload: str, launches_per_step: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when it is missing or was taken on other kernel sources."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other sources of
+    that kernel."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     from decode_attention_paged_02_amd.profiling import source_digest
     t = json.load(open(path))
-    if t.get("source_digest") != source_digest():
+    if t.get("source_digest") != source_digest(kernel):
         return None
     return t.get("bytes_per_launch")
 
@@ -305,10 +306,11 @@ def main():
     case = make_case(args.workload)
     r = run_gpu(case, args.workload, args.steps, args.warmup, args.pools)
     us_step, gbs, kgbs = summarize(r, args.steps)
-    traffic = measured_traffic(args.workload, r["launches"])
+    kernel = "mla_mfma_kernel" if case.mla else "gqa_mfma_kernel"
+    traffic = measured_traffic(args.workload, kernel)
     roof = {"bound": "hbm", "achieved": round(kgbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "mla_mfma_kernel" if case.mla else "gqa_mfma_kernel",
+            "kernel": kernel,
             "launch_us_mean": round(r["kernel_us_mean"], 3),
             "launches_per_step": r["launches"],
             "timing": "HIP events on the launch stream around the timed region / steps",

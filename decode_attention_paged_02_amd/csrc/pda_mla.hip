@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
       }
     tmax = max_x4(tmax);
     if (tmax > m_run + kLazyMax) {  // per head; lanes of one head agree
-      const float alpha = exp2f(m_run - tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - tmax);
       m_run = tmax;
       l_run *= alpha;
 #pragma unroll
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[kb * 4 + i] - m_run);
+        const float p = __builtin_amdgcn_exp2f(s[kb * 4 + i] - m_run);
         l_run += p;
         const __bf16 hi = (__bf16)p;
         const __bf16 lo = (__bf16)(p - (float)hi);

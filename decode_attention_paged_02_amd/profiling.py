@@ -34,12 +34,22 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "decode_attention_paged_02_amd", "csrc")
 
 
-def source_digest() -> str:
-    """Digest of the HIP/C++ sources the counters were taken on."""
+# The sources a kernel is built and launched from: its own file, the shared
+# device and argument headers, and the host code that plans and launches it.
+_COMMON = ["pda_device.h", "pda_internal.h", "pda_host.cpp"]
+KERNEL_SOURCES = {"gqa_mfma_kernel": ["pda_gqa_mfma.hip"] + _COMMON,
+                  "gqa_split_kernel": ["pda_gqa.hip"] + _COMMON,
+                  "mla_mfma_kernel": ["pda_mla.hip"] + _COMMON}
+
+
+def source_digest(kernel: str = None) -> str:
+    """Digest of the HIP/C++ sources the counters were taken on: those of
+    `kernel` (KERNEL_SOURCES), or every source when it is None."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".cpp", ".h")):
-            h.update(open(os.path.join(CSRC, f), "rb").read())
+    files = KERNEL_SOURCES[kernel] if kernel else sorted(
+        f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".h")))
+    for f in files:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -186,7 +196,8 @@ def main(argv=None):
         print(txt)
         return
     r = traffic(a.fetch, a.write, a.kernel, a.copy_kernel, a.copy_bytes)
-    r.update({"workload": a.workload, "source_digest": source_digest(),
+    r.update({"workload": a.workload, "source_digest": source_digest(a.kernel),
+              "source_files": KERNEL_SOURCES[a.kernel],
               "algorithmic_bytes_per_launch": a.bytes_per_launch,
               "fetch_over_algorithmic": r["fetch_bytes"] / a.bytes_per_launch,
               "bytes_per_launch": round(r["fetch_bytes"] + r["write_bytes"]),
