@@ -348,17 +348,28 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
       st[kb] = ((spart[w0][kb][lane] + spart[w0 + 1][kb][lane]) + spart[w0 + 2][kb][lane]) +
                spart[w0 + 3][kb][lane];
     // scale, mask rows past the context; lane holds keys 16 kb + 4 grp + i of head `col`
+    // (a block whose 32 rows every column sees skips the mask: one wave vote)
     float s[8];
     float tmax = -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(rows < kBlock) == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * kb + 4 * grp + i;
-        const float v = key < rows ? st[kb][i] * a.qk_scale_log2 : -INFINITY;
-        s[kb * 4 + i] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int i = 0; i < 4; ++i) {
+          s[kb * 4 + i] = st[kb][i] * a.qk_scale_log2;
+          tmax = fmaxf(tmax, s[kb * 4 + i]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * kb + 4 * grp + i;
+          const float v = key < rows ? st[kb][i] * a.qk_scale_log2 : -INFINITY;
+          s[kb * 4 + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
     tmax = max_x4(tmax);
     if (tmax > m_run + kLazyMax) {  // per head; lanes of one head agree
       const float alpha = __builtin_amdgcn_exp2f(m_run - tmax);
