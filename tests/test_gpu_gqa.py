@@ -230,6 +230,28 @@ def test_ordered_work_with_empty_and_mixed_lengths(variant):
     assert (out.float() - out2.float()).abs().max().item() < 2e-3
 
 
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("schedule", [pda.PDA_SCHEDULE_GRID, pda.PDA_SCHEDULE_BALANCED])
+def test_ordered_batch_beyond_staged_lengths(variant, schedule):
+    """More sequences than the planning pass stages in LDS (8192): it then
+    reads each length from memory whenever it needs it.  9000 short and a few
+    long sequences (MQA, G = 8), every row checked."""
+    rng = np.random.default_rng(31)
+    lens = rng.integers(0, 49, 9000)
+    lens[:6] = [0, 1, 3000, 17, 2049, 4096]
+    lens[-3:] = [5000, 0, 33]
+    case = _gqa(77 + schedule, len(lens), 8, 1, 64, 16, lens.tolist(), extra_pages=2)
+    say("ordered large batch", variant, schedule)
+    dev = pda.to_device(case)
+    shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                          split_min_tokens=1024, schedule=schedule)
+    assert pda.plan(shape, num_splits=4).ordered == 1
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, dev, num_splits=4, split_min_tokens=1024, schedule=schedule,
+                            variant=VARIANTS[variant])
+    check(case, out, lse, ref_o, ref_l, label="large batch %d" % schedule)
+
+
 def test_graph_capture_and_replay():
     """The entry point is capture-safe (no allocation, no memset, no host sync):
     a call with splits, the combine and the ordering pass is captured into a
