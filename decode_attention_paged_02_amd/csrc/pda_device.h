@@ -74,6 +74,31 @@ __device__ __forceinline__ WorkUnit load_unit(const int32_t* units, int idx) {
   return WorkUnit{w[0], w[1], w[2], w[3]};
 }
 
+// Workgroup index i of `groups` x `tiles` workgroups -> (group, tile), where
+// a group is one (sequence or unit, KV head) whose K/V rows each of its
+// `tiles` head tiles reads.  The tiles of a group are placed 8 indices apart:
+// workgroups are dealt to the 8 XCDs in index order, so they run on one XCD,
+// about together, and the tiles after the first find the rows in that XCD's
+// L2.  A last set of fewer than 8 groups keeps its tiles adjacent.  With one
+// tile this is the identity.
+__device__ __forceinline__ void group_tile(int i, int groups, int tiles, int& g, int& t) {
+  if (tiles == 1) {
+    g = i;
+    t = 0;
+    return;
+  }
+  const int g8 = groups & ~7;
+  if (i < g8 * tiles) {
+    const int blk = i / (8 * tiles), rem = i - blk * 8 * tiles;
+    t = rem >> 3;
+    g = blk * 8 + (rem & 7);
+  } else {
+    const int j = i - g8 * tiles;
+    g = g8 + j / tiles;
+    t = j - (j / tiles) * tiles;
+  }
+}
+
 // Cache policy of the K/V stream loads (the buffer instruction's cache-policy
 // field; 2 marks them non-temporal).
 #ifndef PDA_KV_LOAD_POLICY

@@ -112,19 +112,22 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
   const bool ordered = a.units != nullptr;
   int tile, kvh, b, split, ut0 = 0, ut1 = 0;
   if (ordered) {
-    const int nhu = a.num_kv_heads * a.head_tiles;
-    const int hu = blockIdx.x % nhu;
-    const WorkUnit w = load_unit(a.units, blockIdx.x / nhu);
+    int g;
+    group_tile(blockIdx.x, gridDim.x / a.head_tiles, a.head_tiles, g, tile);
+    g = __builtin_amdgcn_readfirstlane(g);  // (uniform: scalar registers)
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    const WorkUnit w = load_unit(a.units, g / a.num_kv_heads);
     if (w.b < 0) return;
     b = w.b;
     split = w.split;
     ut0 = w.t0;
     ut1 = w.t1;
-    kvh = hu / a.head_tiles;
-    tile = hu % a.head_tiles;
+    kvh = g % a.num_kv_heads;
   } else {
-    const int bk = blockIdx.x / a.head_tiles;
-    tile = blockIdx.x % a.head_tiles;
+    int bk;
+    group_tile(blockIdx.x, gridDim.x / a.head_tiles, a.head_tiles, bk, tile);
+    bk = __builtin_amdgcn_readfirstlane(bk);
+    tile = __builtin_amdgcn_readfirstlane(tile);
     kvh = bk % a.num_kv_heads;
     b = bk / a.num_kv_heads;
     split = blockIdx.y;

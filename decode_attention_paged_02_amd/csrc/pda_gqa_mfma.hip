@@ -151,7 +151,9 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, f32x4 c
 // argument preloading (gfx950) they arrive in scalar registers when the wave
 // starts, so the length, table and q requests go out without waiting for a
 // kernel-argument load.  GqaArgs carries everything (the same values too).
-template <class QT, class KT, int D>
+// CT column tiles of 16 rows per workgroup: one, or two for groups of more
+// than 16 rows (d <= 128), so that one load of a K/V tile serves 32 rows.
+template <class QT, class KT, int D, int CT>
 __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     const int32_t* context_lens, const int32_t* block_tables, const void* q, int32_t head_tiles,
     int32_t num_kv_heads, int32_t group, int32_t q_len, int32_t max_pages, int32_t log2_page,
@@ -172,6 +174,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   constexpr int kLdsB = kSeparateMerge ? kMWaves * kTileB + kMergeB
                         : (kMWaves * kTileB > kMergeB ? kMWaves * kTileB : kMergeB);
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+  static_assert(CT == 1 || (CT == 2 && D <= 128), "column tiles");
+  constexpr int kRowsWG = kMHeads * CT;         // (query token, head) rows of a workgroup
   static_assert(kFp8 || std::is_same<QT, KT>::value, "q / cache types");
 
   __shared__ __attribute__((aligned(16))) char lds[kLdsB];
@@ -187,29 +191,32 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   int tile, kvh, b, split, ut0 = 0, ut1 = 0;
   if (ordered) {
     // ordered: the unit list gives (sequence, split, token range) longest
-    // first; the (KV head, head tile) pairs of a unit are consecutive
-    // workgroups
-    const int nhu = num_kv_heads * head_tiles;
-    const int hu = blockIdx.x % nhu;
-    const WorkUnit w = load_unit(units, blockIdx.x / nhu);
+    // first; the (unit, KV head) groups follow it, each with its head tiles
+    // (group_tile)
+    int g;
+    group_tile(blockIdx.x, gridDim.x / head_tiles, head_tiles, g, tile);
+    g = __builtin_amdgcn_readfirstlane(g);  // (uniform: scalar registers)
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    const WorkUnit w = load_unit(units, g / num_kv_heads);
     if (w.b < 0) return;
     b = w.b;
     split = w.split;
     ut0 = w.t0;
     ut1 = w.t1;
-    kvh = hu / head_tiles;
-    tile = hu % head_tiles;
+    kvh = g % num_kv_heads;
   } else {
-    const int bk = blockIdx.x / head_tiles;
-    tile = blockIdx.x % head_tiles;
+    int bk;
+    group_tile(blockIdx.x, gridDim.x / head_tiles, head_tiles, bk, tile);
+    bk = __builtin_amdgcn_readfirstlane(bk);  // (uniform: scalar registers)
+    tile = __builtin_amdgcn_readfirstlane(tile);
     kvh = bk % num_kv_heads;
     b = bk / num_kv_heads;
     split = blockIdx.y;
   }
 
   const int num_q_heads = group * num_kv_heads;
-  const int g0 = tile * kMHeads;                   // the tile's first row
-  const int gvalid = min(kMHeads, q_len * group - g0);
+  const int g0 = tile * kRowsWG;                   // the tile's first row
+  const int gvalid = min(kRowsWG, q_len * group - g0);
   const int log2P = log2_page;
   const int32_t* table = block_tables + (int64_t)b * max_pages;
   const int t0_hint = ordered ? ut0 : max_splits > 1 ? split * pages_per_split << log2P : 0;
@@ -233,25 +240,28 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   int vtbl = load_table(0);
   int n = load_uniform(context_lens + b);
 
-  // Q^T as the B operand of the QK MFMAs: lane (col, grp) holds
-  // q[row col][32 j + 8 grp .. +8] for MFMA j; rows past the group are zero.
-  // Row g0 + col is query token qi of head g of the group.
-  int qi = 0;
-  u32x4 qb[NQK];
-  {
-    const bool hv = col < gvalid;
-    const int r = g0 + (hv ? col : 0);
+  // Q^T as the B operand of the QK MFMAs: lane (col, grp) holds, for column
+  // tile c, q[row 16 c + col][32 j + 8 grp .. +8] for MFMA j; rows past the
+  // group are zero.  Row g0 + 16 c + col is query token qi[c] of head g of
+  // the group.
+  int qi[CT];
+  u32x4 qb[CT][NQK];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const bool hv = 16 * c + col < gvalid;
+    const int r = g0 + (hv ? 16 * c + col : 0);
     int g = r;
+    qi[c] = 0;
     if (q_len > 1) {
-      qi = r / group;
-      g = r - qi * group;
+      qi[c] = r / group;
+      g = r - qi[c] * group;
     }
     const char* qrow =
-        (const char*)q + ((((int64_t)b * q_len + qi) * num_q_heads + kvh * group + g) * D) * 2;
+        (const char*)q + ((((int64_t)b * q_len + qi[c]) * num_q_heads + kvh * group + g) * D) * 2;
 #pragma unroll
     for (int j = 0; j < NQK; ++j) {
       const u32x4 w = *(const u32x4*)(qrow + (32 * j + 8 * grp) * 2);
-      qb[j] = hv ? w : u32x4{0u, 0u, 0u, 0u};
+      qb[c][j] = hv ? w : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -265,8 +275,10 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
     if (split >= nsplit) return;
   }
-  // end of the tokens this lane's query token may see (t1 without a mask)
-  const int lim = min(t1, a.causal ? n - (q_len - 1 - qi) : n);
+  // end of the tokens this lane's query tokens may see (t1 without a mask)
+  int lim[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) lim[c] = min(t1, a.causal ? n - (q_len - 1 - qi[c]) : n);
 
   const int tok_bytes = a.tok_stride * ESZ;
   // load j of a tile: token 4 grp + j, piece col of the row (relative to the
@@ -274,10 +286,17 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   const int off0 = (4 * grp) * tok_bytes + (col * NE) * ESZ;
   const int64_t head_elem = (int64_t)kvh * a.head_stride;
 
-  f32x4 acc[NE];  // O^T: rows (4 grp + i) * NE + e of the value, column = head col
+  // O^T of column tile c: rows (4 grp + i) * NE + e of the value, column =
+  // row 16 c + col of the workgroup
+  f32x4 acc[CT][NE];
+  float m_run[CT], l_run[CT];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kMaxStart, l_run = 0.f;
+  for (int c = 0; c < CT; ++c) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[c] = kMaxStart;
+    l_run[c] = 0.f;
+  }
   const float pinf = opaque_inf();
 
   const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
@@ -304,66 +323,76 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
         store_piece<PW>(dst, kf[j]);
       }
     }
-    // ---- S^T = K Q^T: lane reads token col, elements 32 j + 8 grp .. +8
-    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+    // ---- S^T = K Q^T: lane reads token col, elements 32 j + 8 grp .. +8 (one
+    // K operand for every column tile)
+    f32x4 st[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) st[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NQK; ++j) {
       const u32x4 kk = *(const u32x4*)(ktile + col * kRowB + (32 * j + 8 * grp) * 2);
-      st = mfma_qk<QT>(kk, qb[j], st);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) st[c] = mfma_qk<QT>(kk, qb[c][j], st[c]);
     }
-    // ---- online softmax (log2 domain, lazily moved reference max); this lane
-    // holds tokens 4 grp + i of row col
-    const int rl = min(rows, lim - tok);
-    float s[4];
+    // ---- online softmax per column tile (log2 domain, lazily moved
+    // reference max); this lane holds tokens 4 grp + i of row 16 c + col
+    u32x2 pb[CT], pb_lo[CT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s[i] = fminf(st[i] * a.qk_scale_log2, 4 * grp + i < rl ? INFINITY : -INFINITY);
-    float tmax = max2(max2(s[0], s[1], pinf), max2(s[2], s[3], pinf), pinf);
-    {
-      float x, y;
-      swap16(tmax, tmax, x, y);
-      tmax = max2(x, y, pinf);
-      swap32(tmax, tmax, x, y);
-      tmax = max2(x, y, pinf);
-    }
-    const bool move = tmax > m_run + kLazyMax;
-    const float m_new = move ? tmax : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float p[4];
+    for (int c = 0; c < CT; ++c) {
+      const int rl = min(rows, lim[c] - tok);
+      float s[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
-    u32x2 pb, pb_lo;
-    if constexpr (!kBf16) {
-      // binary16 probabilities (round to nearest even); the denominator sums
-      // the same rounded values
-      const f16x2 p01 = __builtin_convertvector((f32x2{p[0], p[1]}), f16x2);
-      const f16x2 p23 = __builtin_convertvector((f32x2{p[2], p[3]}), f16x2);
-      const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-      l_run = __builtin_amdgcn_fdot2(p23, one, __builtin_amdgcn_fdot2(p01, one, l_run * alpha, false),
-                                     false);
-      pb = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-    } else {
-      // p = p_hi + p_lo, two bfloat16 terms (bfloat16 alone leaves 2^-9
-      // relative error per weight)
-      uint16_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 h = (__bf16)p[i];
-        const __bf16 l = (__bf16)(p[i] - (float)h);
-        hi[i] = __builtin_bit_cast(uint16_t, h);
-        lo[i] = __builtin_bit_cast(uint16_t, l);
+      for (int i = 0; i < 4; ++i)
+        s[i] = fminf(st[c][i] * a.qk_scale_log2, 4 * grp + i < rl ? INFINITY : -INFINITY);
+      float tmax = max2(max2(s[0], s[1], pinf), max2(s[2], s[3], pinf), pinf);
+      {
+        float x, y;
+        swap16(tmax, tmax, x, y);
+        tmax = max2(x, y, pinf);
+        swap32(tmax, tmax, x, y);
+        tmax = max2(x, y, pinf);
       }
-      l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-      pb = u32x2{(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
-      pb_lo = u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
-    }
-    if (__builtin_amdgcn_read_exec() & __ballot(move)) {
+      const bool move = tmax > m_run[c] + kLazyMax;
+      const float m_new = move ? tmax : m_run[c];
+      const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_new);
+      m_run[c] = m_new;
+      float p[4];
 #pragma unroll
-      for (int e = 0; e < NE; ++e) acc[e] *= alpha;
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
+      if constexpr (!kBf16) {
+        // binary16 probabilities (round to nearest even); the denominator sums
+        // the same rounded values
+        const f16x2 p01 = __builtin_convertvector((f32x2{p[0], p[1]}), f16x2);
+        const f16x2 p23 = __builtin_convertvector((f32x2{p[2], p[3]}), f16x2);
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        l_run[c] = __builtin_amdgcn_fdot2(
+            p23, one, __builtin_amdgcn_fdot2(p01, one, l_run[c] * alpha, false), false);
+        pb[c] = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+      } else {
+        // p = p_hi + p_lo, two bfloat16 terms (bfloat16 alone leaves 2^-9
+        // relative error per weight)
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 h = (__bf16)p[i];
+          const __bf16 l = (__bf16)(p[i] - (float)h);
+          hi[i] = __builtin_bit_cast(uint16_t, h);
+          lo[i] = __builtin_bit_cast(uint16_t, l);
+        }
+        l_run[c] = l_run[c] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        pb[c] = u32x2{(uint32_t)hi[0] | ((uint32_t)hi[1] << 16),
+                      (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
+        pb_lo[c] = u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16),
+                         (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
+      }
+      if (__builtin_amdgcn_read_exec() & __ballot(move)) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[c][e] *= alpha;
+      }
     }
     // ---- O^T += V^T P^T.  A operand of MFMA e: V^T row col (value element
-    // col NE + e) over tokens 4 grp + 0..3 = element e of the four loads.
+    // col NE + e) over tokens 4 grp + 0..3 = element e of the four loads (one
+    // V operand for every column tile).
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       u32x2 va;
@@ -380,8 +409,11 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
         va = u32x2{__builtin_amdgcn_perm(vf[1].w[w], vf[0].w[w], sel),
                    __builtin_amdgcn_perm(vf[3].w[w], vf[2].w[w], sel)};
       }
-      acc[e] = mfma_pv<QT>(va, pb, acc[e]);
-      if constexpr (kBf16) acc[e] = mfma_pv<QT>(va, pb_lo, acc[e]);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        acc[c][e] = mfma_pv<QT>(va, pb[c], acc[c][e]);
+        if constexpr (kBf16) acc[c][e] = mfma_pv<QT>(va, pb_lo[c], acc[c][e]);
+      }
     }
   };
 
@@ -442,74 +474,80 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     if (sbase < ns_wave) vtbl = load_table(sbase);
   }
 
-  // ---- merge the four waves (the split-combine algebra) through LDS.  When
-  // the merge area overlays the K tiles, every wave must be done with them.
-  l_run = pair_sum<5>(pair_sum<4>(l_run));
-  if constexpr (!kSeparateMerge) __syncthreads();
+  // ---- merge the four waves (the split-combine algebra) through LDS, one
+  // column tile after the other through the same 16-row area.  When the
+  // merge area overlays the K tiles, every wave must be done with them; a
+  // second column tile waits for the readers of the first.
   float* acc_sh = (float*)(lds + kMergeOff);  // [wave][head][kAccStride]
-  if (grp == 0) {
-    m_sh[wave][col] = m_run;
-    l_sh[wave][col] = l_run;
-  }
-  if (col < gvalid) {  // only the rows of the group
-    float* dst = acc_sh + (wave * kMHeads + col) * kAccStride;
+  constexpr int kQ = D / 4;                   // four-value items per row
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int c = 0; c < CT; ++c) {
+    const float l_c = pair_sum<5>(pair_sum<4>(l_run[c]));
+    if (c > 0 || !kSeparateMerge) __syncthreads();
+    const int gv = min(kMHeads, gvalid - 16 * c);  // valid rows of this column tile
+    if (grp == 0) {
+      m_sh[wave][col] = m_run[c];
+      l_sh[wave][col] = l_c;
+    }
+    if (col < gv) {  // only the rows of the group
+      float* dst = acc_sh + (wave * kMHeads + col) * kAccStride;
 #pragma unroll
-      for (int e = 0; e < NE; e += 4)
-        *(f32x4*)(dst + (4 * grp + i) * NE + e) =
-            f32x4{acc[e][i], acc[e + 1][i], acc[e + 2][i], acc[e + 3][i]};
-  }
-  __syncthreads();
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < NE; e += 4)
+          *(f32x4*)(dst + (4 * grp + i) * NE + e) =
+              f32x4{acc[c][e][i], acc[c][e + 1][i], acc[c][e + 2][i], acc[c][e + 3][i]};
+    }
+    __syncthreads();
 
-  // Work items: four consecutive values of one valid row, spread over all
-  // threads; each item issues its LDS reads (the four waves' max, sum and
-  // values) before any arithmetic: weights exp2(m_w - max), one reciprocal.
-  // (A row no wave saw a token of keeps max kMaxStart and sum 0: out 0.)
-  constexpr int kQ = D / 4;  // four-value items per head
-  for (int it = threadIdx.x; it < gvalid * kQ; it += kMWaves * 64) {
-    const int g = it / kQ, d0 = 4 * (it % kQ);
-    float mw[kMWaves], lw[kMWaves];
-    f32x4 xw[kMWaves];
+    // Work items: four consecutive values of one valid row, spread over all
+    // threads; each item issues its LDS reads (the four waves' max, sum and
+    // values) before any arithmetic: weights exp2(m_w - max), one reciprocal.
+    // (A row no wave saw a token of keeps max kMaxStart and sum 0: out 0.)
+    for (int it = threadIdx.x; it < gv * kQ; it += kMWaves * 64) {
+      const int g = it / kQ, d0 = 4 * (it % kQ);
+      float mw[kMWaves], lw[kMWaves];
+      f32x4 xw[kMWaves];
 #pragma unroll
-    for (int w = 0; w < kMWaves; ++w) {
-      mw[w] = m_sh[w][g];
-      lw[w] = l_sh[w][g];
-      xw[w] = *(const f32x4*)(acc_sh + (w * kMHeads + g) * kAccStride + d0);
-    }
-    float mx = mw[0];
+      for (int w = 0; w < kMWaves; ++w) {
+        mw[w] = m_sh[w][g];
+        lw[w] = l_sh[w][g];
+        xw[w] = *(const f32x4*)(acc_sh + (w * kMHeads + g) * kAccStride + d0);
+      }
+      float mx = mw[0];
 #pragma unroll
-    for (int w = 1; w < kMWaves; ++w) mx = fmaxf(mx, mw[w]);
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
+      for (int w = 1; w < kMWaves; ++w) mx = fmaxf(mx, mw[w]);
+      f32x4 num = {0.f, 0.f, 0.f, 0.f};
+      float den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kMWaves; ++w) {
-      const float wt = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mx);
-      den += wt * lw[w];
-      num += wt * xw[w];
-    }
-    const float inv = den > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(den) : 0.f;
-    const float o[4] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv};
-    // row g0 + g of the group: query token i, head h; out row (b, i, h),
-    // lse [B, Hq, q_len]
-    int i = 0, gh = g0 + g;
-    if (q_len > 1) {
-      i = gh / group;
-      gh -= i * group;
-    }
-    const int h = kvh * group + gh;
-    const int64_t row = ((int64_t)b * q_len + i) * num_q_heads + h;
-    if (nsplit == 1) {
-      store_row<QT, 4>(a.out, row * D + d0, o);
-      if (d0 == 0 && a.lse)
-        a.lse[((int64_t)b * num_q_heads + h) * q_len + i] =
-            den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
-    } else {
-      float* po = a.part_o + (row * a.split.max_splits + split) * D + d0;
-      *(f32x4*)po = f32x4{o[0], o[1], o[2], o[3]};
-      if (d0 == 0)
-        a.part_lse[row * a.split.max_splits + split] =
-            den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+      for (int w = 0; w < kMWaves; ++w) {
+        const float wt = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mx);
+        den += wt * lw[w];
+        num += wt * xw[w];
+      }
+      const float inv = den > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(den) : 0.f;
+      const float o[4] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv};
+      // row g0 + 16 c + g of the group: query token i, head h; out row
+      // (b, i, h), lse [B, Hq, q_len]
+      int i = 0, gh = g0 + 16 * c + g;
+      if (q_len > 1) {
+        i = gh / group;
+        gh -= i * group;
+      }
+      const int h = kvh * group + gh;
+      const int64_t row = ((int64_t)b * q_len + i) * num_q_heads + h;
+      if (nsplit == 1) {
+        store_row<QT, 4>(a.out, row * D + d0, o);
+        if (d0 == 0 && a.lse)
+          a.lse[((int64_t)b * num_q_heads + h) * q_len + i] =
+              den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+      } else {
+        float* po = a.part_o + (row * a.split.max_splits + split) * D + d0;
+        *(f32x4*)po = f32x4{o[0], o[1], o[2], o[3]};
+        if (d0 == 0)
+          a.part_lse[row * a.split.max_splits + split] =
+              den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+      }
     }
   }
 }
@@ -520,13 +558,24 @@ hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStr
   const unsigned nhu = (unsigned)(a.num_kv_heads * a.head_tiles);
   dim3 grid(a.units ? nhu * (unsigned)a.unit_count : units, a.units ? 1u : (unsigned)max_splits);
   dim3 block(kMWaves * 64);
+  const bool two = gqa_mfma_col_tiles(a.q_len * a.group, head_dim) == 2;
   switch (head_dim) {
 #define PDA_MFMA_ARGS                                                                        \
   a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.q_len,        \
       a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a.units, a
-    case 64: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64>), grid, block, 0, s, PDA_MFMA_ARGS); break;
-    case 128: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128>), grid, block, 0, s, PDA_MFMA_ARGS); break;
-    case 256: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 256>), grid, block, 0, s, PDA_MFMA_ARGS); break;
+    case 64:
+      if (two)
+        hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64, 2>), grid, block, 0, s, PDA_MFMA_ARGS);
+      else
+        hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64, 1>), grid, block, 0, s, PDA_MFMA_ARGS);
+      break;
+    case 128:
+      if (two)
+        hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128, 2>), grid, block, 0, s, PDA_MFMA_ARGS);
+      else
+        hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128, 1>), grid, block, 0, s, PDA_MFMA_ARGS);
+      break;
+    case 256: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 256, 1>), grid, block, 0, s, PDA_MFMA_ARGS); break;
 #undef PDA_MFMA_ARGS
     default: return hipErrorInvalidValue;
   }

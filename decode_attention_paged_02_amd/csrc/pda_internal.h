@@ -163,6 +163,13 @@ struct CheckArgs {
   int32_t batch, max_pages, page_size, num_pages, s_new;
 };
 
+// Column tiles of 16 rows in a workgroup of the GQA matrix-core kernel for
+// `rows` (query token, head) rows per KV group: two when there are more than
+// 16 (and d <= 128, for registers), so that one K/V load serves 32 rows.
+inline int gqa_mfma_col_tiles(int rows, int head_dim) {
+  return rows > 16 && head_dim <= 128 ? 2 : 1;
+}
+
 // Column groups of 16 rows in a workgroup of the MLA matrix-core kernel for
 // `rows` (query token, head) rows per sequence: two (512 threads) once there
 // are more than 16, so that one staged block serves 32 rows.

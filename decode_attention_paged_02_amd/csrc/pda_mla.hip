@@ -230,16 +230,20 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   const bool ordered = a.units != nullptr;
   int tile, b, split, ut0 = 0, ut1 = 0;
   if (ordered) {
-    tile = blockIdx.x % a.head_tiles;
-    const WorkUnit w = load_unit(a.units, blockIdx.x / a.head_tiles);
+    int u;  // head tiles of one unit on one XCD (group_tile)
+    group_tile(blockIdx.x, gridDim.x / a.head_tiles, a.head_tiles, u, tile);
+    u = __builtin_amdgcn_readfirstlane(u);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    const WorkUnit w = load_unit(a.units, u);
     if (w.b < 0) return;
     b = w.b;
     split = w.split;
     ut0 = w.t0;
     ut1 = w.t1;
   } else {
-    tile = blockIdx.x % a.head_tiles;
-    b = blockIdx.x / a.head_tiles;
+    group_tile(blockIdx.x, gridDim.x / a.head_tiles, a.head_tiles, b, tile);
+    b = __builtin_amdgcn_readfirstlane(b);
+    tile = __builtin_amdgcn_readfirstlane(tile);
     split = blockIdx.y;
   }
   // One batch of kernel-argument loads; then the sequence length, the
@@ -491,16 +495,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
   const bool ordered = a.units != nullptr;
   int tile, b, split, ut0 = 0, ut1 = 0;
   if (ordered) {
-    tile = blockIdx.x % a.head_tiles;
-    const WorkUnit w = load_unit(a.units, blockIdx.x / a.head_tiles);
+    int u;  // head tiles of one unit on one XCD (group_tile)
+    group_tile(blockIdx.x, gridDim.x / a.head_tiles, a.head_tiles, u, tile);
+    u = __builtin_amdgcn_readfirstlane(u);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    const WorkUnit w = load_unit(a.units, u);
     if (w.b < 0) return;
     b = w.b;
     split = w.split;
     ut0 = w.t0;
     ut1 = w.t1;
   } else {
-    tile = blockIdx.x % a.head_tiles;
-    b = blockIdx.x / a.head_tiles;
+    group_tile(blockIdx.x, gridDim.x / a.head_tiles, a.head_tiles, b, tile);
+    b = __builtin_amdgcn_readfirstlane(b);
+    tile = __builtin_amdgcn_readfirstlane(tile);
     split = blockIdx.y;
   }
   // One batch of kernel-argument loads; then the sequence length, the

@@ -104,6 +104,22 @@ def test_group_sizes(Hq, Hkv, variant):
     check(case, out, lse, ref_o, ref_l, label="Hq=%d Hkv=%d" % (Hq, Hkv))
 
 
+@pytest.mark.parametrize("Hq,Hkv,B", [(32, 1, 3), (64, 1, 9), (40, 1, 9), (64, 2, 11)])
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("thr", [0, 100])
+def test_large_groups_several_head_tiles(Hq, Hkv, B, variant, thr, ):
+    """Groups beyond one head tile (G = 20 to 64): the tiles of one (sequence,
+    KV head) run as separate workgroups placed 8 apart in the grid; eight or
+    more groups take the interleaved placement, the rest the adjacent one.
+    thr > 0 orders the work (unit list)."""
+    lens = list(np.random.default_rng(Hq + B).integers(1, 600, B))
+    case = _gqa(Hq * 10 + B, B, Hq, Hkv, 128, 16, lens, extra_pages=2)
+    say("large groups", Hq, Hkv, B, variant, thr)
+    out, lse = pda.run_case(case, num_splits=3, split_min_tokens=thr, variant=VARIANTS[variant])
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label="Hq=%d Hkv=%d B=%d thr=%d" % (Hq, Hkv, B, thr))
+
+
 @pytest.mark.parametrize("d,P,dt", [(64, 16, "f16"), (64, 32, "bf16"), (256, 16, "f16"),
                                     (128, 64, "f16"), (64, 16, "f32"), (128, 32, "f32"),
                                     (256, 16, "bf16")])
