@@ -41,7 +41,7 @@ def make_case(name):
     cache with head-major pages [pages, Hkv, P, d]."""
     from decode_attention_paged_02_amd import workloads as W
     hm = 0
-    if name.endswith("_hm") and name.startswith(("gqa", "ragged")):
+    if name.endswith("_hm") and name.startswith(("gqa", "ragged", "mqa")):
         name, hm = name[:-3], 1
     if name == "gqa_b64":
         return W.gqa_batch64(kv_layout=hm)
@@ -55,6 +55,8 @@ def make_case(name):
         return W.ragged_fp8(kv_layout=hm)
     if name == "gqa_b64_q2":
         return W.gqa_batch64_mtp(2, kv_layout=hm)
+    if name == "mqa_b64_8k":
+        return W.mqa_batch64_8k(kv_layout=hm)
     if name == "mla_b16_q2":
         return W.mla_b16_mtp(2)
     if name == "mla_b16_fp8":
@@ -68,7 +70,7 @@ CALL_KW = {"ragged_fp8": dict(num_splits=8, split_min_tokens=4096),
            # the balanced schedule (device-side chunking) on the same batch
            "ragged_fp8_balanced": dict(num_splits=8, schedule=1)}
 GQA_WORKLOADS = ["gqa_b64", "gqa_b1_split", "gqa_b4_split", "ragged_fp8", "ragged_fp8_balanced",
-                 "gqa_b64_q2"]
+                 "gqa_b64_q2", "mqa_b64_8k"]
 WORKLOADS = GQA_WORKLOADS + [w + "_hm" for w in GQA_WORKLOADS] + [
     "mla_b16", "mla_b16_q2", "mla_b16_fp8", "mla_b16_320"]
 
@@ -283,7 +285,8 @@ def main():
                     help="the timed workload (default: B=64 / ctx 1024 with head-major pages; "
                          "gqa_b64 is the same cache with token-major pages)")
     ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
-    ap.add_argument("--others", default="gqa_b64,gqa_b1_split_hm,gqa_b4_split_hm,kv_append_b64_hm",
+    ap.add_argument("--others",
+                    default="gqa_b64,gqa_b1_split_hm,gqa_b4_split_hm,mqa_b64_8k_hm,kv_append_b64_hm",
                     help="extra workloads measured into 'other_workloads' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)

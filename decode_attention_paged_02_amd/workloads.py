@@ -293,6 +293,15 @@ def gqa_batch64_mtp(q_len: int = 2, kv_layout: int = 0) -> PagedCase:
                     name="gqa_b64_ctx1024_fp16_q%d" % q_len + _layout_tag(kv_layout))
 
 
+def mqa_batch64_8k(kv_layout: int = 0) -> PagedCase:
+    """MQA (one KV head for 32 query heads, G = 32): B=64, d=128, ctx 8192, P=16,
+    fp16 -- the same 268,435,456 KV bytes per step as the B=64 GQA step."""
+    return make_gqa(batch=64, num_q_heads=32, num_kv_heads=1, head_dim=128, page_size=16,
+                    context_lens=[8192] * 64, q_dtype="f16", kv_dtype="f16", seed=1105,
+                    poison=False, kv_layout=kv_layout,
+                    name="mqa_b64_ctx8192_fp16" + _layout_tag(kv_layout))
+
+
 def gqa_long(batch: int, kv_layout: int = 0) -> PagedCase:
     """B in {1, 4}, Hq=32, Hkv=8, d=128, ctx 32768, P=16, fp16 (split-KV)."""
     return make_gqa(batch=batch, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
