@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 
 #include "pda_internal.h"
@@ -13,16 +14,20 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices] = {0};
+// (calls from several host threads may fill an entry at once, with the same value)
+std::atomic<int> g_cu_count[kMaxDevices];
 
 // Compute units of the current device (cached per device id); 0 on failure.
 int device_cus() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < kMaxDevices && g_cu_count[dev] > 0) return g_cu_count[dev];
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < kMaxDevices) g_cu_count[dev] = n;
+  if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
