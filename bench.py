@@ -141,7 +141,20 @@ def run_gpu(case, workload, steps, warmup, pools):
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    return dict(total_ms=total_ms, kernel_us_mean=total_ms * 1000.0 / steps,
+    # then the distribution of single steps (each between its own events)
+    n_dist = min(steps, 100)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_dist)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        step(steps + i)
+        e1.record()
+    torch.cuda.synchronize()
+    each = sorted(e0.elapsed_time(e1) * 1000.0 for e0, e1 in ev)
+    dist = {"steps": n_dist, "median": round(each[n_dist // 2], 3), "min": round(each[0], 3),
+            "p90": round(each[min(n_dist - 1, (9 * n_dist) // 10)], 3)}
+    return dict(total_ms=total_ms, kernel_us_mean=total_ms * 1000.0 / steps, step_us=dist,
+                overhead_bytes=A.case_overhead_bytes(case, plan.max_splits),
                 kv_bytes=nbytes, n_pools=len(caches), max_splits=plan.max_splits,
                 pages_per_split=plan.pages_per_split, workgroups=plan.workgroups,
                 launches=(1 if plan.max_splits == 1 else 2) + (1 if plan.ordered else 0))
@@ -317,7 +330,8 @@ def main():
             "launch_us_mean": round(r["kernel_us_mean"], 3),
             "launches_per_step": r["launches"],
             "timing": "HIP events on the launch stream around the timed region / steps",
-            "algorithmic_bytes_per_launch": r["kv_bytes"]}
+            "algorithmic_bytes_per_launch": r["kv_bytes"],
+            "step_us": r["step_us"], "overhead_bytes_per_step": r["overhead_bytes"]}
     others = {}
     for w in [x for x in args.others.split(",") if x and x not in (args.workload, "none")]:
         _log("other workload", w)

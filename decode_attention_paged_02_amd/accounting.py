@@ -57,3 +57,20 @@ def case_kv_bytes(case) -> int:
 def case_flops(case) -> int:
     return step_flops(case.context_lens, num_q_heads=case.num_q_heads,
                       head_dim=case.head_dim, head_dim_v=case.head_dim_v)
+
+
+def case_overhead_bytes(case, max_splits: int) -> dict:
+    """Bytes a step moves besides the algorithmic KV bytes: q read, out and
+    LSE written, block-table entries and lengths read, and (with splits) the
+    fp32 partial outputs and LSEs written and read back by the combine."""
+    eb_q = ELEM_BYTES[case.q_dtype]
+    rows = case.batch * case.q_len * case.num_q_heads
+    pages = int(((np.asarray(case.context_lens, dtype=np.int64) + case.page_size - 1)
+                 // case.page_size).sum())
+    r = {"q": rows * case.head_dim * eb_q,
+         "out_and_lse": rows * (case.head_dim_v * eb_q + 4),
+         "tables_and_lengths": pages * 4 + case.batch * 4,
+         "split_partials": 0}
+    if max_splits > 1:
+        r["split_partials"] = 2 * rows * max_splits * (case.head_dim_v + 1) * 4
+    return r

@@ -59,3 +59,16 @@ def test_named_workload_bytes():
     lens = W.ragged_fp8_lens()
     assert lens[0] == 1 and lens[1] == 16384 and lens[2] == 17
     assert lens.min() >= 1 and lens.max() <= 16384
+
+
+def test_overhead_bytes_of_the_long_context_step():
+    """B=1, Hq=32, d=128, ctx 32768, P=16, fp16, 64 splits: q 32*128*2 B, out
+    32*(128*2 + 4) B with the LSE, 2048 table entries + one length, and the
+    fp32 partials written and read back: 2 * 32 * 64 * (128 + 1) * 4 B."""
+    from decode_attention_paged_02_amd import accounting as A
+    from decode_attention_paged_02_amd import workloads as W
+    case = W.gqa_long(1)
+    r = A.case_overhead_bytes(case, 64)
+    assert r == {"q": 8192, "out_and_lse": 8320, "tables_and_lengths": 2048 * 4 + 4,
+                 "split_partials": 2 * 32 * 64 * 129 * 4}
+    assert A.case_overhead_bytes(case, 1)["split_partials"] == 0
