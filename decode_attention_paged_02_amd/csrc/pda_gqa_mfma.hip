@@ -558,7 +558,8 @@ hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStr
   const unsigned nhu = (unsigned)(a.num_kv_heads * a.head_tiles);
   dim3 grid(a.units ? nhu * (unsigned)a.unit_count : units, a.units ? 1u : (unsigned)max_splits);
   dim3 block(kMWaves * 64);
-  const bool two = gqa_mfma_col_tiles(a.q_len * a.group, head_dim) == 2;
+  const bool two =
+      gqa_mfma_col_tiles(a.q_len * a.group, head_dim, (int64_t)a.max_pages * a.page_size) == 2;
   switch (head_dim) {
 #define PDA_MFMA_ARGS                                                                        \
   a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.q_len,        \

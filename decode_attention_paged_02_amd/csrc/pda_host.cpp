@@ -130,7 +130,9 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
   const int head_tiles = mla             ? (int)ceil_div(ql * s->num_q_heads, 16 * mla_groups)
                          : gqa_use_mfma(s)
                              ? (int)ceil_div(ql * group,
-                                             16 * pda::gqa_mfma_col_tiles(ql * group, s->head_dim))
+                                             16 * pda::gqa_mfma_col_tiles(
+                                                      ql * group, s->head_dim,
+                                                      (int64_t)s->max_pages_per_seq * s->page_size))
                                            : (int)ceil_div(group, pda::gqa_tile_heads(group));
   const int64_t units = (int64_t)s->batch * s->num_kv_heads * head_tiles;
   const int max_pages = s->max_pages_per_seq;

@@ -115,18 +115,23 @@ def test_plan_head_tiles():
     assert pda.plan(_shape(num_q_heads=16, num_kv_heads=1, **valu), num_cus=256).head_tiles == 2
     # matrix-core kernel (the default for f16 / bf16 queries and groups >= 3):
     # 16 rows per workgroup, or 32 (two column tiles) for groups of more than
-    # 16 rows at d <= 128
+    # 16 rows at d <= 128 -- for 17 to 32 rows only when the table holds at
+    # least 2048 tokens per sequence (the default shape here holds 64 x 16)
+    long = dict(max_pages_per_seq=128)
     assert pda.plan(_shape(num_q_heads=96, num_kv_heads=8), num_cus=256).head_tiles == 1
     assert pda.plan(_shape(num_q_heads=16, num_kv_heads=1), num_cus=256).head_tiles == 1
     assert pda.plan(_shape(num_q_heads=48, num_kv_heads=1), num_cus=256).head_tiles == 2
-    assert pda.plan(_shape(num_q_heads=32, num_kv_heads=1), num_cus=256).head_tiles == 1
+    assert pda.plan(_shape(num_q_heads=32, num_kv_heads=1), num_cus=256).head_tiles == 2
+    assert pda.plan(_shape(num_q_heads=32, num_kv_heads=1, **long), num_cus=256).head_tiles == 1
     assert pda.plan(_shape(num_q_heads=64, num_kv_heads=1), num_cus=256).head_tiles == 2
     assert pda.plan(_shape(num_q_heads=48, num_kv_heads=1, head_dim=256, head_dim_v=256),
                     num_cus=256).head_tiles == 3
     assert pda.plan(_shape(num_q_heads=8, num_kv_heads=8), num_cus=256).head_tiles == 1
     mf = dict(variant=pda.PDA_GQA_MFMA)
     assert pda.plan(_shape(num_q_heads=8, num_kv_heads=8, **mf), num_cus=256).head_tiles == 1
-    assert pda.plan(_shape(num_q_heads=24, num_kv_heads=1, **mf), num_cus=256).head_tiles == 1
+    assert pda.plan(_shape(num_q_heads=24, num_kv_heads=1, **mf), num_cus=256).head_tiles == 2
+    assert pda.plan(_shape(num_q_heads=24, num_kv_heads=1, **mf, **long),
+                    num_cus=256).head_tiles == 1
     p = pda.plan(_shape(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512,
                         page_size=64, q_dtype=pda.PDA_BF16, kv_dtype=pda.PDA_BF16),
                  mla=True, num_cus=256)
@@ -137,9 +142,12 @@ def test_plan_multi_token_rows():
     """With q_len query tokens the matrix-core tiles hold q_len * group rows
     (query token, head), and the partials cover every (b, token, head) row."""
     assert pda.plan(_shape(q_len=4), num_cus=256).head_tiles == 1          # 4 x 4 rows
-    assert pda.plan(_shape(q_len=5), num_cus=256).head_tiles == 1          # 20 rows: 32-row tile
+    assert pda.plan(_shape(q_len=5), num_cus=256).head_tiles == 2          # 20 rows, short table
+    assert pda.plan(_shape(q_len=5, max_pages_per_seq=128),
+                    num_cus=256).head_tiles == 1                           # 20 rows: 32-row tile
     assert pda.plan(_shape(q_len=9), num_cus=256).head_tiles == 2          # 36 rows
-    assert pda.plan(_shape(num_q_heads=64, q_len=3), num_cus=256).head_tiles == 1   # 24 rows
+    assert pda.plan(_shape(num_q_heads=64, q_len=3, max_pages_per_seq=128),
+                    num_cus=256).head_tiles == 1                           # 24 rows
     assert pda.plan(_shape(num_q_heads=64, q_len=3, head_dim=256, head_dim_v=256),
                     num_cus=256).head_tiles == 2                           # 16-row tiles at d 256
     # a group of 1 or 2 takes the matrix-core kernel once q_len > 1
