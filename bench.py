@@ -299,7 +299,8 @@ def main():
                          "gqa_b64 is the same cache with token-major pages)")
     ap.add_argument("--pools", type=int, default=4, help="rotating KV pool copies (0: one, warm)")
     ap.add_argument("--others",
-                    default="gqa_b64,gqa_b1_split_hm,gqa_b4_split_hm,mqa_b64_8k_hm,kv_append_b64_hm",
+                    default="gqa_b64,gqa_b1_split_hm,gqa_b4_split_hm,mqa_b64_8k_hm,"
+                            "ragged_fp8_balanced_hm,mla_b16,kv_append_b64_hm",
                     help="extra workloads measured into 'other_workloads' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -344,7 +345,8 @@ def main():
         u2, g2, k2 = summarize(r2, st)
         others[w] = {"us_per_step": round(u2, 2), "GB/s": round(g2, 1),
                      "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4),
-                     "max_splits": r2["max_splits"], "kv_bytes": r2["kv_bytes"]}
+                     "max_splits": r2["max_splits"], "kv_bytes": r2["kv_bytes"],
+                     "step_us_median": r2["step_us"]["median"]}
         del c2
     if not args.no_bw_probe:
         _log("bandwidth probe")
