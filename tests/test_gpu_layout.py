@@ -66,6 +66,21 @@ def test_head_major_full_size_long_split():
     check(case, out, lse, ref_o, ref_l, label=case.name)
 
 
+def test_mqa_full_size_two_column_tiles():
+    """MQA, B=64, 32 query heads on one KV head, ctx 8192, head-major: the
+    workgroups carry two 16-row column tiles (one K/V load for 32 heads) and
+    the sequences split eight ways."""
+    case = W.mqa_batch64_8k(kv_layout=HEAD_MAJOR)
+    say(case.name)
+    dev = pda.to_device(case)
+    shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                          kv_layout=HEAD_MAJOR)
+    assert pda.plan(shape).head_tiles == 1
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, dev)
+    check(case, out, lse, ref_o, ref_l, label=case.name)
+
+
 def test_head_major_equals_token_major_bitwise():
     """The two layouts of one case read the same elements in the same order:
     the kernels' outputs are bit-identical."""
