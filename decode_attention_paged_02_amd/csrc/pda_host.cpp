@@ -271,7 +271,7 @@ int pda_check_inputs(const pda_shape* shape, const int32_t* block_tables,
   return pda::launch_check(a, (hipStream_t)stream) == hipSuccess ? PDA_OK : PDA_ERR_HIP;
 }
 
-int pda_version(void) { return 100; }
+int pda_version(void) { return 200; }
 
 const char* pda_status_string(int status) {
   switch (status) {

@@ -279,7 +279,9 @@ int pda_check_inputs(const pda_shape* shape, const int32_t* block_tables,
 /* Static description of a status code. */
 const char* pda_status_string(int status);
 
-/* Library version, major * 10000 + minor * 100 + patch. */
+/* Library version, major * 10000 + minor * 100 + patch: 200 (0.2.0).  0.2
+ * appended kv_layout to pda_shape and added pda_check_inputs; a caller built
+ * against an older header passes a shorter pda_shape and must be rebuilt. */
 int pda_version(void);
 
 #ifdef __cplusplus

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(pda.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pda_version() == 100
+    assert lib.pda_version() == 200
     assert lib.pda_status_string(3) == b"workspace missing or too small"
 
 
