@@ -60,6 +60,26 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     return LIB
 
 
+EXAMPLE_SRC = os.path.join(HERE, "examples", "c_abi_decode.cpp")
+EXAMPLE_BIN = os.path.join(HERE, "examples", "c_abi_decode")
+EXAMPLE_LIB = os.path.join(HERE, "examples", "libc_abi_decode.so")
+
+
+def build_example(verbose: bool = False) -> str:
+    """The C-ABI example (host code only, linked against libpda.so): the
+    program, and the same code as a shared library for in-process tests."""
+    common = [HIPCC, "-O2", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"),
+              EXAMPLE_SRC, "-L", HERE, "-lpda", "-Wl,-rpath,$ORIGIN/.."]
+    for out, extra in ((EXAMPLE_BIN, []),
+                       (EXAMPLE_LIB, ["-shared", "-fPIC", "-DPDA_EXAMPLE_LIBRARY"])):
+        cmd = common + extra + ["-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        subprocess.run(cmd, check=True)
+        os.replace(out + ".tmp", out)
+    return EXAMPLE_BIN
+
+
 def _wait(item):
     src, p = item
     _, err = p.communicate()
@@ -73,3 +93,4 @@ def _wait(item):
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_example(verbose="-v" in sys.argv))
