@@ -162,7 +162,10 @@ typedef struct pda_plan_info {
   int32_t max_splits;      /* split-axis extent of the launch grid          */
   int32_t pages_per_split; /* pages per split for sequences that split      */
                            /* (GRID; 0 with BALANCED: chosen on the device) */
-  int32_t head_tiles;      /* query-head tiles per KV head                   */
+  int32_t head_tiles;      /* query-head tiles per KV head (workgroups per   */
+                           /* KV head and split: 8 heads a tile for the     */
+                           /* vector kernel, 16 or 32 (query, head) rows    */
+                           /* for the matrix-core kernels)                  */
   int32_t workgroups;      /* workgroups of the main kernel                  */
   int32_t num_cus;         /* compute units the plan was made for           */
   int32_t ordered;         /* 1: the call orders its work longest first     */
@@ -192,7 +195,8 @@ int pda_plan(const pda_shape* shape, int is_mla, int num_splits, int num_cus,
  * prescribe a schedule).  The result does not depend on the order. */
 size_t pda_workspace_bytes(const pda_shape* shape, int is_mla, int num_splits);
 
-/* GQA / MQA / MHA paged decode attention (layouts above).
+/* GQA / MQA / MHA paged decode attention (layouts above; the caches' page
+ * order is shape->kv_layout's).
  * group must equal num_q_heads / num_kv_heads.  scale multiplies q.K before
  * the softmax (k_scale/v_scale are applied on top for FP8 caches).
  * Supported: (q, kv) dtypes (F32,F32), (F16,F16), (BF16,BF16), (F16,FP8),
