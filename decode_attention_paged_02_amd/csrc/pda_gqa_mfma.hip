@@ -153,7 +153,8 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, f32x4 c
 // kernel-argument load.  GqaArgs carries everything (the same values too).
 // CT column tiles of 16 rows per workgroup: one, or two for groups of more
 // than 16 rows (d <= 128), so that one load of a K/V tile serves 32 rows.
-template <class QT, class KT, int D, int CT>
+// SD steps of tiles in flight per wave (see kGqaStepsInFlight).
+template <class QT, class KT, int D, int CT, int SD>
 __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     const int32_t* context_lens, const int32_t* block_tables, const void* q, int32_t head_tiles,
     int32_t num_kv_heads, int32_t group, int32_t q_len, int32_t max_pages, int32_t log2_page,
@@ -421,7 +422,6 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   // it is computed; other waves cover the latency).  Each step issues the
   // loads of its ST tiles back to back.  Steps are grouped in chunks of
   // kStepsPerChunk (one table entry per lane per tile).
-  constexpr int SD = kGqaStepsInFlight;
   Words<PW> kb[SD][ST][4], vb[SD][ST][4];
   int rows_b[SD][ST], tok_b[SD][ST];
   auto issue = [&](int sidx, int send, int u) {
@@ -552,6 +552,22 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   }
 }
 
+// grid calls with kGqaStepsInFlight steps in flight, ordered ones with
+// kGqaStepsInFlightOrdered
+template <class QT, class KT, int D, int CT>
+void launch_sd(const GqaArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+#define PDA_MFMA_ARGS                                                                        \
+  a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.q_len,        \
+      a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a.units, a
+  if (a.units)
+    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlightOrdered>), grid, block,
+                       0, s, PDA_MFMA_ARGS);
+  else
+    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlight>), grid, block, 0, s,
+                       PDA_MFMA_ARGS);
+#undef PDA_MFMA_ARGS
+}
+
 template <class QT, class KT>
 hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStream_t s) {
   const unsigned units = (unsigned)(a.batch * a.num_kv_heads * a.head_tiles);
@@ -561,23 +577,15 @@ hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStr
   const bool two =
       gqa_mfma_col_tiles(a.q_len * a.group, head_dim, (int64_t)a.max_pages * a.page_size) == 2;
   switch (head_dim) {
-#define PDA_MFMA_ARGS                                                                        \
-  a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.q_len,        \
-      a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a.units, a
     case 64:
-      if (two)
-        hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64, 2>), grid, block, 0, s, PDA_MFMA_ARGS);
-      else
-        hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 64, 1>), grid, block, 0, s, PDA_MFMA_ARGS);
+      if (two) launch_sd<QT, KT, 64, 2>(a, grid, block, s);
+      else launch_sd<QT, KT, 64, 1>(a, grid, block, s);
       break;
     case 128:
-      if (two)
-        hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128, 2>), grid, block, 0, s, PDA_MFMA_ARGS);
-      else
-        hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 128, 1>), grid, block, 0, s, PDA_MFMA_ARGS);
+      if (two) launch_sd<QT, KT, 128, 2>(a, grid, block, s);
+      else launch_sd<QT, KT, 128, 1>(a, grid, block, s);
       break;
-    case 256: hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, 256, 1>), grid, block, 0, s, PDA_MFMA_ARGS); break;
-#undef PDA_MFMA_ARGS
+    case 256: launch_sd<QT, KT, 256, 1>(a, grid, block, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
