@@ -312,16 +312,22 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kMaxStart, l_run = 0.f;
 
-  // Two blocks in flight in registers while one is computed from LDS: block k
-  // sits in ld[k % 2] until it is staged into LDS buffer k % 2, and the loads
-  // of block k + 2 go into the registers it leaves.  Loads of blocks past the
-  // range have empty resources (no memory access), so they need no branch.
-  // (A deeper ring for the 512-thread workgroups measured no gain.)
-  BlockLoader<T, KT, DM> ld[2];
+  // kRing blocks in flight in registers while one is computed from LDS.
+  // With one (four-wave workgroups, two per CU), block k + 1 is loaded while
+  // block k is computed and staged right after; with two (the 512-thread
+  // workgroups, one per CU), block k sits in ld[k % 2] until it is staged and
+  // the loads of block k + 2 go into the registers it leaves.  Fewer loads in
+  // flight contend less where two workgroups share a CU (bf16 record 195
+  // against 200 us, (320, 256) 119 against 121); the lone 512-thread
+  // workgroup keeps two (a deeper ring measured no gain, a shallower one
+  // 1% less).  Loads of blocks past the range have empty resources (no
+  // memory access), so they need no branch.
+  constexpr int kRing = NG == 1 ? 1 : 2;
+  BlockLoader<T, KT, DM> ld[kRing];
   ld[0].load(a, pt, t0, t1, 0, log2P, tid);
   ld[0].store(lds[0], tid);
-  ld[1].load(a, pt, t0, t1, 1, log2P, tid);
-  ld[0].load(a, pt, t0, t1, 2, log2P, tid);
+  ld[kRing - 1].load(a, pt, t0, t1, 1, log2P, tid);
+  if constexpr (kRing == 2) ld[0].load(a, pt, t0, t1, 2, log2P, tid);
   __syncthreads();
 
   // block blk from LDS
@@ -433,20 +439,20 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
     for (int mb = 0; mb < MB; ++mb)
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mb], pk_lo, acc[mb], 0, 0, 0);
   };
-  // block blk, then: stage the next block, start loading the one three
+  // block blk, then: stage the next block, start loading the one 1 + kRing
   // ahead, hand over the buffer (`nxt` holds block blk + 1 and then receives
-  // blk + 3).  No branches around loads and stores (nor exits from the
+  // blk + 1 + kRing).  No branches around loads and stores (nor exits from the
   // unrolled pair): the wait counts then stay exact across iterations, and a
   // block past the range is all zero rows (an odd block count computes one
   // such block, fully masked).
   auto body = [&](int blk, BlockLoader<T, KT, DM>& nxt) {
     compute(blk);
     nxt.store(lds[(blk + 1) & 1], tid);
-    nxt.load(a, pt, t0, t1, blk + 3, log2P, tid);
+    nxt.load(a, pt, t0, t1, blk + 1 + kRing, log2P, tid);
     __syncthreads();
   };
   for (int blk = 0; blk < nblocks; blk += 2) {
-    body(blk, ld[1]);
+    body(blk, ld[kRing - 1]);
     body(blk + 1, ld[0]);
   }
 
