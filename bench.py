@@ -293,7 +293,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first (the GPU reaches its steady clocks within ~10 ms)")
     ap.add_argument("--workload", default="gqa_b64_hm", choices=WORKLOADS,
                     help="the timed workload (default: B=64 / ctx 1024 with head-major pages; "
                          "gqa_b64 is the same cache with token-major pages)")
@@ -341,7 +342,7 @@ def main():
             continue
         c2 = make_case(w)
         st = max(20, args.steps // 4)
-        r2 = run_gpu(c2, w, st, 5, args.pools)
+        r2 = run_gpu(c2, w, st, args.warmup, args.pools)
         u2, g2, k2 = summarize(r2, st)
         others[w] = {"us_per_step": round(u2, 2), "GB/s": round(g2, 1),
                      "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4),
