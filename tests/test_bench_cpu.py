@@ -21,7 +21,7 @@ def test_more_than_one_gpu_exits(argv):
     assert r.stdout == ""
 
 
-def test_every_workload_builds_its_case():
+def test_workload_cases_build_on_the_host():
     # one workload of each kind (GQA, split, MQA, MLA), built on the host
     for w in ["gqa_b64_hm", "gqa_b1_split_hm", "mqa_b64_8k_hm", "mla_b16_320"]:
         c = bench.make_case(w)
