@@ -18,9 +18,9 @@ def _gpu():
     need_gpu()
 
 
-def _skip_unsupported(variant, q_dtype):
-    if variant == "mfma" and q_dtype == "f32":
-        pytest.skip("matrix-core kernel takes f16 / bf16 queries")
+def _supported(variant, q_dtype):
+    # the matrix-core kernel takes f16 / bf16 queries only
+    return not (variant == "mfma" and q_dtype == "f32")
 
 
 def _gqa(seed, B, Hq, Hkv, d, P, lens, q_dtype="f16", kv_dtype="f16", **kw):
@@ -80,11 +80,11 @@ def test_ragged_fp8_sampled_rows():
 
 
 @pytest.mark.parametrize("lens", [[1], [15, 16, 17], [31, 32, 33, 47], [100, 1, 64, 129]])
-@pytest.mark.parametrize("dt", [("f16", "f16"), ("bf16", "bf16"), ("f32", "f32"),
-                                ("f16", "e4m3"), ("bf16", "e4m3")])
-@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("dt,variant", [
+    (dt, v) for dt in [("f16", "f16"), ("bf16", "bf16"), ("f32", "f32"), ("f16", "e4m3"),
+                       ("bf16", "e4m3")]
+    for v in VARIANTS if _supported(v, dt[0])])
 def test_page_boundaries_and_dtypes(lens, dt, variant):
-    _skip_unsupported(variant, dt[0])
     case = _gqa(len(lens) * 7 + len(dt[1]), len(lens), 8, 2, 128, 16, lens, *dt, extra_pages=3)
     say("boundaries", lens, dt, variant)
     out, lse = pda.run_case(case, variant=VARIANTS[variant])
@@ -120,12 +120,12 @@ def test_large_groups_several_head_tiles(Hq, Hkv, B, variant, thr, ):
     check(case, out, lse, ref_o, ref_l, label="Hq=%d Hkv=%d B=%d thr=%d" % (Hq, Hkv, B, thr))
 
 
-@pytest.mark.parametrize("d,P,dt", [(64, 16, "f16"), (64, 32, "bf16"), (256, 16, "f16"),
-                                    (128, 64, "f16"), (64, 16, "f32"), (128, 32, "f32"),
-                                    (256, 16, "bf16")])
-@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("d,P,dt,variant", [
+    (d, P, dt, v) for d, P, dt in [(64, 16, "f16"), (64, 32, "bf16"), (256, 16, "f16"),
+                                   (128, 64, "f16"), (64, 16, "f32"), (128, 32, "f32"),
+                                   (256, 16, "bf16")]
+    for v in VARIANTS if _supported(v, dt)])
 def test_head_dims_and_page_sizes(d, P, dt, variant):
-    _skip_unsupported(variant, dt)
     case = _gqa(d + P, 2, 16, 4, d, P, [333, 70], dt, dt, extra_pages=2)
     say("d/P", d, P, dt, variant)
     for s in (1, 3):
