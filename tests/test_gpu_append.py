@@ -143,3 +143,31 @@ def test_decode_step_append_then_attend(cache):
     out, lse = pda.run_case(case, dev)
     ref_o, ref_l = oracle_ref(case)
     check(case, out, lse, ref_o, ref_l, label="append then attend %s" % cache)
+
+
+def test_append_into_pages_past_5_gib():
+    """Destination pages past 5 GiB of the pool (int64 page addressing in the
+    append kernel); the pages below are left untouched."""
+    case, k_new, v_new, pos = _append_case(19, B=3, s_new=2, Hkv=2, d=128, P=16, src="f16",
+                                           cache="f16", lens=[40, 3, 17])
+    base = (5 << 30) // (16 * 2 * 128 * 2)
+    say("append large pool", base + case.num_pages, "pages")
+    shape = (base + case.num_pages,) + case.k_cache.shape[1:]
+    kc = torch.zeros(shape, dtype=torch.float16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kc[base:] = _dev(case.k_cache, "f16")
+    vc[base:] = _dev(case.v_cache, "f16")
+    pda.paged_kv_append(_dev(k_new, "f16"), _dev(v_new, "f16"),
+                        _dev(case.block_tables, "i32") + base, torch.from_numpy(pos).cuda(),
+                        kc, vc)
+    torch.cuda.synchronize()
+    want_k = oracle.kv_append(k_new, case.k_cache, case.block_tables, pos, src_dtype="f16",
+                              cache_dtype="f16")
+    want_v = oracle.kv_append(v_new, case.v_cache, case.block_tables, pos, src_dtype="f16",
+                              cache_dtype="f16")
+    assert np.array_equal(_host_bytes(kc[base:]), want_k.view(np.uint8).reshape(
+        _host_bytes(kc[base:]).shape))
+    assert np.array_equal(_host_bytes(vc[base:]), want_v.view(np.uint8).reshape(
+        _host_bytes(vc[base:]).shape))
+    assert int(torch.count_nonzero(kc[:base])) == 0 and int(torch.count_nonzero(vc[:base])) == 0
+    del kc, vc

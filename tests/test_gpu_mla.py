@@ -183,3 +183,21 @@ def test_record_320_value_256(Hq, q_len, kv):
         check(case, out, lse, ref_o, ref_l, label="mla320 Hq=%d q=%d %s S=%d" % (Hq, q_len, kv, s))
     out, lse = pda.run_case(case, schedule=pda.PDA_SCHEDULE_BALANCED)
     check(case, out, lse, ref_o, ref_l, label="mla320 balanced")
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_large_pool_64bit_offsets(variant):
+    """Latent pages past 5 GiB of the pool (int64 page addressing)."""
+    small = _mla(91, [300, 65], poison=False)
+    dev = pda.to_device(small)
+    page_bytes = dev.k_cache[0].numel() * dev.k_cache.element_size()
+    base = (5 << 30) // page_bytes
+    say("mla large pool", base + small.num_pages, "pages")
+    kv = torch.zeros((base + small.num_pages,) + tuple(dev.k_cache.shape[1:]),
+                     dtype=dev.k_cache.dtype, device="cuda")
+    kv[base:] = dev.k_cache
+    out, lse = pda.paged_decode_attn_mla(dev.q, kv, dev.block_tables + base, dev.context_lens,
+                                         scale=small.scale, variant=VARIANTS[variant])
+    ref_o, ref_l = oracle_ref(small)
+    check(small, out, lse, ref_o, ref_l, label="mla large pool")
+    del kv
