@@ -365,3 +365,25 @@ def test_balanced_schedule_multi_token():
     ref_o, ref_l = oracle_ref(case)
     out, lse = pda.run_case(case, schedule=BAL)
     check(case, out, lse, ref_o, ref_l, label="balanced q_len=3")
+
+
+@pytest.fixture(scope="module")
+def very_long():
+    case = _gqa(31, 2, 16, 2, 128, 16, [262144, 5000], poison=False)
+    return case, oracle_ref(case)
+
+
+@pytest.mark.parametrize("splits", [0, 200, 1024])
+def test_very_long_context_many_splits(very_long, splits):
+    """262144 and 5000 tokens: 16384 table entries per row, and split counts
+    past the 64 per row that the combine keeps in registers (the rest take its
+    loop)."""
+    case, (ref_o, ref_l) = very_long
+    say("very long context", splits)
+    dev = pda.to_device(case)
+    p = pda.plan(pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables),
+                 num_splits=splits)
+    assert splits == 0 or p.max_splits > 64
+    for name, v in VARIANTS.items():
+        out, lse = pda.run_case(case, dev, num_splits=splits, variant=v)
+        check(case, out, lse, ref_o, ref_l, label="very long %d %s" % (splits, name))

@@ -201,3 +201,18 @@ def test_large_pool_64bit_offsets(variant):
     ref_o, ref_l = oracle_ref(small)
     check(small, out, lse, ref_o, ref_l, label="mla large pool")
     del kv
+
+
+def test_many_splits_combine_loop():
+    """Split counts past the 64 per row that the combine keeps in registers,
+    up to one page per split, on the 512-wide rows (four column chunks)."""
+    case = _mla(92, [20000, 3, 700], poison=False)
+    say("mla many splits")
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case)
+    for splits in (100, 313):
+        p = pda.plan(pda.mla_shape(dev.q, dev.k_cache, dev.block_tables), mla=True,
+                     num_splits=splits)
+        assert p.max_splits > 64
+        out, lse = pda.run_case(case, dev, num_splits=splits)
+        check(case, out, lse, ref_o, ref_l, label="mla splits %d" % splits)
