@@ -93,7 +93,7 @@ def measured_traffic(workload: str, kernel: str):
     return t.get("bytes_per_launch")
 
 
-def run_gpu(case, workload, steps, warmup, pools):
+def run_gpu(case, workload, steps, warmup, pools, min_warmup_ms=100.0):
     import torch
     from decode_attention_paged_02_amd import accounting as A
     from decode_attention_paged_02_amd import pda
@@ -129,9 +129,27 @@ def run_gpu(case, workload, steps, warmup, pools):
                             scale=case.scale, out=out, lse=lse, shape=shape,
                             num_splits=nsplit, workspace=ws)
 
+    # untimed warm-up: `warmup` steps, then more until at least min_warmup_ms
+    # of GPU time has passed (the clocks settle during the first ~10 ms of
+    # work after an idle period)
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    w0.record()
+    done = 0
     for i in range(warmup):
         step(i)
+    done = warmup
+    w1.record()
     torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1)
+    while warm_ms < min_warmup_ms:
+        w1b = torch.cuda.Event(enable_timing=True)
+        for i in range(50):
+            step(done + i)
+        done += 50
+        w1b.record()
+        torch.cuda.synchronize()
+        warm_ms = w0.elapsed_time(w1b)
     # whole-job time over exactly `steps` back-to-back steps
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -141,8 +159,8 @@ def run_gpu(case, workload, steps, warmup, pools):
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    # then the distribution of single steps (each between its own events)
-    n_dist = min(steps, 100)
+    # then the distribution of 100 single steps (each between its own events)
+    n_dist = 100
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_dist)]
     for i, (e0, e1) in enumerate(ev):
@@ -154,6 +172,7 @@ def run_gpu(case, workload, steps, warmup, pools):
     dist = {"steps": n_dist, "median": round(each[n_dist // 2], 3), "min": round(each[0], 3),
             "p90": round(each[min(n_dist - 1, (9 * n_dist) // 10)], 3)}
     return dict(total_ms=total_ms, kernel_us_mean=total_ms * 1000.0 / steps, step_us=dist,
+                warmup_steps=done, warmup_ms=round(warm_ms, 2),
                 overhead_bytes=A.case_overhead_bytes(case, plan.max_splits),
                 kv_bytes=nbytes, n_pools=len(caches), max_splits=plan.max_splits,
                 pages_per_split=plan.pages_per_split, workgroups=plan.workgroups,
@@ -215,51 +234,79 @@ def run_append(base: str, steps: int, warmup: int):
             "note": "HIP events around back-to-back calls; one token per sequence per step"}
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(case, budget_s=20.0):
-    """The fp64 oracle on the host cores over a bounded sample of the workload:
-    whole sequences in order, repeated as whole passes, until about budget_s
-    of CPU time (core-seconds) has been spent."""
+    """The fp64 oracle on the host over a bounded sample of the workload: the
+    first whole sequences (all heads), timed at one thread and at every thread
+    the oracle may use, each the median of 3 wall-clock runs.  The sample is
+    sized per thread count so that the six runs take about budget_s together."""
+    import statistics
     import numpy as np
     import oracle
     from decode_attention_paged_02_amd import accounting as A
-    threads = oracle.max_threads()
+    all_threads = oracle.max_threads()
     rows = np.zeros(case.q.shape[:-1], dtype=bool)     # [B, Hq] or [B, s_q, Hq]
-    # time one sequence to size the sample
     rows[0] = True
     t = time.perf_counter()
-    _oracle_call(case, rows)
-    one = max(time.perf_counter() - t, 1e-4)
-    wall = budget_s / max(threads, 1)
-    nseq = int(min(case.batch, max(1, wall / one)))
-    rows[:nseq] = True
-    passes, dt = 0, 0.0
-    while passes == 0 or dt < wall:
-        t = time.perf_counter()
-        _oracle_call(case, rows)
-        dt += time.perf_counter() - t
-        passes += 1
-    nbytes = passes * A.step_kv_bytes(case.context_lens[:nseq], num_kv_heads=case.num_kv_heads,
-                                      head_dim=case.head_dim, head_dim_v=case.head_dim_v,
-                                      kv_dtype=case.kv_dtype, mla=case.mla)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+    _oracle_call(case, rows, 1)
+    one_seq_1t = max(time.perf_counter() - t, 1e-4)    # one sequence on one thread
+    per_run = budget_s / 6.0
+    res = {}
+    for threads in (1, all_threads):
+        # whole sequences; with several threads, at least one per thread
+        nseq = int(min(case.batch, max(1 if threads == 1 else threads,
+                                       per_run * threads / one_seq_1t)))
+        rows[:] = False
+        rows[:nseq] = True
+        times = []
+        for _ in range(3):
+            t = time.perf_counter()
+            _oracle_call(case, rows, threads)
+            times.append(time.perf_counter() - t)
+        dt = statistics.median(times)
+        nbytes = A.step_kv_bytes(case.context_lens[:nseq], num_kv_heads=case.num_kv_heads,
+                                 head_dim=case.head_dim, head_dim_v=case.head_dim_v,
+                                 kv_dtype=case.kv_dtype, mla=case.mla)
+        res[threads] = dict(gbs=nbytes / dt / 1e9, nseq=nseq, median_s=dt,
+                            us_step=dt * 1e6 * case.batch / nseq)
+    top = res[all_threads]
+    return {"value": round(top["gbs"], 4), "unit": "GB/s", "cores": all_threads,
             "kind": "oracle",
-            "sample": "%d of %d sequences (all heads) of the timed workload x %d passes, fp64 "
-                      "oracle, %.2f s wall on %d threads" % (nseq, case.batch, passes, dt, threads),
-            "us_per_step_equiv": round(dt * 1e6 * case.batch / nseq / passes, 1)}
+            "sample": "the first %d of %d sequences (all heads) of the timed workload, fp64 "
+                      "oracle, median of 3 runs (%.2f s) on %d threads; one thread: the first "
+                      "%d sequences, median %.2f s" % (
+                          top["nseq"], case.batch, top["median_s"], all_threads,
+                          res[1]["nseq"], res[1]["median_s"]),
+            "one_thread": {"value": round(res[1]["gbs"], 5), "unit": "GB/s",
+                           "us_per_step_equiv": round(res[1]["us_step"], 1)},
+            "us_per_step_equiv": round(top["us_step"], 1),
+            "host": {"cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+                     "affinity": len(os.sched_getaffinity(0))}}
 
 
-def _oracle_call(case, rows):
+def _oracle_call(case, rows, threads):
     import oracle
     if case.mla:
         return oracle.mla_attention(case.q, case.k_cache, case.block_tables, case.context_lens,
                                     scale=case.scale, d_latent=case.d_latent,
                                     q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
-                                    kv_scale=case.k_scale, causal=case.causal, rows=rows)
+                                    kv_scale=case.k_scale, causal=case.causal, rows=rows,
+                                    num_threads=threads)
     return oracle.paged_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
                                   case.context_lens, scale=case.scale, q_dtype=case.q_dtype,
                                   kv_dtype=case.kv_dtype, k_scale=case.k_scale,
                                   v_scale=case.v_scale, causal=case.causal, rows=rows,
-                                  kv_layout=case.kv_layout)
+                                  kv_layout=case.kv_layout, num_threads=threads)
 
 
 def bandwidth_probe(nbytes=2 << 30, reps=10):
@@ -295,6 +342,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500,
                     help="untimed steps first (the GPU reaches its steady clocks within ~10 ms)")
+    ap.add_argument("--min-warmup-ms", type=float, default=100.0,
+                    help="after --warmup steps, keep warming up until this much GPU time has "
+                         "passed (untimed)")
     ap.add_argument("--workload", default="gqa_b64_hm", choices=WORKLOADS,
                     help="the timed workload (default: B=64 / ctx 1024 with head-major pages; "
                          "gqa_b64 is the same cache with token-major pages)")
@@ -322,7 +372,7 @@ def main():
 
     _log("workload", args.workload)
     case = make_case(args.workload)
-    r = run_gpu(case, args.workload, args.steps, args.warmup, args.pools)
+    r = run_gpu(case, args.workload, args.steps, args.warmup, args.pools, args.min_warmup_ms)
     us_step, gbs, kgbs = summarize(r, args.steps)
     kernel = "mla_mfma_kernel" if case.mla else "gqa_mfma_kernel"
     traffic = measured_traffic(args.workload, kernel)
@@ -332,6 +382,11 @@ def main():
             "launch_us_mean": round(r["kernel_us_mean"], 3),
             "launches_per_step": r["launches"],
             "timing": "HIP events on the launch stream around the timed region / steps",
+            "step_definitions": {
+                "us_per_step": "GPU time of the timed back-to-back steps (HIP events on the "
+                               "launch stream around all of them) / steps",
+                "step_us": "100 more steps, each between its own pair of events: median, min "
+                           "and 90th percentile (per-step event overhead included)"},
             "algorithmic_bytes_per_launch": r["kv_bytes"],
             "step_us": r["step_us"], "overhead_bytes_per_step": r["overhead_bytes"]}
     others = {}
@@ -342,7 +397,7 @@ def main():
             continue
         c2 = make_case(w)
         st = max(20, args.steps // 4)
-        r2 = run_gpu(c2, w, st, args.warmup, args.pools)
+        r2 = run_gpu(c2, w, st, args.warmup, args.pools, args.min_warmup_ms)
         u2, g2, k2 = summarize(r2, st)
         others[w] = {"us_per_step": round(u2, 2), "GB/s": round(g2, 1),
                      "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4),
@@ -361,7 +416,9 @@ def main():
         dt = "e4m3 cache, " + dt
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us_step / 1000, 5),
+        "steps": args.steps, "warmup": args.warmup,
+        "warmup_done": {"steps": r["warmup_steps"], "gpu_ms": r["warmup_ms"]},
+        "ms_per_step": round(us_step / 1000, 5),
         "us_per_step": round(us_step, 3), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic",

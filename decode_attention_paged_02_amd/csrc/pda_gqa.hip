@@ -617,7 +617,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(OrderArgs a) {
   __shared__ unsigned long long pages_sh;
   __shared__ int lens_sh[kOrderStagedLens];
   const int S = a.split.max_splits;
-  const int U = a.batch * S;
+  const int64_t U = (int64_t)a.batch * S;  // (b, split) candidates; may pass 2^31
   const int P = a.page_size;
   // the lengths are read from memory once (staged in LDS up to
   // kOrderStagedLens sequences), together with the batch's page count
@@ -660,8 +660,8 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(OrderArgs a) {
     }
   };
   // unit u = (b, s): its token range, or false past the sequence's splits
-  auto unit_of = [&](int u, WorkUnit& w, int& ns) -> bool {
-    const int b = u / S, s = u % S;
+  auto unit_of = [&](int64_t u, WorkUnit& w, int& ns) -> bool {
+    const int b = (int)(u / S), s = (int)(u % S);
     const int n = len_of(b);
     int pps;
     layout(n, ns, pps);
@@ -676,7 +676,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(OrderArgs a) {
     const int tok = w.t1 - w.t0;
     return tok > 0 ? 32 - __clz(tok) : 0;
   };
-  for (int u = threadIdx.x; u < U; u += kOrderThreads) {
+  for (int64_t u = threadIdx.x; u < U; u += kOrderThreads) {
     WorkUnit w;
     int ns;
     if (unit_of(u, w, ns)) {
@@ -696,7 +696,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(OrderArgs a) {
   }
   __syncthreads();
   typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-  for (int u = threadIdx.x; u < U; u += kOrderThreads) {
+  for (int64_t u = threadIdx.x; u < U; u += kOrderThreads) {
     WorkUnit w;
     int ns;
     if (unit_of(u, w, ns)) {

@@ -116,6 +116,10 @@ struct Plan {
   int32_t target_units;   // balanced schedule: chunks per KV head and head tile
 };
 
+// Balanced schedules split a sequence at most this many times (the unit list
+// and the grid are bounded by batch + target units either way).
+constexpr int kBalancedMaxSplits = 64;
+
 int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* plan) {
   if (!plan || num_splits < 0 || num_cus < 0) return PDA_ERR_INVALID_ARG;
   pda_plan_info* p = &plan->info;
@@ -147,12 +151,13 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
   int splits = 1;
   if (num_splits > 0) {
     splits = std::min(num_splits, max_pages);
+    if (balanced) splits = std::min(splits, kBalancedMaxSplits);
   } else if (balanced) {
     // at most as many splits as units per KV head and head tile fill the
     // GPU, and no more than chunks of the smallest size fit a table row
     splits = (int)std::min<int64_t>(
         std::max<int64_t>(1, (int64_t)wg_per_cu * num_cus / (s->num_kv_heads * head_tiles)),
-        std::min<int64_t>(ceil_div(max_pages, kMinChunkPages), 64));
+        std::min<int64_t>(ceil_div(max_pages, kMinChunkPages), kBalancedMaxSplits));
   } else {
     // split only when the (sequence, head tile) units alone cannot fill the
     // compute units
@@ -184,6 +189,9 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
   // for the balanced schedule
   p->ordered = (s->split_min_tokens > 0 || balanced) &&
                ucap * s->num_kv_heads * head_tiles <= INT32_MAX;
+  // a balanced schedule exists only as ordered work (its split sizes are
+  // chosen on the device)
+  if (balanced && !p->ordered) return PDA_ERR_UNSUPPORTED;
   plan->unit_capacity = p->ordered ? (int32_t)ucap : 0;
   p->workgroups = (int)std::min<int64_t>(
       p->ordered ? ucap * s->num_kv_heads * head_tiles : units * splits, INT32_MAX);
@@ -201,9 +209,9 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
 }
 
 // Workspace layout: partial outputs [B, q_len, Hq, S, dv] fp32, partial LSE
-// [B, q_len, Hq, S] fp32 (both only when S > 1, each 256-byte aligned), then
-// for ordered calls the work units [B * S][4] int32 (256-byte aligned) and
-// the split count of each sequence [B] int32.
+// [B, q_len, Hq, S] fp32 (both only when S > 1), then for ordered calls the
+// work units [units][4] int32 and the split count of each sequence [B]
+// int32; every part starts 256-byte aligned.
 void workspace_parts(const pda_shape* s, const Plan& plan, void* ws, float** po, float** pl,
                      int32_t** un, int32_t** ss) {
   const pda_plan_info& p = plan.info;
@@ -271,7 +279,58 @@ int pda_check_inputs(const pda_shape* shape, const int32_t* block_tables,
   return pda::launch_check(a, (hipStream_t)stream) == hipSuccess ? PDA_OK : PDA_ERR_HIP;
 }
 
-int pda_version(void) { return 200; }
+int pda_stream_probe(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, const pda_shape* shape, int num_splits,
+                     int steps_in_flight, uint32_t* sink, void* stream) {
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !sink || !shape)
+    return PDA_ERR_INVALID_ARG;
+  if (steps_in_flight < 1 || steps_in_flight > 4 || num_splits < 0) return PDA_ERR_INVALID_ARG;
+  int rc = check_shape(shape, false);
+  if (rc != PDA_OK) return rc;
+  const pda_shape& s = *shape;
+  if (s.schedule != PDA_SCHEDULE_GRID) return PDA_ERR_UNSUPPORTED;
+  if (s.head_dim != s.head_dim_v) return PDA_ERR_UNSUPPORTED;
+  const int elem = s.kv_dtype == PDA_F32 ? 4 : s.kv_dtype == PDA_FP8_E4M3 ? 1 : 2;
+  const int row_bytes = s.head_dim * elem;
+  if (row_bytes != 64 && row_bytes != 128 && row_bytes != 256 && row_bytes != 512)
+    return PDA_ERR_UNSUPPORTED;
+  if (s.batch == 0) return PDA_OK;
+  // the split layout of the same call with the matrix-core kernel's tiling
+  // of one head tile (the probe reads each KV head's rows once)
+  pda_shape one = s;
+  one.num_q_heads = s.num_kv_heads;
+  one.variant = PDA_GQA_VALU;
+  one.q_len = 1;
+  Plan plan;
+  rc = plan_impl(&one, false, num_splits, 0, &plan);
+  if (rc != PDA_OK) return rc;
+  pda::ProbeArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.sink = sink;
+  a.batch = s.batch;
+  a.num_kv_heads = s.num_kv_heads;
+  a.page_size = s.page_size;
+  a.max_pages = s.max_pages_per_seq;
+  a.log2_page = 0;
+  while ((1 << a.log2_page) < s.page_size) ++a.log2_page;
+  a.elem_bytes = elem;
+  const bool head_major = s.kv_layout == PDA_KV_HEAD_MAJOR;
+  a.tok_stride = head_major ? s.head_dim : s.num_kv_heads * s.head_dim;
+  a.head_stride = head_major ? s.page_size * s.head_dim : s.head_dim;
+  a.page_stride = (int64_t)s.page_size * s.num_kv_heads * s.head_dim;
+  a.split.pages_per_split = plan.info.pages_per_split;
+  a.split.max_splits = plan.info.max_splits;
+  a.split.split_min_tokens = s.split_min_tokens;
+  return pda::launch_probe(a, row_bytes, plan.info.max_splits, steps_in_flight,
+                           (hipStream_t)stream) == hipSuccess
+             ? PDA_OK
+             : PDA_ERR_HIP;
+}
+
+int pda_version(void) { return 300; }
 
 const char* pda_status_string(int status) {
   switch (status) {

@@ -162,6 +162,19 @@ struct AppendArgs {
   float k_scale, v_scale;        // E4M3 caches: stored byte = e4m3(x / scale)
 };
 
+// Streaming-read probe (pda_stream_probe): the K/V reads of a GQA grid call.
+struct ProbeArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  uint32_t* sink;  // [max_splits][B * Hkv]: one word per workgroup
+  int32_t batch, num_kv_heads, page_size, max_pages, log2_page, elem_bytes;
+  int32_t tok_stride, head_stride;  // elements, as in GqaArgs
+  int64_t page_stride;
+  SplitLayout split;
+};
+
 // Precondition check of device-resident inputs (see pda_check_inputs).
 struct CheckArgs {
   const int32_t* block_tables;  // [batch, max_pages]
@@ -205,5 +218,7 @@ hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int head_dim,
                       hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int src_dtype, int cache_dtype, hipStream_t stream);
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
+hipError_t launch_probe(const ProbeArgs& a, int row_bytes, int max_splits, int steps_in_flight,
+                        hipStream_t stream);
 
 }  // namespace pda

@@ -52,7 +52,8 @@ class PlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("pda_plan", "pda_workspace_bytes", "paged_decode_attn", "paged_decode_attn_mla",
-           "paged_kv_append", "pda_check_inputs", "pda_status_string", "pda_version")
+           "paged_kv_append", "pda_check_inputs", "pda_stream_probe", "pda_status_string",
+           "pda_version")
 
 _lib = None
 
@@ -80,6 +81,8 @@ def load() -> ctypes.CDLL:
     lib.paged_kv_append.restype = i32
     lib.pda_check_inputs.argtypes = [sp, vp, vp, vp, vp, vp]
     lib.pda_check_inputs.restype = i32
+    lib.pda_stream_probe.argtypes = [vp, vp, vp, vp, sp, i32, i32, vp, vp]
+    lib.pda_stream_probe.restype = i32
     lib.pda_status_string.argtypes = [i32]
     lib.pda_status_string.restype = ctypes.c_char_p
     lib.pda_version.argtypes = []
@@ -198,11 +201,34 @@ def _check_device(*ts):
             _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
 
 
-def workspace_for(shape: Shape, *, mla: bool, num_splits: int, device) -> Optional[torch.Tensor]:
+def workspace_for(shape: Shape, *, mla: bool, num_splits: int, device,
+                  stream=None) -> Optional[torch.Tensor]:
+    """A workspace for calls with this plan (None when they need none).
+    With `stream`, the memory is allocated for use on that stream."""
     nbytes = plan(shape, mla=mla, num_splits=num_splits).workspace_bytes
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with _on_stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+class _on_stream:
+    """Make `stream` torch's current stream (no-op for None), so that tensors
+    a call allocates for itself belong to the stream its kernels run on: the
+    caching allocator then never hands their memory to other work before those
+    kernels are done with it."""
+
+    def __init__(self, stream):
+        self._ctx = torch.cuda.stream(stream) if stream is not None else None
+
+    def __enter__(self):
+        if self._ctx is not None:
+            self._ctx.__enter__()
+
+    def __exit__(self, *exc):
+        if self._ctx is not None:
+            return self._ctx.__exit__(*exc)
+        return False
 
 
 def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, scale: float,
@@ -227,14 +253,16 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, scale:
           "block_tables and context_lens must be int32")
     Hq = shape.num_q_heads
     o_shape, l_shape = _result_shapes(q, shape.head_dim_v)
-    if out is None:
-        out = torch.empty(o_shape, dtype=q.dtype, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty(l_shape, dtype=torch.float32, device=q.device)
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty(o_shape, dtype=q.dtype, device=q.device)
+        if lse is None and return_lse:
+            lse = torch.empty(l_shape, dtype=torch.float32, device=q.device)
     _need(tuple(out.shape) == o_shape and (lse is None or tuple(lse.shape) == l_shape),
           "out / lse shapes do not match q")
     if workspace is None:
-        workspace = workspace_for(shape, mla=False, num_splits=num_splits, device=q.device)
+        workspace = workspace_for(shape, mla=False, num_splits=num_splits, device=q.device,
+                                  stream=stream)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     group = Hq // shape.num_kv_heads
     rc = load().paged_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
@@ -261,14 +289,16 @@ def paged_decode_attn_mla(q, kv_cache, block_tables, context_lens, *, scale: flo
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
     o_shape, l_shape = _result_shapes(q, head_dim_v)
-    if out is None:
-        out = torch.empty(o_shape, dtype=q.dtype, device=q.device)
-    if lse is None and return_lse:
-        lse = torch.empty(l_shape, dtype=torch.float32, device=q.device)
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty(o_shape, dtype=q.dtype, device=q.device)
+        if lse is None and return_lse:
+            lse = torch.empty(l_shape, dtype=torch.float32, device=q.device)
     _need(tuple(out.shape) == o_shape and (lse is None or tuple(lse.shape) == l_shape),
           "out / lse shapes do not match q")
     if workspace is None:
-        workspace = workspace_for(shape, mla=True, num_splits=num_splits, device=q.device)
+        workspace = workspace_for(shape, mla=True, num_splits=num_splits, device=q.device,
+                                  stream=stream)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load().paged_decode_attn_mla(_ptr(q), _ptr(kv_cache), _ptr(block_tables),
                                       _ptr(context_lens), float(scale), int(num_splits),
@@ -320,6 +350,30 @@ def paged_kv_append(k_new, v_new, block_tables, positions, k_cache, v_cache=None
                                 _stream_handle(stream))
     if rc:
         raise PdaError(rc, "paged_kv_append")
+
+
+class StreamProbe:
+    """pda_stream_probe with marshalled arguments: reads the K/V bytes a
+    GQA call with `shape` and `num_splits` reads, with its access pattern and
+    no arithmetic (the practical bandwidth ceiling of that call).  caches:
+    (k_cache, v_cache) pairs to rotate over, as in PreparedCall."""
+
+    def __init__(self, shape: Shape, caches, block_tables, context_lens, *, num_splits=0,
+                 steps_in_flight=1, stream=None):
+        info = plan(shape, num_splits=num_splits)
+        self._lib = load()
+        self._sink = torch.empty(max(1, shape.batch * shape.num_kv_heads * info.max_splits),
+                                 dtype=torch.int32, device=block_tables.device)
+        self._keep = (shape, caches, block_tables, context_lens)
+        st = _stream_handle(stream)
+        self._args = [(_ptr(k), _ptr(v), _ptr(block_tables), _ptr(context_lens),
+                       ctypes.byref(shape), int(num_splits), int(steps_in_flight),
+                       _ptr(self._sink), st) for k, v in caches]
+
+    def __call__(self, i: int = 0):
+        rc = self._lib.pda_stream_probe(*self._args[i % len(self._args)])
+        if rc:
+            raise PdaError(rc, "pda_stream_probe")
 
 
 def check_inputs(block_tables, context_lens, *, page_size: int, num_pages: int,

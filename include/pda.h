@@ -172,19 +172,30 @@ typedef struct pda_plan_info {
   uint64_t workspace_bytes; /* bytes the call needs in `workspace`          */
 } pda_plan_info;
 
-/* Choose the split layout for a call (host only, no device work).
+/* Choose the split layout for a call (host only, no device work).  The pages
+ * leave the split count to the caller and its heuristic: "From MHA to MLA"
+ * sec. 4 (the closing paragraph) chooses num_splits from the batch size, the
+ * head tiles, the context length and the number of SMs, splitting only when
+ * the (sequence, head) work alone leaves compute units idle; the drill page
+ * sec. 6 shows the cost of not splitting at batch 1.  This planner fills two
+ * workgroups per compute unit.
  * num_splits: 0 = automatic (fill the GPU's compute units), otherwise the
- * largest number of splits any sequence may use.  num_cus: compute units to
- * plan for; 0 = query the current HIP device.  Sequences longer than
- * shape->split_min_tokens use ceil(pages / pages_per_split) splits, others one.
- * is_mla selects the MLA kernel's tiling.  Returns PDA_OK or an error code. */
+ * largest number of splits any sequence may use (at most 64 with the BALANCED
+ * schedule).  num_cus: compute units to plan for; 0 = query the current HIP
+ * device.  Sequences longer than shape->split_min_tokens use ceil(pages /
+ * pages_per_split) splits, others one.  is_mla selects the MLA kernel's
+ * tiling.  Returns PDA_OK or an error code (PDA_ERR_UNSUPPORTED when a
+ * BALANCED call's unit list would exceed 32-bit grid indexing). */
 int pda_plan(const pda_shape* shape, int is_mla, int num_splits, int num_cus,
              pda_plan_info* plan);
 
 /* Workspace bytes a call with these arguments needs (0 when no sequence can
- * split and the work is not ordered).  Queries the current device's CU count
- * when num_splits == 0 or the schedule is BALANCED.  Returns 0 on invalid
- * arguments as well.
+ * split and the work is not ordered): the split partials of "From MHA to MLA"
+ * sec. 4 (an fp32 output row and an fp32 LSE per split and query row) and
+ * the ordered work list.  Queries the current device's CU count when
+ * num_splits == 0 or the schedule is BALANCED.  Returns 0 on invalid
+ * arguments as well.  The workspace needs no initialization: every call
+ * writes what it reads.
  *
  * Work ordering: when shape->split_min_tokens > 0 (a batch of mixed lengths,
  * as the threshold signals) or the schedule is BALANCED, each call first
@@ -205,7 +216,8 @@ size_t pda_workspace_bytes(const pda_shape* shape, int is_mla, int num_splits);
  * queries and a variant other than PDA_GQA_VALU (the matrix-core kernel,
  * whose columns are the q_len * group (query, head) rows of a KV group).
  * workspace: at least pda_workspace_bytes(shape, 0, num_splits) bytes, may
- * be NULL when that is 0. */
+ * be NULL when that is 0.  Calls that share a workspace must not overlap
+ * (order them on one stream). */
 int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens, int group,
                       float scale, int num_splits, void* out, float* lse,
@@ -280,12 +292,34 @@ int pda_check_inputs(const pda_shape* shape, const int32_t* block_tables,
                      const int32_t* context_lens, const int32_t* positions, int32_t* result,
                      void* stream);
 
+/* Streaming-read probe: a measurement aid, not a step of the decode path.
+ * Reads exactly the K and V bytes that paged_decode_attn reads for the same
+ * arguments (the pages of each sequence through block_tables, the valid
+ * rows of the last page; "From MHA to MLA" sec. 5, the drill page sec. 4)
+ * with the attention kernels' access pattern -- one workgroup per
+ * (sequence, KV head, split) as the GRID schedule plans it for num_splits,
+ * 16-token tiles, row pieces of up to 16 bytes per lane, non-temporal
+ * loads -- but does no arithmetic: it folds the words it loads into one
+ * 32-bit word per workgroup of `sink`.  Its duration is the practical
+ * ceiling for that access pattern on the device (the attention kernel's
+ * time over it is the fraction of that ceiling the kernel reaches).
+ *   steps_in_flight: 1..4, tiles each wave keeps in flight;
+ *   sink: DEVICE array of at least batch * num_kv_heads * max_splits uint32
+ *         (pda_plan_info.max_splits of the same call), contents unspecified.
+ * Needs head_dim == head_dim_v with rows of 64, 128, 256 or 512 bytes and the
+ * GRID schedule; other shape fields as for paged_decode_attn (q_dtype and
+ * q_len are ignored).  Asynchronous on `stream`; returns a pda_status. */
+int pda_stream_probe(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, const pda_shape* shape, int num_splits,
+                     int steps_in_flight, uint32_t* sink, void* stream);
+
 /* Static description of a status code. */
 const char* pda_status_string(int status);
 
-/* Library version, major * 10000 + minor * 100 + patch: 200 (0.2.0).  0.2
- * appended kv_layout to pda_shape and added pda_check_inputs; a caller built
- * against an older header passes a shorter pda_shape and must be rebuilt. */
+/* Library version, major * 10000 + minor * 100 + patch: 300 (0.3.0).  0.2
+ * appended kv_layout to pda_shape and added pda_check_inputs (a caller built
+ * against an older header passes a shorter pda_shape and must be rebuilt);
+ * 0.3 added pda_stream_probe and caps BALANCED calls at 64 splits. */
 int pda_version(void);
 
 #ifdef __cplusplus

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(pda.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pda_version() == 200
+    assert lib.pda_version() == 300
     assert lib.pda_status_string(3) == b"workspace missing or too small"
 
 
@@ -105,6 +105,23 @@ def test_plan_balanced_schedule():
     bad = _shape(schedule=2)
     assert pda.load().paged_decode_attn(fake, fake, fake, fake, fake, 4, 0.1, 1, fake, None,
                                         ctypes.byref(bad), None, 0, None) == 1
+
+
+def test_plan_balanced_split_cap_and_limits():
+    """BALANCED with an explicit split count is capped at 64 splits (its unit
+    list is bounded by batch + target anyway); a batch whose unit list would
+    pass 32-bit grid indexing is refused instead of running unordered."""
+    bal = dict(schedule=pda.PDA_SCHEDULE_BALANCED)
+    p = pda.plan(_shape(batch=4, max_pages_per_seq=4096, **bal), num_splits=4000, num_cus=256)
+    assert (p.max_splits, p.ordered) == (64, 1)
+    p = pda.plan(_shape(batch=4, max_pages_per_seq=4096), num_splits=4000, num_cus=256)
+    assert p.max_splits == 2048                               # GRID: 2-page splits
+    s = _shape(batch=300_000_000, **bal)
+    info = pda.PlanInfo()
+    assert pda.load().pda_plan(ctypes.byref(s), 0, 0, 256, ctypes.byref(info)) == 2
+    # GRID with a threshold may still run unordered when the list is too long
+    p = pda.plan(_shape(batch=300_000_000, split_min_tokens=64), num_splits=2, num_cus=256)
+    assert p.ordered == 0
 
 
 def test_plan_head_tiles():
@@ -315,3 +332,17 @@ def test_check_inputs_validation():
     for kw in (dict(page_size=0), dict(num_pages=0), dict(batch=-1), dict(q_len=-1)):
         assert lib.pda_check_inputs(ctypes.byref(_shape(**kw)), fake, fake, None, fake,
                                     None) == 1, kw
+
+
+def test_stream_probe_validation():
+    fake = ctypes.c_void_p(0x1000)
+    lib = pda.load()
+    s = _shape()
+    args = lambda sh, steps=1, sink=fake: (fake, fake, fake, fake, ctypes.byref(sh), 0, steps,
+                                           sink, None)
+    assert lib.pda_stream_probe(*args(s, steps=0)) == 1
+    assert lib.pda_stream_probe(*args(s, steps=5)) == 1
+    assert lib.pda_stream_probe(*args(s, sink=None)) == 1
+    assert lib.pda_stream_probe(*args(_shape(schedule=pda.PDA_SCHEDULE_BALANCED))) == 2
+    assert lib.pda_stream_probe(*args(_shape(head_dim_v=64))) == 2
+    assert lib.pda_stream_probe(*args(_shape(batch=0), steps=2)) == 0   # nothing to read

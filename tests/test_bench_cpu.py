@@ -39,3 +39,14 @@ def test_committed_traffic_records(name):
     assert 1.0 <= t["fetch_over_algorithmic"] < 1.02
     assert t["bytes_per_launch"] == pytest.approx(t["fetch_bytes"] + t["write_bytes"], rel=1e-6)
     assert t["command"] and t["source_files"]
+
+
+def test_cpu_baseline_times_one_thread_and_all_threads():
+    """The oracle baseline reports the all-thread and the one-thread rate
+    (each a median of 3 runs), the thread count and the host's CPU model."""
+    from decode_attention_paged_02_amd import workloads as W
+    r = bench.cpu_baseline(W.tiny_gqa(), budget_s=0.3)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
+    assert r["cores"] >= 1 and r["one_thread"]["value"] > 0
+    assert "median of 3" in r["sample"]
+    assert r["host"]["cpu_model"] and r["host"]["nproc"] >= 1

@@ -387,3 +387,4 @@ def test_very_long_context_many_splits(very_long, splits):
     for name, v in VARIANTS.items():
         out, lse = pda.run_case(case, dev, num_splits=splits, variant=v)
         check(case, out, lse, ref_o, ref_l, label="very long %d %s" % (splits, name))
+

@@ -122,3 +122,47 @@ def test_append_head_major_bit_exact(src, cache):
                                 cache_dtype=cache, scale=sc, kv_layout=HEAD_MAJOR)
         got = dev.cpu().view(torch.uint8).numpy() if dev.dtype != torch.uint8 else dev.cpu().numpy()
         assert np.array_equal(got.reshape(-1), want.view(np.uint8).reshape(-1))
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("kv_dtype,num_splits,thr", [("f16", 1, 0), ("f16", 3, 0),
+                                                      ("e4m3", 4, 100), ("bf16", 0, 0)])
+def test_stream_probe_reads_exactly_the_call_bytes(layout, kv_dtype, num_splits, thr):
+    """The streaming probe reads the bytes the attention call reads: each
+    workgroup's sink word equals the XOR of the 32-bit words of its K and V
+    rows (its sequence, KV head and split range), computed on the host from
+    the stored cache.  Rows past the context are NaN-poisoned, so a probe that
+    read them would fold different words."""
+    import numpy as np
+    q_dt = "f16" if kv_dtype != "bf16" else "bf16"
+    case = W.make_gqa(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                      context_lens=[37, 300, 1], q_dtype=q_dt, kv_dtype=kv_dtype, seed=61,
+                      kv_layout=layout, extra_pages=2)
+    say("stream probe", layout, kv_dtype, num_splits, thr)
+    dev = pda.to_device(case)
+    shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                          split_min_tokens=thr, kv_layout=layout, k_scale=case.k_scale,
+                          v_scale=case.v_scale)
+    info = pda.plan(shape, num_splits=num_splits)
+    probe = pda.StreamProbe(shape, [(dev.k_cache, dev.v_cache)], dev.block_tables,
+                            dev.context_lens, num_splits=num_splits, steps_in_flight=2)
+    probe()
+    torch.cuda.synchronize()
+    got = probe._sink.cpu().numpy().view(np.uint32).reshape(info.max_splits, 3, 2)
+    kc, vc = np.ascontiguousarray(case.k_cache), np.ascontiguousarray(case.v_cache)
+    P = case.page_size
+    for b in range(3):
+        n = int(case.context_lens[b])
+        pages = -(-n // P)
+        split = n > thr and info.max_splits > 1
+        pps = info.pages_per_split if split else max(pages, 1)
+        for kvh in range(2):
+            for sp in range(info.max_splits):
+                t0, t1 = sp * pps * P, min((sp + 1) * pps * P, n)
+                want = 0
+                for t in range(t0, t1) if (split or sp == 0) else []:
+                    pg = int(case.block_tables[b][t // P])
+                    for c in (kc, vc):
+                        row = c[pg, kvh, t % P] if layout else c[pg, t % P, kvh]
+                        want ^= int(np.bitwise_xor.reduce(row.view(np.uint32)))
+                assert int(got[sp, b, kvh]) == want, (b, kvh, sp)
