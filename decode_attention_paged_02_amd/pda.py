@@ -53,7 +53,7 @@ class PlanInfo(ctypes.Structure):
 
 EXPORTS = ("pda_plan", "pda_workspace_bytes", "paged_decode_attn", "paged_decode_attn_mla",
            "paged_kv_append", "pda_check_inputs", "pda_stream_probe", "pda_status_string",
-           "pda_version")
+           "pda_version", "paged_decode_attn_noalloc")
 
 _lib = None
 
@@ -75,6 +75,8 @@ def load() -> ctypes.CDLL:
     lib.pda_workspace_bytes.restype = sz
     lib.paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, sp, vp, sz, vp]
     lib.paged_decode_attn.restype = i32
+    lib.paged_decode_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, f32, i32, vp, vp, sp, vp]
+    lib.paged_decode_attn_noalloc.restype = i32
     lib.paged_decode_attn_mla.argtypes = [vp, vp, vp, vp, f32, i32, vp, vp, sp, vp, sz, vp]
     lib.paged_decode_attn_mla.restype = i32
     lib.paged_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, sp, vp]

@@ -224,6 +224,23 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                       const pda_shape* shape, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* paged_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, hosts that forbid hipMalloc):
+ * the same arguments without the workspace.  The call's workspace (split
+ * partials, the ordered work list) lives in a device array that the library
+ * holds on each GPU it runs on until the process ends: 64 MiB
+ * (67,108,864 bytes) per GPU.  A call whose plan needs more
+ * (pda_plan_info.workspace_bytes) returns PDA_ERR_WORKSPACE before any
+ * device work.  The call allocates nothing; its first call on a device
+ * looks up that device's array once.  Every call on one GPU uses the same
+ * array: calls that overlap on one GPU (on different streams) race, so order
+ * them on one stream.  Nothing in the array needs initializing: each call
+ * writes what it reads. */
+int paged_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int group, float scale, int num_splits, void* out, float* lse,
+                              const pda_shape* shape, void* stream);
+
 /* MLA paged decode attention over a latent cache (FlashMLA-ETAP "Usage";
  * "From MHA to MLA" sec. 6).  shape->num_kv_heads must be 1, (head_dim,
  * head_dim_v) (576, 512) or (320, 256) (a 512- or 256-wide latent + 64 rope

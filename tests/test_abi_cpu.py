@@ -346,3 +346,21 @@ def test_stream_probe_validation():
     assert lib.pda_stream_probe(*args(_shape(schedule=pda.PDA_SCHEDULE_BALANCED))) == 2
     assert lib.pda_stream_probe(*args(_shape(head_dim_v=64))) == 2
     assert lib.pda_stream_probe(*args(_shape(batch=0), steps=2)) == 0   # nothing to read
+
+
+def test_no_alloc_entry_point_refuses_before_device_work():
+    """paged_decode_attn_noalloc validates like paged_decode_attn and refuses a
+    plan beyond its 64 MiB array (PDA_ERR_WORKSPACE) without any HIP call."""
+    fake = ctypes.c_void_p(0x1000)
+    lib = pda.load()
+    big = _shape(batch=512, num_q_heads=64, max_pages_per_seq=1024, num_pages=1 << 20)
+    assert pda.plan(big, num_splits=8, num_cus=256).workspace_bytes > 64 << 20
+    call = lambda sh, group=8, ns=8, q=fake: lib.paged_decode_attn_noalloc(
+        q, fake, fake, fake, fake, group, ctypes.c_float(0.1), ns, fake, None,
+        ctypes.byref(sh), None)
+    assert call(big) == 3
+    assert call(big, q=None) == 1
+    assert call(big, group=4) == 1
+    assert call(big, ns=-1) == 1
+    assert call(_shape(head_dim=96, head_dim_v=96), group=4) == 2
+    assert call(_shape(batch=0), group=4) == 0
