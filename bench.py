@@ -176,7 +176,42 @@ def run_gpu(case, workload, steps, warmup, pools, min_warmup_ms=100.0):
                 overhead_bytes=A.case_overhead_bytes(case, plan.max_splits),
                 kv_bytes=nbytes, n_pools=len(caches), max_splits=plan.max_splits,
                 pages_per_split=plan.pages_per_split, workgroups=plan.workgroups,
-                launches=(1 if plan.max_splits == 1 else 2) + (1 if plan.ordered else 0))
+                launches=(1 if plan.max_splits == 1 else 2) + (1 if plan.ordered else 0),
+                probe=read_probe(case, dev, caches, shape, nsplit, steps) if not case.mla else None)
+
+
+def read_probe(case, dev, caches, shape, num_splits, steps):
+    """The streaming-read probe (pda_stream_probe) over the same pools: the
+    K/V bytes of this call read with the attention kernels' access pattern
+    and no arithmetic, on the GRID split layout of the same split count (1
+    and 2 tiles in flight per wave; the faster counts).  Its time is the
+    practical ceiling of that access pattern on this device."""
+    import torch
+    from decode_attention_paged_02_amd import pda
+    sh = pda.Shape.from_buffer_copy(shape)
+    sh.schedule = pda.PDA_SCHEDULE_GRID
+    best = None
+    for sd in (1, 2):
+        pr = pda.StreamProbe(sh, caches, dev.block_tables, dev.context_lens,
+                             num_splits=num_splits, steps_in_flight=sd)
+        for i in range(200):
+            pr(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            pr(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / steps
+        if best is None or us < best[0]:
+            best = (us, sd)
+    return {"us": round(best[0], 3), "steps_in_flight": best[1],
+            "GB/s": round(A_kv_bytes(case) / (best[0] * 1e-6) / 1e9, 1)}
+
+
+def A_kv_bytes(case):
+    from decode_attention_paged_02_amd import accounting as A
+    return A.case_kv_bytes(case)
 
 
 APPEND_WORKLOADS = {"kv_append_b64": "gqa_b64", "kv_append_ragged_fp8": "ragged_fp8",
@@ -389,6 +424,9 @@ def main():
                            "and 90th percentile (per-step event overhead included)"},
             "algorithmic_bytes_per_launch": r["kv_bytes"],
             "step_us": r["step_us"], "overhead_bytes_per_step": r["overhead_bytes"]}
+    if r.get("probe"):
+        roof["read_probe"] = r["probe"]
+        roof["frac_of_practical_ceiling"] = round(r["probe"]["us"] / us_step, 4)
     others = {}
     for w in [x for x in args.others.split(",") if x and x not in (args.workload, "none")]:
         _log("other workload", w)
@@ -403,10 +441,23 @@ def main():
                      "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4),
                      "max_splits": r2["max_splits"], "kv_bytes": r2["kv_bytes"],
                      "step_us_median": r2["step_us"]["median"]}
+        if r2.get("probe"):
+            others[w]["read_probe_us"] = r2["probe"]["us"]
+            others[w]["frac_of_practical_ceiling"] = round(r2["probe"]["us"] / u2, 4)
         del c2
     if not args.no_bw_probe:
         _log("bandwidth probe")
         roof["measured_device_bw"] = bandwidth_probe()
+    # the read ceiling of the B=64 step per page layout (streaming probe)
+    reads = {}
+    if r.get("probe") and case.kv_layout == 1 and not case.mla:
+        reads["head-major %s" % case.name] = r["probe"]["GB/s"]
+    for w, o in others.items():
+        if "read_probe_us" in o and w in ("gqa_b64", "gqa_b64_hm"):
+            reads[("head-major " if w.endswith("_hm") else "token-major ") + w] = round(
+                o["kv_bytes"] / (o["read_probe_us"] * 1e-6) / 1e9, 1)
+    if reads:
+        roof.setdefault("measured_device_bw", {})["read_probe_GBs"] = reads
     cpu = None
     if not args.no_cpu_baseline:
         _log("cpu baseline (oracle)")
