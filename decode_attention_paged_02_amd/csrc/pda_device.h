@@ -358,6 +358,150 @@ __device__ __forceinline__ float wave_sum_from(float x) {
   return x;
 }
 
+// ------------------------------------------------------------ unit planning
+
+// LDS scratch of plan_unit.
+struct PlanShared {
+  unsigned long long pages[16];  // per-wave page sums
+  int bucket_count[33];          // units per token-count bit length
+  int wave_sum[16];              // per-wave unit counts of the chosen bucket
+  int result[5];                 // b, split, t0, t1, split count of b
+};
+
+// Splits of a sequence of n tokens under an ordered call's rules (the same
+// rules as the planning kernel): ns splits of pps pages.
+__device__ __forceinline__ void unit_layout(const UnitPlan& p, int n, int chunk, int& ns,
+                                            int& pps) {
+  const int P = p.page_size;
+  const int pages = (n + P - 1) / P;
+  const int S = p.split.max_splits;
+  if (S <= 1 || n <= p.split.split_min_tokens || (p.balanced && pages <= chunk)) {
+    ns = 1;
+    pps = pages > 0 ? pages : 1;
+  } else if (!p.balanced) {
+    pps = p.split.pages_per_split;
+    ns = (pages + pps - 1) / pps;
+  } else {
+    ns = min(S, (pages + chunk - 1) / chunk);
+    pps = (pages + ns - 1) / ns;
+    ns = (pages + pps - 1) / pps;
+  }
+}
+
+__device__ __forceinline__ int token_bucket(int tok) { return tok > 0 ? 32 - __clz(tok) : 0; }
+
+// Work unit `rank` of an ordered call, computed by a whole workgroup of NT
+// threads from the sequence lengths (batch <= kInKernelPlanMaxBatch), so that
+// no planning launch precedes the attention kernel.  The units are the
+// planning kernel's: every sequence cut into its splits, listed by decreasing
+// bit length of their token count (longest first).  Inside a bit length they
+// follow (sequence, split) order, so the list is a function of the lengths
+// alone and every workgroup derives the same one.  Returns b = -1 past the
+// last unit; ns_b is the unit's sequence's split count.  Every thread of the
+// workgroup must call it (it synchronizes the workgroup).
+template <int NT>
+__device__ WorkUnit plan_unit(const int32_t* lens, const UnitPlan& p, int rank, PlanShared& sh,
+                              int& ns_b) {
+  constexpr int NW = NT / 64;
+  constexpr int PERMAX = (kInKernelPlanMaxBatch + NT - 1) / NT;
+  static_assert(NW <= 16, "workgroup size");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = p.batch;
+  const int per = (B + NT - 1) / NT;  // sequences per thread, contiguous
+  int n[PERMAX];
+  unsigned long long my_pages = 0;
+#pragma unroll
+  for (int i = 0; i < PERMAX; ++i) {
+    const int b = tid * per + i;
+    n[i] = (i < per && b < B) ? load_uniform_v(lens + b) : -1;
+    if (n[i] >= 0) my_pages += (unsigned)((n[i] + p.page_size - 1) / p.page_size);
+  }
+  if (tid < 33) sh.bucket_count[tid] = 0;
+  if (p.balanced) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) my_pages += __shfl_xor(my_pages, o, 64);
+    if (lane == 0) sh.pages[wave] = my_pages;
+  }
+  __syncthreads();
+  int chunk = 0;
+  if (p.balanced) {  // a chunk of the batch's total pages over the target unit count
+    unsigned long long total = 0;
+    for (int w = 0; w < NW; ++w) total += sh.pages[w];
+    const unsigned long long c = (total + p.target_units - 1) / p.target_units;
+    chunk = (int)(c > (unsigned long long)p.min_chunk_pages ? c : p.min_chunk_pages);
+  }
+  // splits of this thread's sequences; units per token-count bucket: the
+  // ns - 1 full splits and the last one
+  int ns[PERMAX], pps[PERMAX], bf[PERMAX], bl[PERMAX];
+#pragma unroll
+  for (int i = 0; i < PERMAX; ++i) {
+    ns[i] = 0;
+    pps[i] = 1;
+    bf[i] = bl[i] = -1;
+    if (n[i] < 0) continue;
+    unit_layout(p, n[i], chunk, ns[i], pps[i]);
+    const int full = pps[i] * p.page_size;
+    bf[i] = token_bucket(full);
+    bl[i] = token_bucket(n[i] - (ns[i] - 1) * full);
+    if (ns[i] > 1) atomicAdd(&sh.bucket_count[bf[i]], ns[i] - 1);
+    atomicAdd(&sh.bucket_count[bl[i]], 1);
+  }
+  __syncthreads();
+  // the bucket that holds `rank`, from the longest down, and the rank in it
+  int bucket = -1, k = rank;
+  for (int q = 32; q >= 0; --q) {
+    const int c = sh.bucket_count[q];
+    if (k < c) {
+      bucket = q;
+      break;
+    }
+    k -= c;
+  }
+  if (bucket < 0) {  // (the same for every thread)
+    ns_b = 0;
+    return WorkUnit{-1, -1, 0, 0};
+  }
+  // this thread's units in that bucket, then an exclusive scan over the
+  // threads (sequence order)
+  int cnt[PERMAX], mine = 0;
+#pragma unroll
+  for (int i = 0; i < PERMAX; ++i) {
+    cnt[i] = ns[i] == 0 ? 0
+                        : (ns[i] > 1 && bf[i] == bucket ? ns[i] - 1 : 0) + (bl[i] == bucket ? 1 : 0);
+    mine += cnt[i];
+  }
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sh.wave_sum[wave] = incl;
+  __syncthreads();
+  int before = incl - mine;
+  for (int w = 0; w < wave; ++w) before += sh.wave_sum[w];
+  if (k >= before && k < before + mine) {  // exactly one thread
+    int kk = k - before;
+#pragma unroll
+    for (int i = 0; i < PERMAX; ++i) {
+      if (kk >= 0 && kk < cnt[i]) {
+        // the full splits of the bucket come first, then the last split
+        const int sp = (ns[i] > 1 && bf[i] == bucket && kk < ns[i] - 1) ? kk : ns[i] - 1;
+        const int full = pps[i] * p.page_size;
+        sh.result[0] = tid * per + i;
+        sh.result[1] = ns[i] == 1 ? -1 : sp;
+        sh.result[2] = sp * full;
+        sh.result[3] = min((sp + 1) * full, n[i]);
+        sh.result[4] = ns[i];
+      }
+      kk -= cnt[i];
+    }
+  }
+  __syncthreads();
+  ns_b = sh.result[4];
+  return WorkUnit{sh.result[0], sh.result[1], sh.result[2], sh.result[3]};
+}
+
 __device__ __forceinline__ void split_range(const SplitLayout& sp, int n, int P, int split,
                                             int& nsplit, int& t0, int& t1) {
   const int pages = (n + P - 1) / P;

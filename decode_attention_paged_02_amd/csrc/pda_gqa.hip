@@ -463,6 +463,12 @@ __global__ __launch_bounds__(kGqaWaves * 64, 2) void gqa_split_kernel(GqaArgs a)
 // ---------------------------------------------------------------- combine
 
 constexpr int kCombineThreads = 256;
+// Split counts up to this take combine_rows_kernel (every split of a row in
+// one thread), larger ones combine_kernel (a row's splits spread over threads).
+#ifndef PDA_COMBINE_ROWS_MAX_SPLITS
+#define PDA_COMBINE_ROWS_MAX_SPLITS 16
+#endif
+constexpr int kCombineRowsMaxSplits = PDA_COMBINE_ROWS_MAX_SPLITS;
 
 // One workgroup per (sequence, query token, query head) row whose sequence
 // was split and per CW-wide column chunk of it (CW = min(DV, 128)):
@@ -591,6 +597,78 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       const int i = ih / a.num_q_heads, h = ih - i * a.num_q_heads;
       a.lse[((int64_t)b * a.num_q_heads + h) * a.q_len + i] = d > 0.f ? M + __logf(d) : -INFINITY;
     }
+  }
+}
+
+// Combine for calls with at most MAXS splits per sequence: a workgroup takes
+// kCombineThreads / (DV / 4) consecutive rows, each thread one four-column
+// chunk of one row and every split of it at once (one memory round trip after
+// the split count is known, no LDS, no barrier).  The same algebra as
+// combine_kernel: L = M + ln sum_s exp(L_s - M), O = sum_s exp(L_s - M) O_s /
+// sum_s exp(L_s - M), M = max_s L_s, in split order.
+template <class OT, int DV, int MAXS>
+__global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(
+    const float* part_o, const float* part_lse, const int32_t* context_lens, int32_t rows_per_seq,
+    int32_t max_splits, int32_t pages_per_split, int32_t split_min_tokens, int32_t page_size,
+    CombineArgs a) {
+  constexpr int DC = DV / 4;                  // four-float chunks per row
+  constexpr int RPW = kCombineThreads / DC;   // rows per workgroup
+  static_assert(RPW * DC == kCombineThreads, "row width");
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / DC;
+  const int c = threadIdx.x % DC;
+  const int64_t nrows = (int64_t)a.batch * rows_per_seq;
+  if (row >= nrows) return;
+  const int b = (int)(row / rows_per_seq);
+  const int S = max_splits;
+  const SplitLayout sp{pages_per_split, max_splits, split_min_tokens};
+  const float* pl = part_lse + row * S;
+  const f32x4* po = (const f32x4*)(part_o + row * S * DV) + c;
+  const bool guarded = split_min_tokens > 0 || a.seq_splits;
+  int nsplit = S, t0, t1;
+  if (a.seq_splits) {
+    nsplit = load_uniform_v(a.seq_splits + b);
+  } else if (guarded) {
+    split_range(sp, load_uniform_v(context_lens + b), page_size, 0, nsplit, t0, t1);
+  }
+  if (guarded && nsplit <= 1) return;  // the attention kernel wrote this row
+  float l[MAXS];
+  f32x4 o[MAXS];
+#pragma unroll
+  for (int j = 0; j < MAXS; ++j) {
+    const bool ok = j < (guarded ? nsplit : S);
+    l[j] = ok ? pl[j] : -INFINITY;
+    o[j] = ok ? po[(int64_t)j * (DV / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (!guarded) {  // (the length comes with the partials, in the same round trip)
+    split_range(sp, load_uniform_v(context_lens + b), page_size, 0, nsplit, t0, t1);
+    if (nsplit <= 1) return;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < MAXS; ++j)
+    if (j < nsplit) M = fmaxf(M, l[j]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < MAXS; ++j) {
+      if (j < nsplit && l[j] != -INFINITY) {
+        const float w = __expf(l[j] - M);
+        den += w;
+        acc += w * o[j];
+      }
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const int64_t o0 = row * DV + 4 * c;
+  store_out<OT>(a.out, o0, acc.x * inv);
+  store_out<OT>(a.out, o0 + 1, acc.y * inv);
+  store_out<OT>(a.out, o0 + 2, acc.z * inv);
+  store_out<OT>(a.out, o0 + 3, acc.w * inv);
+  if (c == 0 && a.lse) {  // lse is [B, Hq, q_len]
+    const int ih = (int)(row - (int64_t)b * rows_per_seq);
+    const int i = ih / a.num_q_heads, h = ih - i * a.num_q_heads;
+    a.lse[((int64_t)b * a.num_q_heads + h) * a.q_len + i] = den > 0.f ? M + __logf(den) : -INFINITY;
   }
 }
 
@@ -766,14 +844,42 @@ hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
   return hipErrorInvalidValue;
 }
 
-template <class OT>
-hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
-  const int nch = a.head_dim_v > 128 ? a.head_dim_v / 128 : 1;
-  dim3 grid((unsigned)(a.batch * a.q_len * a.num_q_heads * nch));
+// Rows kernel for up to MAXS splits (rows of DV columns, RPW per workgroup).
+template <class OT, int DV>
+hipError_t launch_combine_rows(const CombineArgs& a, hipStream_t s) {
+  constexpr int RPW = kCombineThreads / (DV / 4);
+  const int64_t rows = (int64_t)a.batch * a.q_len * a.num_q_heads;
+  dim3 grid((unsigned)((rows + RPW - 1) / RPW));
   dim3 block(kCombineThreads);
 #define PDA_COMBINE_ARGS                                                                    \
   a.part_o, a.part_lse, a.context_lens, a.q_len * a.num_q_heads, a.split.max_splits,       \
       a.split.pages_per_split, a.split.split_min_tokens, a.page_size, a
+  if (a.split.max_splits <= 8)
+    hipLaunchKernelGGL((combine_rows_kernel<OT, DV, 8>), grid, block, 0, s, PDA_COMBINE_ARGS);
+  else
+    hipLaunchKernelGGL((combine_rows_kernel<OT, DV, 16>), grid, block, 0, s, PDA_COMBINE_ARGS);
+  return hipGetLastError();
+}
+
+template <class OT>
+hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
+  // rows kernel: few splits and enough rows for at least 64 workgroups (with
+  // fewer rows, one workgroup per row and its splits spread over the threads
+  // finish sooner: B=4 at 32768 tokens, 16 splits, 84.5 against 85.2 us)
+  const int64_t row_wgs = (int64_t)a.batch * a.q_len * a.num_q_heads * a.head_dim_v / 4 /
+                          kCombineThreads;
+  if (a.split.max_splits <= kCombineRowsMaxSplits && row_wgs >= 64) {
+    switch (a.head_dim_v) {
+      case 64: return launch_combine_rows<OT, 64>(a, s);
+      case 128: return launch_combine_rows<OT, 128>(a, s);
+      case 256: return launch_combine_rows<OT, 256>(a, s);
+      case 512: return launch_combine_rows<OT, 512>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  const int nch = a.head_dim_v > 128 ? a.head_dim_v / 128 : 1;
+  dim3 grid((unsigned)(a.batch * a.q_len * a.num_q_heads * nch));
+  dim3 block(kCombineThreads);
   switch (a.head_dim_v) {
     case 64: hipLaunchKernelGGL((combine_kernel<OT, 64>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
     case 128: hipLaunchKernelGGL((combine_kernel<OT, 128>), grid, block, 0, s, PDA_COMBINE_ARGS); break;

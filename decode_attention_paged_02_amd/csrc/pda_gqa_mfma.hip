@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   const int grp = lane >> 4;  // lane group
 
   // which (sequence, KV head, head tile, split) this workgroup computes
-  const bool ordered = units != nullptr;
+  const bool ordered = units != nullptr || a.plan_in_kernel;
   int tile, kvh, b, split, ut0 = 0, ut1 = 0;
   if (ordered) {
     // ordered: the unit list gives (sequence, split, token range) longest
@@ -198,7 +198,21 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     group_tile(blockIdx.x, gridDim.x / head_tiles, head_tiles, g, tile);
     g = __builtin_amdgcn_readfirstlane(g);  // (uniform: scalar registers)
     tile = __builtin_amdgcn_readfirstlane(tile);
-    const WorkUnit w = load_unit(units, g / num_kv_heads);
+    WorkUnit w;
+    if (units) {  // the planning kernel's list
+      w = load_unit(units, g / num_kv_heads);
+    } else {      // this workgroup derives its unit from the lengths
+      __shared__ PlanShared plan_sh;
+      int ns_b;
+      w = plan_unit<kMWaves * 64>(context_lens, a.plan, g / num_kv_heads, plan_sh, ns_b);
+      w.b = __builtin_amdgcn_readfirstlane(w.b);
+      w.split = __builtin_amdgcn_readfirstlane(w.split);
+      w.t0 = __builtin_amdgcn_readfirstlane(w.t0);
+      w.t1 = __builtin_amdgcn_readfirstlane(w.t1);
+      // the sequence's split count, for the combine kernel (written once)
+      if (w.b >= 0 && w.split <= 0 && g % num_kv_heads == 0 && tile == 0 && threadIdx.x == 0)
+        a.seq_splits[w.b] = ns_b;
+    }
     if (w.b < 0) return;
     b = w.b;
     split = w.split;
@@ -559,7 +573,7 @@ void launch_sd(const GqaArgs& a, dim3 grid, dim3 block, hipStream_t s) {
 #define PDA_MFMA_ARGS                                                                        \
   a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.q_len,        \
       a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a.units, a
-  if (a.units)
+  if (a.units || a.plan_in_kernel)
     hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlightOrdered>), grid, block,
                        0, s, PDA_MFMA_ARGS);
   else
@@ -572,7 +586,8 @@ template <class QT, class KT>
 hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStream_t s) {
   const unsigned units = (unsigned)(a.batch * a.num_kv_heads * a.head_tiles);
   const unsigned nhu = (unsigned)(a.num_kv_heads * a.head_tiles);
-  dim3 grid(a.units ? nhu * (unsigned)a.unit_count : units, a.units ? 1u : (unsigned)max_splits);
+  const bool ordered = a.units || a.plan_in_kernel;
+  dim3 grid(ordered ? nhu * (unsigned)a.unit_count : units, ordered ? 1u : (unsigned)max_splits);
   dim3 block(kMWaves * 64);
   const bool two =
       gqa_mfma_col_tiles(a.q_len * a.group, head_dim, (int64_t)a.max_pages * a.page_size) == 2;

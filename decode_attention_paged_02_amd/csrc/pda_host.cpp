@@ -415,7 +415,24 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   a.split.split_min_tokens = s.split_min_tokens;
 
   hipStream_t st = (hipStream_t)stream;
-  if (units) {
+  // BALANCED calls on the matrix-core kernel with a moderate batch: each
+  // workgroup derives its unit from the lengths (no planning launch).  Their
+  // grid is bounded by batch + target units, close to the real unit count;
+  // a GRID schedule with a threshold launches batch x splits workgroups for
+  // far fewer units, where the planning kernel's list lets the surplus
+  // workgroups leave after one load.
+  if (units && s.schedule == PDA_SCHEDULE_BALANCED && gqa_use_mfma(shape) &&
+      s.batch <= pda::kInKernelPlanMaxBatch) {
+    a.plan_in_kernel = 1;
+    a.plan.batch = s.batch;
+    a.plan.page_size = s.page_size;
+    a.plan.balanced = s.schedule == PDA_SCHEDULE_BALANCED;
+    a.plan.target_units = plan.target_units;
+    a.plan.min_chunk_pages = kMinChunkPages;
+    a.plan.split = a.split;
+    a.seq_splits = seq_splits;
+    a.units = nullptr;
+  } else if (units) {
     rc = run_order(s, plan, context_lens, units, seq_splits, a.split, st);
     if (rc != PDA_OK) return rc;
   }

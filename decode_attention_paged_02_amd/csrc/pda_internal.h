@@ -64,6 +64,17 @@ struct SplitLayout {
   int32_t split_min_tokens;
 };
 
+// The rules of an ordered call's work-unit list (see OrderArgs): the
+// sequences' splits and the longest-first order.
+struct UnitPlan {
+  int32_t batch, page_size, balanced, target_units, min_chunk_pages;
+  SplitLayout split;
+};
+
+// Largest batch whose workgroups plan their own units (each reads every
+// length; beyond it a planning kernel writes the list).
+constexpr int kInKernelPlanMaxBatch = 1024;
+
 struct GqaArgs {
   const void* q;
   const void* k_cache;
@@ -95,6 +106,12 @@ struct GqaArgs {
   // tile) in x and the split in y, ranges from SplitLayout.
   const int32_t* units;
   int32_t unit_count;
+  // Ordered calls whose workgroups derive their own unit from context_lens
+  // (no planning launch; units is null then): the list's rules, and where
+  // each sequence's split count goes for the combine kernel.
+  int32_t plan_in_kernel;
+  UnitPlan plan;
+  int32_t* seq_splits;
 };
 
 struct CombineArgs {

@@ -388,3 +388,31 @@ def test_very_long_context_many_splits(very_long, splits):
         out, lse = pda.run_case(case, dev, num_splits=splits, variant=v)
         check(case, out, lse, ref_o, ref_l, label="very long %d %s" % (splits, name))
 
+
+
+@pytest.mark.parametrize("d,dt", [(64, "f16"), (128, "bf16"), (256, "f16")])
+@pytest.mark.parametrize("num_splits,thr", [(2, 0), (7, 0), (16, 0), (8, 600)])
+def test_combine_of_many_rows_with_few_splits(d, dt, num_splits, thr):
+    """Batches with many (sequence, head) rows and at most 16 splits merge in
+    the row-per-thread combine (at least 64 workgroups of rows); lengths from 1
+    token to several splits, with and without a split threshold."""
+    rng = np.random.default_rng(d + num_splits + thr)
+    lens = [int(x) for x in rng.integers(1, 2500, 32)]
+    lens[:3] = [1, 17, 2499]
+    case = _gqa(200 + d + num_splits, 32, 32, 8, d, 16, lens, q_dtype=dt, kv_dtype=dt)
+    say("combine rows", d, dt, num_splits, thr)
+    out, lse = pda.run_case(case, num_splits=num_splits, split_min_tokens=thr)
+    ref_o, ref_l = oracle_ref(case)
+    check(case, out, lse, ref_o, ref_l, label="rows combine d=%d S=%d thr=%d" % (d, num_splits, thr))
+
+
+def test_combine_of_many_rows_multi_token():
+    lens = [int(x) for x in np.random.default_rng(5).integers(2, 3000, 24)]
+    case = W.make_gqa(batch=24, num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16,
+                      context_lens=lens, q_dtype="f16", kv_dtype="f16", seed=207, q_len=2,
+                      causal=True)
+    say("combine rows multi-token")
+    for s in (4, 12):
+        out, lse = pda.run_case(case, num_splits=s)
+        ref_o, ref_l = oracle_ref(case)
+        check(case, out, lse, ref_o, ref_l, label="rows combine q_len=2 S=%d" % s)
