@@ -41,6 +41,8 @@ def make_case(name):
     cache with head-major pages [pages, Hkv, P, d]."""
     from decode_attention_paged_02_amd import workloads as W
     hm = 0
+    if name.startswith("mla") and name.endswith("_qm"):   # the same case, queries on M
+        name = name[:-3]
     if name.endswith("_hm") and name.startswith(("gqa", "ragged", "mqa")):
         name, hm = name[:-3], 1
     if name == "gqa_b64":
@@ -71,11 +73,15 @@ CALL_KW = {"ragged_fp8": dict(num_splits=8, split_min_tokens=4096),
            "ragged_fp8_balanced": dict(num_splits=8, schedule=1)}
 GQA_WORKLOADS = ["gqa_b64", "gqa_b1_split", "gqa_b4_split", "ragged_fp8", "ragged_fp8_balanced",
                  "gqa_b64_q2", "mqa_b64_8k"]
-WORKLOADS = GQA_WORKLOADS + [w + "_hm" for w in GQA_WORKLOADS] + [
-    "mla_b16", "mla_b16_q2", "mla_b16_fp8", "mla_b16_320"]
+MLA_WORKLOADS = ["mla_b16", "mla_b16_q2", "mla_b16_fp8", "mla_b16_320"]
+# "_qm": the MLA kernel with the queries on the MFMA M dimension instead of the keys
+WORKLOADS = GQA_WORKLOADS + [w + "_hm" for w in GQA_WORKLOADS] + MLA_WORKLOADS + [
+    w + "_qm" for w in MLA_WORKLOADS]
 
 
 def call_kw(workload):
+    if workload.startswith("mla") and workload.endswith("_qm"):
+        return dict(CALL_KW.get(workload[:-3], {}), variant=3)
     return dict(CALL_KW.get(workload[:-3] if workload.endswith("_hm") else workload, {}))
 
 
@@ -113,7 +119,7 @@ def run_gpu(case, workload, steps, warmup, pools, min_warmup_ms=100.0):
         shape = pda.mla_shape(dev.q, dev.k_cache, dev.block_tables, head_dim_v=case.d_latent,
                               split_min_tokens=kw.get("split_min_tokens", 0),
                               causal=case.causal, schedule=kw.get("schedule", 0),
-                              kv_scale=case.k_scale)
+                              kv_scale=case.k_scale, variant=kw.get("variant", 0))
     else:
         shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
                               k_scale=case.k_scale, v_scale=case.v_scale,

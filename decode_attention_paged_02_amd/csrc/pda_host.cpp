@@ -66,7 +66,7 @@ int check_shape(const pda_shape* s, bool mla) {
     if (s->page_size % 64 != 0 || (s->page_size & (s->page_size - 1)) != 0)
       return PDA_ERR_UNSUPPORTED;
     if (s->num_q_heads > 16 && s->num_q_heads % 16 != 0) return PDA_ERR_UNSUPPORTED;
-    if (s->variant < PDA_MLA_DEFAULT || s->variant > PDA_MLA_VALU) return PDA_ERR_INVALID_ARG;
+    if (s->variant < PDA_MLA_DEFAULT || s->variant > PDA_MLA_MFMA_QM) return PDA_ERR_INVALID_ARG;
     // several query tokens: the matrix-core kernel only
     if (query_len(s) > 1 && s->variant == PDA_MLA_VALU) return PDA_ERR_UNSUPPORTED;
   } else {

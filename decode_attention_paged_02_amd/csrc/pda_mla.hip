@@ -205,8 +205,15 @@ __device__ __forceinline__ void store_bf16x4(void* out, int64_t i, f32x4 v) {
 
 // NG column groups of four waves; a workgroup owns 16 NG rows.  KT: the
 // latent's storage type (BF16, or E4M3 with a dequantization scale); DM: the
-// record widths.
-template <int NG, class KT, class DM>
+// record widths.  QM: queries on the MFMA M dimension instead of the keys
+// (FlashMLA's own layout): S = Q K^T with Q the A operand (rows of the tile)
+// and K the B operand (16 keys), then O = P V with P the A operand and V the
+// B operand.  The four waves' shares of S go through LDS as a [row][key]
+// tile and are read back one row per lane, which is the softmax layout of the
+// keys-on-M pipeline, so the softmax and the P operand are the same
+// registers; the accumulator then holds rows 4 grp + i of 16 value columns,
+// and the rescale factors and 1 / l of those rows come from the rows' lanes.
+template <int NG, class KT, class DM, bool QM>
 __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs a) {
   constexpr int T = kThreads * NG;
   constexpr int kRec = DM::kRec, kDv = DM::kDv;
@@ -215,7 +222,9 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   constexpr int MB = DM::kMB;            // 16-column MFMA tiles of a wave's values
   constexpr int CPW = DM::kColsPerWave;  // value columns a wave owns
   __shared__ __attribute__((aligned(16))) char lds[2][kBlock * DM::kRowBytes];
-  __shared__ f32x4 spart[4 * NG][2][64];  // per-wave partial S^T of a block
+  // per-wave partial S^T of a block (QM: a [16 rows][32 keys] float tile in
+  // the same bytes, 4-key groups placed at group ^ (row % 8))
+  __shared__ f32x4 spart[4 * NG][2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -345,18 +354,44 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
       for (int j = 0; j < NWMAX; ++j) {
         if (j < n_w) {
           const bf16x8 kv = *(const bf16x8*)(L + lds_off<DM>(r, 4 * (c_lo + j) + grp));
-          sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[j], sp, 0, 0, 0);
+          if constexpr (QM)  // S = Q K^T: rows 4 grp + i, key 16 kb + col
+            sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[j], kv, sp, 0, 0, 0);
+          else               // S^T = K Q^T: keys 16 kb + 4 grp + i, row col
+            sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[j], sp, 0, 0, 0);
         }
       }
-      spart[wid][kb][lane] = sp;
+      if constexpr (QM) {
+        float* sq = (float*)&spart[wid][0][0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * grp + i, kg = 4 * kb + (col >> 2);
+          sq[row * 32 + 4 * (kg ^ (row & 7)) + (col & 3)] = sp[i];
+        }
+      } else {
+        spart[wid][kb][lane] = sp;
+      }
     }
     __syncthreads();
     f32x4 st[2];
     const int w0 = 4 * cg;  // the group's four shares
+    if constexpr (QM) {
+      // row col, keys 16 kb + 4 grp + 0..3 (the keys-on-M layout), summed over
+      // the four shares in the same order
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      st[kb] = ((spart[w0][kb][lane] + spart[w0 + 1][kb][lane]) + spart[w0 + 2][kb][lane]) +
-               spart[w0 + 3][kb][lane];
+      for (int kb = 0; kb < 2; ++kb) {
+        const int off = col * 32 + 4 * ((4 * kb + grp) ^ (col & 7));
+        const f32x4* s0 = (const f32x4*)((const float*)&spart[w0][0][0] + off);
+        const f32x4* s1 = (const f32x4*)((const float*)&spart[w0 + 1][0][0] + off);
+        const f32x4* s2 = (const f32x4*)((const float*)&spart[w0 + 2][0][0] + off);
+        const f32x4* s3 = (const f32x4*)((const float*)&spart[w0 + 3][0][0] + off);
+        st[kb] = ((*s0 + *s1) + *s2) + *s3;
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        st[kb] = ((spart[w0][kb][lane] + spart[w0 + 1][kb][lane]) + spart[w0 + 2][kb][lane]) +
+                 spart[w0 + 3][kb][lane];
+    }
     // scale, mask rows past the context; lane holds keys 16 kb + 4 grp + i of head `col`
     // (a block whose 32 rows every column sees skips the mask: one wave vote)
     float s[8];
@@ -381,7 +416,26 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
         }
     }
     tmax = max_x4(tmax);
-    if (tmax > m_run + kLazyMax) {  // per head; lanes of one head agree
+    if constexpr (QM) {
+      // per row; the accumulator rows 4 grp + i take their factors from the
+      // rows' lanes (only when some row's reference moved)
+      const bool move = tmax > m_run + kLazyMax;
+      float alpha = 1.f;
+      if (move) {
+        alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+        m_run = tmax;
+        l_run *= alpha;
+      }
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i, 64);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][i] *= al[i];
+      }
+    } else if (tmax > m_run + kLazyMax) {  // per head; lanes of one head agree
       const float alpha = __builtin_amdgcn_exp2f(m_run - tmax);
       m_run = tmax;
       l_run *= alpha;
@@ -432,12 +486,21 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
       va[mb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vt[0], vt[1], 0, 1, 2, 3, 4, 5,
                                                                   6, 7));
     }
+    if constexpr (QM) {  // O = P V: rows 4 grp + i, value column col of tile mb
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mb], pk_hi, acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pk_hi, va[mb], acc[mb], 0, 0, 0);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mb], pk_lo, acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pk_lo, va[mb], acc[mb], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mb], pk_hi, acc[mb], 0, 0, 0);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[mb], pk_lo, acc[mb], 0, 0, 0);
+    }
   };
   // block blk, then: stage the next block, start loading the one 1 + kRing
   // ahead, hand over the buffer (`nxt` holds block blk + 1 and then receives
@@ -459,6 +522,44 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
   // epilogue: l over the four lane groups; lane holds 4 consecutive columns
   // (out row (b, qi, h); lse [B, Hq, q_len])
   const float l = sum_x4(l_run);
+  if constexpr (QM) {
+    // lane: rows 4 grp + i of value column col of each tile mb; their 1 / l
+    // from the rows' lanes (every lane takes part in the exchange)
+    const float inv_row = l > 0.f ? a.v_scale / l : 0.f;
+    float inv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) inv[i] = __shfl(inv_row, 4 * grp + i, 64);
+    const int nrows = q_len * a.num_q_heads;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ri = tile * (kHeads * NG) + kHeads * cg + 4 * grp + i;
+      if (ri >= nrows) continue;
+      int qi_i = 0, h_i = ri;
+      if (q_len > 1) {
+        qi_i = ri / a.num_q_heads;
+        h_i = ri - qi_i * a.num_q_heads;
+      }
+      const int64_t row_i = ((int64_t)b * q_len + qi_i) * a.num_q_heads + h_i;
+      if (nsplit == 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          store_out<BF16>(a.out, row_i * kDv + CPW * wave + 16 * mb + col, acc[mb][i] * inv[i]);
+      } else {
+        float* po = a.part_o + (row_i * a.split.max_splits + split) * kDv + CPW * wave + col;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) po[16 * mb] = acc[mb][i] * inv[i];
+      }
+    }
+    if (!hvalid || wave != 0 || grp != 0) return;
+    const float lse = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+    const int64_t row = ((int64_t)b * q_len + qi) * a.num_q_heads + h;
+    if (nsplit == 1) {
+      if (a.lse) a.lse[((int64_t)b * a.num_q_heads + h) * q_len + qi] = lse;
+    } else {
+      a.part_lse[row * a.split.max_splits + split] = lse;
+    }
+    return;
+  }
   if (!hvalid) return;
   const float inv = l > 0.f ? a.v_scale / l : 0.f;
   const float lse = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
@@ -672,14 +773,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
   }
 }
 
-template <class DM>
+template <class DM, bool QM>
 void launch_mfma(const MlaArgs& a, bool two, bool fp8, dim3 grid, hipStream_t s) {
   if (two) {
-    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<2, E4M3, DM>), grid, dim3(2 * kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mla_mfma_kernel<2, BF16, DM>), grid, dim3(2 * kThreads), 0, s, a);
+    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<2, E4M3, DM, QM>), grid, dim3(2 * kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mla_mfma_kernel<2, BF16, DM, QM>), grid, dim3(2 * kThreads), 0, s, a);
   } else {
-    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<1, E4M3, DM>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((mla_mfma_kernel<1, BF16, DM>), grid, dim3(kThreads), 0, s, a);
+    if (fp8) hipLaunchKernelGGL((mla_mfma_kernel<1, E4M3, DM, QM>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((mla_mfma_kernel<1, BF16, DM, QM>), grid, dim3(kThreads), 0, s, a);
   }
 }
 
@@ -697,9 +798,11 @@ hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int head_dim,
     if (fp8) hipLaunchKernelGGL(mla_valu_kernel<E4M3>, grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(mla_valu_kernel<BF16>, grid, dim3(kThreads), 0, s, a);
   } else if (head_dim == 576) {
-    launch_mfma<Dims576>(a, two, fp8, grid, s);
+    if (variant == 3) launch_mfma<Dims576, true>(a, two, fp8, grid, s);
+    else launch_mfma<Dims576, false>(a, two, fp8, grid, s);
   } else if (head_dim == 320) {
-    launch_mfma<Dims320>(a, two, fp8, grid, s);
+    if (variant == 3) launch_mfma<Dims320, true>(a, two, fp8, grid, s);
+    else launch_mfma<Dims320, false>(a, two, fp8, grid, s);
   } else {
     return hipErrorInvalidValue;
   }

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpda.so")
 
 PDA_F32, PDA_F16, PDA_BF16, PDA_FP8_E4M3 = 0, 1, 2, 3
-PDA_MLA_DEFAULT, PDA_MLA_MFMA, PDA_MLA_VALU = 0, 1, 2
+PDA_MLA_DEFAULT, PDA_MLA_MFMA, PDA_MLA_VALU, PDA_MLA_MFMA_QM = 0, 1, 2, 3
 PDA_GQA_DEFAULT, PDA_GQA_MFMA, PDA_GQA_VALU = 0, 1, 2
 PDA_SCHEDULE_GRID, PDA_SCHEDULE_BALANCED = 0, 1
 PDA_KV_TOKEN_MAJOR, PDA_KV_HEAD_MAJOR = 0, 1

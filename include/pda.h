@@ -156,6 +156,7 @@ typedef struct pda_shape {
 #define PDA_MLA_DEFAULT 0 /* the fastest available                          */
 #define PDA_MLA_MFMA 1    /* bf16 matrix cores, keys on the M dimension     */
 #define PDA_MLA_VALU 2    /* plain vector dot products (reference path)     */
+#define PDA_MLA_MFMA_QM 3 /* bf16 matrix cores, queries on the M dimension  */
 
 /* What the planner chose for a call (host struct). */
 typedef struct pda_plan_info {

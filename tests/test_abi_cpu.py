@@ -279,6 +279,7 @@ def test_mla_validation():
                                      ctypes.byref(f8), None, 0, None) == 0   # B = 0: no-op
     # record widths: (576, 512) and (320, 256); 320 only on the matrix cores
     for dk, dv, variant, want in [(320, 256, pda.PDA_MLA_DEFAULT, 0), (320, 256, pda.PDA_MLA_MFMA, 0),
+                                  (320, 256, pda.PDA_MLA_MFMA_QM, 0), (576, 512, 4, 1),
                                   (320, 256, pda.PDA_MLA_VALU, 2), (320, 512, 0, 2),
                                   (576, 256, 0, 2), (448, 384, 0, 2)]:
         w = _shape(num_q_heads=16, num_kv_heads=1, head_dim=dk, head_dim_v=dv, page_size=64,

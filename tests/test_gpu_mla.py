@@ -11,7 +11,8 @@ from decode_attention_paged_02_amd import workloads as W
 from gpu_util import check, need_gpu, oracle_ref, say
 
 pytestmark = pytest.mark.gpu
-VARIANTS = {"mfma": pda.PDA_MLA_MFMA, "valu": pda.PDA_MLA_VALU}
+# keys on the MFMA M dimension, queries on M, vector dot products
+VARIANTS = {"mfma": pda.PDA_MLA_MFMA, "qm": pda.PDA_MLA_MFMA_QM, "valu": pda.PDA_MLA_VALU}
 
 
 @pytest.fixture(autouse=True)
@@ -166,22 +167,24 @@ def test_fp8_latent_b16_sampled():
     check(case, out, lse, ref_o, ref_l, rows=rows, label=case.name)
 
 
+@pytest.mark.parametrize("variant", ["mfma", "qm"])
 @pytest.mark.parametrize("Hq,q_len,kv", [(16, 1, "bf16"), (32, 1, "bf16"), (16, 2, "bf16"),
                                          (8, 1, "e4m3"), (16, 1, "e4m3")])
-def test_record_320_value_256(Hq, q_len, kv):
+def test_record_320_value_256(Hq, q_len, kv, variant):
     """The (320, 256) record: a 256-wide latent + 64 rope values (FlashMLA-ETAP's
     second head-dimension pair), matrix-core kernel."""
     case = W.make_mla(batch=4, num_q_heads=Hq, d_latent=256, d_rope=64, page_size=64,
                       context_lens=[1, 65, 700, 3000], dtype="bf16", seed=90 + Hq + q_len,
                       std=0.5, scale=1.0 / math.sqrt(192.0), extra_pages=2, q_len=q_len,
                       kv_dtype=kv)
-    say("mla 320/256", Hq, q_len, kv)
+    say("mla 320/256", Hq, q_len, kv, variant)
     ref_o, ref_l = oracle_ref(case)
+    v = VARIANTS[variant]
     for s in (1, 5):
-        out, lse = pda.run_case(case, num_splits=s)
+        out, lse = pda.run_case(case, num_splits=s, variant=v)
         assert out.shape[-1] == 256
         check(case, out, lse, ref_o, ref_l, label="mla320 Hq=%d q=%d %s S=%d" % (Hq, q_len, kv, s))
-    out, lse = pda.run_case(case, schedule=pda.PDA_SCHEDULE_BALANCED)
+    out, lse = pda.run_case(case, schedule=pda.PDA_SCHEDULE_BALANCED, variant=v)
     check(case, out, lse, ref_o, ref_l, label="mla320 balanced")
 
 
@@ -216,3 +219,21 @@ def test_many_splits_combine_loop():
         assert p.max_splits > 64
         out, lse = pda.run_case(case, dev, num_splits=splits)
         check(case, out, lse, ref_o, ref_l, label="mla splits %d" % splits)
+
+
+def test_queries_on_m_full_size_sampled():
+    """The MLA decode shape (B=16, Hq=16, ctx 65536) with queries on the MFMA
+    M dimension, sampled rows, and bitwise run-to-run determinism."""
+    case = W.mla_b16()
+    rng = np.random.default_rng(11)
+    rows = rng.random((16, 16)) < 0.05
+    rows[0, :2] = True
+    say(case.name, "qm")
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case, rows=rows)
+    out, lse = pda.run_case(case, dev, variant=pda.PDA_MLA_MFMA_QM)
+    check(case, out, lse, ref_o, ref_l, rows=rows, label="%s qm" % case.name)
+    out2, lse2 = pda.run_case(case, dev, variant=pda.PDA_MLA_MFMA_QM)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    del dev
+    torch.cuda.empty_cache()

@@ -119,13 +119,14 @@ def _mla(seed, lens, Hq, q_len, causal=True, P=64):
 
 @pytest.mark.parametrize("Hq,q_len", [(16, 2), (8, 3), (32, 2), (1, 4)])
 @pytest.mark.parametrize("causal", [True, False])
-def test_mla_rows_and_masks(Hq, q_len, causal):
+@pytest.mark.parametrize("variant", [pda.PDA_MLA_MFMA, pda.PDA_MLA_MFMA_QM])
+def test_mla_rows_and_masks(Hq, q_len, causal, variant):
     lens = [1, 2, 65, 700, 128]
     case = _mla(Hq * 10 + q_len, lens, Hq, q_len, causal)
-    say("multi-token mla", Hq, q_len, causal)
+    say("multi-token mla", Hq, q_len, causal, variant)
     ref_o, ref_l = oracle_ref(case)
     for s in (1, 4):
-        out, lse = pda.run_case(case, num_splits=s)
+        out, lse = pda.run_case(case, num_splits=s, variant=variant)
         assert tuple(out.shape) == (len(lens), q_len, Hq, 512)
         check(case, out, lse, ref_o, ref_l, label="mla Hq=%d q_len=%d S=%d" % (Hq, q_len, s))
 
