@@ -155,8 +155,9 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, f32x4 c
 // kernel-argument load.  GqaArgs carries everything (the same values too).
 // CT column tiles of 16 rows per workgroup: one, or two for groups of more
 // than 16 rows (d <= 128), so that one load of a K/V tile serves 32 rows.
-// SD steps of tiles in flight per wave (see kGqaStepsInFlight).
-template <class QT, class KT, int D, int CT, int SD>
+// SD steps of tiles in flight per wave (see kGqaStepsInFlight), ST tiles per
+// step.
+template <class QT, class KT, int D, int CT, int SD, int ST>
 __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     const int32_t* context_lens, const int32_t* block_tables, const void* q, int32_t head_tiles,
     int32_t num_kv_heads, int32_t group, int32_t q_len, int32_t max_pages, int32_t log2_page,
@@ -242,7 +243,6 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   // w, w + kMWaves, ...  Sequence length, block-table entries (lane j: tile
   // j % ST of the wave's step sbase + j / ST, clamped into the row, unused
   // past the sequence) and q are requested together.
-  constexpr int ST = kGqaStepTiles;
   constexpr int kStepsPerChunk = 64 / ST;
   auto load_table = [&](int sbase) -> int {
     const int T = (wave + (sbase + lane / ST) * kMWaves) * ST + lane % ST;
@@ -569,20 +569,38 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   }
 }
 
-// grid calls with kGqaStepsInFlight steps in flight, ordered ones with
-// kGqaStepsInFlightOrdered
-template <class QT, class KT, int D, int CT>
+// grid calls with kGqaStepsInFlight steps in flight (kGqaStepsInFlightFp8 for
+// fp8 caches), ordered ones with kGqaStepsInFlightOrdered; ST tiles per step
+template <class QT, class KT, int D, int CT, int ST>
 void launch_sd(const GqaArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  constexpr int kGridSD = std::is_same<KT, E4M3>::value ? kGqaStepsInFlightFp8 : kGqaStepsInFlight;
 #define PDA_MFMA_ARGS                                                                        \
   a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.q_len,        \
       a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a.units, a
   if (a.units || a.plan_in_kernel)
-    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlightOrdered>), grid, block,
-                       0, s, PDA_MFMA_ARGS);
+    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlightOrdered, ST>), grid,
+                       block, 0, s, PDA_MFMA_ARGS);
   else
-    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlight>), grid, block, 0, s,
+    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGridSD, ST>), grid, block, 0, s,
                        PDA_MFMA_ARGS);
 #undef PDA_MFMA_ARGS
+}
+
+// Tiles per step: kGqaStepTilesFp8 for fp8 caches whose tile rows are
+// contiguous (head-major pages, or a single KV head), else kGqaStepTiles.  An
+// fp8 tile is half the bytes of a 16-bit one; two per step issue as many
+// (head-major B=64 at 2048 tokens: 43.3 against 44.2 us; the ragged batch,
+// balanced: 86.6 against 88.0) -- but with token-major rows 1 KiB apart they
+// slow down (48.1 against 44.9 us; ragged 95.5 against 93.9).
+template <class QT, class KT, int D, int CT>
+void launch_st(const GqaArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if constexpr (std::is_same<KT, E4M3>::value && kGqaStepTilesFp8 != kGqaStepTiles) {
+    if (a.tok_stride == D) {
+      launch_sd<QT, KT, D, CT, kGqaStepTilesFp8>(a, grid, block, s);
+      return;
+    }
+  }
+  launch_sd<QT, KT, D, CT, kGqaStepTiles>(a, grid, block, s);
 }
 
 template <class QT, class KT>
@@ -596,14 +614,14 @@ hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStr
       gqa_mfma_col_tiles(a.q_len * a.group, head_dim, (int64_t)a.max_pages * a.page_size) == 2;
   switch (head_dim) {
     case 64:
-      if (two) launch_sd<QT, KT, 64, 2>(a, grid, block, s);
-      else launch_sd<QT, KT, 64, 1>(a, grid, block, s);
+      if (two) launch_st<QT, KT, 64, 2>(a, grid, block, s);
+      else launch_st<QT, KT, 64, 1>(a, grid, block, s);
       break;
     case 128:
-      if (two) launch_sd<QT, KT, 128, 2>(a, grid, block, s);
-      else launch_sd<QT, KT, 128, 1>(a, grid, block, s);
+      if (two) launch_st<QT, KT, 128, 2>(a, grid, block, s);
+      else launch_st<QT, KT, 128, 1>(a, grid, block, s);
       break;
-    case 256: launch_sd<QT, KT, 256, 1>(a, grid, block, s); break;
+    case 256: launch_st<QT, KT, 256, 1>(a, grid, block, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

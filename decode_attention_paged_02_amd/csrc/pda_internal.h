@@ -30,6 +30,15 @@ constexpr int kTileTokens = 16;
 #ifndef PDA_GQA_STEPS_IN_FLIGHT
 #define PDA_GQA_STEPS_IN_FLIGHT 1
 #endif
+// Tiles per step and grid steps in flight for 1-byte (fp8) caches: their tiles
+// hold half the bytes of a 16-bit tile, so a step of two tiles issues as many
+// bytes as one 16-bit tile does.
+#ifndef PDA_GQA_STEP_TILES_FP8
+#define PDA_GQA_STEP_TILES_FP8 2
+#endif
+#ifndef PDA_GQA_STEPS_IN_FLIGHT_FP8
+#define PDA_GQA_STEPS_IN_FLIGHT_FP8 1
+#endif
 #ifndef PDA_GQA_STEPS_IN_FLIGHT_ORDERED
 #define PDA_GQA_STEPS_IN_FLIGHT_ORDERED 2
 #endif
@@ -51,6 +60,8 @@ constexpr int kGqaRingRegs = PDA_GQA_RING_REGS;
 constexpr int kGqaStepTiles = PDA_GQA_STEP_TILES;
 constexpr int kGqaStepsInFlight = PDA_GQA_STEPS_IN_FLIGHT;
 constexpr int kGqaStepsInFlightOrdered = PDA_GQA_STEPS_IN_FLIGHT_ORDERED;
+constexpr int kGqaStepTilesFp8 = PDA_GQA_STEP_TILES_FP8;
+constexpr int kGqaStepsInFlightFp8 = PDA_GQA_STEPS_IN_FLIGHT_FP8;
 
 // Split layout shared by the attention kernels and the combine kernel.  For
 // sequence b with n = context_lens[b] tokens and pages = ceil(n / P):
