@@ -50,6 +50,29 @@ def test_head_major_multi_token_and_balanced(q_len, schedule):
     check(case, out, lse, ref_o, ref_l, label="head-major q%d sched %d" % (q_len, schedule))
 
 
+# fp8 caches whose tile rows are contiguous (head-major pages, or one KV
+# head) load two 16-token tiles per step: grid and ordered (threshold,
+# balanced) calls, odd tile counts and a last step whose second tile lies past
+# the range, several query tokens.
+@pytest.mark.parametrize("layout,Hkv,q_len,splits,thr,schedule", [
+    (HEAD_MAJOR, 4, 1, 3, 0, pda.PDA_SCHEDULE_GRID),
+    (HEAD_MAJOR, 4, 1, 4, 256, pda.PDA_SCHEDULE_GRID),
+    (HEAD_MAJOR, 4, 1, 4, 0, pda.PDA_SCHEDULE_BALANCED),
+    (HEAD_MAJOR, 2, 3, 2, 0, pda.PDA_SCHEDULE_GRID),
+    (0, 1, 1, 3, 0, pda.PDA_SCHEDULE_GRID),
+    (0, 1, 1, 0, 0, pda.PDA_SCHEDULE_BALANCED)])
+def test_fp8_two_tile_steps(layout, Hkv, q_len, splits, thr, schedule):
+    case = W.make_gqa(batch=6, num_q_heads=8 * Hkv, num_kv_heads=Hkv, head_dim=128,
+                      page_size=16, context_lens=[1, 17, 48, 529, 2000, 3001], q_dtype="f16",
+                      kv_dtype="e4m3", seed=83 + Hkv + q_len + splits + schedule, extra_pages=3,
+                      q_len=q_len, kv_layout=layout)
+    say("fp8 two-tile steps", layout, Hkv, q_len, splits, thr, schedule)
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case, num_splits=splits, split_min_tokens=thr, schedule=schedule)
+    check(case, out, lse, ref_o, ref_l, label="fp8 steps L%d Hkv%d q%d S%d t%d s%d" % (
+        layout, Hkv, q_len, splits, thr, schedule))
+
+
 def test_head_major_full_size_batch64():
     case = W.gqa_batch64(kv_layout=HEAD_MAJOR)
     say(case.name)
