@@ -447,15 +447,25 @@ __device__ WorkUnit plan_unit(const int32_t* lens, const UnitPlan& p, int rank, 
     atomicAdd(&sh.bucket_count[bl[i]], 1);
   }
   __syncthreads();
-  // the bucket that holds `rank`, from the longest down, and the rank in it
+  // the bucket that holds `rank`, from the longest down, and the rank in it:
+  // lane j takes bucket 32 - j, a scan over the lanes gives the units up to
+  // and including each bucket, and the first lane whose total exceeds `rank`
+  // holds it (one LDS read per lane instead of a dependent walk)
   int bucket = -1, k = rank;
-  for (int q = 32; q >= 0; --q) {
-    const int c = sh.bucket_count[q];
-    if (k < c) {
-      bucket = q;
-      break;
+  {
+    const int c = lane <= 32 ? sh.bucket_count[32 - lane] : 0;
+    int upto = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(upto, o, 64);
+      if (lane >= o) upto += y;
     }
-    k -= c;
+    const unsigned long long hit = __ballot(rank < upto);
+    if (hit != 0) {
+      const int j = __builtin_ctzll(hit);
+      bucket = 32 - j;
+      k = rank - __shfl(upto - c, j, 64);
+    }
   }
   if (bucket < 0) {  // (the same for every thread)
     ns_b = 0;
