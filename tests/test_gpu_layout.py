@@ -81,12 +81,28 @@ def test_head_major_full_size_batch64():
     check(case, out, lse, ref_o, ref_l, label=case.name)
 
 
-def test_head_major_full_size_long_split():
-    case = W.gqa_long(1, kv_layout=HEAD_MAJOR)
+@pytest.mark.parametrize("batch", [1, 4])
+def test_head_major_full_size_long_split(batch):
+    case = W.gqa_long(batch, kv_layout=HEAD_MAJOR)
     say(case.name)
     ref_o, ref_l = oracle_ref(case)
     out, lse = pda.run_case(case)
     check(case, out, lse, ref_o, ref_l, label=case.name)
+
+
+def test_head_major_full_size_ragged_fp8_balanced_sampled_rows():
+    """The ragged fp8 batch with head-major pages under the balanced schedule
+    (at most 8 splits), as the bench times it: fp8 tiles two per step, units
+    planned in the attention kernel; a quarter of the rows checked."""
+    case = W.ragged_fp8(kv_layout=HEAD_MAJOR)
+    say(case.name, "balanced")
+    rng = np.random.default_rng(7)
+    rows = rng.random((case.batch, case.num_q_heads)) < 0.25
+    rows[:3] = True
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case, rows=rows)
+    out, lse = pda.run_case(case, dev, num_splits=8, schedule=pda.PDA_SCHEDULE_BALANCED)
+    check(case, out, lse, ref_o, ref_l, rows=rows, label="head-major balanced ragged")
 
 
 def test_mqa_full_size_two_column_tiles():
