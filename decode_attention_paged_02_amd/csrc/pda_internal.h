@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace pda {
@@ -192,16 +193,19 @@ struct AppendArgs {
 
 // Streaming-read probe (pda_stream_probe): the K/V reads of a GQA grid call.
 struct ProbeArgs {
+  // (the first 16 dwords arrive preloaded in scalar registers: everything the
+  // first loads need)
   const void* k_cache;
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  uint32_t* sink;  // [max_splits][B * Hkv]: one word per workgroup
-  int32_t batch, num_kv_heads, page_size, max_pages, log2_page, elem_bytes;
-  int32_t tok_stride, head_stride;  // elements, as in GqaArgs
-  int64_t page_stride;
   SplitLayout split;
+  int32_t num_kv_heads, page_size, max_pages, log2_page, tok_stride;  // tok_stride: elements
+  uint32_t* sink;  // [max_splits][B * Hkv]: one word per workgroup
+  int32_t batch, elem_bytes, head_stride;  // head_stride: elements, as in GqaArgs
+  int64_t page_stride;
 };
+static_assert(offsetof(ProbeArgs, sink) == 64, "probe arguments: prologue values preloaded");
 
 // Precondition check of device-resident inputs (see pda_check_inputs).
 struct CheckArgs {

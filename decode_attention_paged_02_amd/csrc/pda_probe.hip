@@ -9,10 +9,12 @@
 // as four 16-byte (or 8-/4-byte) row pieces per lane of K and of V with
 // non-temporal buffer loads sized to the valid rows, the wave's block-table
 // entries fetched 64 at a time and handed out with v_readlane.  Instead of
-// attention it folds the loaded words into one word per workgroup (written
-// to `sink`, so no load is dead).  The time of such a launch is the floor any
-// kernel with this access pattern can reach: bench.py reports the attention
-// kernels against it ("fraction of the practical ceiling").
+// attention each wave folds the words it loaded into one word (written to
+// `sink`, so no load is dead).  The time of such a launch is the floor any
+// kernel with this access pattern that writes a result can reach: bench.py
+// reports the attention kernels against it ("fraction of the practical
+// ceiling").  (Writing nothing at all would be ~0.4 us faster at B=64: the
+// last stores' completion is part of any such kernel's time.)
 #include "pda_device.h"
 
 namespace pda {
@@ -59,11 +61,25 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
   const int split = blockIdx.y;
   const int log2P = a.log2_page;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
+  // The first 64 table entries of this wave (lane j: tile wave + 4 j of the
+  // split) are requested together with the length, as the attention kernels
+  // do, before the split's range is known (entries past the sequence are
+  // loaded from the table row but never used).
+  const int t0_hint = a.split.max_splits > 1 ? split * a.split.pages_per_split << log2P : 0;
+  auto load_entries = [&](int base) -> int {
+    const int64_t tok = (int64_t)t0_hint + (int64_t)(wave + (base + lane) * kProbeWaves) * kTileTokens;
+    const int64_t pg = tok >> log2P;
+    return table[pg < a.max_pages ? pg : a.max_pages - 1];
+  };
+  int vtbl = load_entries(0);
   const int n = load_uniform(a.context_lens + b);
+  __builtin_amdgcn_sched_barrier(0);  // the table request goes out before waiting for n
   int nsplit, t0, t1;
-  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);
+  split_range(a.split, n, a.page_size, split, nsplit, t0, t1);  // (t0 == t0_hint)
+  // one sink word per wave: [split][workgroup][wave]
+  uint32_t* sink = a.sink + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kProbeWaves + wave;
   if (split >= nsplit) {
-    if (threadIdx.x == 0) a.sink[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = 0;
+    if (lane == 0) *sink = 0;
     return;
   }
   const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
@@ -75,11 +91,15 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
   PWords<PW> kb[SD][4], vb[SD][4];
   for (int base = 0; base < nw; base += 64) {
     // lane j: the page of this wave's tile base + j
-    const int64_t tok = (int64_t)t0 + (int64_t)(wave + (base + lane) * kProbeWaves) * kTileTokens;
-    const int64_t pg = tok >> log2P;
-    const int vtbl = table[pg < a.max_pages ? pg : a.max_pages - 1];
+    if (base > 0) vtbl = load_entries(base);
     const int cnt = min(64, nw - base);
-    auto issue = [&](int i, int u) {
+    // A tile's two resources, computed one tile ahead: the scalar address
+    // arithmetic of tile i + 1 runs while tile i's loads are in flight,
+    // not between its data's arrival and the next loads.
+    struct TileRes {
+      __amdgpu_buffer_rsrc_t k, v;
+    };
+    auto prep = [&](int i) -> TileRes {
       const bool live = i < cnt;
       const int entry = __builtin_amdgcn_readlane(vtbl, i & 63);
       const int tk = t0 + (wave + (base + i) * kProbeWaves) * kTileTokens;
@@ -87,19 +107,23 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
       const int slot = tk & ((1 << log2P) - 1);
       const int64_t elem =
           (int64_t)(live ? entry : 0) * a.page_stride + (int64_t)slot * a.tok_stride + head_elem;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const char*)a.k_cache + elem * a.elem_bytes), 0, rows * tok_bytes, kRsrcFlags);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const char*)a.v_cache + elem * a.elem_bytes), 0, rows * tok_bytes, kRsrcFlags);
+      return TileRes{__builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.k_cache + elem * a.elem_bytes),
+                                                       0, rows * tok_bytes, kRsrcFlags),
+                     __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.v_cache + elem * a.elem_bytes),
+                                                       0, rows * tok_bytes, kRsrcFlags)};
+    };
+    auto fire = [&](const TileRes& r, int u) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        kb[u][j] = probe_load<PW>(rk, off0 + j * tok_bytes);
-        vb[u][j] = probe_load<PW>(rv, off0 + j * tok_bytes);
+        kb[u][j] = probe_load<PW>(r.k, off0 + j * tok_bytes);
+        vb[u][j] = probe_load<PW>(r.v, off0 + j * tok_bytes);
       }
     };
+    TileRes pend = prep(0);  // the next tile to issue
 #pragma unroll
     for (int u = 0; u < SD - 1; ++u) {
-      issue(u, u);
+      fire(pend, u);
+      pend = prep(u + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     for (int i0 = 0; i0 < cnt; i0 += SD) {
@@ -107,7 +131,8 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
       for (int u = 0; u < SD; ++u) {
         const int i = i0 + u;
         if (i >= cnt) break;
-        issue(i + SD - 1, (u + SD - 1) % SD);
+        fire(pend, (u + SD - 1) % SD);  // tile i + SD - 1
+        pend = prep(i + SD);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -116,19 +141,13 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
       }
     }
   }
-  // one word per workgroup keeps every load live: the XOR of every 32-bit
-  // word the workgroup read (so a host can check which bytes were read)
+  // one word per wave keeps every load live: the XOR of every 32-bit word the
+  // wave read (so a host can check which bytes were read).  Per wave, with no
+  // barrier or LDS: a merge across the waves at the end costs the step time
+  // of such a kernel (0.6-1 us at B=64), which a read ceiling should not pay.
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
-  __shared__ uint32_t wave_acc[kProbeWaves];
-  if (lane == 0) wave_acc[wave] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t x = 0;
-#pragma unroll
-    for (int w = 0; w < kProbeWaves; ++w) x ^= wave_acc[w];
-    a.sink[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = x;
-  }
+  if (lane == 0) *sink = acc;
 }
 
 template <int PW>

@@ -364,7 +364,7 @@ class StreamProbe:
                  steps_in_flight=1, stream=None):
         info = plan(shape, num_splits=num_splits)
         self._lib = load()
-        self._sink = torch.empty(max(1, shape.batch * shape.num_kv_heads * info.max_splits),
+        self._sink = torch.empty(max(1, 4 * shape.batch * shape.num_kv_heads * info.max_splits),
                                  dtype=torch.int32, device=block_tables.device)
         self._keep = (shape, caches, block_tables, context_lens)
         st = _stream_handle(stream)

@@ -317,13 +317,15 @@ int pda_check_inputs(const pda_shape* shape, const int32_t* block_tables,
  * with the attention kernels' access pattern -- one workgroup per
  * (sequence, KV head, split) as the GRID schedule plans it for num_splits,
  * 16-token tiles, row pieces of up to 16 bytes per lane, non-temporal
- * loads -- but does no arithmetic: it folds the words it loads into one
- * 32-bit word per workgroup of `sink`.  Its duration is the practical
- * ceiling for that access pattern on the device (the attention kernel's
- * time over it is the fraction of that ceiling the kernel reaches).
+ * loads -- but does no arithmetic: each of a workgroup's four waves folds
+ * the words it loads into one 32-bit word of `sink`.  Its duration is the
+ * practical ceiling for that access pattern on the device (the attention
+ * kernel's time over it is the fraction of that ceiling the kernel reaches).
  *   steps_in_flight: 1..4, tiles each wave keeps in flight;
- *   sink: DEVICE array of at least batch * num_kv_heads * max_splits uint32
- *         (pda_plan_info.max_splits of the same call), contents unspecified.
+ *   sink: DEVICE array of at least 4 * batch * num_kv_heads * max_splits
+ *         uint32 (pda_plan_info.max_splits of the same call), contents
+ *         unspecified; word ((split * batch + b) * num_kv_heads + kvh) * 4 +
+ *         w is the XOR of the 32-bit words wave w of that workgroup read.
  * Needs head_dim == head_dim_v with rows of 64, 128, 256 or 512 bytes and the
  * GRID schedule; other shape fields as for paged_decode_attn (q_dtype and
  * q_len are ignored).  Asynchronous on `stream`; returns a pda_status. */

@@ -168,7 +168,7 @@ def test_append_head_major_bit_exact(src, cache):
                                                       ("e4m3", 4, 100), ("bf16", 0, 0)])
 def test_stream_probe_reads_exactly_the_call_bytes(layout, kv_dtype, num_splits, thr):
     """The streaming probe reads the bytes the attention call reads: each
-    workgroup's sink word equals the XOR of the 32-bit words of its K and V
+    workgroup's sink words (one per wave) XOR to the 32-bit words of its K and V
     rows (its sequence, KV head and split range), computed on the host from
     the stored cache.  Rows past the context are NaN-poisoned, so a probe that
     read them would fold different words."""
@@ -187,7 +187,9 @@ def test_stream_probe_reads_exactly_the_call_bytes(layout, kv_dtype, num_splits,
                             dev.context_lens, num_splits=num_splits, steps_in_flight=2)
     probe()
     torch.cuda.synchronize()
-    got = probe._sink.cpu().numpy().view(np.uint32).reshape(info.max_splits, 3, 2)
+    # one word per wave: the workgroup's XOR is the XOR of its four waves' words
+    got = np.bitwise_xor.reduce(
+        probe._sink.cpu().numpy().view(np.uint32).reshape(info.max_splits, 3, 2, 4), axis=3)
     kc, vc = np.ascontiguousarray(case.k_cache), np.ascontiguousarray(case.v_cache)
     P = case.page_size
     for b in range(3):
