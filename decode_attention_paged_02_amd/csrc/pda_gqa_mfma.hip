@@ -17,12 +17,16 @@
 //    value dimensions and the columns heads, so a lane rescales only its own
 //    head's accumulators when the running max moves.
 //
-// Loads stay row-coalesced: load j of a tile gives lane (g, u) token 4g + j,
-// elements [u D/16, (u+1) D/16) of the row, so every load instruction covers
-// four whole token rows.  That is already the A-operand layout of V^T (lane
-// row u, contraction over the 4 tokens: two v_perm_b32 per operand).  K needs
-// the transposed assignment (lane row = token), so each wave writes its K
-// tile into its own padded LDS tile and reads it back in the MFMA layout.
+// Loads stay row-coalesced: load j of a tile gives lane (g, u) token 4j + g
+// (fp8 caches: 4g + j), elements [u D/16, (u+1) D/16) of the row, so every
+// load instruction covers four whole token rows (consecutive ones for 16-bit
+// caches).  That is already the A-operand layout of V^T (lane row u,
+// contraction over 4 tokens: two v_perm_b32 per operand), with contraction
+// index 4g + i standing for token g + 4i (fp8: 4g + i).  K needs the
+// transposed assignment (lane row = token), so each wave writes its K tile
+// into its own padded LDS tile and reads it back in the MFMA layout; it is
+// written in the same permuted row order, so the score rows S^T come out in
+// the contraction order of V^T and P^T needs no exchange.
 // Rows are padded by 32 bytes: the hardware's bank-conflict counter reads
 // zero for the tile's writes and reads at d = 128 (with 16 or 64 bytes of
 // padding it counts 16 conflict cycles per tile and wave, with none 112).
@@ -298,9 +302,17 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   for (int c = 0; c < CT; ++c) lim[c] = min(t1, a.causal ? n - (q_len - 1 - qi[c]) : n);
 
   const int tok_bytes = a.tok_stride * ESZ;
-  // load j of a tile: token 4 grp + j, piece col of the row (relative to the
-  // tile's first token row of this KV head)
-  const int off0 = (4 * grp) * tok_bytes + (col * NE) * ESZ;
+  // load j of a tile, 16-bit caches: token 4 j + grp, piece col of the row
+  // (relative to the tile's first token row of this KV head), so that one
+  // load instruction covers four consecutive rows (1 KiB at d = 128: with
+  // head-major pages one contiguous run; B=64 41.8 against 42.0 us with
+  // four runs of 256 bytes).  The tokens of the MFMA k index follow from it:
+  // k = 4 grp + i is token grp + 4 i, in V^T (load i) and in S^T alike.
+  // fp8 caches keep token 4 grp + j (k = 4 grp + i is token 4 grp + i): with
+  // their 128-byte rows consecutive rows measured 0.2% slower.
+  constexpr bool kConsec = !kFp8;
+  const int off0 = (kConsec ? grp : 4 * grp) * tok_bytes + (col * NE) * ESZ;
+  const int row_step = kConsec ? 4 * tok_bytes : tok_bytes;
   const int64_t head_elem = (int64_t)kvh * a.head_stride;
 
   // O^T of column tile c: rows (4 grp + i) * NE + e of the value, column =
@@ -324,7 +336,9 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
 
   // rows: valid token rows of the tile, tok: its first token
   auto compute_tile = [&](const Words<PW> (&kf)[4], const Words<PW> (&vf)[4], int rows, int tok) {
-    // ---- K tile into LDS in 16-bit form: row = token, piece col at 2 NE col bytes
+    // ---- K tile into LDS in 16-bit form: LDS row 4 grp + j holds load j
+    // (token 4 j + grp, or 4 grp + j for fp8), piece col at 2 NE col bytes;
+    // so S^T row r is token (r % 4) * 4 + r / 4 (fp8: r)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       char* dst = ktile + (4 * grp + j) * kRowB + col * NE * 2;
@@ -352,7 +366,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
       for (int c = 0; c < CT; ++c) st[c] = mfma_qk<QT>(kk, qb[c][j], st[c]);
     }
     // ---- online softmax per column tile (log2 domain, lazily moved
-    // reference max); this lane holds tokens 4 grp + i of row 16 c + col
+    // reference max); this lane holds S^T rows 4 grp + i (tokens grp + 4 i;
+    // fp8: 4 grp + i) of row 16 c + col
     u32x2 pb[CT], pb_lo[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
@@ -360,7 +375,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
       float s[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        s[i] = fminf(st[c][i] * a.qk_scale_log2, 4 * grp + i < rl ? INFINITY : -INFINITY);
+        s[i] = fminf(st[c][i] * a.qk_scale_log2,
+                     (kConsec ? grp + 4 * i : 4 * grp + i) < rl ? INFINITY : -INFINITY);
       float tmax = max2(max2(s[0], s[1], pinf), max2(s[2], s[3], pinf), pinf);
       {
         float x, y;
@@ -409,8 +425,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
       for (int e = 0; e < NE; ++e) acc[c][e] *= alpha;
     }
     // ---- O^T += V^T P^T.  A operand of MFMA e: V^T row col (value element
-    // col NE + e) over tokens 4 grp + 0..3 = element e of the four loads (one
-    // V operand for every column tile).
+    // col NE + e) at k = 4 grp + i (the token of load i) = element e of the
+    // four loads (one V operand for every column tile).
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       u32x2 va;
@@ -460,8 +476,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
           (void*)((const char*)a.v_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        kb[u][t][j] = load_piece<PW>(rk, off0 + j * tok_bytes);
-        vb[u][t][j] = load_piece<PW>(rv, off0 + j * tok_bytes);
+        kb[u][t][j] = load_piece<PW>(rk, off0 + j * row_step);
+        vb[u][t][j] = load_piece<PW>(rv, off0 + j * row_step);
       }
     }
   };

@@ -85,7 +85,11 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
   const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
   const int nw = ntiles > wave ? (ntiles - wave + kProbeWaves - 1) / kProbeWaves : 0;
   const int tok_bytes = a.tok_stride * a.elem_bytes;
-  const int off0 = (4 * grp) * tok_bytes + col * PW * 4;
+  // load j: token 4 j + grp for 16-bit caches (four consecutive rows per
+  // load instruction), 4 grp + j for fp8 ones, as the attention kernel
+  const bool consec = a.elem_bytes != 1;
+  const int off0 = (consec ? grp : 4 * grp) * tok_bytes + col * PW * 4;
+  const int row_step = consec ? 4 * tok_bytes : tok_bytes;
   const int64_t head_elem = (int64_t)kvh * a.head_stride;
   uint32_t acc = 0;
   PWords<PW> kb[SD][4], vb[SD][4];
@@ -115,8 +119,8 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
     auto fire = [&](const TileRes& r, int u) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        kb[u][j] = probe_load<PW>(r.k, off0 + j * tok_bytes);
-        vb[u][j] = probe_load<PW>(r.v, off0 + j * tok_bytes);
+        kb[u][j] = probe_load<PW>(r.k, off0 + j * row_step);
+        vb[u][j] = probe_load<PW>(r.v, off0 + j * row_step);
       }
     };
     TileRes pend = prep(0);  // the next tile to issue
