@@ -313,7 +313,12 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   constexpr bool kConsec = !kFp8;
   const int off0 = (kConsec ? grp : 4 * grp) * tok_bytes + (col * NE) * ESZ;
   const int row_step = kConsec ? 4 * tok_bytes : tok_bytes;
-  const int64_t head_elem = (int64_t)kvh * a.head_stride;
+  // this KV head's rows in page 0, and the bytes of a page: a tile's rows
+  // start at page * page_bytes + slot * tok_bytes from there (page indices
+  // are non-negative, so one unsigned 32 x 64-bit product per tile)
+  const char* kbase = (const char*)a.k_cache + (int64_t)kvh * a.head_stride * ESZ;
+  const char* vbase = (const char*)a.v_cache + (int64_t)kvh * a.head_stride * ESZ;
+  const uint64_t page_bytes = (uint64_t)a.page_stride * ESZ;
 
   // O^T of column tile c: rows (4 grp + i) * NE + e of the value, column =
   // row 16 c + col of the workgroup
@@ -469,11 +474,11 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
       rows_b[u][t] = rows;
       tok_b[u][t] = tok;
       const int slot = tok & ((1 << log2P) - 1);
-      const int64_t elem = (int64_t)phys * a.page_stride + (int64_t)slot * a.tok_stride + head_elem;
+      const uint64_t off = (uint64_t)(uint32_t)phys * page_bytes + (uint32_t)(slot * tok_bytes);
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const char*)a.k_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
+          (void*)(kbase + off), 0, rows * tok_bytes, kRsrcFlags);
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const char*)a.v_cache + elem * ESZ), 0, rows * tok_bytes, kRsrcFlags);
+          (void*)(vbase + off), 0, rows * tok_bytes, kRsrcFlags);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         kb[u][t][j] = load_piece<PW>(rk, off0 + j * row_step);
