@@ -15,6 +15,7 @@ namespace pda {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -60,6 +61,20 @@ __device__ __forceinline__ int load_uniform(const int32_t* p) {
 
 // The same read where the address differs per lane (a vector load).
 __device__ __forceinline__ int load_uniform_v(const int32_t* p) { return *p; }
+
+// Split partial outputs: fp32, or binary16 (PT = _Float16) for calls whose
+// output is bfloat16, whose rounding step is 8 times binary16's.  Four
+// consecutive values at p (16- or 8-byte aligned).
+template <class PT>
+__device__ __forceinline__ f32x4 load_part4(const PT* p) {
+  if constexpr (std::is_same<PT, float>::value) return *(const f32x4*)p;
+  else return __builtin_convertvector(*(const f16x4*)p, f32x4);
+}
+template <class PT>
+__device__ __forceinline__ void store_part4(PT* p, f32x4 v) {
+  if constexpr (std::is_same<PT, float>::value) *(f32x4*)p = v;
+  else *(f16x4*)p = __builtin_convertvector(v, f16x4);
+}
 
 // A work unit of an ordered call (written by the planning kernel): sequence
 // b (negative: no unit, the workgroup exits), split index (-1: the

@@ -482,9 +482,9 @@ constexpr int kCombineRowsMaxSplits = PDA_COMBINE_ROWS_MAX_SPLITS;
 // for up to MAXL splits per group.
 // The values needed before the first loads come as separate (preloaded)
 // arguments ahead of CombineArgs, as in the attention kernels.
-template <class OT, int DV>
+template <class OT, int DV, class PT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    const float* part_o, const float* part_lse, const int32_t* context_lens, int32_t rows_per_seq,
+    const void* part_o, const float* part_lse, const int32_t* context_lens, int32_t rows_per_seq,
     int32_t max_splits, int32_t pages_per_split, int32_t split_min_tokens, int32_t page_size,
     CombineArgs a) {
   constexpr int CW = DV > 128 ? 128 : DV;       // columns per workgroup
@@ -502,9 +502,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int S = max_splits;
   const SplitLayout sp{pages_per_split, max_splits, split_min_tokens};
   const float* pl = part_lse + row * S;
-  // split s of this chunk starts at float4 index s * (DV / 4)
-  const f32x4* po = (const f32x4*)(part_o + row * S * DV + chunk * CW);
-  constexpr int SSTR = DV / 4;
+  // split s of this chunk starts at element s * DV
+  const PT* po = (const PT*)part_o + row * S * DV + chunk * CW + 4 * (threadIdx.x % DC);
   const int sg = threadIdx.x / DC, dc = threadIdx.x % DC;
 
   // In ordered calls (ragged batches) many rows belong to unsplit sequences:
@@ -529,7 +528,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   for (int j = 0; j < MAXL; ++j) {
     const int s2 = sg + j * SG;
     l[j] = s2 < bound ? pl[s2] : -INFINITY;
-    o[j] = s2 < bound ? po[(int64_t)s2 * SSTR + dc] : f32x4{0.f, 0.f, 0.f, 0.f};
+    o[j] = s2 < bound ? load_part4(po + (int64_t)s2 * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if (!guarded) {
     __builtin_amdgcn_sched_barrier(0);  // the partial loads go out before waiting for n
@@ -560,7 +559,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       if (ls == -INFINITY) continue;
       const float w = __expf(ls - mx);
       den += w;
-      acc += w * po[(int64_t)s2 * SSTR + dc];
+      acc += w * load_part4(po + (int64_t)s2 * DV);
     }
   }
   acc_sh[sg][dc] = acc;
@@ -606,9 +605,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 // the split count is known, no LDS, no barrier).  The same algebra as
 // combine_kernel: L = M + ln sum_s exp(L_s - M), O = sum_s exp(L_s - M) O_s /
 // sum_s exp(L_s - M), M = max_s L_s, in split order.
-template <class OT, int DV, int MAXS>
+template <class OT, int DV, int MAXS, class PT>
 __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(
-    const float* part_o, const float* part_lse, const int32_t* context_lens, int32_t rows_per_seq,
+    const void* part_o, const float* part_lse, const int32_t* context_lens, int32_t rows_per_seq,
     int32_t max_splits, int32_t pages_per_split, int32_t split_min_tokens, int32_t page_size,
     CombineArgs a) {
   constexpr int DC = DV / 4;                  // four-float chunks per row
@@ -622,7 +621,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(
   const int S = max_splits;
   const SplitLayout sp{pages_per_split, max_splits, split_min_tokens};
   const float* pl = part_lse + row * S;
-  const f32x4* po = (const f32x4*)(part_o + row * S * DV) + c;
+  const PT* po = (const PT*)part_o + row * S * DV + 4 * c;
   const bool guarded = split_min_tokens > 0 || a.seq_splits;
   int nsplit = S, t0, t1;
   if (a.seq_splits) {
@@ -637,7 +636,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(
   for (int j = 0; j < MAXS; ++j) {
     const bool ok = j < (guarded ? nsplit : S);
     l[j] = ok ? pl[j] : -INFINITY;
-    o[j] = ok ? po[(int64_t)j * (DV / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+    o[j] = ok ? load_part4(po + (int64_t)j * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if (!guarded) {  // (the length comes with the partials, in the same round trip)
     split_range(sp, load_uniform_v(context_lens + b), page_size, 0, nsplit, t0, t1);
@@ -845,7 +844,7 @@ hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
 }
 
 // Rows kernel for up to MAXS splits (rows of DV columns, RPW per workgroup).
-template <class OT, int DV>
+template <class OT, int DV, class PT>
 hipError_t launch_combine_rows(const CombineArgs& a, hipStream_t s) {
   constexpr int RPW = kCombineThreads / (DV / 4);
   const int64_t rows = (int64_t)a.batch * a.q_len * a.num_q_heads;
@@ -855,13 +854,13 @@ hipError_t launch_combine_rows(const CombineArgs& a, hipStream_t s) {
   a.part_o, a.part_lse, a.context_lens, a.q_len * a.num_q_heads, a.split.max_splits,       \
       a.split.pages_per_split, a.split.split_min_tokens, a.page_size, a
   if (a.split.max_splits <= 8)
-    hipLaunchKernelGGL((combine_rows_kernel<OT, DV, 8>), grid, block, 0, s, PDA_COMBINE_ARGS);
+    hipLaunchKernelGGL((combine_rows_kernel<OT, DV, 8, PT>), grid, block, 0, s, PDA_COMBINE_ARGS);
   else
-    hipLaunchKernelGGL((combine_rows_kernel<OT, DV, 16>), grid, block, 0, s, PDA_COMBINE_ARGS);
+    hipLaunchKernelGGL((combine_rows_kernel<OT, DV, 16, PT>), grid, block, 0, s, PDA_COMBINE_ARGS);
   return hipGetLastError();
 }
 
-template <class OT>
+template <class OT, class PT>
 hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
   // rows kernel: few splits and enough rows for at least 64 workgroups (with
   // fewer rows, one workgroup per row and its splits spread over the threads
@@ -870,10 +869,10 @@ hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
                           kCombineThreads;
   if (a.split.max_splits <= kCombineRowsMaxSplits && row_wgs >= 64) {
     switch (a.head_dim_v) {
-      case 64: return launch_combine_rows<OT, 64>(a, s);
-      case 128: return launch_combine_rows<OT, 128>(a, s);
-      case 256: return launch_combine_rows<OT, 256>(a, s);
-      case 512: return launch_combine_rows<OT, 512>(a, s);
+      case 64: return launch_combine_rows<OT, 64, PT>(a, s);
+      case 128: return launch_combine_rows<OT, 128, PT>(a, s);
+      case 256: return launch_combine_rows<OT, 256, PT>(a, s);
+      case 512: return launch_combine_rows<OT, 512, PT>(a, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -881,10 +880,10 @@ hipError_t launch_combine_t(const CombineArgs& a, hipStream_t s) {
   dim3 grid((unsigned)(a.batch * a.q_len * a.num_q_heads * nch));
   dim3 block(kCombineThreads);
   switch (a.head_dim_v) {
-    case 64: hipLaunchKernelGGL((combine_kernel<OT, 64>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<OT, 128>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
-    case 256: hipLaunchKernelGGL((combine_kernel<OT, 256>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
-    case 512: hipLaunchKernelGGL((combine_kernel<OT, 512>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
+    case 64: hipLaunchKernelGGL((combine_kernel<OT, 64, PT>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<OT, 128, PT>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<OT, 256, PT>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
+    case 512: hipLaunchKernelGGL((combine_kernel<OT, 512, PT>), grid, block, 0, s, PDA_COMBINE_ARGS); break;
     default: return hipErrorInvalidValue;
   }
 #undef PDA_COMBINE_ARGS
@@ -896,11 +895,15 @@ hipError_t launch_order(const OrderArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t s) {
+hipError_t launch_combine(const CombineArgs& a, int out_dtype, bool part_f16, hipStream_t s) {
+  if (part_f16) {
+    if (out_dtype == 2) return launch_combine_t<BF16, _Float16>(a, s);
+    return hipErrorInvalidValue;
+  }
   switch (out_dtype) {
-    case 0: return launch_combine_t<F32>(a, s);
-    case 1: return launch_combine_t<F16>(a, s);
-    case 2: return launch_combine_t<BF16>(a, s);
+    case 0: return launch_combine_t<F32, float>(a, s);
+    case 1: return launch_combine_t<F16, float>(a, s);
+    case 2: return launch_combine_t<BF16, float>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

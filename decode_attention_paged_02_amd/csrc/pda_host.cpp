@@ -456,7 +456,7 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
     c.page_size = s.page_size;
     c.split = a.split;
     c.seq_splits = seq_splits;
-    if (pda::launch_combine(c, s.q_dtype, st) != hipSuccess) return PDA_ERR_HIP;
+    if (pda::launch_combine(c, s.q_dtype, false, st) != hipSuccess) return PDA_ERR_HIP;
   }
   return PDA_OK;
 }
@@ -530,7 +530,7 @@ int paged_decode_attn_mla(const void* q, const void* kv_cache, const int32_t* bl
     c.page_size = s.page_size;
     c.split = a.split;
     c.seq_splits = seq_splits;
-    if (pda::launch_combine(c, s.q_dtype, st) != hipSuccess) return PDA_ERR_HIP;
+    if (pda::launch_combine(c, s.q_dtype, true, st) != hipSuccess) return PDA_ERR_HIP;
   }
   return PDA_OK;
 }

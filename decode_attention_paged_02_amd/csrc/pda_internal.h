@@ -127,7 +127,7 @@ struct GqaArgs {
 };
 
 struct CombineArgs {
-  const float* part_o;
+  const void* part_o;  // fp32, or binary16 when part_f16 (see launch_combine)
   const float* part_lse;
   const int32_t* context_lens;
   void* out;
@@ -147,7 +147,8 @@ struct MlaArgs {
   const int32_t* context_lens;
   void* out;               // [B, q_len, Hq, 512 or 256] bf16
   float* lse;
-  float* part_o;
+  float* part_o;           // binary16 partial rows [B, q_len, Hq, max_splits, dv]
+                           // (in the workspace's fp32-sized area)
   float* part_lse;
   int32_t batch, num_q_heads, head_tiles;
   int32_t q_len, causal;   // as in GqaArgs; tile rows are (query i, head h), i * Hq + h
@@ -244,7 +245,9 @@ hipError_t launch_gqa_mfma(const GqaArgs& a, int q_dtype, int kv_dtype, int head
                            int max_splits, hipStream_t stream);
 hipError_t launch_gqa(const GqaArgs& a, int q_dtype, int kv_dtype, int head_dim,
                       int tile_heads, int max_splits, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs& a, int out_dtype, hipStream_t stream);
+// part_f16: the partial outputs are binary16 (the MLA kernels write them so;
+// the GQA kernels write fp32)
+hipError_t launch_combine(const CombineArgs& a, int out_dtype, bool part_f16, hipStream_t stream);
 hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
 hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int head_dim, int max_splits,
                       hipStream_t stream);

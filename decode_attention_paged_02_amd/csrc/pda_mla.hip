@@ -545,9 +545,9 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
         for (int mb = 0; mb < MB; ++mb)
           store_out<BF16>(a.out, row_i * kDv + CPW * wave + 16 * mb + col, acc[mb][i] * inv[i]);
       } else {
-        float* po = a.part_o + (row_i * a.split.max_splits + split) * kDv + CPW * wave + col;
+        _Float16* po = (_Float16*)a.part_o + (row_i * a.split.max_splits + split) * kDv + CPW * wave + col;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) po[16 * mb] = acc[mb][i] * inv[i];
+        for (int mb = 0; mb < MB; ++mb) po[16 * mb] = (_Float16)(acc[mb][i] * inv[i]);
       }
     }
     if (!hvalid || wave != 0 || grp != 0) return;
@@ -570,9 +570,9 @@ __global__ __launch_bounds__(kThreads * NG, 2 / NG) void mla_mfma_kernel(MlaArgs
       store_bf16x4<0>(a.out, row * kDv + CPW * wave + 16 * mb + 4 * grp, acc[mb] * inv);
     if (wave == 0 && grp == 0 && a.lse) a.lse[((int64_t)b * a.num_q_heads + h) * q_len + qi] = lse;
   } else {
-    float* po = a.part_o + (row * a.split.max_splits + split) * kDv;
+    _Float16* po = (_Float16*)a.part_o + (row * a.split.max_splits + split) * kDv;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) *(f32x4*)(po + CPW * wave + 16 * mb + 4 * grp) = acc[mb] * inv;
+    for (int mb = 0; mb < MB; ++mb) store_part4(po + CPW * wave + 16 * mb + 4 * grp, acc[mb] * inv);
     if (wave == 0 && grp == 0) a.part_lse[row * a.split.max_splits + split] = lse;
   }
 }
@@ -765,9 +765,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_valu_kernel(MlaArgs a) {
       store_bf16x4<0>(a.out, row * kDv + 8 * c8 + 4, o1);
       if (c8 == 0 && a.lse) a.lse[row] = lse;
     } else {
-      float* po = a.part_o + (row * a.split.max_splits + split) * kDv + 8 * c8;
-      *(f32x4*)po = o0;
-      *(f32x4*)(po + 4) = o1;
+      _Float16* po = (_Float16*)a.part_o + (row * a.split.max_splits + split) * kDv + 8 * c8;
+      store_part4(po, o0);
+      store_part4(po + 4, o1);
       if (c8 == 0) a.part_lse[row * a.split.max_splits + split] = lse;
     }
   }

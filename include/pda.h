@@ -192,8 +192,10 @@ int pda_plan(const pda_shape* shape, int is_mla, int num_splits, int num_cus,
 
 /* Workspace bytes a call with these arguments needs (0 when no sequence can
  * split and the work is not ordered): the split partials of "From MHA to MLA"
- * sec. 4 (an fp32 output row and an fp32 LSE per split and query row) and
- * the ordered work list.  Queries the current device's CU count when
+ * sec. 4 (an output row and an fp32 LSE per split and query row) and the
+ * ordered work list.  The output rows are fp32 for GQA calls; MLA calls,
+ * whose output is bfloat16, store them as binary16 in the first half of the
+ * same fp32-sized area.  Queries the current device's CU count when
  * num_splits == 0 or the schedule is BALANCED.  Returns 0 on invalid
  * arguments as well.  The workspace needs no initialization: every call
  * writes what it reads.
