@@ -62,7 +62,8 @@ def case_flops(case) -> int:
 def case_overhead_bytes(case, max_splits: int) -> dict:
     """Bytes a step moves besides the algorithmic KV bytes: q read, out and
     LSE written, block-table entries and lengths read, and (with splits) the
-    fp32 partial outputs and LSEs written and read back by the combine."""
+    partial outputs (fp32; binary16 for MLA) and fp32 LSEs written and read
+    back by the combine."""
     eb_q = ELEM_BYTES[case.q_dtype]
     rows = case.batch * case.q_len * case.num_q_heads
     pages = int(((np.asarray(case.context_lens, dtype=np.int64) + case.page_size - 1)
@@ -72,5 +73,6 @@ def case_overhead_bytes(case, max_splits: int) -> dict:
          "tables_and_lengths": pages * 4 + case.batch * 4,
          "split_partials": 0}
     if max_splits > 1:
-        r["split_partials"] = 2 * rows * max_splits * (case.head_dim_v + 1) * 4
+        eb_part = 2 if case.mla else 4
+        r["split_partials"] = 2 * rows * max_splits * (case.head_dim_v * eb_part + 4)
     return r
