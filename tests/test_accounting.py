@@ -76,11 +76,11 @@ def test_overhead_bytes_of_the_long_context_step():
 
 def test_overhead_bytes_of_mla_split_partials():
     """MLA writes its split partials as binary16 (the output is bfloat16):
-    B=16, Hq=128, dv=512, 32 splits: 2 * 16 * 128 * 32 * (512 * 2 + 4) B, the
+    B=16, Hq=16, dv=512, 32 splits: 2 * 16 * 16 * 32 * (512 * 2 + 4) B, the
     fp32 LSE included."""
     from decode_attention_paged_02_amd import accounting as A
     from decode_attention_paged_02_amd import workloads as W
     case = W.mla_b16(ctx=256)
-    assert case.batch == 16 and case.num_q_heads == 128 and case.head_dim_v == 512
+    assert case.batch == 16 and case.num_q_heads == 16 and case.head_dim_v == 512
     r = A.case_overhead_bytes(case, 32)
-    assert r["split_partials"] == 2 * 16 * 128 * 32 * (512 * 2 + 4)
+    assert r["split_partials"] == 2 * 16 * 16 * 32 * (512 * 2 + 4)
