@@ -62,9 +62,18 @@ __device__ __forceinline__ int load_uniform(const int32_t* p) {
 // The same read where the address differs per lane (a vector load).
 __device__ __forceinline__ int load_uniform_v(const int32_t* p) { return *p; }
 
-// Split partial outputs: fp32, or binary16 (PT = _Float16) for calls whose
-// output is bfloat16, whose rounding step is 8 times binary16's.  Four
-// consecutive values at p (16- or 8-byte aligned).
+// Split partial outputs: fp32, or binary16 for calls whose output is
+// bfloat16, whose rounding step is 8 times binary16's.  Four consecutive
+// values at p (16- or 8-byte aligned).  Kernels name the format by the tags
+// F32 / F16 (PartElem gives the element type).
+template <class PT>
+struct PartElem {
+  using type = float;
+};
+template <>
+struct PartElem<F16> {
+  using type = _Float16;
+};
 template <class PT>
 __device__ __forceinline__ f32x4 load_part4(const PT* p) {
   if constexpr (std::is_same<PT, float>::value) return *(const f32x4*)p;

@@ -503,7 +503,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const SplitLayout sp{pages_per_split, max_splits, split_min_tokens};
   const float* pl = part_lse + row * S;
   // split s of this chunk starts at element s * DV
-  const PT* po = (const PT*)part_o + row * S * DV + chunk * CW + 4 * (threadIdx.x % DC);
+  using PE = typename PartElem<PT>::type;
+  const PE* po = (const PE*)part_o + row * S * DV + chunk * CW + 4 * (threadIdx.x % DC);
   const int sg = threadIdx.x / DC, dc = threadIdx.x % DC;
 
   // In ordered calls (ragged batches) many rows belong to unsplit sequences:
@@ -621,7 +622,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(
   const int S = max_splits;
   const SplitLayout sp{pages_per_split, max_splits, split_min_tokens};
   const float* pl = part_lse + row * S;
-  const PT* po = (const PT*)part_o + row * S * DV + 4 * c;
+  using PE = typename PartElem<PT>::type;
+  const PE* po = (const PE*)part_o + row * S * DV + 4 * c;
   const bool guarded = split_min_tokens > 0 || a.seq_splits;
   int nsplit = S, t0, t1;
   if (a.seq_splits) {
@@ -897,13 +899,13 @@ hipError_t launch_order(const OrderArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, bool part_f16, hipStream_t s) {
   if (part_f16) {
-    if (out_dtype == 2) return launch_combine_t<BF16, _Float16>(a, s);
+    if (out_dtype == 2) return launch_combine_t<BF16, F16>(a, s);
     return hipErrorInvalidValue;
   }
   switch (out_dtype) {
-    case 0: return launch_combine_t<F32, float>(a, s);
-    case 1: return launch_combine_t<F16, float>(a, s);
-    case 2: return launch_combine_t<BF16, float>(a, s);
+    case 0: return launch_combine_t<F32, F32>(a, s);
+    case 1: return launch_combine_t<F16, F32>(a, s);
+    case 2: return launch_combine_t<BF16, F32>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
