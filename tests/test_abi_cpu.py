@@ -37,17 +37,24 @@ def _shape(**kw):
 
 
 def test_plan_fills_compute_units():
-    # 512 (sequence, KV head) units already cover 2 workgroups per CU: no split
+    # The matrix-core GQA kernel (f16 q, G = 4) splits until the units fill one
+    # workgroup per CU.  512 (sequence, KV head) units: no split
     p = pda.plan(_shape(), num_cus=256)
     assert (p.max_splits, p.pages_per_split, p.head_tiles, p.workgroups) == (1, 64, 1, 512)
     assert p.workspace_bytes == 0
-    # B=1, 32768 tokens: 8 units -> 64 splits of 32 pages
+    # B=1, 32768 tokens: 8 units -> 32 splits of 64 pages
     p = pda.plan(_shape(batch=1, max_pages_per_seq=2048), num_cus=256)
-    assert (p.max_splits, p.pages_per_split, p.workgroups) == (64, 32, 512)
-    assert p.workspace_bytes == 32 * 64 * 128 * 4 + 32 * 64 * 4
-    # B=4 -> 16 splits of 128 pages
+    assert (p.max_splits, p.pages_per_split, p.workgroups) == (32, 64, 256)
+    assert p.workspace_bytes == 32 * 32 * 128 * 4 + 32 * 32 * 4
+    # B=4 -> 8 splits of 256 pages; B=32 (256 units) -> no split
     p = pda.plan(_shape(batch=4, max_pages_per_seq=2048), num_cus=256)
-    assert (p.max_splits, p.pages_per_split) == (16, 128)
+    assert (p.max_splits, p.pages_per_split) == (8, 256)
+    p = pda.plan(_shape(batch=32, max_pages_per_seq=2048), num_cus=256)
+    assert p.max_splits == 1
+    # the VALU kernel (fp32 q) fills two workgroups per CU: B=1 -> 64 splits
+    p = pda.plan(_shape(batch=1, max_pages_per_seq=2048, q_dtype=pda.PDA_F32,
+                        kv_dtype=pda.PDA_F32), num_cus=256)
+    assert (p.max_splits, p.pages_per_split) == (64, 32)
 
 
 def test_plan_explicit_and_threshold():
