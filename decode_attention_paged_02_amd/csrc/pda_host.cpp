@@ -131,13 +131,14 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
   // 512-thread workgroup, which then runs one per compute unit)
   const int mla_groups =
       mla && s->variant != PDA_MLA_VALU ? pda::mla_column_groups(ql * s->num_q_heads) : 1;
-  const int head_tiles = mla             ? (int)ceil_div(ql * s->num_q_heads, 16 * mla_groups)
-                         : gqa_use_mfma(s)
-                             ? (int)ceil_div(ql * group,
-                                             16 * pda::gqa_mfma_col_tiles(
-                                                      ql * group, s->head_dim,
-                                                      (int64_t)s->max_pages_per_seq * s->page_size))
-                                           : (int)ceil_div(group, pda::gqa_tile_heads(group));
+  const bool mfma_gqa = !mla && gqa_use_mfma(s);
+  const int col_tiles = mfma_gqa ? pda::gqa_mfma_col_tiles(ql * group, s->head_dim,
+                                                           (int64_t)s->max_pages_per_seq *
+                                                               s->page_size)
+                                 : 1;
+  const int head_tiles = mla      ? (int)ceil_div(ql * s->num_q_heads, 16 * mla_groups)
+                         : mfma_gqa ? (int)ceil_div(ql * group, 16 * col_tiles)
+                                    : (int)ceil_div(group, pda::gqa_tile_heads(group));
   const int64_t units = (int64_t)s->batch * s->num_kv_heads * head_tiles;
   const int max_pages = s->max_pages_per_seq;
   const bool balanced = s->schedule == PDA_SCHEDULE_BALANCED;
@@ -160,11 +161,14 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
         std::min<int64_t>(ceil_div(max_pages, kMinChunkPages), kBalancedMaxSplits));
   } else {
     // split only when the (sequence, head tile) units alone cannot fill the
-    // compute units.  The matrix-core GQA kernel fills one workgroup per CU:
-    // at 32768 tokens that measured 0-6% faster than two at every batch from
-    // 1 to 32 in both page layouts (B=8: 161 against 168-170 us, B=32 with
-    // no split: 624-626 against 645-663 us) and the same for MQA.
-    const int fill_per_cu = (!mla && gqa_use_mfma(s)) ? 1 : wg_per_cu;
+    // compute units.  The matrix-core GQA kernel with one column tile fills
+    // one workgroup per CU: at 32768 tokens that measured 0-6% faster than
+    // two at every batch from 1 to 32 in both page layouts (B=8: 161 against
+    // 168-170 us, B=32 with no split: 624-626 against 645-663 us).  Two
+    // column tiles (MQA) carry twice the arithmetic per tile and keep two
+    // workgroups per CU (4 splits against 8 at B=64 measured from equal to
+    // 2 us slower).
+    const int fill_per_cu = (mfma_gqa && col_tiles == 1) ? 1 : wg_per_cu;
     const int64_t target = fill_per_cu * (int64_t)num_cus;
     if (units > 0 && units < target)
       splits = (int)std::min<int64_t>(ceil_div(target, units), max_pages);

@@ -51,6 +51,10 @@ def test_plan_fills_compute_units():
     assert (p.max_splits, p.pages_per_split) == (8, 256)
     p = pda.plan(_shape(batch=32, max_pages_per_seq=2048), num_cus=256)
     assert p.max_splits == 1
+    # two column tiles (MQA, 32 heads on one KV head, 8192 tokens) keep two
+    # workgroups per CU: 64 units -> 8 splits
+    p = pda.plan(_shape(num_kv_heads=1, max_pages_per_seq=512), num_cus=256)
+    assert (p.head_tiles, p.max_splits, p.workgroups) == (1, 8, 512)
     # the VALU kernel (fp32 q) fills two workgroups per CU: B=1 -> 64 splits
     p = pda.plan(_shape(batch=1, max_pages_per_seq=2048, q_dtype=pda.PDA_F32,
                         kv_dtype=pda.PDA_F32), num_cus=256)
