@@ -144,3 +144,14 @@ def test_mla_b16_two_tokens_sampled():
     out, lse = pda.run_case(case)
     check(case, out, lse, ref_o, ref_l, rows=(rows, rows.transpose(0, 2, 1)),
           label="mla b16 q_len=2")
+
+
+def test_mla_b16_two_tokens_full_size():
+    """The timed two-token MLA workload: B=16, Hq=16, ctx 65536, two causal
+    query tokens per sequence, every (sequence, token, head) row."""
+    case = W.mla_b16_mtp(2)
+    say(case.name)
+    ref_o, ref_l = oracle_ref(case)
+    out, lse = pda.run_case(case)
+    assert tuple(out.shape) == (16, 2, 16, 512)
+    check(case, out, lse, ref_o, ref_l, label=case.name)
