@@ -178,8 +178,10 @@ typedef struct pda_plan_info {
  * sec. 4 (the closing paragraph) chooses num_splits from the batch size, the
  * head tiles, the context length and the number of SMs, splitting only when
  * the (sequence, head) work alone leaves compute units idle; the drill page
- * sec. 6 shows the cost of not splitting at batch 1.  This planner fills two
- * workgroups per compute unit.
+ * sec. 6 shows the cost of not splitting at batch 1.  This planner splits
+ * until the grid fills one workgroup per compute unit for the matrix-core
+ * GQA kernel with 16-row tiles, and two for its 32-row tiles, the vector
+ * kernel and MLA (one of MLA's 512-thread workgroups).
  * num_splits: 0 = automatic (fill the GPU's compute units), otherwise the
  * largest number of splits any sequence may use (at most 64 with the BALANCED
  * schedule).  num_cus: compute units to plan for; 0 = query the current HIP
