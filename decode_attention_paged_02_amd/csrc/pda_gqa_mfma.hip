@@ -581,7 +581,17 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
               den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
       } else {
         float* po = a.part_o + (row * a.split.max_splits + split) * D + d0;
-        *(f32x4*)po = f32x4{o[0], o[1], o[2], o[3]};
+        const f32x4 ov = {o[0], o[1], o[2], o[3]};
+        if constexpr (CT == 2) {
+          // 32-row workgroups write 16 KiB of partials each (MQA: 8.4 MB
+          // per call, most of it in the last microseconds): written through
+          // to memory (sc0 sc1) rather than left dirty in L2 for the end of
+          // the kernel, 51.0-51.3 against 51.7-51.9 us per MQA step.  With
+          // 16-row workgroups (2 KiB) plain stores measured faster.
+          asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(po), "v"(ov) : "memory");
+        } else {
+          *(f32x4*)po = ov;
+        }
         if (d0 == 0)
           a.part_lse[row * a.split.max_splits + split] =
               den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
