@@ -161,8 +161,8 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, f32x4 c
 // than 16 rows (d <= 128), so that one load of a K/V tile serves 32 rows.
 // SD steps of tiles in flight per wave (see kGqaStepsInFlight), ST tiles per
 // step.
-template <class QT, class KT, int D, int CT, int SD, int ST>
-__global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
+template <class QT, class KT, int D, int CT, int SD, int ST, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void gqa_mfma_kernel(
     const int32_t* context_lens, const int32_t* block_tables, const void* q, int32_t head_tiles,
     int32_t num_kv_heads, int32_t group, int32_t q_len, int32_t max_pages, int32_t log2_page,
     int32_t pages_per_split, int32_t max_splits, const int32_t* units, GqaArgs a) {
@@ -175,19 +175,19 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   constexpr bool kFp8 = std::is_same<KT, E4M3>::value;
   constexpr bool kBf16 = std::is_same<QT, BF16>::value;
   constexpr int kAccStride = D + 4;             // floats per head row of the merge area
-  constexpr int kMergeB = kMWaves * kMHeads * kAccStride * 4;
+  constexpr int kMergeB = NW > 1 ? NW * kMHeads * kAccStride * 4 : 0;
   // the merge area gets its own LDS when both fit two workgroups per CU
-  constexpr bool kSeparateMerge = kMWaves * kTileB + kMergeB <= 72 * 1024;
-  constexpr int kMergeOff = kSeparateMerge ? kMWaves * kTileB : 0;
-  constexpr int kLdsB = kSeparateMerge ? kMWaves * kTileB + kMergeB
-                        : (kMWaves * kTileB > kMergeB ? kMWaves * kTileB : kMergeB);
+  constexpr bool kSeparateMerge = NW * kTileB + kMergeB <= 72 * 1024;
+  constexpr int kMergeOff = kSeparateMerge ? NW * kTileB : 0;
+  constexpr int kLdsB = kSeparateMerge ? NW * kTileB + kMergeB
+                        : (NW * kTileB > kMergeB ? NW * kTileB : kMergeB);
   static_assert(D == 64 || D == 128 || D == 256, "head_dim");
   static_assert(CT == 1 || (CT == 2 && D <= 128), "column tiles");
   constexpr int kRowsWG = kMHeads * CT;         // (query token, head) rows of a workgroup
   static_assert(kFp8 || std::is_same<QT, KT>::value, "q / cache types");
 
   __shared__ __attribute__((aligned(16))) char lds[kLdsB];
-  __shared__ float m_sh[kMWaves][kMHeads], l_sh[kMWaves][kMHeads];
+  __shared__ float m_sh[NW][kMHeads], l_sh[NW][kMHeads];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -195,7 +195,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   const int grp = lane >> 4;  // lane group
 
   // which (sequence, KV head, head tile, split) this workgroup computes
-  const bool ordered = units != nullptr || a.plan_in_kernel;
+  // (one-wave workgroups serve grid calls only)
+  const bool ordered = NW > 1 && (units != nullptr || a.plan_in_kernel);
   int tile, kvh, b, split, ut0 = 0, ut1 = 0;
   if (ordered) {
     // ordered: the unit list gives (sequence, split, token range) longest
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     } else {      // this workgroup derives its unit from the lengths
       __shared__ PlanShared plan_sh;
       int ns_b;
-      w = plan_unit<kMWaves * 64>(context_lens, a.plan, g / num_kv_heads, plan_sh, ns_b);
+      w = plan_unit<NW * 64>(context_lens, a.plan, g / num_kv_heads, plan_sh, ns_b);
       w.b = __builtin_amdgcn_readfirstlane(w.b);
       w.split = __builtin_amdgcn_readfirstlane(w.split);
       w.t0 = __builtin_amdgcn_readfirstlane(w.t0);
@@ -244,12 +245,12 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   const int t0_hint = ordered ? ut0 : max_splits > 1 ? split * pages_per_split << log2P : 0;
 
   // The range is walked in steps of ST consecutive tiles; wave w takes steps
-  // w, w + kMWaves, ...  Sequence length, block-table entries (lane j: tile
+  // w, w + NW, ...  Sequence length, block-table entries (lane j: tile
   // j % ST of the wave's step sbase + j / ST, clamped into the row, unused
   // past the sequence) and q are requested together.
   constexpr int kStepsPerChunk = 64 / ST;
   auto load_table = [&](int sbase) -> int {
-    const int T = (wave + (sbase + lane / ST) * kMWaves) * ST + lane % ST;
+    const int T = (wave + (sbase + lane / ST) * NW) * ST + lane % ST;
     const int64_t tok = (int64_t)t0_hint + (int64_t)T * kTileTokens;
     const int64_t pg = tok >> log2P;
     return table[pg < max_pages ? pg : max_pages - 1];
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
 
   const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
   const int nsteps = (ntiles + ST - 1) / ST;
-  const int ns_wave = nsteps > wave ? (nsteps - wave + kMWaves - 1) / kMWaves : 0;
+  const int ns_wave = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;
 
   char* ktile = lds + wave * kTileB;
 
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   auto issue = [&](int sidx, int send, int u) {
 #pragma unroll
     for (int t = 0; t < ST; ++t) {
-      const int T = (wave + sidx * kMWaves) * ST + t;
+      const int T = (wave + sidx * NW) * ST + t;
       const bool live = sidx < send && T < ntiles;
       const int entry = __builtin_amdgcn_readlane(vtbl, ((sidx % kStepsPerChunk) * ST + t) & 63);
       const int phys = live ? entry : 0;
@@ -516,6 +517,48 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
   // column tile after the other through the same 16-row area.  When the
   // merge area overlays the K tiles, every wave must be done with them; a
   // second column tile waits for the readers of the first.
+  if constexpr (NW == 1) {
+    // One wave owns the unit: nothing to merge.  Lane (col, grp) holds, for
+    // column tile c, values (4 grp + i) NE .. + NE of row 16 c + col (i = 0..3),
+    // and a quarter of that row's sum (its four lane groups add it up); the
+    // running max is the same in the four.
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const float den = pair_sum<5>(pair_sum<4>(l_run[c]));
+      if (16 * c + col >= gvalid) continue;
+      const float inv = den > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(den) : 0.f;
+      const float lse_v = den > 0.f ? (m_run[c] + __log2f(den)) * kLn2 : -INFINITY;
+      int i = 0, gh = g0 + 16 * c + col;
+      if (q_len > 1) {
+        i = gh / group;
+        gh -= i * group;
+      }
+      const int h = kvh * group + gh;
+      const int64_t row = ((int64_t)b * q_len + i) * num_q_heads + h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = (4 * grp + r) * NE;
+        float o[NE];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) o[e] = acc[c][e][r] * inv;
+        if (nsplit == 1) {
+          store_row<QT, NE>(a.out, row * D + d0, o);
+        } else {
+          float* po = a.part_o + (row * a.split.max_splits + split) * D + d0;
+#pragma unroll
+          for (int e = 0; e < NE; e += 4) *(f32x4*)(po + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+        }
+      }
+      if (grp == 0) {
+        if (nsplit == 1) {
+          if (a.lse) a.lse[((int64_t)b * num_q_heads + h) * q_len + i] = lse_v;
+        } else {
+          a.part_lse[row * a.split.max_splits + split] = lse_v;
+        }
+      }
+    }
+    return;
+  }
   float* acc_sh = (float*)(lds + kMergeOff);  // [wave][head][kAccStride]
   constexpr int kQ = D / 4;                   // four-value items per row
 #pragma unroll
@@ -542,23 +585,23 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
     // threads; each item issues its LDS reads (the four waves' max, sum and
     // values) before any arithmetic: weights exp2(m_w - max), one reciprocal.
     // (A row no wave saw a token of keeps max kMaxStart and sum 0: out 0.)
-    for (int it = threadIdx.x; it < gv * kQ; it += kMWaves * 64) {
+    for (int it = threadIdx.x; it < gv * kQ; it += NW * 64) {
       const int g = it / kQ, d0 = 4 * (it % kQ);
-      float mw[kMWaves], lw[kMWaves];
-      f32x4 xw[kMWaves];
+      float mw[NW], lw[NW];
+      f32x4 xw[NW];
 #pragma unroll
-      for (int w = 0; w < kMWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         mw[w] = m_sh[w][g];
         lw[w] = l_sh[w][g];
         xw[w] = *(const f32x4*)(acc_sh + (w * kMHeads + g) * kAccStride + d0);
       }
       float mx = mw[0];
 #pragma unroll
-      for (int w = 1; w < kMWaves; ++w) mx = fmaxf(mx, mw[w]);
+      for (int w = 1; w < NW; ++w) mx = fmaxf(mx, mw[w]);
       f32x4 num = {0.f, 0.f, 0.f, 0.f};
       float den = 0.f;
 #pragma unroll
-      for (int w = 0; w < kMWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float wt = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mx);
         den += wt * lw[w];
         num += wt * xw[w];
@@ -601,19 +644,25 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void gqa_mfma_kernel(
 }
 
 // grid calls with kGqaStepsInFlight steps in flight (kGqaStepsInFlightFp8 for
-// fp8 caches), ordered ones with kGqaStepsInFlightOrdered; ST tiles per step
+// fp8 caches), ordered ones with kGqaStepsInFlightOrdered; ST tiles per step.
+// Workgroups of four waves, or of one (a.waves == 1: grid calls with one
+// column tile) with kGqaStepsInFlightWave steps in flight.
 template <class QT, class KT, int D, int CT, int ST>
-void launch_sd(const GqaArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+void launch_sd(const GqaArgs& a, dim3 grid, hipStream_t s) {
   constexpr int kGridSD = std::is_same<KT, E4M3>::value ? kGqaStepsInFlightFp8 : kGqaStepsInFlight;
 #define PDA_MFMA_ARGS                                                                        \
   a.context_lens, a.block_tables, a.q, a.head_tiles, a.num_kv_heads, a.group, a.q_len,        \
       a.max_pages, a.log2_page, a.split.pages_per_split, a.split.max_splits, a.units, a
-  if (a.units || a.plan_in_kernel)
-    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlightOrdered, ST>), grid,
-                       block, 0, s, PDA_MFMA_ARGS);
+  const bool ordered = a.units || a.plan_in_kernel;
+  if (ordered)
+    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlightOrdered, ST, kMWaves>),
+                       grid, dim3(kMWaves * 64), 0, s, PDA_MFMA_ARGS);
+  else if (CT == 1 && a.waves == 1)
+    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, 1, kGqaStepsInFlightWave, ST, 1>), grid,
+                       dim3(64), 0, s, PDA_MFMA_ARGS);
   else
-    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGridSD, ST>), grid, block, 0, s,
-                       PDA_MFMA_ARGS);
+    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGridSD, ST, kMWaves>), grid,
+                       dim3(kMWaves * 64), 0, s, PDA_MFMA_ARGS);
 #undef PDA_MFMA_ARGS
 }
 
@@ -624,14 +673,14 @@ void launch_sd(const GqaArgs& a, dim3 grid, dim3 block, hipStream_t s) {
 // balanced: 86.6 against 88.0) -- but with token-major rows 1 KiB apart they
 // slow down (48.1 against 44.9 us; ragged 95.5 against 93.9).
 template <class QT, class KT, int D, int CT>
-void launch_st(const GqaArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+void launch_st(const GqaArgs& a, dim3 grid, hipStream_t s) {
   if constexpr (std::is_same<KT, E4M3>::value && kGqaStepTilesFp8 != kGqaStepTiles) {
     if (a.tok_stride == D) {
-      launch_sd<QT, KT, D, CT, kGqaStepTilesFp8>(a, grid, block, s);
+      launch_sd<QT, KT, D, CT, kGqaStepTilesFp8>(a, grid, s);
       return;
     }
   }
-  launch_sd<QT, KT, D, CT, kGqaStepTiles>(a, grid, block, s);
+  launch_sd<QT, KT, D, CT, kGqaStepTiles>(a, grid, s);
 }
 
 template <class QT, class KT>
@@ -640,19 +689,18 @@ hipError_t launch_mfma_qk(const GqaArgs& a, int head_dim, int max_splits, hipStr
   const unsigned nhu = (unsigned)(a.num_kv_heads * a.head_tiles);
   const bool ordered = a.units || a.plan_in_kernel;
   dim3 grid(ordered ? nhu * (unsigned)a.unit_count : units, ordered ? 1u : (unsigned)max_splits);
-  dim3 block(kMWaves * 64);
   const bool two =
       gqa_mfma_col_tiles(a.q_len * a.group, head_dim, (int64_t)a.max_pages * a.page_size) == 2;
   switch (head_dim) {
     case 64:
-      if (two) launch_st<QT, KT, 64, 2>(a, grid, block, s);
-      else launch_st<QT, KT, 64, 1>(a, grid, block, s);
+      if (two) launch_st<QT, KT, 64, 2>(a, grid, s);
+      else launch_st<QT, KT, 64, 1>(a, grid, s);
       break;
     case 128:
-      if (two) launch_st<QT, KT, 128, 2>(a, grid, block, s);
-      else launch_st<QT, KT, 128, 1>(a, grid, block, s);
+      if (two) launch_st<QT, KT, 128, 2>(a, grid, s);
+      else launch_st<QT, KT, 128, 1>(a, grid, s);
       break;
-    case 256: launch_st<QT, KT, 256, 1>(a, grid, block, s); break;
+    case 256: launch_st<QT, KT, 256, 1>(a, grid, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -72,8 +72,9 @@ int check_shape(const pda_shape* s, bool mla) {
   } else {
     if (!pda::gqa_supported(s->q_dtype, s->kv_dtype, s->head_dim, s->head_dim_v))
       return PDA_ERR_UNSUPPORTED;
-    if (s->variant < PDA_GQA_DEFAULT || s->variant > PDA_GQA_VALU) return PDA_ERR_INVALID_ARG;
-    if (s->variant == PDA_GQA_MFMA && !pda::gqa_mfma_supported(s->q_dtype, s->kv_dtype, s->head_dim))
+    if (s->variant < PDA_GQA_DEFAULT || s->variant > PDA_GQA_MFMA_1WAVE) return PDA_ERR_INVALID_ARG;
+    if (s->variant != PDA_GQA_DEFAULT && s->variant != PDA_GQA_VALU &&
+        !pda::gqa_mfma_supported(s->q_dtype, s->kv_dtype, s->head_dim))
       return PDA_ERR_UNSUPPORTED;
     // several query tokens: the matrix-core kernel only
     if (query_len(s) > 1 &&
@@ -96,6 +97,32 @@ int check_shape(const pda_shape* s, bool mla) {
 // Smallest chunk of the balanced schedule, in pages.
 constexpr int kMinChunkPages = 16;
 
+// One-wave GQA workgroups the split planner aims at per compute unit.
+constexpr int kOneWaveUnitsPerCu = 2;
+
+// Whether a call that may give each work unit to one wave of the matrix-core
+// GQA kernel does so by default (units: (sequence, KV head, head tile)
+// units before splitting).  Measured on MI355X (us per step, one wave against
+// four): B=64 Hq=32 Hkv=8 d=128 fp16 at 128..4096 tokens 8.1 / 8.6 ..
+// 158.0 / 164.3, token-major pages at 1024 tokens 41.1 / 44.3, bfloat16 44.4 /
+// 44.9, d=256 45.9 / 47.1, two query tokens 41.2 / 43.6, B=128 at 512 tokens
+// 42.5 / 47.8; with splits B=1 at 32768 tokens (64 splits against 32) 26.3 /
+// 27.1, B=2 45.1 / 45.8, B=4 equal, B=16 at 8192 tokens 83.7 / 86.2.  A lone
+// wave computes its tiles with no other wave of its unit to hide their
+// latency: fp8 caches (66.1 / 43.4 at 2048 tokens) and d=64 (62.1 / 44.0)
+// stay with four waves, and so do calls whose units fill the compute units
+// with four-wave workgroups but not with two one-wave ones per unit of work
+// (B=32 at 4096 tokens: one wave would split, 83.7 against 80.0).  With an
+// explicit split count (num_splits > 0) one wave needs two units per compute
+// unit after splitting (B=1 with 32 splits: 39.5 against 27.1).
+bool one_wave_default(const pda_shape* s, int64_t units, int num_splits, int num_cus) {
+  const bool wide16 = (s->kv_dtype == PDA_F16 || s->kv_dtype == PDA_BF16) && s->head_dim >= 128;
+  const int64_t fill = (int64_t)kOneWaveUnitsPerCu * num_cus;
+  if (!wide16) return false;
+  if (num_splits > 0) return units * std::min(num_splits, s->max_pages_per_seq) >= fill;
+  return units >= fill || units < num_cus;
+}
+
 // Smallest group size for which the default GQA variant takes the matrix-core
 // kernel (its 16 head columns are mostly padding below that).
 constexpr int kMfmaMinGroup = 3;
@@ -104,14 +131,14 @@ constexpr int kMfmaMinGroup = 3;
 // are the q_len * group rows of a KV group).
 bool gqa_use_mfma(const pda_shape* s) {
   if (s->variant == PDA_GQA_VALU) return false;
-  if (s->variant == PDA_GQA_MFMA || query_len(s) > 1) return true;
+  if (s->variant != PDA_GQA_DEFAULT || query_len(s) > 1) return true;
   return pda::gqa_mfma_supported(s->q_dtype, s->kv_dtype, s->head_dim) &&
          s->num_q_heads / s->num_kv_heads >= kMfmaMinGroup;
 }
 
 // The plan of a call: the public summary plus what only the library uses.
 struct Plan {
-  pda_plan_info info;
+  pda_plan_info info;  // (info.waves_per_unit: 1 selects the one-wave GQA kernel)
   int32_t unit_capacity;  // ordered calls: length of the work-unit list
   int32_t target_units;   // balanced schedule: chunks per KV head and head tile
 };
@@ -144,6 +171,22 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
   const bool balanced = s->schedule == PDA_SCHEDULE_BALANCED;
   // Eight waves per compute unit (two four-wave workgroups, or one of eight)
   const int wg_per_cu = mla_groups == 2 ? 1 : 2;
+  // The matrix-core GQA kernel with one column tile can give each work unit
+  // to one wave (workgroups of one wave, no merge) on the GRID schedule
+  // without a threshold (no ordered work).
+  const bool one_wave_ok = mfma_gqa && col_tiles == 1 && !balanced && s->split_min_tokens == 0;
+  if (s->variant == PDA_GQA_MFMA_1WAVE && !mla && !one_wave_ok) return PDA_ERR_UNSUPPORTED;
+  // (the default choice needs the compute units; with an explicit split
+  // count and no device to ask, the call keeps four waves)
+  int wave_cus = num_cus;
+  if (one_wave_ok && s->variant != PDA_GQA_MFMA_1WAVE && s->variant != PDA_GQA_MFMA_4WAVE &&
+      wave_cus == 0)
+    wave_cus = device_cus();
+  const bool one_wave =
+      !mla && one_wave_ok &&
+      (s->variant == PDA_GQA_MFMA_1WAVE ||
+       (s->variant != PDA_GQA_MFMA_4WAVE && wave_cus > 0 &&
+        one_wave_default(s, units, num_splits, wave_cus)));
 
   if ((num_splits == 0 || balanced) && num_cus == 0) {
     num_cus = device_cus();
@@ -168,7 +211,9 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
     // column tiles (MQA) carry twice the arithmetic per tile and keep two
     // workgroups per CU (4 splits against 8 at B=64 measured from equal to
     // 2 us slower).
-    const int fill_per_cu = (mfma_gqa && col_tiles == 1) ? 1 : wg_per_cu;
+    // One-wave workgroups fill two per compute unit.
+    const int fill_per_cu = one_wave ? kOneWaveUnitsPerCu
+                            : (mfma_gqa && col_tiles == 1) ? 1 : wg_per_cu;
     const int64_t target = fill_per_cu * (int64_t)num_cus;
     if (units > 0 && units < target)
       splits = (int)std::min<int64_t>(ceil_div(target, units), max_pages);
@@ -181,6 +226,8 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
 
   p->max_splits = splits;
   p->pages_per_split = balanced ? 0 : pps;
+  p->waves_per_unit = one_wave ? 1 : mla ? 4 * mla_groups : mfma_gqa ? 4 : pda::kGqaWaves;
+  p->reserved = 0;
   p->head_tiles = head_tiles;
   p->num_cus = num_cus;
   // The balanced schedule aims at twice the (sequence, split) units that fill
@@ -338,7 +385,7 @@ int pda_stream_probe(const void* k_cache, const void* v_cache, const int32_t* bl
              : PDA_ERR_HIP;
 }
 
-int pda_version(void) { return 300; }
+int pda_version(void) { return 400; }
 
 const char* pda_status_string(int status) {
   switch (status) {
@@ -421,6 +468,7 @@ int paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
   a.split.pages_per_split = p.pages_per_split;
   a.split.max_splits = p.max_splits;
   a.split.split_min_tokens = s.split_min_tokens;
+  a.waves = p.waves_per_unit;
 
   hipStream_t st = (hipStream_t)stream;
   // BALANCED calls on the matrix-core kernel with a moderate batch: each

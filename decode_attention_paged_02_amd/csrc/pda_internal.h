@@ -43,6 +43,11 @@ constexpr int kTileTokens = 16;
 #ifndef PDA_GQA_STEPS_IN_FLIGHT_ORDERED
 #define PDA_GQA_STEPS_IN_FLIGHT_ORDERED 2
 #endif
+// Steps in flight per wave when one wave owns a work unit (no other wave of
+// the workgroup covers its latency).
+#ifndef PDA_GQA_STEPS_IN_FLIGHT_WAVE
+#define PDA_GQA_STEPS_IN_FLIGHT_WAVE 2
+#endif
 // Registers the GQA kernels may spend on the ring of in-flight tiles (caps
 // the prefetch depth for wide rows).
 #ifndef PDA_GQA_RING_REGS
@@ -63,6 +68,7 @@ constexpr int kGqaStepsInFlight = PDA_GQA_STEPS_IN_FLIGHT;
 constexpr int kGqaStepsInFlightOrdered = PDA_GQA_STEPS_IN_FLIGHT_ORDERED;
 constexpr int kGqaStepTilesFp8 = PDA_GQA_STEP_TILES_FP8;
 constexpr int kGqaStepsInFlightFp8 = PDA_GQA_STEPS_IN_FLIGHT_FP8;
+constexpr int kGqaStepsInFlightWave = PDA_GQA_STEPS_IN_FLIGHT_WAVE;
 
 // Split layout shared by the attention kernels and the combine kernel.  For
 // sequence b with n = context_lens[b] tokens and pages = ceil(n / P):
@@ -124,6 +130,10 @@ struct GqaArgs {
   int32_t plan_in_kernel;
   UnitPlan plan;
   int32_t* seq_splits;
+  // waves per workgroup of the matrix-core kernel: 4 (a unit's tiles dealt
+  // over four waves, merged in LDS) or 1 (one wave per unit; grid calls with
+  // one column tile)
+  int32_t waves;
 };
 
 struct CombineArgs {

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpda.so")
 
 PDA_F32, PDA_F16, PDA_BF16, PDA_FP8_E4M3 = 0, 1, 2, 3
 PDA_MLA_DEFAULT, PDA_MLA_MFMA, PDA_MLA_VALU, PDA_MLA_MFMA_QM = 0, 1, 2, 3
-PDA_GQA_DEFAULT, PDA_GQA_MFMA, PDA_GQA_VALU = 0, 1, 2
+PDA_GQA_DEFAULT, PDA_GQA_MFMA, PDA_GQA_VALU, PDA_GQA_MFMA_4WAVE, PDA_GQA_MFMA_1WAVE = 0, 1, 2, 3, 4
 PDA_SCHEDULE_GRID, PDA_SCHEDULE_BALANCED = 0, 1
 PDA_KV_TOKEN_MAJOR, PDA_KV_HEAD_MAJOR = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
@@ -48,7 +48,8 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("max_splits", ctypes.c_int32), ("pages_per_split", ctypes.c_int32),
                 ("head_tiles", ctypes.c_int32), ("workgroups", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("ordered", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("waves_per_unit", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 EXPORTS = ("pda_plan", "pda_workspace_bytes", "paged_decode_attn", "paged_decode_attn_mla",

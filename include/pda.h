@@ -151,6 +151,11 @@ typedef struct pda_shape {
                           /* at least 3 query heads, else vector ALUs       */
 #define PDA_GQA_MFMA 1    /* matrix cores (F16/BF16 queries only)           */
 #define PDA_GQA_VALU 2    /* vector dot products                            */
+#define PDA_GQA_MFMA_4WAVE 3 /* matrix cores, four waves per work unit        */
+#define PDA_GQA_MFMA_1WAVE 4 /* matrix cores, one wave per work unit (GRID    */
+                             /* schedule without a split threshold, at most  */
+                             /* 16 (query token, head) rows per KV group or  */
+                             /* head_dim 256; else PDA_ERR_UNSUPPORTED)      */
 
 /* MLA kernel variants (pda_shape.variant for paged_decode_attn_mla). */
 #define PDA_MLA_DEFAULT 0 /* the fastest available                          */
@@ -171,6 +176,10 @@ typedef struct pda_plan_info {
   int32_t num_cus;         /* compute units the plan was made for           */
   int32_t ordered;         /* 1: the call orders its work longest first     */
   uint64_t workspace_bytes; /* bytes the call needs in `workspace`          */
+  int32_t waves_per_unit;  /* waves of the main kernel that share one work  */
+                           /* unit (4, or 1 for the matrix-core GQA kernel  */
+                           /* when each wave takes a unit of its own)       */
+  int32_t reserved;
 } pda_plan_info;
 
 /* Choose the split layout for a call (host only, no device work).  The pages
@@ -340,10 +349,12 @@ int pda_stream_probe(const void* k_cache, const void* v_cache, const int32_t* bl
 /* Static description of a status code. */
 const char* pda_status_string(int status);
 
-/* Library version, major * 10000 + minor * 100 + patch: 300 (0.3.0).  0.2
+/* Library version, major * 10000 + minor * 100 + patch: 400 (0.4.0).  0.2
  * appended kv_layout to pda_shape and added pda_check_inputs (a caller built
  * against an older header passes a shorter pda_shape and must be rebuilt);
- * 0.3 added pda_stream_probe and caps BALANCED calls at 64 splits. */
+ * 0.3 added pda_stream_probe and caps BALANCED calls at 64 splits; 0.4 added
+ * the one-wave GQA variant and appended waves_per_unit to pda_plan_info (a
+ * caller built against an older header must be rebuilt). */
 int pda_version(void);
 
 #ifdef __cplusplus

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(pda.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pda_version() == 300
+    assert lib.pda_version() == 400
     assert lib.pda_status_string(3) == b"workspace missing or too small"
 
 
@@ -37,24 +37,47 @@ def _shape(**kw):
 
 
 def test_plan_fills_compute_units():
-    # The matrix-core GQA kernel (f16 q, G = 4) splits until the units fill one
-    # workgroup per CU.  512 (sequence, KV head) units: no split
+    # The matrix-core GQA kernel with f16 q and caches, d = 128, G = 4 gives
+    # each (sequence, KV head[, split]) unit to one wave and splits until the
+    # units fill two per CU.  512 (sequence, KV head) units: no split
     p = pda.plan(_shape(), num_cus=256)
     assert (p.max_splits, p.pages_per_split, p.head_tiles, p.workgroups) == (1, 64, 1, 512)
-    assert p.workspace_bytes == 0
-    # B=1, 32768 tokens: 8 units -> 32 splits of 64 pages
+    assert p.waves_per_unit == 1 and p.workspace_bytes == 0
+    # B=1, 32768 tokens: 8 units -> 64 splits of 32 pages
     p = pda.plan(_shape(batch=1, max_pages_per_seq=2048), num_cus=256)
-    assert (p.max_splits, p.pages_per_split, p.workgroups) == (32, 64, 256)
-    assert p.workspace_bytes == 32 * 32 * 128 * 4 + 32 * 32 * 4
-    # B=4 -> 8 splits of 256 pages; B=32 (256 units) -> no split
+    assert (p.max_splits, p.pages_per_split, p.workgroups, p.waves_per_unit) == (64, 32, 512, 1)
+    assert p.workspace_bytes == 32 * 64 * 128 * 4 + 32 * 64 * 4
+    # B=4 -> 16 splits of 128 pages
     p = pda.plan(_shape(batch=4, max_pages_per_seq=2048), num_cus=256)
-    assert (p.max_splits, p.pages_per_split) == (8, 256)
+    assert (p.max_splits, p.pages_per_split, p.waves_per_unit) == (16, 128, 1)
+    # B=32 (256 units fill one four-wave workgroup per CU, not two one-wave
+    # ones): four waves, no split
     p = pda.plan(_shape(batch=32, max_pages_per_seq=2048), num_cus=256)
-    assert p.max_splits == 1
+    assert (p.max_splits, p.waves_per_unit) == (1, 4)
+    # four-wave workgroups fill one per CU: B=1 -> 32 splits, B=4 -> 8
+    four = dict(variant=pda.PDA_GQA_MFMA_4WAVE)
+    p = pda.plan(_shape(batch=1, max_pages_per_seq=2048, **four), num_cus=256)
+    assert (p.max_splits, p.pages_per_split, p.workgroups, p.waves_per_unit) == (32, 64, 256, 4)
+    assert p.workspace_bytes == 32 * 32 * 128 * 4 + 32 * 32 * 4
+    p = pda.plan(_shape(batch=4, max_pages_per_seq=2048, **four), num_cus=256)
+    assert (p.max_splits, p.pages_per_split) == (8, 256)
+    assert pda.plan(_shape(**four), num_cus=256).waves_per_unit == 4
+    # one wave on request, even where the default keeps four
+    p = pda.plan(_shape(batch=32, max_pages_per_seq=2048, variant=pda.PDA_GQA_MFMA_1WAVE),
+                 num_cus=256)
+    assert (p.max_splits, p.waves_per_unit) == (2, 1)
+    # fp8 caches and d = 64 keep four waves (a lone wave's arithmetic shows)
+    assert pda.plan(_shape(kv_dtype=pda.PDA_FP8_E4M3), num_cus=256).waves_per_unit == 4
+    assert pda.plan(_shape(head_dim=64, head_dim_v=64), num_cus=256).waves_per_unit == 4
+    # an explicit split count: one wave only when the split units fill two per CU
+    p = pda.plan(_shape(batch=4, max_pages_per_seq=2048), num_splits=8, num_cus=256)
+    assert (p.max_splits, p.waves_per_unit) == (8, 4)
+    p = pda.plan(_shape(batch=4, max_pages_per_seq=2048), num_splits=16, num_cus=256)
+    assert (p.max_splits, p.waves_per_unit) == (16, 1)
     # two column tiles (MQA, 32 heads on one KV head, 8192 tokens) keep two
-    # workgroups per CU: 64 units -> 8 splits
+    # four-wave workgroups per CU: 64 units -> 8 splits
     p = pda.plan(_shape(num_kv_heads=1, max_pages_per_seq=512), num_cus=256)
-    assert (p.head_tiles, p.max_splits, p.workgroups) == (1, 8, 512)
+    assert (p.head_tiles, p.max_splits, p.workgroups, p.waves_per_unit) == (1, 8, 512, 4)
     # the VALU kernel (fp32 q) fills two workgroups per CU: B=1 -> 64 splits
     p = pda.plan(_shape(batch=1, max_pages_per_seq=2048, q_dtype=pda.PDA_F32,
                         kv_dtype=pda.PDA_F32), num_cus=256)
@@ -218,7 +241,10 @@ def test_plan_multi_token_rows():
     (dict(kv_dtype=pda.PDA_FP8_E4M3, k_scale=0.0), 1),          # fp8 needs a positive scale
     (dict(batch=-1), 1),
     (dict(q_dtype=7), 1),
-    (dict(variant=3), 1),                                       # no such GQA variant
+    (dict(variant=5), 1),                                       # no such GQA variant
+    (dict(variant=pda.PDA_GQA_MFMA_1WAVE, split_min_tokens=64), 2),   # ordered: four waves
+    (dict(variant=pda.PDA_GQA_MFMA_1WAVE, schedule=pda.PDA_SCHEDULE_BALANCED), 2),
+    (dict(q_dtype=pda.PDA_F32, kv_dtype=pda.PDA_F32, variant=pda.PDA_GQA_MFMA_1WAVE), 2),
     (dict(q_dtype=pda.PDA_F32, kv_dtype=pda.PDA_F32, variant=pda.PDA_GQA_MFMA), 2),
     (dict(q_len=-1), 1),                                        # negative query count
     (dict(q_len=2, causal=2), 1),                               # causal is 0 or 1

@@ -9,8 +9,11 @@ from decode_attention_paged_02_amd import workloads as W
 from gpu_util import check, need_gpu, oracle_ref, say
 
 pytestmark = pytest.mark.gpu
-# both GQA kernels; the matrix-core one takes f16 / bf16 queries only
-VARIANTS = {"mfma": pda.PDA_GQA_MFMA, "valu": pda.PDA_GQA_VALU}
+# both GQA kernels; the matrix-core one takes f16 / bf16 queries only.  "mfma"
+# lets the planner choose its wave layout (one wave per unit on the GRID
+# schedule with 16-bit caches and d >= 128, else four), "mfma4" keeps four
+# waves per unit everywhere.
+VARIANTS = {"mfma": pda.PDA_GQA_MFMA, "mfma4": pda.PDA_GQA_MFMA_4WAVE, "valu": pda.PDA_GQA_VALU}
 
 
 @pytest.fixture(autouse=True)
@@ -20,7 +23,7 @@ def _gpu():
 
 def _supported(variant, q_dtype):
     # the matrix-core kernel takes f16 / bf16 queries only
-    return not (variant == "mfma" and q_dtype == "f32")
+    return not (variant.startswith("mfma") and q_dtype == "f32")
 
 
 def _gqa(seed, B, Hq, Hkv, d, P, lens, q_dtype="f16", kv_dtype="f16", **kw):
@@ -411,3 +414,39 @@ def test_combine_of_many_rows_multi_token():
         out, lse = pda.run_case(case, num_splits=s)
         ref_o, ref_l = oracle_ref(case)
         check(case, out, lse, ref_o, ref_l, label="rows combine q_len=2 S=%d" % s)
+
+
+@pytest.mark.parametrize("d,dt,kv", [(128, "f16", "f16"), (128, "bf16", "bf16"), (64, "f16", "f16"),
+                                     (256, "bf16", "bf16"), (128, "f16", "e4m3"),
+                                     (128, "bf16", "e4m3"), (64, "bf16", "e4m3")])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_one_wave_variant(d, dt, kv, layout):
+    """The matrix-core kernel with one wave per work unit (PDA_GQA_MFMA_1WAVE),
+    requested explicitly for every cache type and head dim it takes: lengths
+    across page and tile boundaries, an empty sequence, no split and several
+    splits, both page layouts."""
+    lens = [0, 1, 15, 16, 17, 333, 1030, 70]
+    case = _gqa(d * 3 + len(kv) + layout, len(lens), 32, 8, d, 16, lens, dt, kv, extra_pages=3,
+                kv_layout=layout)
+    say("one wave", d, dt, kv, layout)
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case)
+    for s in (1, 4, 0):
+        sh = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                           variant=pda.PDA_GQA_MFMA_1WAVE, kv_layout=layout)
+        assert pda.plan(sh, num_splits=s).waves_per_unit == 1
+        out, lse = pda.run_case(case, dev, num_splits=s, variant=pda.PDA_GQA_MFMA_1WAVE)
+        check(case, out, lse, ref_o, ref_l, label="one wave d=%d %s/%s S=%d" % (d, dt, kv, s))
+
+
+@pytest.mark.parametrize("q_len", [2, 4])
+def test_one_wave_variant_multi_token(q_len):
+    """Several query tokens (causal) on one-wave workgroups: the (query token,
+    head) rows of a KV group fill one 16-column tile (G = 4, q_len <= 4)."""
+    case = _gqa(70 + q_len, 3, 32, 8, 128, 16, [q_len, 200, 1500], q_len=q_len, extra_pages=2)
+    say("one wave multi-token", q_len)
+    dev = pda.to_device(case)
+    ref_o, ref_l = oracle_ref(case)
+    for s in (1, 5):
+        out, lse = pda.run_case(case, dev, num_splits=s, variant=pda.PDA_GQA_MFMA_1WAVE)
+        check(case, out, lse, ref_o, ref_l, label="one wave q_len=%d S=%d" % (q_len, s))
