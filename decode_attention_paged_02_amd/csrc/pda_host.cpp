@@ -350,14 +350,10 @@ int pda_stream_probe(const void* k_cache, const void* v_cache, const int32_t* bl
   if (row_bytes != 64 && row_bytes != 128 && row_bytes != 256 && row_bytes != 512)
     return PDA_ERR_UNSUPPORTED;
   if (s.batch == 0) return PDA_OK;
-  // the split layout of the same call with the matrix-core kernel's tiling
-  // of one head tile (the probe reads each KV head's rows once)
-  pda_shape one = s;
-  one.num_q_heads = s.num_kv_heads;
-  one.variant = PDA_GQA_VALU;
-  one.q_len = 1;
+  // the split layout and wave layout the call itself would take (the probe
+  // reads each KV head's rows once per split, whatever its head tiles)
   Plan plan;
-  rc = plan_impl(&one, false, num_splits, 0, &plan);
+  rc = plan_impl(&s, false, num_splits, 0, &plan);
   if (rc != PDA_OK) return rc;
   pda::ProbeArgs a{};
   a.k_cache = k_cache;
@@ -380,7 +376,7 @@ int pda_stream_probe(const void* k_cache, const void* v_cache, const int32_t* bl
   a.split.max_splits = plan.info.max_splits;
   a.split.split_min_tokens = s.split_min_tokens;
   return pda::launch_probe(a, row_bytes, plan.info.max_splits, steps_in_flight,
-                           (hipStream_t)stream) == hipSuccess
+                           plan.info.waves_per_unit == 1 ? 1 : 4, (hipStream_t)stream) == hipSuccess
              ? PDA_OK
              : PDA_ERR_HIP;
 }

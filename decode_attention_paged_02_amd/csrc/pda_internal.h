@@ -264,6 +264,6 @@ hipError_t launch_mla(const MlaArgs& a, int variant, int kv_dtype, int head_dim,
 hipError_t launch_append(const AppendArgs& a, int src_dtype, int cache_dtype, hipStream_t stream);
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 hipError_t launch_probe(const ProbeArgs& a, int row_bytes, int max_splits, int steps_in_flight,
-                        hipStream_t stream);
+                        int waves, hipStream_t stream);
 
 }  // namespace pda

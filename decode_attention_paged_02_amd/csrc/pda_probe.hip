@@ -4,8 +4,9 @@
 // The kernel reads exactly the K and V bytes a GQA decode call reads ("From
 // MHA to MLA" sec. 5 and the drill page sec. 4: the pages of each sequence
 // through its block-table row, the valid rows of the last page only), with
-// the attention kernel's access pattern: one workgroup per (sequence, KV
-// head, split), four waves taking 16-token tiles w, w + 4, ..., a tile read
+// the attention kernels' access pattern: one workgroup per (sequence, KV
+// head, split), of four waves taking 16-token tiles w, w + 4, ... or of one
+// wave taking them all (the wave layout the call's plan picks), a tile read
 // as four 16-byte (or 8-/4-byte) row pieces per lane of K and of V with
 // non-temporal buffer loads sized to the valid rows, the wave's block-table
 // entries fetched 64 at a time and handed out with v_readlane.  Instead of
@@ -19,8 +20,6 @@
 
 namespace pda {
 namespace {
-
-constexpr int kProbeWaves = 4;
 
 template <int W>
 struct PWords {
@@ -50,9 +49,10 @@ __device__ __forceinline__ PWords<W> probe_load(__amdgpu_buffer_rsrc_t r, int of
 }
 
 // PW: words of a lane's row piece (row bytes / 64); SD: tiles in flight per
-// wave (the loads of tile i + SD - 1 are issued before tile i is folded).
-template <int PW, int SD>
-__global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(ProbeArgs a) {
+// wave (the loads of tile i + SD - 1 are issued before tile i is folded); NW:
+// waves per workgroup (4 or 1).
+template <int PW, int SD, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void stream_probe_kernel(ProbeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -61,13 +61,13 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
   const int split = blockIdx.y;
   const int log2P = a.log2_page;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_pages;
-  // The first 64 table entries of this wave (lane j: tile wave + 4 j of the
+  // The first 64 table entries of this wave (lane j: tile wave + NW j of the
   // split) are requested together with the length, as the attention kernels
   // do, before the split's range is known (entries past the sequence are
   // loaded from the table row but never used).
   const int t0_hint = a.split.max_splits > 1 ? split * a.split.pages_per_split << log2P : 0;
   auto load_entries = [&](int base) -> int {
-    const int64_t tok = (int64_t)t0_hint + (int64_t)(wave + (base + lane) * kProbeWaves) * kTileTokens;
+    const int64_t tok = (int64_t)t0_hint + (int64_t)(wave + (base + lane) * NW) * kTileTokens;
     const int64_t pg = tok >> log2P;
     return table[pg < a.max_pages ? pg : a.max_pages - 1];
   };
@@ -77,13 +77,13 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
   int nsplit, t0, t1;
   split_range(a.split, n, a.page_size, split, nsplit, t0, t1);  // (t0 == t0_hint)
   // one sink word per wave: [split][workgroup][wave]
-  uint32_t* sink = a.sink + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kProbeWaves + wave;
+  uint32_t* sink = a.sink + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * NW + wave;
   if (split >= nsplit) {
     if (lane == 0) *sink = 0;
     return;
   }
   const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
-  const int nw = ntiles > wave ? (ntiles - wave + kProbeWaves - 1) / kProbeWaves : 0;
+  const int nw = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
   const int tok_bytes = a.tok_stride * a.elem_bytes;
   // load j: token 4 j + grp for 16-bit caches (four consecutive rows per
   // load instruction), 4 grp + j for fp8 ones, as the attention kernel
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
     auto prep = [&](int i) -> TileRes {
       const bool live = i < cnt;
       const int entry = __builtin_amdgcn_readlane(vtbl, i & 63);
-      const int tk = t0 + (wave + (base + i) * kProbeWaves) * kTileTokens;
+      const int tk = t0 + (wave + (base + i) * NW) * kTileTokens;
       const int rows = live ? min(kTileTokens, t1 - tk) : 0;
       const int slot = tk & ((1 << log2P) - 1);
       const int64_t elem =
@@ -154,29 +154,34 @@ __global__ __launch_bounds__(kProbeWaves * 64, 2) void stream_probe_kernel(Probe
   if (lane == 0) *sink = acc;
 }
 
-template <int PW>
+template <int PW, int NW>
 hipError_t launch_pw(const ProbeArgs& a, int max_splits, int sd, hipStream_t s) {
   dim3 grid((unsigned)(a.batch * a.num_kv_heads), (unsigned)max_splits);
-  dim3 block(kProbeWaves * 64);
+  dim3 block(NW * 64);
   switch (sd) {
-    case 1: hipLaunchKernelGGL((stream_probe_kernel<PW, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((stream_probe_kernel<PW, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((stream_probe_kernel<PW, 3>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((stream_probe_kernel<PW, 4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((stream_probe_kernel<PW, 1, NW>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((stream_probe_kernel<PW, 2, NW>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((stream_probe_kernel<PW, 3, NW>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((stream_probe_kernel<PW, 4, NW>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int PW>
+hipError_t launch_nw(const ProbeArgs& a, int max_splits, int sd, int waves, hipStream_t s) {
+  return waves == 1 ? launch_pw<PW, 1>(a, max_splits, sd, s) : launch_pw<PW, 4>(a, max_splits, sd, s);
+}
+
 }  // namespace
 
 hipError_t launch_probe(const ProbeArgs& a, int row_bytes, int max_splits, int steps_in_flight,
-                        hipStream_t s) {
+                        int waves, hipStream_t s) {
   switch (row_bytes) {
-    case 64: return launch_pw<1>(a, max_splits, steps_in_flight, s);
-    case 128: return launch_pw<2>(a, max_splits, steps_in_flight, s);
-    case 256: return launch_pw<4>(a, max_splits, steps_in_flight, s);
-    case 512: return launch_pw<8>(a, max_splits, steps_in_flight, s);
+    case 64: return launch_nw<1>(a, max_splits, steps_in_flight, waves, s);
+    case 128: return launch_nw<2>(a, max_splits, steps_in_flight, waves, s);
+    case 256: return launch_nw<4>(a, max_splits, steps_in_flight, waves, s);
+    case 512: return launch_nw<8>(a, max_splits, steps_in_flight, waves, s);
     default: return hipErrorInvalidValue;
   }
 }

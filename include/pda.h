@@ -328,20 +328,24 @@ int pda_check_inputs(const pda_shape* shape, const int32_t* block_tables,
  * arguments (the pages of each sequence through block_tables, the valid
  * rows of the last page; "From MHA to MLA" sec. 5, the drill page sec. 4)
  * with the attention kernels' access pattern -- one workgroup per
- * (sequence, KV head, split) as the GRID schedule plans it for num_splits,
- * 16-token tiles, row pieces of up to 16 bytes per lane, non-temporal
- * loads -- but does no arithmetic: each of a workgroup's four waves folds
- * the words it loads into one 32-bit word of `sink`.  Its duration is the
- * practical ceiling for that access pattern on the device (the attention
- * kernel's time over it is the fraction of that ceiling the kernel reaches).
+ * (sequence, KV head, split) with the split count and the wave layout that
+ * pda_plan gives the same call (GRID schedule, num_splits), 16-token tiles,
+ * row pieces of up to 16 bytes per lane, non-temporal loads -- but does no
+ * arithmetic: each wave of a workgroup (four, or one when the plan's
+ * waves_per_unit is 1) folds the words it loads into one 32-bit word of
+ * `sink`.  Its duration is the practical ceiling for that access pattern on
+ * the device (the attention kernel's time over it is the fraction of that
+ * ceiling the kernel reaches).
  *   steps_in_flight: 1..4, tiles each wave keeps in flight;
  *   sink: DEVICE array of at least 4 * batch * num_kv_heads * max_splits
  *         uint32 (pda_plan_info.max_splits of the same call), contents
- *         unspecified; word ((split * batch + b) * num_kv_heads + kvh) * 4 +
- *         w is the XOR of the 32-bit words wave w of that workgroup read.
+ *         unspecified; word ((split * batch + b) * num_kv_heads + kvh) * W +
+ *         w is the XOR of the 32-bit words wave w of that workgroup read
+ *         (W: its waves, 4 or 1).
  * Needs head_dim == head_dim_v with rows of 64, 128, 256 or 512 bytes and the
- * GRID schedule; other shape fields as for paged_decode_attn (q_dtype and
- * q_len are ignored).  Asynchronous on `stream`; returns a pda_status. */
+ * GRID schedule; other shape fields as for paged_decode_attn (they select
+ * the plan as they would for the call).  Asynchronous on `stream`; returns a
+ * pda_status. */
 int pda_stream_probe(const void* k_cache, const void* v_cache, const int32_t* block_tables,
                      const int32_t* context_lens, const pda_shape* shape, int num_splits,
                      int steps_in_flight, uint32_t* sink, void* stream);

@@ -161,14 +161,16 @@ def test_append_head_major_bit_exact(src, cache):
 
 
 @pytest.mark.parametrize("layout", [0, 1])
-@pytest.mark.parametrize("kv_dtype,num_splits,thr", [("f16", 1, 0), ("f16", 3, 0),
-                                                      ("e4m3", 4, 100), ("bf16", 0, 0)])
-def test_stream_probe_reads_exactly_the_call_bytes(layout, kv_dtype, num_splits, thr):
+@pytest.mark.parametrize("kv_dtype,num_splits,thr,variant", [
+    ("f16", 1, 0, 0), ("f16", 3, 0, 0), ("e4m3", 4, 100, 0), ("bf16", 0, 0, 0),
+    ("f16", 1, 0, pda.PDA_GQA_MFMA_1WAVE), ("f16", 3, 0, pda.PDA_GQA_MFMA_1WAVE)])
+def test_stream_probe_reads_exactly_the_call_bytes(layout, kv_dtype, num_splits, thr, variant):
     """The streaming probe reads the bytes the attention call reads: each
-    workgroup's sink words (one per wave) XOR to the 32-bit words of its K and V
-    rows (its sequence, KV head and split range), computed on the host from
-    the stored cache.  Rows past the context are NaN-poisoned, so a probe that
-    read them would fold different words."""
+    workgroup's sink words (one per wave: four, or one with the one-wave
+    layout) XOR to the 32-bit words of its K and V rows (its sequence, KV head
+    and split range), computed on the host from the stored cache.  Rows past
+    the context are NaN-poisoned, so a probe that read them would fold
+    different words."""
     import numpy as np
     q_dt = "f16" if kv_dtype != "bf16" else "bf16"
     case = W.make_gqa(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
@@ -178,15 +180,17 @@ def test_stream_probe_reads_exactly_the_call_bytes(layout, kv_dtype, num_splits,
     dev = pda.to_device(case)
     shape = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
                           split_min_tokens=thr, kv_layout=layout, k_scale=case.k_scale,
-                          v_scale=case.v_scale)
+                          v_scale=case.v_scale, variant=variant)
     info = pda.plan(shape, num_splits=num_splits)
+    nw = info.waves_per_unit
+    assert nw in (1, 4) and (nw == 1) == (variant == pda.PDA_GQA_MFMA_1WAVE or num_splits == 0)
     probe = pda.StreamProbe(shape, [(dev.k_cache, dev.v_cache)], dev.block_tables,
                             dev.context_lens, num_splits=num_splits, steps_in_flight=2)
     probe()
     torch.cuda.synchronize()
-    # one word per wave: the workgroup's XOR is the XOR of its four waves' words
-    got = np.bitwise_xor.reduce(
-        probe._sink.cpu().numpy().view(np.uint32).reshape(info.max_splits, 3, 2, 4), axis=3)
+    # one word per wave: the workgroup's XOR is the XOR of its waves' words
+    words = probe._sink.cpu().numpy().view(np.uint32)[:info.max_splits * 3 * 2 * nw]
+    got = np.bitwise_xor.reduce(words.reshape(info.max_splits, 3, 2, nw), axis=3)
     kc, vc = np.ascontiguousarray(case.k_cache), np.ascontiguousarray(case.v_cache)
     P = case.page_size
     for b in range(3):
