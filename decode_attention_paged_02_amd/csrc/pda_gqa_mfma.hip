@@ -3,9 +3,14 @@
 //
 // Same contract as gqa_split_kernel (pda_gqa.hip): a workgroup owns a tile of
 // up to 16 query heads of one KV group of one sequence (one split of its
-// pages), four waves walk 16-token tiles (wave w takes tiles w, w+4, ...),
-// keep an online softmax each, and merge through LDS at the end.  What
-// changes is the arithmetic of a tile:
+// pages).  Either four waves walk its 16-token tiles (wave w takes tiles w,
+// w+4, ...), keep an online softmax each and merge through LDS at the end, or
+// (NW = 1, grid calls with one column tile) one wave walks them all with two
+// steps in flight and writes its result from registers.  A lone wave per
+// unit keeps fewer bytes in flight per compute unit and has no merge; on
+// MI355X it streams the B=64 / 1024-token fp16 cache in 40.6-41.1 us against
+// 42.0-42.5 with four waves (token-major pages 40.7-41.4 against 43.9-44.3).
+// What changes against the vector kernel is the arithmetic of a tile:
 //
 //  - scores as S^T = K Q^T with the tile's 16 tokens on the MFMA M dimension
 //    and the 16 heads on N (v_mfma_f32_16x16x32, D/32 of them).  The result
@@ -424,11 +429,21 @@ __global__ __launch_bounds__(NW * 64, 2) void gqa_mfma_kernel(
         pb_lo[c] = u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16),
                          (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
       }
-      // unconditional: alpha is exactly 1 while the reference max stays, and
-      // a branch around the multiplies makes the compiler copy both column
-      // tiles' accumulators on every tile (0.4 us of the MQA step)
+      // alpha is exactly 1 while the reference max stays.  One-wave
+      // workgroups skip the multiplies unless a lane's max moved (a wave-
+      // uniform branch; B=64 bfloat16 41.5 against 42.3 us, float16 0.1-0.2 us
+      // faster).  Four-wave ones multiply unconditionally: there a branch
+      // made the compiler copy both column tiles' accumulators on every tile
+      // (0.4 us of the MQA step).
+      if constexpr (NW == 1) {
+        if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
-      for (int e = 0; e < NE; ++e) acc[c][e] *= alpha;
+          for (int e = 0; e < NE; ++e) acc[c][e] *= alpha;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[c][e] *= alpha;
+      }
     }
     // ---- O^T += V^T P^T.  A operand of MFMA e: V^T row col (value element
     // col NE + e) at k = 4 grp + i (the token of load i) = element e of the
