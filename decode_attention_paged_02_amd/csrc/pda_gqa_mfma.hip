@@ -5,7 +5,7 @@
 // up to 16 query heads of one KV group of one sequence (one split of its
 // pages).  Either four waves walk its 16-token tiles (wave w takes tiles w,
 // w+4, ...), keep an online softmax each and merge through LDS at the end, or
-// (NW = 1, grid calls with one column tile) one wave walks them all with two
+// (NW = 1, grid calls) one wave walks them all with two
 // steps in flight and writes its result from registers.  A lone wave per
 // unit keeps fewer bytes in flight per compute unit and has no merge; on
 // MI355X it streams the B=64 / 1024-token fp16 cache in 40.6-41.1 us against
@@ -660,8 +660,8 @@ __global__ __launch_bounds__(NW * 64, 2) void gqa_mfma_kernel(
 
 // grid calls with kGqaStepsInFlight steps in flight (kGqaStepsInFlightFp8 for
 // fp8 caches), ordered ones with kGqaStepsInFlightOrdered; ST tiles per step.
-// Workgroups of four waves, or of one (a.waves == 1: grid calls with one
-// column tile) with kGqaStepsInFlightWave steps in flight.
+// Workgroups of four waves, or of one (a.waves == 1: grid calls) with
+// kGqaStepsInFlightWave steps in flight.
 template <class QT, class KT, int D, int CT, int ST>
 void launch_sd(const GqaArgs& a, dim3 grid, hipStream_t s) {
   constexpr int kGridSD = std::is_same<KT, E4M3>::value ? kGqaStepsInFlightFp8 : kGqaStepsInFlight;
@@ -672,8 +672,8 @@ void launch_sd(const GqaArgs& a, dim3 grid, hipStream_t s) {
   if (ordered)
     hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlightOrdered, ST, kMWaves>),
                        grid, dim3(kMWaves * 64), 0, s, PDA_MFMA_ARGS);
-  else if (CT == 1 && a.waves == 1)
-    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, 1, kGqaStepsInFlightWave, ST, 1>), grid,
+  else if (a.waves == 1)
+    hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGqaStepsInFlightWave, ST, 1>), grid,
                        dim3(64), 0, s, PDA_MFMA_ARGS);
   else
     hipLaunchKernelGGL((gqa_mfma_kernel<QT, KT, D, CT, kGridSD, ST, kMWaves>), grid,

@@ -114,11 +114,16 @@ constexpr int kOneWaveUnitsPerCu = 2;
 // with four-wave workgroups but not with two one-wave ones per unit of work
 // (B=32 at 4096 tokens: one wave would split, 83.7 against 80.0).  With an
 // explicit split count (num_splits > 0) one wave needs two units per compute
-// unit after splitting (B=1 with 32 splits: 39.5 against 27.1).
-bool one_wave_default(const pda_shape* s, int64_t units, int num_splits, int num_cus) {
+// unit after splitting (B=1 with 32 splits: 39.5 against 27.1).  Several
+// head tiles per KV group count as units (B=64, G=8, three query tokens at
+// 1024 tokens, two 16-row tiles: 48.1 against 67.3 us).  Two column tiles
+// (32 rows per unit) double a wave's arithmetic per tile and keep four waves
+// (MQA, B=64, 32 heads, 8192 tokens, 8 splits: 53.2 against 51.0 us).
+bool one_wave_default(const pda_shape* s, int64_t units, int col_tiles, int num_splits,
+                      int num_cus) {
   const bool wide16 = (s->kv_dtype == PDA_F16 || s->kv_dtype == PDA_BF16) && s->head_dim >= 128;
   const int64_t fill = (int64_t)kOneWaveUnitsPerCu * num_cus;
-  if (!wide16) return false;
+  if (!wide16 || col_tiles > 1) return false;
   if (num_splits > 0) return units * std::min(num_splits, s->max_pages_per_seq) >= fill;
   return units >= fill || units < num_cus;
 }
@@ -171,10 +176,10 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
   const bool balanced = s->schedule == PDA_SCHEDULE_BALANCED;
   // Eight waves per compute unit (two four-wave workgroups, or one of eight)
   const int wg_per_cu = mla_groups == 2 ? 1 : 2;
-  // The matrix-core GQA kernel with one column tile can give each work unit
-  // to one wave (workgroups of one wave, no merge) on the GRID schedule
-  // without a threshold (no ordered work).
-  const bool one_wave_ok = mfma_gqa && col_tiles == 1 && !balanced && s->split_min_tokens == 0;
+  // The matrix-core GQA kernel can give each work unit to one wave
+  // (workgroups of one wave, no merge) on the GRID schedule without a
+  // threshold (no ordered work).
+  const bool one_wave_ok = mfma_gqa && !balanced && s->split_min_tokens == 0;
   if (s->variant == PDA_GQA_MFMA_1WAVE && !mla && !one_wave_ok) return PDA_ERR_UNSUPPORTED;
   // (the default choice needs the compute units; with an explicit split
   // count and no device to ask, the call keeps four waves)
@@ -186,7 +191,7 @@ int plan_impl(const pda_shape* s, bool mla, int num_splits, int num_cus, Plan* p
       !mla && one_wave_ok &&
       (s->variant == PDA_GQA_MFMA_1WAVE ||
        (s->variant != PDA_GQA_MFMA_4WAVE && wave_cus > 0 &&
-        one_wave_default(s, units, num_splits, wave_cus)));
+        one_wave_default(s, units, col_tiles, num_splits, wave_cus)));
 
   if ((num_splits == 0 || balanced) && num_cus == 0) {
     num_cus = device_cus();

@@ -153,9 +153,8 @@ typedef struct pda_shape {
 #define PDA_GQA_VALU 2    /* vector dot products                            */
 #define PDA_GQA_MFMA_4WAVE 3 /* matrix cores, four waves per work unit        */
 #define PDA_GQA_MFMA_1WAVE 4 /* matrix cores, one wave per work unit (GRID    */
-                             /* schedule without a split threshold, at most  */
-                             /* 16 (query token, head) rows per KV group or  */
-                             /* head_dim 256; else PDA_ERR_UNSUPPORTED)      */
+                             /* schedule without a split threshold; else     */
+                             /* PDA_ERR_UNSUPPORTED)                         */
 
 /* MLA kernel variants (pda_shape.variant for paged_decode_attn_mla). */
 #define PDA_MLA_DEFAULT 0 /* the fastest available                          */
@@ -190,7 +189,16 @@ typedef struct pda_plan_info {
  * sec. 6 shows the cost of not splitting at batch 1.  This planner splits
  * until the grid fills one workgroup per compute unit for the matrix-core
  * GQA kernel with 16-row tiles, and two for its 32-row tiles, the vector
- * kernel and MLA (one of MLA's 512-thread workgroups).
+ * kernel and MLA (one of MLA's 512-thread workgroups).  The matrix-core GQA
+ * kernel gives each work unit to one wave instead of four (waves_per_unit
+ * 1, two units per compute unit) for GRID calls without a threshold on
+ * 16-bit caches with head_dim >= 128 and 16-row tiles when the units fill
+ * two per compute unit unsplit, or less than one (then split to two per
+ * compute unit); with an explicit num_splits, when the split units fill two
+ * per compute unit.  PDA_GQA_MFMA_1WAVE and
+ * PDA_GQA_MFMA_4WAVE fix the choice.  That choice needs the compute units:
+ * with an explicit num_splits and num_cus = 0 the device is asked, and when
+ * it cannot answer the call keeps four waves.
  * num_splits: 0 = automatic (fill the GPU's compute units), otherwise the
  * largest number of splits any sequence may use (at most 64 with the BALANCED
  * schedule).  num_cus: compute units to plan for; 0 = query the current HIP

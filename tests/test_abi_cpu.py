@@ -78,6 +78,17 @@ def test_plan_fills_compute_units():
     # four-wave workgroups per CU: 64 units -> 8 splits
     p = pda.plan(_shape(num_kv_heads=1, max_pages_per_seq=512), num_cus=256)
     assert (p.head_tiles, p.max_splits, p.workgroups, p.waves_per_unit) == (1, 8, 512, 4)
+    # ... or one wave per unit on request (the same 8 splits fill two per CU)
+    p = pda.plan(_shape(num_kv_heads=1, max_pages_per_seq=512,
+                        variant=pda.PDA_GQA_MFMA_1WAVE), num_cus=256)
+    assert (p.head_tiles, p.max_splits, p.workgroups, p.waves_per_unit) == (1, 8, 512, 1)
+    # B=64, G=8, three query tokens (24 rows per KV group) at 1024 tokens:
+    # two 16-row head tiles, 1024 units -> one wave; at 2048 tokens one
+    # 32-row tile (two column tiles) -> four waves
+    p = pda.plan(_shape(num_q_heads=64, q_len=3), num_cus=256)
+    assert (p.head_tiles, p.max_splits, p.workgroups, p.waves_per_unit) == (2, 1, 1024, 1)
+    p = pda.plan(_shape(num_q_heads=64, q_len=3, max_pages_per_seq=128), num_cus=256)
+    assert (p.head_tiles, p.max_splits, p.workgroups, p.waves_per_unit) == (1, 1, 512, 4)
     # the VALU kernel (fp32 q) fills two workgroups per CU: B=1 -> 64 splits
     p = pda.plan(_shape(batch=1, max_pages_per_seq=2048, q_dtype=pda.PDA_F32,
                         kv_dtype=pda.PDA_F32), num_cus=256)

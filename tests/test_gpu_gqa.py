@@ -439,14 +439,19 @@ def test_one_wave_variant(d, dt, kv, layout):
         check(case, out, lse, ref_o, ref_l, label="one wave d=%d %s/%s S=%d" % (d, dt, kv, s))
 
 
-@pytest.mark.parametrize("q_len", [2, 4])
-def test_one_wave_variant_multi_token(q_len):
-    """Several query tokens (causal) on one-wave workgroups: the (query token,
-    head) rows of a KV group fill one 16-column tile (G = 4, q_len <= 4)."""
-    case = _gqa(70 + q_len, 3, 32, 8, 128, 16, [q_len, 200, 1500], q_len=q_len, extra_pages=2)
-    say("one wave multi-token", q_len)
+@pytest.mark.parametrize("Hq,Hkv,q_len", [(32, 8, 2), (32, 8, 4), (64, 8, 3), (32, 1, 1),
+                                         (24, 1, 1)])
+def test_one_wave_variant_multi_token(Hq, Hkv, q_len):
+    """Several query tokens (causal) and large groups on one-wave workgroups:
+    the (query token, head) rows of a KV group fill one 16-column tile (G = 4,
+    q_len <= 4) or two (G = 8 with three tokens, MQA with 32 and 24 heads:
+    32-row units, the last with 8 padded columns)."""
+    case = _gqa(70 + q_len + Hq + Hkv, 3, Hq, Hkv, 128, 16, [q_len, 200, 2500], q_len=q_len,
+                extra_pages=2)
+    say("one wave multi-token", Hq, Hkv, q_len)
     dev = pda.to_device(case)
     ref_o, ref_l = oracle_ref(case)
     for s in (1, 5):
         out, lse = pda.run_case(case, dev, num_splits=s, variant=pda.PDA_GQA_MFMA_1WAVE)
-        check(case, out, lse, ref_o, ref_l, label="one wave q_len=%d S=%d" % (q_len, s))
+        check(case, out, lse, ref_o, ref_l, label="one wave Hq=%d Hkv=%d q_len=%d S=%d"
+              % (Hq, Hkv, q_len, s))
