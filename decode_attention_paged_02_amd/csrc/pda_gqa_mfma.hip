@@ -200,7 +200,13 @@ __global__ __launch_bounds__(NW * 64, 2) void gqa_mfma_kernel(
   const int grp = lane >> 4;  // lane group
 
   // which (sequence, KV head, head tile, split) this workgroup computes
-  // (one-wave workgroups serve grid calls only)
+  // One-wave workgroups serve grid calls only: their grid is (units, splits).
+  // An ordered launch (x = KV heads x head tiles x listed units) would map
+  // workgroups past the batch, so such a launch leaves at once (launch_sd
+  // never makes one).
+  if constexpr (NW == 1) {
+    if (units != nullptr || a.plan_in_kernel) return;
+  }
   const bool ordered = NW > 1 && (units != nullptr || a.plan_in_kernel);
   int tile, kvh, b, split, ut0 = 0, ut1 = 0;
   if (ordered) {
