@@ -1,6 +1,7 @@
 // pda_host.cpp -- the C ABI of libpda (include/pda.h): argument validation,
 // the split planner and kernel dispatch.  Every host-checkable argument is
-// validated before the first HIP call, so invalid calls never touch a device.
+// validated before any work is queued, so invalid calls never touch a device
+// (the planner may only ask the runtime for the device's compute units).
 #include "pda.h"
 
 #include <hip/hip_runtime.h>

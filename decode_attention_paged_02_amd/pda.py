@@ -247,7 +247,11 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, scale:
 
     q [B, Hq, d] returns (out [B, Hq, dv], lse [B, Hq] fp32); q [B, s_q, Hq, d]
     (s_q query tokens per sequence, the last s_q positions; causal: bottom-right
-    mask) returns (out [B, s_q, Hq, dv], lse [B, Hq, s_q] fp32)."""
+    mask) returns (out [B, s_q, Hq, dv], lse [B, Hq, s_q] fp32).
+
+    variant: PDA_GQA_DEFAULT / PDA_GQA_MFMA (the planner picks one or four
+    waves per work unit of the matrix-core kernel), PDA_GQA_MFMA_4WAVE,
+    PDA_GQA_MFMA_1WAVE (grid schedule without a threshold) or PDA_GQA_VALU."""
     shape = gqa_shape(q, k_cache, v_cache, block_tables, k_scale=k_scale, v_scale=v_scale,
                       split_min_tokens=split_min_tokens, variant=variant, causal=causal,
                       schedule=schedule, kv_layout=kv_layout)
