@@ -435,13 +435,14 @@ __global__ __launch_bounds__(NW * 64, 2) void gqa_mfma_kernel(
         pb_lo[c] = u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16),
                          (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
       }
-      // alpha is exactly 1 while the reference max stays.  One-wave
-      // workgroups skip the multiplies unless a lane's max moved (a wave-
-      // uniform branch; B=64 bfloat16 41.5 against 42.3 us, float16 0.1-0.2 us
-      // faster).  Four-wave ones multiply unconditionally: there a branch
-      // made the compiler copy both column tiles' accumulators on every tile
-      // (0.4 us of the MQA step).
-      if constexpr (NW == 1) {
+      // alpha is exactly 1 while the reference max stays.  With one column
+      // tile the multiplies are skipped unless a lane's max moved (a wave-
+      // uniform branch; one wave, B=64: bfloat16 41.5 against 42.3 us,
+      // float16 0.1-0.2 us faster; four waves: the ragged fp8 batch 0.2-1.2
+      // us faster, fp8 B=64 at 2048 tokens 0.2-0.4).  Two column tiles
+      // multiply unconditionally: there a branch made the compiler copy both
+      // tiles' accumulators on every tile (0.4 us of the MQA step).
+      if constexpr (NW == 1 || CT == 1) {
         if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
           for (int e = 0; e < NE; ++e) acc[c][e] *= alpha;
