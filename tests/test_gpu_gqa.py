@@ -437,6 +437,11 @@ def test_one_wave_variant(d, dt, kv, layout):
         assert pda.plan(sh, num_splits=s).waves_per_unit == 1
         out, lse = pda.run_case(case, dev, num_splits=s, variant=pda.PDA_GQA_MFMA_1WAVE)
         check(case, out, lse, ref_o, ref_l, label="one wave d=%d %s/%s S=%d" % (d, dt, kv, s))
+        out2, lse2 = pda.run_case(case, dev, num_splits=s, variant=pda.PDA_GQA_MFMA_1WAVE)
+        assert torch.equal(out, out2) and torch.equal(lse, lse2), "run-to-run differs"
+        # against the four-wave layout: the same rows, another summation order
+        out4, _ = pda.run_case(case, dev, num_splits=s, variant=pda.PDA_GQA_MFMA_4WAVE)
+        assert (out4.float() - out.float()).abs().max().item() < 2e-3
 
 
 @pytest.mark.parametrize("Hq,Hkv,q_len", [(32, 8, 2), (32, 8, 4), (64, 8, 3), (32, 1, 1),
