@@ -175,9 +175,10 @@ typedef struct pda_plan_info {
   int32_t num_cus;         /* compute units the plan was made for           */
   int32_t ordered;         /* 1: the call orders its work longest first     */
   uint64_t workspace_bytes; /* bytes the call needs in `workspace`          */
-  int32_t waves_per_unit;  /* waves of the main kernel that share one work  */
-                           /* unit (4, or 1 for the matrix-core GQA kernel  */
-                           /* when each wave takes a unit of its own)       */
+  int32_t waves_per_unit;  /* waves of a main-kernel workgroup, which share */
+                           /* one work unit: 1 (the matrix-core GQA kernel  */
+                           /* with a unit per wave), 4, or 8 (MLA with two  */
+                           /* column groups)                                */
   int32_t reserved;
 } pda_plan_info;
 
