@@ -460,3 +460,26 @@ def test_one_wave_variant_multi_token(Hq, Hkv, q_len):
         out, lse = pda.run_case(case, dev, num_splits=s, variant=pda.PDA_GQA_MFMA_1WAVE)
         check(case, out, lse, ref_o, ref_l, label="one wave Hq=%d Hkv=%d q_len=%d S=%d"
               % (Hq, Hkv, q_len, s))
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,lens", [(24, 1, 128, [700, 5, 1200]), (48, 2, 256, [300, 999, 64]),
+                                          (40, 1, 128, [3000, 1, 2100])])
+def test_one_wave_several_head_tiles(Hq, Hkv, d, lens):
+    """One-wave units of groups that take several workgroups per KV group:
+    16-row head tiles (G = 24 with a short table, G = 24 at d = 256) and
+    32-row ones (G = 40 with a long table: two column tiles, two head
+    tiles), with and without splits, against the oracle and the four-wave
+    layout."""
+    case = _gqa(Hq + d + len(lens), len(lens), Hq, Hkv, d, 16, lens, extra_pages=1)
+    say("one wave head tiles", Hq, Hkv, d, lens)
+    dev = pda.to_device(case)
+    sh = pda.gqa_shape(dev.q, dev.k_cache, dev.v_cache, dev.block_tables,
+                       variant=pda.PDA_GQA_MFMA_1WAVE)
+    assert pda.plan(sh, num_splits=1).head_tiles >= 2
+    ref_o, ref_l = oracle_ref(case)
+    for s in (1, 3):
+        out, lse = pda.run_case(case, dev, num_splits=s, variant=pda.PDA_GQA_MFMA_1WAVE)
+        check(case, out, lse, ref_o, ref_l, label="one wave Hq=%d Hkv=%d d=%d S=%d"
+              % (Hq, Hkv, d, s))
+        out4, _ = pda.run_case(case, dev, num_splits=s, variant=pda.PDA_GQA_MFMA_4WAVE)
+        assert (out4.float() - out.float()).abs().max().item() < 2e-3
