@@ -126,7 +126,7 @@ def test_head_major_equals_token_major_bitwise():
     t = W.make_gqa(kv_layout=0, **kw)
     h = W.make_gqa(kv_layout=HEAD_MAJOR, **kw)
     say("layouts bitwise")
-    for v in (pda.PDA_GQA_MFMA, pda.PDA_GQA_VALU):
+    for v in (pda.PDA_GQA_MFMA, pda.PDA_GQA_MFMA_1WAVE, pda.PDA_GQA_VALU):
         ot, lt = pda.run_case(t, num_splits=2, variant=v)
         oh, lh = pda.run_case(h, num_splits=2, variant=v)
         assert torch.equal(ot.view(torch.int16), oh.view(torch.int16))
