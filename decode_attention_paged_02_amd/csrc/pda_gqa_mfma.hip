@@ -535,10 +535,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gqa_mfma_kernel(
     if (sbase < ns_wave) vtbl = load_table(sbase);
   }
 
-  // ---- merge the four waves (the split-combine algebra) through LDS, one
-  // column tile after the other through the same 16-row area.  When the
-  // merge area overlays the K tiles, every wave must be done with them; a
-  // second column tile waits for the readers of the first.
+  // ---- epilogue
   if constexpr (NW == 1) {
     // One wave owns the unit: nothing to merge.  Lane (col, grp) holds, for
     // column tile c, values (4 grp + i) NE .. + NE of row 16 c + col (i = 0..3),
@@ -581,6 +578,10 @@ __global__ __launch_bounds__(NW * 64, 2) void gqa_mfma_kernel(
     }
     return;
   }
+  // ---- merge the four waves (the split-combine algebra) through LDS, one
+  // column tile after the other through the same 16-row area.  When the
+  // merge area overlays the K tiles, every wave must be done with them; a
+  // second column tile waits for the readers of the first.
   float* acc_sh = (float*)(lds + kMergeOff);  // [wave][head][kAccStride]
   constexpr int kQ = D / 4;                   // four-value items per row
 #pragma unroll
